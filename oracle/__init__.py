@@ -1,0 +1,224 @@
+"""fp64 CPU oracle for grouped-query softmax attention forward -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls it, and this package uses
+nothing from the product path: inputs arrive as plain 16-bit bit patterns and
+integer arrays, results leave as float64 numpy arrays.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, fp64, fixed summation
+order); this module only compiles it with gcc and marshals arguments.  See the
+header of ``attn_oracle.c`` for the definition it follows and its sources on
+the pages (TileOPs "Attention Operators" GQADenseFwdOp stages 1, 4, 5 and 7 and
+MHADecodePagedWithKVCacheFwdOp; RL-Kernel "Standard Softmax Attention";
+MATE "QSA" Core Attention for the natural-log LSE and empty rows).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+BF16 = 0
+FP16 = 1
+
+# -ffp-contract=off and no fast-math keep every sum in the written order.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build() -> str:
+    """Compile the oracle with gcc into oracle/liboracle.so (always rebuilds)."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        lib.oracle_decode.argtypes = [ctypes.c_uint16, i32]
+        lib.oracle_decode.restype = ctypes.c_double
+        lib.oracle_resolve_scale.argtypes = [f32, i32]
+        lib.oracle_resolve_scale.restype = ctypes.c_double
+        lib.oracle_attn_dense.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                          P, P, P]
+        lib.oracle_attn_dense_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
+                                               i32, P, P, i64, P, P]
+        lib.oracle_attn_paged.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32,
+                                          f32, i32, P, P]
+        lib.oracle_attn_paged_rows.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                               i32, f32, i32, P, i64, P, P]
+        for name in ("oracle_attn_dense", "oracle_attn_dense_rows", "oracle_attn_paged",
+                     "oracle_attn_paged_rows", "oracle_num_threads"):
+            getattr(lib, name).restype = i32
+        _lib = lib
+    return _lib
+
+
+def _bits(x) -> np.ndarray:
+    """16-bit bit patterns of a bf16/fp16 torch tensor (CPU copy) or uint16 array."""
+    if isinstance(x, np.ndarray):
+        assert x.dtype == np.uint16
+        return np.ascontiguousarray(x)
+    import torch
+    assert x.dtype in (torch.bfloat16, torch.float16), x.dtype
+    return np.ascontiguousarray(x.detach().cpu().contiguous().view(torch.int16).numpy()
+                                .view(np.uint16))
+
+
+def _dtype_code(x) -> int:
+    if isinstance(x, np.ndarray):
+        raise TypeError("pass dtype explicitly for raw bit arrays")
+    import torch
+    return BF16 if x.dtype == torch.bfloat16 else FP16
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _scale_arg(scale) -> float:
+    return float("nan") if scale is None else float(scale)
+
+
+def decode(bits: int, dtype: int) -> float:
+    """Exact value of one 16-bit pattern (BF16 or FP16 code)."""
+    return _load().oracle_decode(bits, dtype)
+
+
+def resolve_scale(scale, D: int) -> float:
+    """alpha as the oracle applies it: None -> float(1/sqrt(D)), else verbatim."""
+    return _load().oracle_resolve_scale(_scale_arg(scale), D)
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def _as_mask(mask, B, Skv):
+    if mask is None:
+        return None
+    import torch
+    if isinstance(mask, torch.Tensor):
+        mask = mask.detach().cpu().numpy()
+    m = np.ascontiguousarray(np.asarray(mask).astype(np.uint8))
+    assert m.shape == (B, Skv), m.shape
+    return m
+
+
+def attn_dense(q, k, v, *, scale=None, causal=True, key_padding_mask=None, dtype=None):
+    """o [B,Sq,Hq,D] float64, lse [B,Hq,Sq] float64 for a dense call.
+
+    q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D]: bf16/fp16 torch tensors (or uint16 bit
+    arrays with ``dtype`` given)."""
+    dt = _dtype_code(q) if dtype is None else dtype
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    B, Sq, Hq, D = qb.shape
+    _, Skv, Hkv, _ = kb.shape
+    m = _as_mask(key_padding_mask, B, Skv)
+    o = np.zeros((B, Sq, Hq, D), np.float64)
+    lse = np.zeros((B, Hq, Sq), np.float64)
+    rc = _load().oracle_attn_dense(_ptr(qb), _ptr(kb), _ptr(vb), dt, B, Hq, Hkv, Sq, Skv, D,
+                                   _scale_arg(scale), int(bool(causal)),
+                                   None if m is None else _ptr(m), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_dense rejected the call (rc={rc})")
+    return o, lse
+
+
+def _sel_array(rows) -> np.ndarray:
+    sel = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
+    return sel
+
+
+def attn_dense_rows(q, k, v, rows, *, scale=None, causal=True, key_padding_mask=None,
+                    dtype=None):
+    """Selected rows (b, i, h) of a dense call: o [n, D], lse [n]."""
+    dt = _dtype_code(q) if dtype is None else dtype
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    B, Sq, Hq, D = qb.shape
+    _, Skv, Hkv, _ = kb.shape
+    m = _as_mask(key_padding_mask, B, Skv)
+    sel = _sel_array(rows)
+    n = sel.shape[0]
+    o = np.zeros((n, D), np.float64)
+    lse = np.zeros((n,), np.float64)
+    rc = _load().oracle_attn_dense_rows(_ptr(qb), _ptr(kb), _ptr(vb), dt, B, Hq, Hkv, Sq, Skv,
+                                        D, _scale_arg(scale), int(bool(causal)),
+                                        None if m is None else _ptr(m), _ptr(sel), n, _ptr(o),
+                                        _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_dense_rows rejected the call (rc={rc})")
+    return o, lse
+
+
+def _paged_args(q, k_cache, v_cache, real_seqlen_kv, block_table):
+    qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
+    B, Sq, Hq, D = qb.shape
+    Hkv = kb.shape[-2]
+    import torch
+    lens = real_seqlen_kv.detach().cpu().numpy() if isinstance(real_seqlen_kv, torch.Tensor) \
+        else np.asarray(real_seqlen_kv)
+    bt = block_table.detach().cpu().numpy() if isinstance(block_table, torch.Tensor) \
+        else np.asarray(block_table)
+    lens = np.ascontiguousarray(lens.astype(np.int32))
+    bt = np.ascontiguousarray(bt.astype(np.int32))
+    assert lens.shape == (B,) and bt.ndim == 2 and bt.shape[0] == B
+    return qb, kb, vb, lens, bt, B, Sq, Hq, Hkv, D
+
+
+def attn_paged(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, *, causal=True,
+               scale=None, dtype=None):
+    """o [B,Sq,Hq,D], lse [B,Hq,Sq] (float64) for a paged call.
+
+    k_cache/v_cache: [pages*page_size, Hkv, D] or [pages, page_size, Hkv, D]."""
+    dt = _dtype_code(q) if dtype is None else dtype
+    qb, kb, vb, lens, bt, B, Sq, Hq, Hkv, D = _paged_args(q, k_cache, v_cache, real_seqlen_kv,
+                                                          block_table)
+    o = np.zeros((B, Sq, Hq, D), np.float64)
+    lse = np.zeros((B, Hq, Sq), np.float64)
+    rc = _load().oracle_attn_paged(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(lens), _ptr(bt),
+                                   int(page_size), int(bool(causal)), B, Sq, Hq, Hkv, D,
+                                   bt.shape[1], _scale_arg(scale), dt, _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_paged rejected the call (rc={rc})")
+    return o, lse
+
+
+def attn_paged_rows(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, rows, *,
+                    causal=True, scale=None, dtype=None):
+    """Selected rows (b, i, h) of a paged call: o [n, D], lse [n]."""
+    dt = _dtype_code(q) if dtype is None else dtype
+    qb, kb, vb, lens, bt, B, Sq, Hq, Hkv, D = _paged_args(q, k_cache, v_cache, real_seqlen_kv,
+                                                          block_table)
+    sel = _sel_array(rows)
+    n = sel.shape[0]
+    o = np.zeros((n, D), np.float64)
+    lse = np.zeros((n,), np.float64)
+    rc = _load().oracle_attn_paged_rows(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(lens), _ptr(bt),
+                                        int(page_size), int(bool(causal)), B, Sq, Hq, Hkv, D,
+                                        bt.shape[1], _scale_arg(scale), dt, _ptr(sel), n,
+                                        _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_paged_rows rejected the call (rc={rc})")
+    return o, lse
+
+
+__all__ = ["BF16", "FP16", "build", "decode", "resolve_scale", "num_threads", "attn_dense",
+           "attn_dense_rows", "attn_paged", "attn_paged_rows"]

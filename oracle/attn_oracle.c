@@ -1,0 +1,399 @@
+/*
+ * attn_oracle.c -- TEST INFRASTRUCTURE ONLY (not part of the product path).
+ *
+ * A plain, slow, fp64 CPU evaluation of grouped-query softmax attention
+ * forward, written from its definition.  Only the tests, the smoke check and
+ * the benchmark's CPU-baseline leg load this library; the HIP library never
+ * links, includes or calls it, and this file includes nothing from it.
+ *
+ * What is computed, and where the pages define it:
+ *   - TileOPs "Attention Operators", GQADenseFwdOp: stage 1 (query position
+ *     p_i = i + S_kv - S_q), stage 4 (scores Z = alpha <Q, K_r(h)>), stage 5
+ *     (visibility: not causal, or j <= p_i), stage 7 (softmax over the KV
+ *     axis, then the value reduction); the head map r(h) = floor(h / g) with
+ *     g = H / H_kv; BSHD layout with D contiguous.
+ *   - TileOPs "Attention Operators", MHADecodePagedWithKVCacheFwdOp: physical
+ *     cache [rows, H_kv, D], real_seqlen_kv[B] (the cache length, its query
+ *     tokens included), block_table[B, num_pages]; query i sees keys up to
+ *     i + real_seqlen_kv - S_q; a query that sees no key outputs zeros.
+ *   - TileOPs "Attention Operators", PagedKVCacheWriteFwdOp: a flattened cache
+ *     row is page * page_size + offset.
+ *   - RL-Kernel "Standard Softmax Attention", Tensor Contract: scale None means
+ *     1/sqrt(D), an explicit value (0.0 included) is used verbatim;
+ *     key_padding_mask [B, S_kv], True = keep, False sets the column to -inf.
+ *   - MATE "QSA", Core Attention: the log-sum-exp is natural-log and an empty
+ *     selection returns zero output with -inf LSE.
+ *
+ * Readings where the pages leave a step open (each also listed in the design
+ * notes): the scale multiplies the finished dot product; the LSE is
+ * ln sum_j exp(alpha <q, k_j>) over the visible keys; a causal call with
+ * S_q > S_kv is accepted and its first S_q - S_kv rows are empty; a masked
+ * key and a causally hidden key are combined with AND.
+ *
+ * Arithmetic: every element is decoded exactly to double; every sum runs in
+ * double with its index ascending (d for dot products, j for the softmax and
+ * the value reduction).  Build with -ffp-contract=off and no fast-math so the
+ * compiler keeps that order.  Rows are independent, so the OpenMP schedule
+ * does not change any bit of the result.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_BF16 0
+#define ORACLE_FP16 1
+
+/* bfloat16 is the top half of an IEEE binary32: widen by a 16-bit shift. */
+static double decode_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Exponent 0 holds zero and subnormals (fraction * 2^-24); exponent 31 holds
+ * infinities and NaN; otherwise the value is (1024 + fraction) * 2^(e - 25). */
+static double decode_fp16(uint16_t bits)
+{
+    int sign = (bits >> 15) & 1;
+    int e = (bits >> 10) & 0x1f;
+    int frac = bits & 0x3ff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)frac, -24);
+    else if (e == 31)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + frac), e - 25);
+    return sign ? -mag : mag;
+}
+
+static double decode(const uint16_t *base, int64_t idx, int dtype)
+{
+    return dtype == ORACLE_BF16 ? decode_bf16(base[idx]) : decode_fp16(base[idx]);
+}
+
+/* Exposed so the tests can pin both decoders against library conversions. */
+double oracle_decode(uint16_t bits, int dtype)
+{
+    return dtype == ORACLE_BF16 ? decode_bf16(bits) : decode_fp16(bits);
+}
+
+/* The score scale alpha: the sentinel NaN selects 1/sqrt(D), computed once in
+ * double and rounded to float (the type the scale is passed in); any other
+ * value is used as given. */
+double oracle_resolve_scale(float scale, int D)
+{
+    if (isnan(scale))
+        return (double)(float)(1.0 / sqrt((double)D));
+    return (double)scale;
+}
+
+/* Everything that locates a key or value row for one call. */
+typedef struct {
+    const uint16_t *q, *k, *v;
+    int dtype;
+    int B, Sq, Hq, Hkv, D;
+    int causal;
+    double alpha;
+    /* dense */
+    int Skv;
+    const uint8_t *mask; /* [B, Skv] or NULL */
+    /* paged */
+    int paged;
+    const int32_t *seqlen;      /* [B] */
+    const int32_t *block_table; /* [B, max_pages] */
+    int page_size, max_pages;
+} call_t;
+
+/* Number of keys request b holds. */
+static int64_t kv_length(const call_t *c, int b)
+{
+    return c->paged ? (int64_t)c->seqlen[b] : (int64_t)c->Skv;
+}
+
+/* Element offset of key/value row (b, j, r): dense BSHD, or the page-table
+ * translation row = block_table[b, j / page_size] * page_size + j % page_size. */
+static int64_t kv_row_offset(const call_t *c, int b, int64_t j, int r)
+{
+    int64_t row;
+    if (c->paged) {
+        int64_t logical_page = j / c->page_size;
+        int64_t in_page = j % c->page_size;
+        int64_t phys_page = c->block_table[(int64_t)b * c->max_pages + logical_page];
+        row = phys_page * c->page_size + in_page;
+    } else {
+        row = (int64_t)b * c->Skv + j;
+    }
+    return (row * c->Hkv + r) * c->D;
+}
+
+/* Key j is visible to query i iff (not causal or j <= p_i) and the padding
+ * mask keeps column j. */
+static int visible(const call_t *c, int b, int i, int64_t j)
+{
+    int64_t p = (int64_t)i + kv_length(c, b) - c->Sq;
+    if (c->causal && j > p)
+        return 0;
+    if (c->mask && c->mask[(int64_t)b * c->Skv + j] == 0)
+        return 0;
+    return 1;
+}
+
+/* One output row (b, i, h): o_row[D] and *lse_out.  `s` and `w` are scratch
+ * arrays of at least kv_length(b) doubles. */
+static void attend_row(const call_t *c, int b, int i, int h, double *o_row,
+                       double *lse_out, double *s, double *w)
+{
+    const int D = c->D;
+    const int g = c->Hq / c->Hkv;
+    const int r = h / g; /* query head h reads KV head floor(h / g) */
+    const int64_t n = kv_length(c, b);
+    const int64_t q_off = (((int64_t)b * c->Sq + i) * c->Hq + h) * D;
+
+    /* scores of the visible keys; s[j] is left unused for hidden keys */
+    int64_t n_visible = 0;
+    for (int64_t j = 0; j < n; ++j) {
+        if (!visible(c, b, i, j))
+            continue;
+        int64_t k_off = kv_row_offset(c, b, j, r);
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+            dot += decode(c->q, q_off + d, c->dtype) * decode(c->k, k_off + d, c->dtype);
+        s[j] = c->alpha * dot;
+        ++n_visible;
+    }
+
+    if (n_visible == 0) { /* no visible key: zero output, -inf LSE */
+        for (int d = 0; d < D; ++d)
+            o_row[d] = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
+
+    /* softmax over the visible keys, shifted by their maximum */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j)
+        if (visible(c, b, i, j) && s[j] > m)
+            m = s[j];
+    double l = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        if (!visible(c, b, i, j))
+            continue;
+        w[j] = exp(s[j] - m);
+        l += w[j];
+    }
+
+    for (int d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            if (!visible(c, b, i, j))
+                continue;
+            acc += w[j] * decode(c->v, kv_row_offset(c, b, j, r) + d, c->dtype);
+        }
+        o_row[d] = acc / l;
+    }
+    *lse_out = m + log(l);
+}
+
+static int check_common(int B, int Sq, int Hq, int Hkv, int D, int dtype)
+{
+    if (B < 0 || Sq < 0 || Hq <= 0 || Hkv <= 0 || D <= 0)
+        return -1;
+    if (Hq % Hkv != 0)
+        return -1;
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16)
+        return -1;
+    return 0;
+}
+
+static int64_t max_kv_length(const call_t *c)
+{
+    int64_t mx = 0;
+    for (int b = 0; b < c->B; ++b)
+        if (kv_length(c, b) > mx)
+            mx = kv_length(c, b);
+    return mx;
+}
+
+/* Evaluate the rows listed in sel (triples b, i, h).  o: [nsel, D], lse: [nsel]. */
+static int run_rows(const call_t *c, const int32_t *sel, int64_t nsel, double *o, double *lse)
+{
+    int64_t scratch = max_kv_length(c);
+    if (scratch < 1)
+        scratch = 1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)scratch);
+        double *w = (double *)malloc(sizeof(double) * (size_t)scratch);
+        if (!s || !w) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t t = 0; t < nsel; ++t) {
+                int b = sel[3 * t], i = sel[3 * t + 1], h = sel[3 * t + 2];
+                attend_row(c, b, i, h, o + t * c->D, lse + t, s, w);
+            }
+        }
+        free(s);
+        free(w);
+    }
+    return failed ? -2 : 0;
+}
+
+/* Evaluate every row: o [B, Sq, Hq, D], lse [B, Hq, Sq]. */
+static int run_all(const call_t *c, double *o, double *lse)
+{
+    int64_t nrows = (int64_t)c->B * c->Sq * c->Hq;
+    if (nrows == 0)
+        return 0;
+    int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * 3 * (size_t)nrows);
+    double *lse_rows = (double *)malloc(sizeof(double) * (size_t)nrows);
+    if (!sel || !lse_rows) {
+        free(sel);
+        free(lse_rows);
+        return -2;
+    }
+    /* row order b, i, h matches the BSHD output, so o can be written in place */
+    int64_t t = 0;
+    for (int b = 0; b < c->B; ++b)
+        for (int i = 0; i < c->Sq; ++i)
+            for (int h = 0; h < c->Hq; ++h) {
+                sel[3 * t] = b;
+                sel[3 * t + 1] = i;
+                sel[3 * t + 2] = h;
+                ++t;
+            }
+    int rc = run_rows(c, sel, nrows, o, lse_rows);
+    t = 0;
+    for (int b = 0; b < c->B; ++b)
+        for (int i = 0; i < c->Sq; ++i)
+            for (int h = 0; h < c->Hq; ++h)
+                lse[((int64_t)b * c->Hq + h) * c->Sq + i] = lse_rows[t++];
+    free(sel);
+    free(lse_rows);
+    return rc;
+}
+
+static int make_dense(call_t *c, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                      int causal, const uint8_t *mask)
+{
+    if (check_common(B, Sq, Hq, Hkv, D, dtype) || Skv < 0)
+        return -1;
+    memset(c, 0, sizeof *c);
+    c->q = q; c->k = k; c->v = v; c->dtype = dtype;
+    c->B = B; c->Sq = Sq; c->Hq = Hq; c->Hkv = Hkv; c->D = D; c->Skv = Skv;
+    c->causal = causal != 0;
+    c->alpha = oracle_resolve_scale(scale, D);
+    c->mask = mask;
+    return 0;
+}
+
+static int make_paged(call_t *c, const uint16_t *q, const uint16_t *k_cache,
+                      const uint16_t *v_cache, const int32_t *seqlen,
+                      const int32_t *block_table, int page_size, int causal, int B, int Sq,
+                      int Hq, int Hkv, int D, int max_pages, float scale, int dtype)
+{
+    if (check_common(B, Sq, Hq, Hkv, D, dtype) || page_size <= 0 || max_pages < 0)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (seqlen[b] < 0 || (int64_t)seqlen[b] > (int64_t)max_pages * page_size)
+            return -1;
+    memset(c, 0, sizeof *c);
+    c->q = q; c->k = k_cache; c->v = v_cache; c->dtype = dtype;
+    c->B = B; c->Sq = Sq; c->Hq = Hq; c->Hkv = Hkv; c->D = D;
+    c->causal = causal != 0;
+    c->alpha = oracle_resolve_scale(scale, D);
+    c->paged = 1;
+    c->seqlen = seqlen;
+    c->block_table = block_table;
+    c->page_size = page_size;
+    c->max_pages = max_pages;
+    return 0;
+}
+
+/* Dense call: q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (16-bit bit patterns), mask
+ * [B,Skv] or NULL.  Writes o [B,Sq,Hq,D] and lse [B,Hq,Sq] in double.
+ * Returns 0, -1 on invalid arguments, -2 on allocation failure. */
+int oracle_attn_dense(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype,
+                      int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                      const uint8_t *key_padding_mask, double *o, double *lse)
+{
+    call_t c;
+    if (make_dense(&c, q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, scale, causal, key_padding_mask))
+        return -1;
+    return run_all(&c, o, lse);
+}
+
+/* Dense call, selected rows only: sel holds nsel triples (b, i, h).
+ * Writes o [nsel, D] and lse [nsel]. */
+int oracle_attn_dense_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype,
+                           int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                           int causal, const uint8_t *key_padding_mask, const int32_t *sel,
+                           int64_t nsel, double *o, double *lse)
+{
+    call_t c;
+    if (make_dense(&c, q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, scale, causal, key_padding_mask))
+        return -1;
+    for (int64_t t = 0; t < nsel; ++t)
+        if (sel[3 * t] < 0 || sel[3 * t] >= B || sel[3 * t + 1] < 0 || sel[3 * t + 1] >= Sq ||
+            sel[3 * t + 2] < 0 || sel[3 * t + 2] >= Hq)
+            return -1;
+    return run_rows(&c, sel, nsel, o, lse);
+}
+
+/* Paged call: q [B,Sq,Hq,D]; k_cache/v_cache [pages*page_size, Hkv, D];
+ * real_seqlen_kv [B]; block_table [B, max_pages].  Writes o and lse as the
+ * dense call does. */
+int oracle_attn_paged(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                      const int32_t *real_seqlen_kv, const int32_t *block_table, int page_size,
+                      int causal, int B, int Sq, int Hq, int Hkv, int D, int max_pages,
+                      float scale, int dtype, double *o, double *lse)
+{
+    call_t c;
+    if (make_paged(&c, q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, causal, B,
+                   Sq, Hq, Hkv, D, max_pages, scale, dtype))
+        return -1;
+    return run_all(&c, o, lse);
+}
+
+/* Paged call, selected rows only (triples b, i, h). */
+int oracle_attn_paged_rows(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                           const int32_t *real_seqlen_kv, const int32_t *block_table,
+                           int page_size, int causal, int B, int Sq, int Hq, int Hkv, int D,
+                           int max_pages, float scale, int dtype, const int32_t *sel,
+                           int64_t nsel, double *o, double *lse)
+{
+    call_t c;
+    if (make_paged(&c, q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, causal, B,
+                   Sq, Hq, Hkv, D, max_pages, scale, dtype))
+        return -1;
+    for (int64_t t = 0; t < nsel; ++t)
+        if (sel[3 * t] < 0 || sel[3 * t] >= B || sel[3 * t + 1] < 0 || sel[3 * t + 1] >= Sq ||
+            sel[3 * t + 2] < 0 || sel[3 * t + 2] >= Hq)
+            return -1;
+    return run_rows(&c, sel, nsel, o, lse);
+}
+
+/* Number of threads an OpenMP parallel region uses here. */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}

@@ -1,0 +1,72 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check
+that the pin suite rejects every one of them.
+
+Each mutant is the oracle's C source with one textual change, compiled with
+the same flags into a temporary library; the pin tests then run against it in
+a child process and must fail.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "attn_oracle.c")
+
+MUTANTS = {
+    "head_map_modulo": ("const int r = h / g;", "const int r = h % c->Hkv;"),
+    "causal_not_end_aligned": ("int64_t p = (int64_t)i + kv_length(c, b) - c->Sq;",
+                               "int64_t p = (int64_t)i;"),
+    "causal_off_by_one": ("if (c->causal && j > p)", "if (c->causal && j >= p)"),
+    "mask_ignored": ("if (c->mask && c->mask[(int64_t)b * c->Skv + j] == 0)", "if (0)"),
+    "default_scale_wrong": ("return (double)(float)(1.0 / sqrt((double)D));",
+                            "return 1.0 / (double)D;"),
+    "lse_base_two": ("*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
+    "lse_shift_dropped": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
+    "empty_row_nan": ("o_row[d] = 0.0;", "o_row[d] = NAN;"),
+    "page_offset_unscaled": ("row = phys_page * c->page_size + in_page;",
+                             "row = phys_page + in_page;"),
+    "scores_read_v": ("decode(c->k, k_off + d, c->dtype);", "decode(c->v, k_off + d, c->dtype);"),
+    "fp16_exponent_bias": ("mag = ldexp((double)(1024 + frac), e - 25);",
+                           "mag = ldexp((double)(1024 + frac), e - 24);"),
+    "bf16_low_bit": ("uint32_t u = (uint32_t)bits << 16;",
+                     "uint32_t u = ((uint32_t)bits << 16) | 1u;"),
+    "score_sign": ("s[j] = c->alpha * dot;", "s[j] = -c->alpha * dot;"),
+    "dot_drops_last_term": ("for (int d = 0; d < D; ++d)\n            dot +=",
+                            "for (int d = 0; d < D - 1; ++d)\n            dot +="),
+    "value_sum_skips_first_key": ("for (int64_t j = 0; j < n; ++j) {\n            if (!visible(c, b, i, j))\n                continue;\n            acc +=",
+                                  "for (int64_t j = 1; j < n; ++j) {\n            if (!visible(c, b, i, j))\n                continue;\n            acc +="),
+}
+
+PLUGIN = "import os, oracle\noracle._LIB = os.environ['ORACLE_MUTANT_LIB']\n"
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    with tempfile.TemporaryDirectory() as d:
+        with open(os.path.join(d, "oracle_mutant_plugin.py"), "w") as f:
+            f.write(PLUGIN)
+        yield d
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_planted_mistake(name, workdir):
+    before, after = MUTANTS[name]
+    with open(SRC) as f:
+        src = f.read()
+    assert before in src, f"mutation site for {name} no longer exists in the oracle"
+    csrc = os.path.join(workdir, f"{name}.c")
+    lib = os.path.join(workdir, f"{name}.so")
+    with open(csrc, "w") as f:
+        f.write(src.replace(before, after, 1))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                    "-ffp-contract=off", csrc, "-o", lib, "-lm"], check=True)
+    env = dict(os.environ, ORACLE_MUTANT_LIB=lib,
+               PYTHONPATH=os.pathsep.join([workdir, ROOT]), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        "-p", "oracle_mutant_plugin", os.path.join(ROOT, "tests",
+                                                                   "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
