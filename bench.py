@@ -1,0 +1,220 @@
+"""Benchmark: causal GQA attention forward on one MI355X.
+
+Prints ONE JSON line.  `value` is the throughput of the dense causal GQA
+prefill at the Qwen3-8B attention shape (B=2, Hq=32, Hkv=8, Sq=Skv=4096,
+D=128, bf16), counting 4*D flops per visible (query, key, query-head) triple,
+with inputs resident in HBM.  The same line carries:
+  roofline      the attention kernel's achieved rate against the dense bf16
+                MFMA peak (its average duration from HIP events recorded by
+                the library around each launch, on the launch stream);
+  paged_decode  KV bytes/s of the paged decode workload (B=64, Sq=1, Hq=32,
+                Hkv=8, D=128, page 64, lengths U[512, 8192]) against HBM peak,
+                timed per call with the last-level cache flushed in between;
+  cpu_baseline  the fp64 CPU oracle on a bounded row sample of the prefill
+                workload, on this host's cores.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("attn fwd TFLOP/s (causal GQA prefill) + KV GB/s (paged decode), % of roofline")
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def visible_pairs(B, Hq, Sq, kv_lens, causal, keep_counts=None):
+    """Visible (query, key, query-head) triples; kv_lens per batch entry.
+    Query i sees keys j <= i + L - Sq (causal) among the first L keys."""
+    total = 0
+    for b in range(B):
+        L = kv_lens[b]
+        if keep_counts is not None:
+            total += Sq * keep_counts[b]
+            continue
+        for i in range(Sq):
+            hi = min(L, i + L - Sq + 1) if causal else L
+            total += max(hi, 0)
+    return total * Hq
+
+
+def kv_bytes(kv_lens, Hkv, D, elem_bytes=2):
+    return sum(kv_lens) * Hkv * D * elem_bytes * 2
+
+
+def time_prefill(mi, w, steps, warmup):
+    import torch
+    dev = "cuda:0"
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        mi.attn_fwd_dense(q, k, v, scale=w.scale, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mi.profile_start()
+    start.record()
+    for _ in range(steps):
+        mi.attn_fwd_dense(q, k, v, scale=w.scale, causal=True, out=o, lse=lse)
+    end.record()
+    torch.cuda.synchronize()
+    prof = mi.profile_stop()
+    total_ms = start.elapsed_time(end)
+    return total_ms / steps, prof["attn_ms"] / max(prof["attn_launches"], 1)
+
+
+def time_decode(mi, w, steps, warmup):
+    import torch
+    dev = "cuda:0"
+    q = w.q.to(dev)
+    kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
+    lens, bt = w.real_seqlen_kv.to(dev), w.block_table.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)  # > the 256 MB last-level cache
+    for _ in range(warmup):
+        mi.attn_fwd_paged(q, kc, vc, lens, bt, w.page_size, out=o, lse=lse)
+    torch.cuda.synchronize()
+    call_ms = []
+    a_ms = m_ms = 0.0
+    a_n = m_n = 0
+    for _ in range(steps):
+        flush.fill_(1)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        mi.profile_start()
+        s.record()
+        mi.attn_fwd_paged(q, kc, vc, lens, bt, w.page_size, out=o, lse=lse)
+        e.record()
+        torch.cuda.synchronize()
+        prof = mi.profile_stop()
+        call_ms.append(s.elapsed_time(e))
+        a_ms += prof["attn_ms"]
+        a_n += prof["attn_launches"]
+        m_ms += prof["merge_ms"]
+        m_n += prof["merge_launches"]
+    del flush
+    call_ms.sort()
+    return {"median_call_ms": call_ms[len(call_ms) // 2], "min_call_ms": call_ms[0],
+            "attn_kernel_ms": a_ms / max(a_n, 1), "merge_kernel_ms": m_ms / max(m_n, 1)}
+
+
+def cpu_baseline(w, target_s=12.0):
+    """The fp64 oracle on a bounded sample of the prefill workload's rows."""
+    import numpy as np
+
+    import oracle
+    rng = np.random.default_rng(1234)
+
+    def sample(n):
+        return [(int(rng.integers(w.B)), int(rng.integers(w.Sq)), int(rng.integers(w.Hq)))
+                for _ in range(n)]
+
+    def run(rows):
+        t = time.perf_counter()
+        oracle.attn_dense_rows(w.q, w.k, w.v, rows, scale=w.scale, causal=True)
+        return time.perf_counter() - t
+
+    probe = sample(256)
+    t_probe = run(probe)
+    n = int(min(w.B * w.Sq * w.Hq, max(256, 256 * target_s / max(t_probe, 1e-3))))
+    rows = sample(n)
+    dt = run(rows)
+    pairs = sum(min(i + 1, w.Skv) for _, i, _ in rows)
+    tflops = 4.0 * w.D * pairs / dt / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} random (b, i, h) rows of the B=2 Hq=32 S=4096 D=128 causal prefill "
+                      f"({pairs} visible pairs, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import softmax_attention_amd as mi
+    from softmax_attention_amd import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mi.lib()
+
+    w = workloads.make(2)
+    flops = 4.0 * w.D * visible_pairs(w.B, w.Hq, w.Sq, [w.Skv] * w.B, True)
+    print(f"[bench] prefill {w.name}: {flops / 1e9:.1f} GFLOP per call", file=sys.stderr,
+          flush=True)
+    ms_step, ms_kernel = time_prefill(mi, w, args.steps, args.warmup)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    print(f"[bench] prefill {ms_step * 1e3:.1f} us/step, kernel {ms_kernel * 1e3:.1f} us, "
+          f"{achieved:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
+                   "Skv": w.Skv, "D": w.D, "causal": True, "scale": w.scale,
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "attn_fwd_kernel<128, bf16, dense>",
+                     "kernel_avg_us": ms_kernel * 1e3},
+    }
+    del w
+
+    if not args.no_decode:
+        wd = workloads.make(3)
+        nbytes = kv_bytes(wd.kv_lengths(), wd.Hkv, wd.D)
+        d = time_decode(mi, wd, max(args.steps, 10), args.warmup)
+        call_gbs = nbytes / (d["median_call_ms"] * 1e-3) / 1e9
+        kern_gbs = nbytes / (d["attn_kernel_ms"] * 1e-3) / 1e9
+        print(f"[bench] decode {wd.name}: call {d['median_call_ms'] * 1e3:.1f} us "
+              f"({call_gbs:.0f} GB/s), attention kernel {d['attn_kernel_ms'] * 1e3:.1f} us, "
+              f"merge {d['merge_kernel_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+        line["paged_decode"] = {
+            "workload": wd.name, "value": call_gbs, "unit": "GB/s", "kv_bytes": nbytes,
+            "median_call_us": d["median_call_ms"] * 1e3, "min_call_us": d["min_call_ms"] * 1e3,
+            "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": kern_gbs / PEAK_HBM_GBS, "traffic": None,
+                         "kernel": "attn_fwd_kernel<128, bf16, paged>",
+                         "kernel_avg_us": d["attn_kernel_ms"] * 1e3,
+                         "merge_kernel_avg_us": d["merge_kernel_ms"] * 1e3}}
+        del wd
+
+    if not args.no_cpu_baseline:
+        w = workloads.make(2)
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/*
+ * miattn.h -- C ABI of libmiattn: grouped-query softmax attention forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ *     O = softmax(alpha * Q K^T + M) V,   accumulated in FP32,
+ *
+ * with a float32 natural-log log-sum-exp per output row.
+ *
+ * Where the operation is defined (the pages):
+ *   - TileOPs "Attention Operators", GQADenseFwdOp: the equation with FP32
+ *     accumulation and the output in the input dtype; stage 1 (query row i sits
+ *     at KV position p_i = i + S_kv - S_q); stage 4 (Z = alpha <Q, K>, alpha
+ *     defaulting to 1/sqrt(D)); stage 5 (causal visibility j <= p_i); stage 7
+ *     (softmax over keys, then the value sum); query head h reads KV head
+ *     floor(h / (H_q / H_kv)); BSHD layout with D contiguous; a refusal names
+ *     the limit it hit.
+ *   - TileOPs "Attention Operators", MHADecodePagedWithKVCacheFwdOp: the paged
+ *     layout (physical cache [rows, H_kv, D], real_seqlen_kv [B],
+ *     block_table [B, num_pages]) and the per-request end-aligned causal rule;
+ *     a query that sees no key outputs zeros.
+ *   - TileOPs "Attention Operators", PagedKVCacheWriteFwdOp: a flattened cache
+ *     row is page * page_size + offset.
+ *   - RL-Kernel "Standard Softmax Attention", Tensor Contract: an explicit
+ *     scale (0.0 included) is used verbatim; key_padding_mask [B, S_kv] with
+ *     True = keep and False = that key column set to -inf.
+ *   - MATE "QSA", Core Attention: the LSE is natural-log, an empty selection
+ *     gives zero output and -inf LSE, split-KV partials are merged in FP32
+ *     without recomputing QK or PV, and wrappers check shapes and layout
+ *     without reading device contents.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device pointers; the caller allocates and
+ *     owns every tensor.  Work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and the call returns without waiting for it, so the
+ *     buffers must stay alive until that work completes.  Inputs are never
+ *     written.
+ *   - Tensors are dense row-major with the last axis contiguous.  q, k, v, o
+ *     and the caches must be 16-byte aligned; lse 4-byte aligned.
+ *   - Element offsets are computed in 64-bit; dimensions are int32.
+ *   - A call returns MIATTN_OK or an error status and never throws.  On an error
+ *     nothing is enqueued, and miattn_last_error() returns a message that names
+ *     the violated limit (thread-local, valid until the next call on the thread).
+ *   - Device-side contents (lengths, page-table entries) are not read by the
+ *     host and not validated unless the environment variable MIATTN_VALIDATE=1
+ *     is set, which copies them to the host (synchronising the stream).
+ *     Out-of-range entries are otherwise the caller's error, with undefined
+ *     results.
+ *   - The library keeps one split-KV workspace per device, grown with hipMalloc
+ *     on first need; a call that needs no larger workspace allocates nothing.
+ *     Calls that share a device and may run concurrently on different streams
+ *     must not both use the workspace; calls on one stream are ordered.
+ */
+#ifndef MIATTN_H
+#define MIATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MIATTN_OK = 0,
+    MIATTN_ERR_INVALID_ARG = 1, /* arguments violate the contract          */
+    MIATTN_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels serve */
+    MIATTN_ERR_HIP = 3          /* a HIP runtime call failed                */
+} miattn_status;
+
+typedef enum { MIATTN_BF16 = 0, MIATTN_FP16 = 1 } miattn_dtype;
+
+/*
+ * Dense attention forward.
+ *
+ *   q    device, [B, Sq, Hq, D]  dtype
+ *   k    device, [B, Skv, Hkv, D] dtype   (may be NULL when Skv == 0)
+ *   v    device, [B, Skv, Hkv, D] dtype   (may be NULL when Skv == 0)
+ *   B, Hq, Hkv, Sq, Skv, D   B, Sq, Skv >= 0; Hq, Hkv > 0; Hq % Hkv == 0;
+ *                            D in {64, 128, 256}
+ *   scale  alpha; NaN selects 1/sqrt(D) (rounded to float); any finite value,
+ *          0.0 included, is used verbatim; +-inf is refused
+ *   causal 0 or 1: key j is visible to query i iff j <= i + Skv - Sq.  Sq > Skv
+ *          is accepted; its first Sq - Skv rows see no key
+ *   key_padding_mask  device, [B, Skv] bytes, nonzero = keep; NULL = no mask.
+ *          Combined with the causal rule by AND
+ *   o      device, [B, Sq, Hq, D] dtype, written in full
+ *   lse    device, [B, Hq, Sq] float32 (natural log), or NULL to skip it.  A
+ *          row that sees no key gets o = 0 and lse = -inf
+ *   dtype  MIATTN_BF16 or MIATTN_FP16, the type of q, k, v and o
+ *   stream hipStream_t or NULL
+ *
+ * B == 0 or Sq == 0 returns MIATTN_OK without enqueuing anything.
+ */
+miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B, int Hq,
+                             int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                             const uint8_t *key_padding_mask, void *o, float *lse,
+                             miattn_dtype dtype, void *stream);
+
+/*
+ * Paged attention forward (decode, Sq = 1, and chunked prefill, Sq > 1).
+ *
+ *   q        device, [B, Sq, Hq, D] dtype
+ *   k_cache  device, [num_phys_pages * page_size, Hkv, D] dtype; the same bytes
+ *            as [num_phys_pages, page_size, Hkv, D]
+ *   v_cache  device, same layout as k_cache
+ *   real_seqlen_kv device, int32 [B]: the number of cached keys of request b,
+ *            its Sq query tokens included (they sit at the end); 0 <= len <=
+ *            max_pages * page_size
+ *   block_table device, int32 [B, max_pages]: physical page of logical page p
+ *            of request b.  Key j of request b lives in cache row
+ *            block_table[b, j / page_size] * page_size + j % page_size.  Entries
+ *            at p >= ceil(len / page_size) are never read
+ *   page_size a power of two >= 16 (others return MIATTN_ERR_UNSUPPORTED)
+ *   causal   0 or 1: key j is visible to query i iff j <= i + len_b - Sq
+ *   o, lse   as for attn_fwd_dense
+ *   B, Sq, Hq, Hkv, D  as for attn_fwd_dense; max_pages > 0
+ *   num_phys_pages  number of physical pages in each cache (only checked under
+ *            MIATTN_VALIDATE=1)
+ *   scale, dtype, stream  as for attn_fwd_dense
+ *
+ * Long key ranges are split across workgroups; the partial results (FP32
+ * output rows and LSEs) are merged by a second kernel on the same stream.
+ */
+miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *real_seqlen_kv, const int32_t *block_table,
+                             int page_size, int causal, void *o, float *lse, int B, int Sq,
+                             int Hq, int Hkv, int D, int max_pages, int num_phys_pages,
+                             float scale, miattn_dtype dtype, void *stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *miattn_last_error(void);
+
+/* Frees the split-KV workspace of the current device (waits for the device). */
+miattn_status miattn_release_workspace(void);
+
+/*
+ * Split-KV control: keys per split (rounded up to the kernel's key tile);
+ * 0 restores the automatic choice.  Applies to both entry points; a value
+ * that yields one split disables the merge.  Mainly for tests and tuning.
+ */
+void miattn_set_split_keys(int keys_per_split);
+
+/*
+ * Kernel timing.  Between miattn_profile_start() and miattn_profile_stop(),
+ * every attention-kernel and merge-kernel launch is bracketed by HIP events
+ * recorded on its own stream.  stop() waits for those events and returns the
+ * summed durations (milliseconds) and launch counts of each kernel kind.
+ */
+void miattn_profile_start(void);
+miattn_status miattn_profile_stop(double *attn_ms, int *attn_launches, double *merge_ms,
+                                  int *merge_launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIATTN_H */

@@ -1,0 +1,204 @@
+"""ctypes binding of libmiattn (include/miattn.h): argument marshalling only.
+
+Every step of the attention runs in the library's HIP kernels; torch supplies
+device memory and the current stream.  There is no fallback: if the library is
+missing or a call is refused, an exception says why.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmiattn.so")
+
+MIATTN_OK, MIATTN_ERR_INVALID_ARG, MIATTN_ERR_UNSUPPORTED, MIATTN_ERR_HIP = 0, 1, 2, 3
+MIATTN_BF16, MIATTN_FP16 = 0, 1
+
+# every symbol include/miattn.h declares
+EXPORTS = ("attn_fwd_dense", "attn_fwd_paged", "miattn_last_error", "miattn_release_workspace",
+           "miattn_set_split_keys", "miattn_profile_start", "miattn_profile_stop")
+
+_lib = None
+
+
+class MiattnError(RuntimeError):
+    """A HIP runtime failure reported by libmiattn."""
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmiattn.so (built in-tree by softmax_attention_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m softmax_attention_amd.build` "
+                "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.attn_fwd_dense.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, P, P,
+                                     i32, P]
+        L.attn_fwd_dense.restype = i32
+        L.attn_fwd_paged.argtypes = [P, P, P, P, P, i32, i32, P, P, i32, i32, i32, i32, i32,
+                                     i32, i32, f32, i32, P]
+        L.attn_fwd_paged.restype = i32
+        L.miattn_last_error.argtypes = []
+        L.miattn_last_error.restype = ctypes.c_char_p
+        L.miattn_release_workspace.argtypes = []
+        L.miattn_release_workspace.restype = i32
+        L.miattn_set_split_keys.argtypes = [i32]
+        L.miattn_set_split_keys.restype = None
+        L.miattn_profile_start.argtypes = []
+        L.miattn_profile_start.restype = None
+        L.miattn_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_int),
+                                          ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_int)]
+        L.miattn_profile_stop.restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status == MIATTN_OK:
+        return
+    msg = lib().miattn_last_error().decode()
+    if status in (MIATTN_ERR_INVALID_ARG, MIATTN_ERR_UNSUPPORTED):
+        raise ValueError(msg)
+    raise MiattnError(msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MIATTN_BF16
+    if t.dtype == torch.float16:
+        return MIATTN_FP16
+    raise ValueError(f"dtype {t.dtype} unsupported (bfloat16, float16)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _scale(scale) -> float:
+    return math.nan if scale is None else float(scale)
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def attn_fwd_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale=None,
+                   causal: bool = True, key_padding_mask: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Dense attention forward on the current stream.
+
+    q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (bf16 or fp16, CUDA); key_padding_mask
+    [B,Skv] bool (True = keep).  Returns (o [B,Sq,Hq,D], lse [B,Hq,Sq] fp32)."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be rank 4 (BSHD)")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} "
+                         f"v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    code = _dtype_code(q)
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one GPU device")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    mask = None
+    if key_padding_mask is not None:
+        if tuple(key_padding_mask.shape) != (B, Skv):
+            raise ValueError(f"key_padding_mask must be [B, Skv] = [{B}, {Skv}]")
+        mask = key_padding_mask.to(device=q.device, dtype=torch.bool).contiguous()
+        mask = mask.view(torch.uint8)
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd_dense(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Sq, Skv, D, _scale(scale),
+                              int(bool(causal)), _ptr(mask), _ptr(o),
+                              _ptr(lse) if return_lse else None, code, _stream())
+    _check(st)
+    return o, (lse if return_lse else None)
+
+
+def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   real_seqlen_kv: torch.Tensor, block_table: torch.Tensor, page_size: int, *,
+                   causal: bool = True, scale=None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, return_lse: bool = True
+                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Paged attention forward on the current stream.
+
+    q [B,Sq,Hq,D]; k_cache/v_cache [pages*page_size, Hkv, D] or
+    [pages, page_size, Hkv, D]; real_seqlen_kv int32 [B] (cache length, the Sq
+    query tokens included); block_table int32 [B, max_pages]."""
+    if q.dim() != 4:
+        raise ValueError("q must be rank 4 (BSHD)")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have one shape")
+    if k_cache.dim() == 4:
+        if k_cache.shape[1] != page_size:
+            raise ValueError("rank-4 caches must be [pages, page_size, Hkv, D]")
+        n_pages = k_cache.shape[0]
+    elif k_cache.dim() == 3:
+        if k_cache.shape[0] % page_size != 0:
+            raise ValueError("flat cache rows must be a multiple of page_size")
+        n_pages = k_cache.shape[0] // page_size
+    else:
+        raise ValueError("caches must be rank 3 or 4")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share one dtype")
+    if real_seqlen_kv.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise ValueError("real_seqlen_kv and block_table must be int32")
+    code = _dtype_code(q)
+    if not all(t.is_cuda and t.device == q.device
+               for t in (q, k_cache, v_cache, real_seqlen_kv, block_table)):
+        raise ValueError("q, the caches, real_seqlen_kv and block_table must be on one GPU device")
+    B, Sq, Hq, D = q.shape
+    Hkv = k_cache.shape[-2]
+    if k_cache.shape[-1] != D:
+        raise ValueError("head dim of the caches differs from q")
+    if block_table.dim() != 2 or block_table.shape[0] != B or real_seqlen_kv.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and real_seqlen_kv [B]")
+    q = q.contiguous()
+    k_cache, v_cache = k_cache.contiguous(), v_cache.contiguous()
+    real_seqlen_kv, block_table = real_seqlen_kv.contiguous(), block_table.contiguous()
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(real_seqlen_kv),
+                              _ptr(block_table), int(page_size), int(bool(causal)), _ptr(o),
+                              _ptr(lse) if return_lse else None, B, Sq, Hq, Hkv, D,
+                              block_table.shape[1], n_pages, _scale(scale), code, _stream())
+    _check(st)
+    return o, (lse if return_lse else None)
+
+
+def set_split_keys(keys_per_split: int) -> None:
+    """Keys per split-KV partition (0 = automatic)."""
+    lib().miattn_set_split_keys(int(keys_per_split))
+
+
+def release_workspace() -> None:
+    _check(lib().miattn_release_workspace())
+
+
+def profile_start() -> None:
+    lib().miattn_profile_start()
+
+
+def profile_stop() -> dict:
+    """Summed kernel durations (ms) and launch counts since profile_start()."""
+    a_ms, m_ms = ctypes.c_double(), ctypes.c_double()
+    a_n, m_n = ctypes.c_int(), ctypes.c_int()
+    _check(lib().miattn_profile_stop(ctypes.byref(a_ms), ctypes.byref(a_n), ctypes.byref(m_ms),
+                                     ctypes.byref(m_n)))
+    return {"attn_ms": a_ms.value, "attn_launches": a_n.value, "merge_ms": m_ms.value,
+            "merge_launches": m_n.value}

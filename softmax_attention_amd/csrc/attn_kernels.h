@@ -1,0 +1,61 @@
+// attn_kernels.h -- launch parameters shared by the host library and the
+// attention kernels of libmiattn (internal; not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miattn {
+
+// Packed-row tiling shared by the host planner and the kernels.
+//
+// The query rows of one (batch, KV head) pair are packed so that the g query
+// heads that read this KV head sit next to each other: packed row r holds
+// query i = r / g of head kvh * g + r % g.  Every packed row reads the same
+// keys, so one K/V tile staged in LDS serves the whole group.
+constexpr int kRowsPerWave = 32;                       // one 32x32 MFMA column block
+constexpr int kWavesPerBlock = 4;
+constexpr int kRowsPerBlock = kRowsPerWave * kWavesPerBlock;  // 128
+constexpr int kThreadsPerBlock = 64 * kWavesPerBlock;         // 256
+
+// Keys per KV tile: the tile holds 8192 elements of K and of V for every D.
+constexpr int keys_per_tile(int D) { return 8192 / D; }
+
+struct FwdParams {
+    const uint16_t *q;   // [B, Sq, Hq, D]
+    const uint16_t *k;   // dense [B, Skv, Hkv, D] or paged cache [rows, Hkv, D]
+    const uint16_t *v;
+    uint16_t *o;         // [B, Sq, Hq, D]
+    float *lse;          // [B, Hq, Sq] or nullptr
+    float *o_part;       // [B*Hkv, n_splits, rows, D] when n_splits > 1
+    float *lse_part;     // [B*Hkv, n_splits, rows]
+    const uint8_t *mask; // dense key padding [B, Skv] or nullptr
+    const int32_t *seqlen;      // paged: [B]
+    const int32_t *block_table; // paged: [B, max_pages]
+    int B, Sq, Hq, Hkv, G, Skv;
+    int page_shift, max_pages;
+    int rows;        // Sq * G packed rows per (batch, KV head)
+    int n_mblocks;   // ceil(rows / kRowsPerBlock)
+    int n_splits;    // key-range splits per (batch, KV head)
+    int split_len;   // keys per split, a multiple of the key tile
+    int causal;
+    float scale_log2;  // alpha * log2(e)
+    int xcd_units;     // (batch*KV head, split) units per XCD, or 0 for linear order
+};
+
+struct MergeParams {
+    const float *o_part;
+    const float *lse_part;
+    uint16_t *o;
+    float *lse;
+    const int32_t *seqlen;  // paged lengths, or nullptr for dense
+    int Skv;
+    int B, Sq, Hq, Hkv, G, rows, n_splits, split_len;
+};
+
+// Launchers: return the hipGetLastError() status of the launch.
+hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int grid,
+                           hipStream_t stream);
+hipError_t launch_lse_merge(const MergeParams &p, int D, bool bf16, hipStream_t stream);
+
+}  // namespace miattn

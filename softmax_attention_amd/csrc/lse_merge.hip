@@ -1,0 +1,98 @@
+// lse_merge.hip -- combine split-KV partial results by their log-sum-exps.
+//
+// Each split s of a row's key range produced a normalised partial output o_s
+// (FP32) and its natural-log LSE lse_s (-inf when the split holds no visible
+// key for that row).  The whole-range result is
+//     lse = M + ln sum_s exp(lse_s - M),  M = max_s lse_s,
+//     o   = sum_s exp(lse_s - lse) o_s,
+// computed in FP32 without recomputing QK or PV (the split-KV merge of MATE
+// "QSA", Core Attention).  A row whose every split is empty gets o = 0 and
+// lse = -inf (TileOPs "Attention Operators", MHADecodePagedWithKVCacheFwdOp:
+// a query that sees no key outputs zeros; MATE "QSA": empty -> -inf LSE).
+//
+// One wave per packed row; lane l owns D/64 consecutive output elements.
+#include "attn_kernels.h"
+
+namespace miattn {
+namespace {
+
+template <bool BF16>
+__device__ __forceinline__ uint16_t to_half_bits(float x) {
+    if constexpr (BF16)
+        return __builtin_bit_cast(uint16_t, (__bf16)x);
+    else
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
+    constexpr int PER = D / 64;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t gr = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t total = (int64_t)p.B * p.Hkv * p.rows;
+    if (gr >= total) return;
+    const int bh = (int)(gr / p.rows);
+    const int r = (int)(gr - (int64_t)bh * p.rows);
+    const int b = bh / p.Hkv;
+    const int kvh = bh - b * p.Hkv;
+    const int i = r / p.G;
+    const int gh = r - i * p.G;
+
+    const int kv_len = p.seqlen ? p.seqlen[b] : p.Skv;
+    // the splits that hold keys of this request (the attention kernel writes
+    // every row of each of them and nothing for the others)
+    const int n_valid = min(p.n_splits, (kv_len + p.split_len - 1) / p.split_len);
+    const int64_t base = (int64_t)bh * p.n_splits * p.rows + r;
+
+    float M = -INFINITY;
+    for (int s = lane; s < n_valid; s += 64) M = fmaxf(M, p.lse_part[base + (int64_t)s * p.rows]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+    float accv[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) accv[e] = 0.f;
+    float den = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < n_valid; ++s) {
+            const int64_t idx = base + (int64_t)s * p.rows;
+            const float ls = p.lse_part[idx];
+            if (ls == -INFINITY) continue;
+            const float w = __expf(ls - M);
+            den += w;
+            const float *src = p.o_part + idx * D + lane * PER;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) accv[e] += w * src[e];
+        }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    uint16_t *dst = p.o + (((int64_t)b * p.Sq + i) * p.Hq + (int64_t)kvh * p.G + gh) * D +
+                    lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) dst[e] = to_half_bits<BF16>(accv[e] * inv);
+    if (p.lse != nullptr && lane == 0)
+        p.lse[((int64_t)b * p.Hq + (int64_t)kvh * p.G + gh) * p.Sq + i] =
+            den > 0.f ? M + __logf(den) : -INFINITY;
+}
+
+template <int D, bool BF16>
+hipError_t launch_one(const MergeParams &p, hipStream_t stream) {
+    const int64_t rows = (int64_t)p.B * p.Hkv * p.rows;
+    const int grid = (int)((rows + 3) / 4);
+    hipLaunchKernelGGL((lse_merge_kernel<D, BF16>), dim3(grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(const MergeParams &p, int D, bool bf16, hipStream_t stream) {
+    switch (D) {
+        case 64: return bf16 ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
+        case 128: return bf16 ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+        case 256: return bf16 ? launch_one<256, true>(p, stream) : launch_one<256, false>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace miattn

@@ -1,0 +1,427 @@
+// miattn.hip -- the C ABI of libmiattn: argument validation, launch planning,
+// the split-KV workspace and kernel timing.  The kernels live in attn_fwd.hip
+// and lse_merge.hip; see include/miattn.h for the contract.
+#include "miattn.h"
+
+#include <limits.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "attn_kernels.h"
+
+using miattn::FwdParams;
+using miattn::MergeParams;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+miattn_status fail(miattn_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+miattn_status hip_fail(hipError_t e, const char *what) {
+    return fail(MIATTN_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// ---------------------------------------------------------------- device state
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+    void *ws = nullptr;  // split-KV partials
+    size_t ws_bytes = 0;
+    int cus = 0;
+};
+
+std::mutex g_mu;
+DeviceState g_dev[kMaxDevices];
+int g_split_keys = 0;  // 0 = automatic
+
+int compute_units(int dev) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_dev[dev].cus == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        g_dev[dev].cus = n;
+    }
+    return g_dev[dev].cus;
+}
+
+miattn_status workspace(int dev, size_t bytes, void **out) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState &d = g_dev[dev];
+    if (d.ws_bytes < bytes) {
+        if (d.ws) {
+            hipError_t e = hipFree(d.ws);  // waits for work that may still use it
+            d.ws = nullptr;
+            d.ws_bytes = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+        }
+        // grow with headroom so that a slightly larger call does not reallocate
+        const size_t want = bytes + bytes / 4;
+        hipError_t e = hipMalloc(&d.ws, want);
+        if (e != hipSuccess) {
+            d.ws = nullptr;
+            return hip_fail(e, "hipMalloc(split-KV workspace)");
+        }
+        d.ws_bytes = want;
+    }
+    *out = d.ws;
+    return MIATTN_OK;
+}
+
+// ---------------------------------------------------------------- timing
+
+struct Timing {
+    bool on = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[2];  // [0] attention, [1] merge
+};
+std::mutex g_prof_mu;
+Timing g_prof;
+
+bool profiling() {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    return g_prof.on;
+}
+
+template <class Launch>
+hipError_t timed_launch(int kind, hipStream_t stream, Launch &&launch) {
+    if (!profiling()) return launch();
+    hipEvent_t a, b;
+    hipError_t e = hipEventCreate(&a);
+    if (e != hipSuccess) return e;
+    e = hipEventCreate(&b);
+    if (e != hipSuccess) return e;
+    hipEventRecord(a, stream);
+    e = launch();
+    hipEventRecord(b, stream);
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof.ev[kind].push_back({a, b});
+    return e;
+}
+
+// ---------------------------------------------------------------- checks
+
+miattn_status check_common(const void *q, const void *o, float *lse, int B, int Sq, int Hq,
+                           int Hkv, int D, float scale, miattn_dtype dtype) {
+    if (B < 0 || Sq < 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "negative dimension: B=%d Sq=%d", B, Sq);
+    if (Hq <= 0 || Hkv <= 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "head counts must be positive: Hq=%d Hkv=%d", Hq,
+                    Hkv);
+    if (D <= 0) return fail(MIATTN_ERR_INVALID_ARG, "D=%d must be positive", D);
+    if (Hq % Hkv != 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "Hq (%d) not divisible by Hkv (%d)", Hq, Hkv);
+    if (D != 64 && D != 128 && D != 256)
+        return fail(MIATTN_ERR_UNSUPPORTED, "D=%d unsupported (64, 128, 256)", D);
+    if (dtype != MIATTN_BF16 && dtype != MIATTN_FP16)
+        return fail(MIATTN_ERR_UNSUPPORTED, "dtype %d unsupported (MIATTN_BF16, MIATTN_FP16)",
+                    (int)dtype);
+    if (isinf(scale)) return fail(MIATTN_ERR_INVALID_ARG, "scale must be finite (or NaN for 1/sqrt(D))");
+    if ((int64_t)Sq * (Hq / Hkv) > INT_MAX / 2)
+        return fail(MIATTN_ERR_UNSUPPORTED, "Sq*Hq/Hkv = %lld exceeds %d packed rows",
+                    (long long)Sq * (Hq / Hkv), INT_MAX / 2);
+    if (B == 0 || Sq == 0) return MIATTN_OK;
+    if (!q || !o) return fail(MIATTN_ERR_INVALID_ARG, "q and o must not be NULL");
+    if (!aligned16(q)) return fail(MIATTN_ERR_INVALID_ARG, "q not 16-byte aligned");
+    if (!aligned16(o)) return fail(MIATTN_ERR_INVALID_ARG, "o not 16-byte aligned");
+    if (lse && ((uintptr_t)lse & 3u))
+        return fail(MIATTN_ERR_INVALID_ARG, "lse not 4-byte aligned");
+    return MIATTN_OK;
+}
+
+float resolve_scale(float scale, int D) {
+    return isnan(scale) ? (float)(1.0 / sqrt((double)D)) : scale;
+}
+
+int env_int(const char *name, int dflt) {
+    const char *s = getenv(name);
+    if (!s || !*s) return dflt;
+    return atoi(s);
+}
+
+// ---------------------------------------------------------------- plan + launch
+
+miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
+                  hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MIATTN_ERR_UNSUPPORTED, "device %d", dev);
+
+    const int BN = miattn::keys_per_tile(D);
+    p.G = p.Hq / p.Hkv;
+    p.rows = p.Sq * p.G;
+    p.n_mblocks = (p.rows + miattn::kRowsPerBlock - 1) / miattn::kRowsPerBlock;
+    const int64_t bhs = (int64_t)p.B * p.Hkv;
+    const int64_t cap_tiles = capacity > 0 ? (capacity + BN - 1) / BN : 1;
+
+    // Split the key axis when the (row block, batch, KV head) units alone
+    // cannot fill the chip, or for decode-shaped calls, whose per-request
+    // lengths vary and are only known on the device.
+    int split_keys = g_split_keys > 0 ? g_split_keys : env_int("MIATTN_SPLIT_KEYS", 0);
+    int64_t tiles_per;
+    if (split_keys > 0) {
+        tiles_per = (split_keys + BN - 1) / BN;
+    } else {
+        const int64_t units0 = (int64_t)p.n_mblocks * bhs;
+        const int cus = compute_units(dev);
+        if (p.n_mblocks == 1 && p.rows <= miattn::kRowsPerWave) {
+            tiles_per = (512 + BN - 1) / BN;  // 512-key splits
+        } else if (units0 >= 2 * (int64_t)cus) {
+            tiles_per = cap_tiles;
+        } else {
+            const int64_t want = (3 * (int64_t)cus + units0 - 1) / units0;
+            tiles_per = (cap_tiles + want - 1) / want;
+        }
+    }
+    if (tiles_per < 1) tiles_per = 1;
+    if (tiles_per > cap_tiles) tiles_per = cap_tiles;
+    const int64_t n_splits = (cap_tiles + tiles_per - 1) / tiles_per;
+    p.n_splits = (int)n_splits;
+    p.split_len = (int)(tiles_per * BN);
+    if (n_splits == 1) p.split_len = (int)(cap_tiles * BN);
+
+    const int64_t grid = (int64_t)p.n_mblocks * bhs * n_splits;
+    if (grid > INT_MAX)
+        return fail(MIATTN_ERR_UNSUPPORTED, "launch of %lld workgroups exceeds %d",
+                    (long long)grid, INT_MAX);
+    const int64_t units = bhs * n_splits;
+    p.xcd_units = (units % 8 == 0) ? (int)(units / 8) : 0;
+
+    if (n_splits > 1) {
+        const int64_t nrow = n_splits * bhs * p.rows;
+        void *ws = nullptr;
+        miattn_status st = workspace(dev, (size_t)nrow * (D + 1) * sizeof(float), &ws);
+        if (st != MIATTN_OK) return st;
+        p.o_part = (float *)ws;
+        p.lse_part = p.o_part + nrow * D;
+    }
+
+    e = timed_launch(0, stream, [&] {
+        return miattn::launch_attn_fwd(p, D, bf16, paged, (int)grid, stream);
+    });
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+
+    if (n_splits > 1) {
+        MergeParams m;
+        m.o_part = p.o_part;
+        m.lse_part = p.lse_part;
+        m.o = p.o;
+        m.lse = p.lse;
+        m.seqlen = paged ? p.seqlen : nullptr;
+        m.Skv = p.Skv;
+        m.B = p.B;
+        m.Sq = p.Sq;
+        m.Hq = p.Hq;
+        m.Hkv = p.Hkv;
+        m.G = p.G;
+        m.rows = p.rows;
+        m.n_splits = p.n_splits;
+        m.split_len = p.split_len;
+        e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
+        if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    }
+    return MIATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *miattn_last_error(void) { return g_err; }
+
+miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B, int Hq,
+                             int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                             const uint8_t *key_padding_mask, void *o, float *lse,
+                             miattn_dtype dtype, void *stream) {
+    g_err[0] = '\0';
+    miattn_status st = check_common(q, o, lse, B, Sq, Hq, Hkv, D, scale, dtype);
+    if (st != MIATTN_OK) return st;
+    if (Skv < 0) return fail(MIATTN_ERR_INVALID_ARG, "negative dimension: Skv=%d", Skv);
+    if (causal != 0 && causal != 1)
+        return fail(MIATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
+    if (B == 0 || Sq == 0) return MIATTN_OK;
+    if (Skv > 0) {
+        if (!k || !v) return fail(MIATTN_ERR_INVALID_ARG, "k and v must not be NULL");
+        if (!aligned16(k)) return fail(MIATTN_ERR_INVALID_ARG, "k not 16-byte aligned");
+        if (!aligned16(v)) return fail(MIATTN_ERR_INVALID_ARG, "v not 16-byte aligned");
+    }
+    if ((int64_t)B * Skv > INT_MAX)
+        return fail(MIATTN_ERR_UNSUPPORTED, "B*Skv = %lld exceeds %d key rows",
+                    (long long)B * Skv, INT_MAX);
+
+    FwdParams p = {};
+    p.q = (const uint16_t *)q;
+    p.k = (const uint16_t *)k;
+    p.v = (const uint16_t *)v;
+    p.o = (uint16_t *)o;
+    p.lse = lse;
+    p.mask = key_padding_mask;
+    p.B = B;
+    p.Sq = Sq;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Skv = Skv;
+    p.causal = causal;
+    p.scale_log2 = resolve_scale(scale, D) * 1.4426950408889634f;
+    return run(p, D, dtype == MIATTN_BF16, false, Skv, (hipStream_t)stream);
+}
+
+miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *real_seqlen_kv, const int32_t *block_table,
+                             int page_size, int causal, void *o, float *lse, int B, int Sq,
+                             int Hq, int Hkv, int D, int max_pages, int num_phys_pages,
+                             float scale, miattn_dtype dtype, void *stream) {
+    g_err[0] = '\0';
+    miattn_status st = check_common(q, o, lse, B, Sq, Hq, Hkv, D, scale, dtype);
+    if (st != MIATTN_OK) return st;
+    if (page_size <= 0) return fail(MIATTN_ERR_INVALID_ARG, "page_size must be > 0 (got %d)",
+                                    page_size);
+    if (page_size < 16 || (page_size & (page_size - 1)) != 0)
+        return fail(MIATTN_ERR_UNSUPPORTED,
+                    "page_size=%d unsupported (a power of two >= 16)", page_size);
+    if (max_pages <= 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "max_pages must be > 0 (got %d)", max_pages);
+    if (num_phys_pages < 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "num_phys_pages=%d is negative", num_phys_pages);
+    if (causal != 0 && causal != 1)
+        return fail(MIATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
+    const int64_t capacity = (int64_t)max_pages * page_size;
+    if (capacity > INT_MAX / 2)
+        return fail(MIATTN_ERR_UNSUPPORTED, "max_pages*page_size = %lld exceeds %d keys",
+                    (long long)capacity, INT_MAX / 2);
+    if (B == 0 || Sq == 0) return MIATTN_OK;
+    if (!k_cache || !v_cache || !real_seqlen_kv || !block_table)
+        return fail(MIATTN_ERR_INVALID_ARG,
+                    "k_cache, v_cache, real_seqlen_kv and block_table must not be NULL");
+    if (!aligned16(k_cache)) return fail(MIATTN_ERR_INVALID_ARG, "k_cache not 16-byte aligned");
+    if (!aligned16(v_cache)) return fail(MIATTN_ERR_INVALID_ARG, "v_cache not 16-byte aligned");
+    if (((uintptr_t)real_seqlen_kv & 3u) || ((uintptr_t)block_table & 3u))
+        return fail(MIATTN_ERR_INVALID_ARG, "real_seqlen_kv/block_table not 4-byte aligned");
+
+    int page_shift = 0;
+    while ((1 << page_shift) < page_size) ++page_shift;
+
+    if (env_int("MIATTN_VALIDATE", 0) == 1) {
+        // opt-in check of the device metadata (synchronises the stream)
+        std::vector<int32_t> lens(B), bt((size_t)B * max_pages);
+        hipStream_t s = (hipStream_t)stream;
+        hipError_t e = hipMemcpyAsync(lens.data(), real_seqlen_kv, sizeof(int32_t) * B,
+                                      hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(bt.data(), block_table, sizeof(int32_t) * bt.size(),
+                               hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "MIATTN_VALIDATE metadata copy");
+        for (int b = 0; b < B; ++b) {
+            if (lens[b] < 0 || lens[b] > capacity)
+                return fail(MIATTN_ERR_INVALID_ARG,
+                            "real_seqlen_kv[%d]=%d outside [0, max_pages*page_size=%lld]", b,
+                            lens[b], (long long)capacity);
+            const int used = (lens[b] + page_size - 1) / page_size;
+            for (int pg = 0; pg < used; ++pg) {
+                const int32_t ph = bt[(size_t)b * max_pages + pg];
+                if (ph < 0 || ph >= num_phys_pages)
+                    return fail(MIATTN_ERR_INVALID_ARG,
+                                "block_table[%d,%d]=%d outside [0, num_phys_pages=%d)", b, pg,
+                                ph, num_phys_pages);
+            }
+        }
+    }
+
+    FwdParams p = {};
+    p.q = (const uint16_t *)q;
+    p.k = (const uint16_t *)k_cache;
+    p.v = (const uint16_t *)v_cache;
+    p.o = (uint16_t *)o;
+    p.lse = lse;
+    p.seqlen = real_seqlen_kv;
+    p.block_table = block_table;
+    p.B = B;
+    p.Sq = Sq;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.page_shift = page_shift;
+    p.max_pages = max_pages;
+    p.causal = causal;
+    p.scale_log2 = resolve_scale(scale, D) * 1.4426950408889634f;
+    return run(p, D, dtype == MIATTN_BF16, true, capacity, (hipStream_t)stream);
+}
+
+miattn_status miattn_release_workspace(void) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState &d = g_dev[dev];
+    if (d.ws) {
+        e = hipFree(d.ws);
+        d.ws = nullptr;
+        d.ws_bytes = 0;
+        if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+    }
+    return MIATTN_OK;
+}
+
+void miattn_set_split_keys(int keys_per_split) {
+    g_split_keys = keys_per_split > 0 ? keys_per_split : 0;
+}
+
+void miattn_profile_start(void) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    for (auto &v : g_prof.ev)
+        for (auto &pr : v) {
+            hipEventDestroy(pr.first);
+            hipEventDestroy(pr.second);
+        }
+    g_prof.ev[0].clear();
+    g_prof.ev[1].clear();
+    g_prof.on = true;
+}
+
+miattn_status miattn_profile_stop(double *attn_ms, int *attn_launches, double *merge_ms,
+                                  int *merge_launches) {
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[2];
+    {
+        std::lock_guard<std::mutex> lock(g_prof_mu);
+        g_prof.on = false;
+        ev[0].swap(g_prof.ev[0]);
+        ev[1].swap(g_prof.ev[1]);
+    }
+    double tot[2] = {0.0, 0.0};
+    miattn_status st = MIATTN_OK;
+    for (int kind = 0; kind < 2; ++kind)
+        for (auto &pr : ev[kind]) {
+            float ms = 0.f;
+            hipError_t e = hipEventSynchronize(pr.second);
+            if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+            if (e != hipSuccess && st == MIATTN_OK) st = hip_fail(e, "hipEventElapsedTime");
+            tot[kind] += ms;
+            hipEventDestroy(pr.first);
+            hipEventDestroy(pr.second);
+        }
+    if (attn_ms) *attn_ms = tot[0];
+    if (attn_launches) *attn_launches = (int)ev[0].size();
+    if (merge_ms) *merge_ms = tot[1];
+    if (merge_launches) *merge_launches = (int)ev[1].size();
+    return st;
+}
+
+}  // extern "C"

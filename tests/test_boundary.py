@@ -1,0 +1,129 @@
+"""The C ABI on the CPU: the library loads, exports every symbol its header
+declares, and refuses invalid arguments with a message naming the limit --
+all before any HIP call, so no GPU is needed (TileOPs "Attention Operators",
+GQADenseFwdOp: a refusal names the limit; RL-Kernel "Standard Softmax
+Attention", Known Limitations: Hq must be divisible by Hkv)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import softmax_attention_amd as mi
+from softmax_attention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "miattn.h")
+
+NAN = float("nan")
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced on refusal
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:miattn_status|void|const char\s*\*)\s*(\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS), names
+    L = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def dense(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, Hq=8, Hkv=2, Sq=4, Skv=4, D=128, scale=NAN, causal=1,
+             mask=None, o=FAKE, lse=None, dtype=0, stream=None)
+    a.update(kw)
+    L = mi.lib()
+    st = L.attn_fwd_dense(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Skv"],
+                          a["D"], a["scale"], a["causal"], a["mask"], a["o"], a["lse"],
+                          a["dtype"], a["stream"])
+    return st, L.miattn_last_error().decode()
+
+
+def paged(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, bt=FAKE, page_size=64, causal=1, o=FAKE,
+             lse=None, B=2, Sq=1, Hq=8, Hkv=2, D=128, max_pages=4, n_phys=8, scale=NAN, dtype=0,
+             stream=None)
+    a.update(kw)
+    L = mi.lib()
+    st = L.attn_fwd_paged(a["q"], a["kc"], a["vc"], a["lens"], a["bt"], a["page_size"],
+                          a["causal"], a["o"], a["lse"], a["B"], a["Sq"], a["Hq"], a["Hkv"],
+                          a["D"], a["max_pages"], a["n_phys"], a["scale"], a["dtype"],
+                          a["stream"])
+    return st, L.miattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(Hq=30, Hkv=8), 1, "Hq (30) not divisible by Hkv (8)"),
+    (dict(D=96), 2, "D=96 unsupported"),
+    (dict(D=0), 1, "D=0"),
+    (dict(B=-1), 1, "negative dimension"),
+    (dict(Sq=-3), 1, "negative dimension"),
+    (dict(Skv=-2), 1, "Skv=-2"),
+    (dict(Hkv=0), 1, "head counts"),
+    (dict(dtype=7), 2, "dtype 7"),
+    (dict(scale=math.inf), 1, "scale must be finite"),
+    (dict(q=None), 1, "must not be NULL"),
+    (dict(o=None), 1, "must not be NULL"),
+    (dict(k=None), 1, "k and v"),
+    (dict(q=FAKE + 8), 1, "q not 16-byte aligned"),
+    (dict(k=FAKE + 2), 1, "k not 16-byte aligned"),
+    (dict(o=FAKE + 4), 1, "o not 16-byte aligned"),
+    (dict(lse=FAKE + 2), 1, "lse not 4-byte aligned"),
+    (dict(causal=2), 1, "causal=2"),
+])
+def test_dense_refusals(kw, status, needle):
+    st, msg = dense(**kw)
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_dense_empty_calls_are_ok_without_touching_the_device():
+    assert dense(B=0, q=None, o=None)[0] == 0
+    assert dense(Sq=0, q=None, o=None)[0] == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(page_size=0), 1, "page_size must be > 0"),
+    (dict(page_size=48), 2, "page_size=48 unsupported"),
+    (dict(page_size=8), 2, "page_size=8 unsupported"),
+    (dict(max_pages=0), 1, "max_pages"),
+    (dict(n_phys=-1), 1, "num_phys_pages"),
+    (dict(lens=None), 1, "must not be NULL"),
+    (dict(bt=None), 1, "must not be NULL"),
+    (dict(kc=FAKE + 8), 1, "k_cache not 16-byte aligned"),
+    (dict(bt=FAKE + 2), 1, "4-byte aligned"),
+    (dict(Hq=12, Hkv=8), 1, "not divisible"),
+    (dict(D=512), 2, "D=512 unsupported"),
+    (dict(max_pages=1 << 30, page_size=64), 2, "exceeds"),
+])
+def test_paged_refusals(kw, status, needle):
+    st, msg = paged(**kw)
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_python_binding_maps_refusals_to_value_error():
+    import torch
+    st, _ = dense(Hq=5, Hkv=2)
+    with pytest.raises(ValueError, match="not divisible"):
+        binding._check(st)
+    st, _ = dense(D=32)
+    with pytest.raises(ValueError, match="D=32"):
+        binding._check(st)
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="dtype"):
+        mi.attn_fwd_dense(q.float(), k.float(), k.float())
+    with pytest.raises(ValueError, match="GPU"):
+        mi.attn_fwd_dense(q, k, k)
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.lib()
