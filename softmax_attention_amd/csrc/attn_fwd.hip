@@ -73,44 +73,86 @@ struct Half<false> {
     }
 };
 
-// Round-to-nearest-even conversion of two floats into one packed dword.
+// Round-to-nearest-even conversion of two floats into one packed dword (a
+// single v_cvt_pk_{bf16,f16}_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
-    using S = typename Half<BF16>::scalar;
-    const S a = (S)lo, b = (S)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2 v = {lo, hi};
+    if constexpr (BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Within each 16-key group of the transposed V tile, the four 4-key units are
-// stored in the order the 32x32 score layout hands them to a lane half: lane
-// half h holds keys {4h..4h+3, 8+4h..8+4h+3} of the group, so units 0 and 2
-// go first (half 0), then units 1 and 3 (half 1).
-__device__ __forceinline__ int unit_slot(int unit) {
-    const int u = unit & 3;
-    return (unit >> 2) * 16 + ((u == 1) ? 2 : (u == 2) ? 1 : u) * 4;
+// ---- LDS tiles.  A K or V tile is stored row-major (one key per row, D
+// contiguous) without padding; the 16-byte chunks of row r are XOR-swizzled
+// (chunk c sits at position c ^ swz(r)) so that both read patterns below hit
+// distinct LDS banks: the QK^T operand (16 rows, one chunk each) and the
+// transposing V read (4 consecutive rows, two adjacent chunks each).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 64)
+        return ((row >> 1) & 3) * 2 + ((row >> 3) & 1);
+    else
+        return (row & 7) * 2 + ((row >> 3) & 1);
 }
 
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {  // bytes
+    return row * (2 * D) + 16 * (chunk ^ swz<D>(row));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Sum of the two 16-bit values packed in `pk`, accumulated into acc in FP32.
+template <bool BF16>
+__device__ __forceinline__ float add_pair(uint32_t pk, float acc) {
+    if constexpr (BF16)
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
+                                               false);
+    else
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk),
+                                      __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+}
+
+// The running max is only raised when a tile's max exceeds it by more than
+// this many powers of two; until then exponentials are taken against the
+// stale max (bounded by 2^kLazy), which leaves the result unchanged in exact
+// arithmetic and saves rescaling O for almost every tile.
+constexpr float kLazy = 8.0f;
+
+template <int D>
+constexpr int waves_per_eu() { return D <= 128 ? 2 : 1; }
+
 template <int D, bool BF16, bool PAGED>
-__global__ __launch_bounds__(kThreadsPerBlock) void attn_fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(kThreadsPerBlock)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<D>(), waves_per_eu<D>())))
+void attn_fwd_kernel(const FwdParams p) {
     using H = Half<BF16>;
     using vec8 = typename H::vec8;
     constexpr int BN = keys_per_tile(D);   // keys per tile
-    constexpr int KSTR = D + 8;            // K tile row stride (elements); +16 B pad
-    constexpr int VSTR = BN + 8;           // V^T tile row stride (elements); +16 B pad
+    constexpr int TILE_BYTES = BN * D * 2; // 16 KB for K, the same for V
     constexpr int NT = BN / 32;            // 32-key score blocks per tile
     constexpr int KSTEPS = D / 16;         // MFMA k-steps over D
     constexpr int DT = D / 32;             // 32-wide d blocks of O^T
     constexpr int PSTEPS = BN / 16;        // MFMA k-steps over the tile's keys
-    constexpr int DCH = D / 8;             // 16-byte chunks per row
-    constexpr int VUNITS = BN / 4;         // 4-key units per tile
-    static_assert(BN * DCH == 4 * kThreadsPerBlock, "K tile: 4 chunks per thread");
-    static_assert(VUNITS * DCH == kThreadsPerBlock, "V tile: one 4x8 block per thread");
+    static_assert(TILE_BYTES == 16 * 1024, "one tile = 16 direct 1 KB loads");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[D * VSTR];
+    // two stages of (K tile, V tile); separate arrays so the compiler can
+    // tell a load into one stage from reads of the other
+    __shared__ __attribute__((aligned(1024))) uint8_t sK0[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV0[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK1[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV1[TILE_BYTES];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -167,15 +209,20 @@ __global__ __launch_bounds__(kThreadsPerBlock) void attn_fwd_kernel(const FwdPar
     const int my_gh = my_row - my_i * p.G;
     const int my_last = !row_ok ? -1 : (p.causal ? min(kv_len - 1, my_i + delta) : kv_len - 1);
 
-    // ---- Q for the whole kernel: B operand, lane = row, 8 d-values per k-step
+    // ---- Q for the whole kernel: B operand, lane = row, 8 d-values per k-step.
+    // The host folds the sign of the scale into Q (an exact sign flip) and
+    // turns a zero scale into a zero Q, so the kernel always scales by c > 0
+    // and the row max stays a max.
     vec8 qf[KSTEPS];
     {
+        const uint32_t flip = p.q_mode == 1 ? 0x80008000u : 0u;
+        const bool load_q = row_ok && p.q_mode != 2;
         const uint16_t *qrow =
             p.q + (((int64_t)b * p.Sq + my_i) * p.Hq + (int64_t)kvh * p.G + my_gh) * D;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4 raw = {0u, 0u, 0u, 0u};
-            if (row_ok) raw = *(const u32x4 *)(qrow + 16 * ks + 8 * hl);
+            if (load_q) raw = *(const u32x4 *)(qrow + 16 * ks + 8 * hl) ^ flip;
             qf[ks] = __builtin_bit_cast(vec8, raw);
         }
     }
@@ -185,7 +232,7 @@ __global__ __launch_bounds__(kThreadsPerBlock) void attn_fwd_kernel(const FwdPar
     for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-    float m_run = -INFINITY;  // running max of the scaled log2-domain scores
+    float m_run = -INFINITY;  // running (possibly stale) max, scaled log2 units
     float l_run = 0.f;        // this lane's part of the running denominator
 
     // ---- key padding mask: one bit per key of a tile, wave-uniform
@@ -225,53 +272,44 @@ __global__ __launch_bounds__(kThreadsPerBlock) void attn_fwd_kernel(const FwdPar
         return row * hstride + (int64_t)kvh * D;
     };
 
-    // ---- HBM -> registers for one tile (keys >= kv_len read as zero)
-    u32x4 kr[4], vr[4];
-    const int v_unit = tid % VUNITS;
-    const int v_chunk = tid / VUNITS;
-    auto gload = [&](int j0) {
+    // ---- HBM -> LDS, no registers: each of the tile's 16 1-KB pieces is one
+    // global_load_lds_dwordx4 (lane l fills bytes [16l, 16l+16) of its piece);
+    // piece e*4 + wave is this wave's e-th.  Lane l therefore always fills the
+    // same (row, chunk) of every tile: fetch the chunk the swizzle puts there.
+    int ld_row[4], ld_chunk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int byte = (e * 4 + wave) * 1024 + 16 * lane;
+        const int row = byte / (2 * D);
+        const int pos = (byte % (2 * D)) / 16;
+        ld_row[e] = row;
+        ld_chunk[e] = pos ^ swz<D>(row);
+    }
+    auto issue = [&](int j0, uint8_t *dk, uint8_t *dv) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int c = tid + kThreadsPerBlock * e;
-            const int kk = c / DCH, dc = c % DCH;
-            const int j = j0 + kk;
-            kr[e] = u32x4{0u, 0u, 0u, 0u};
-            if (j < kv_len) kr[e] = *(const u32x4 *)(p.k + key_row(j) + dc * 8);
-        }
-        const int jv = j0 + 4 * v_unit;  // 4 consecutive keys, one page (page >= 16)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vr[e] = u32x4{0u, 0u, 0u, 0u};
-        if (jv < kv_len) {
-            const uint16_t *src = p.v + key_row(jv) + v_chunk * 8;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (jv + e < kv_len) vr[e] = *(const u32x4 *)(src + e * hstride);
+            // keys past the end load the last key (finite data, masked below)
+            const int j = min(j0 + ld_row[e], kv_len - 1);
+            const int64_t off = key_row(j) + 8 * ld_chunk[e];
+            const int piece = (e * 4 + wave) * 1024;
+            __builtin_amdgcn_global_load_lds((const void *)(p.k + off), (lds_void *)(dk + piece),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(p.v + off), (lds_void *)(dv + piece),
+                                             16, 0, 0);
         }
     };
 
-    // ---- registers -> LDS (K row-major; V transposed to [d][key])
-    auto lstore = [&]() {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = tid + kThreadsPerBlock * e;
-            const int kk = c / DCH, dc = c % DCH;
-            *(u32x4 *)&sK[kk * KSTR + dc * 8] = kr[e];
-        }
-        const int slot = unit_slot(v_unit);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // dword w of each key row holds d = 2w (low half) and 2w + 1 (high)
-            const u32x2 even = {(vr[0][w] & 0xffffu) | (vr[1][w] << 16),
-                                (vr[2][w] & 0xffffu) | (vr[3][w] << 16)};
-            const u32x2 odd = {(vr[0][w] >> 16) | (vr[1][w] & 0xffff0000u),
-                               (vr[2][w] >> 16) | (vr[3][w] & 0xffff0000u)};
-            *(u32x2 *)&sV[(v_chunk * 8 + 2 * w) * VSTR + slot] = even;
-            *(u32x2 *)&sV[(v_chunk * 8 + 2 * w + 1) * VSTR + slot] = odd;
-        }
-    };
+    const float c = p.scale_log2;  // > 0
+
+    // per-lane constants of the transposing V read: in each 16-lane group,
+    // lane 4r+q points at row r (of 4) and d-columns 4q..4q+3 of its block
+    const int tr_g = lane >> 4;
+    const int tr_row = 4 * (tr_g >> 1) + ((lane & 15) >> 2);
+    const int tr_col = 16 * (tr_g & 1) + 4 * (lane & 3);
 
     // ---- one tile of scores, online softmax and P.V for this wave's rows
-    auto compute = [&](int j0, uint64_t mlo, uint64_t mhi) {
+    auto compute = [&](int j0, uint64_t mlo, uint64_t mhi, const uint8_t *sk,
+                       const uint8_t *sv) {
         f32x16 s[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -280,17 +318,10 @@ __global__ __launch_bounds__(kThreadsPerBlock) void attn_fwd_kernel(const FwdPar
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
                 const vec8 a = __builtin_bit_cast(
-                    vec8, *(const u32x4 *)&sK[(32 * t + l32) * KSTR + 16 * ks + 8 * hl]);
+                    vec8, *(const u32x4 *)(sk + tile_off<D>(32 * t + l32, 2 * ks + hl)));
                 s[t] = H::mfma(a, qf[ks], s[t]);
             }
         }
-        // scale into the log2 domain, then mask (so a negative or zero scale
-        // never meets an infinite score)
-        const float c = p.scale_log2;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[t][r] *= c;
 
         bool full = j0 + BN <= wave_full_end;
         if (has_mask) full = full && (mlo == kLoMask) && (BN <= 64 || mhi == ~0ull);
@@ -303,71 +334,95 @@ __global__ __launch_bounds__(kThreadsPerBlock) void attn_fwd_kernel(const FwdPar
                     // 8*(r/4) + 4*hl + r%4 of the 32-key block
                     const int kk = 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3);
                     bool vis = j0 + kk <= my_last;
-                    if (has_mask) vis = vis && (((kk < 64 ? mlo >> kk : mhi >> (kk - 64)) & 1ull) != 0);
+                    if (has_mask)
+                        vis = vis && (((kk < 64 ? mlo >> kk : mhi >> (kk - 64)) & 1ull) != 0);
                     if (!vis) s[t][r] = -INFINITY;
                 }
         }
 
+        // row max of the raw scores (scaling by c >= 0 keeps the order)
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float corr = fast_exp2(m_run - m_use);
-        float rs = 0.f;
+        const float tile_max = (mx == -INFINITY) ? -INFINITY : mx * c;
+        if (__any(tile_max > m_run + kLazy)) {
+            const float m_new = fmaxf(m_run, tile_max);
+            const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+            l_run *= corr;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = fast_exp2(s[t][r] - m_use);
-                s[t][r] = e;
-                rs += e;
-            }
-        l_run = l_run * corr + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[t][r] *= corr;
+                for (int r = 0; r < 16; ++r) acc[t][r] *= corr;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-        // P^T as the B operand: k-step kk takes registers 8u..8u+7 of block kk/2
+        // P = exp2(c*s - m) rounded to 16 bits: the B operand of P.V; the row
+        // sum adds the rounded values, the ones P.V actually uses
         vec8 pb[PSTEPS];
+        float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
         for (int kk = 0; kk < PSTEPS; ++kk) {
             const int t = kk >> 1, u = kk & 1;
             u32x4 packed;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                packed[e] = pack_half2<BF16>(s[t][8 * u + 2 * e], s[t][8 * u + 2 * e + 1]);
+            for (int e = 0; e < 4; ++e) {
+                const float e0 = fast_exp2(__builtin_fmaf(s[t][8 * u + 2 * e], c, -m_use));
+                const float e1 = fast_exp2(__builtin_fmaf(s[t][8 * u + 2 * e + 1], c, -m_use));
+                packed[e] = pack_half2<BF16>(e0, e1);
+                if (e & 1)
+                    rs1 = add_pair<BF16>(packed[e], rs1);
+                else
+                    rs0 = add_pair<BF16>(packed[e], rs0);
+            }
             pb[kk] = __builtin_bit_cast(vec8, packed);
         }
+        l_run += rs0 + rs1;
+
+        // O^T += V^T P^T; the V^T operand comes from two transposing reads of
+        // 4 keys each (k-slots 0..3 and 4..7 of this lane half)
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
             for (int kk = 0; kk < PSTEPS; ++kk) {
-                const vec8 a = __builtin_bit_cast(
-                    vec8, *(const u32x4 *)&sV[(32 * t + l32) * VSTR + 16 * kk + 8 * hl]);
+                const int row = 16 * kk + tr_row;
+                const int col = 32 * t + tr_col;
+                const int within = (col & 7) * 2;
+                const s16x4 lo =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(sv + tile_off<D>(row, col >> 3) + within));
+                const s16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(sv + tile_off<D>(row + 8, col >> 3) + within));
+                const short vals[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                vec8 a;
+                __builtin_memcpy(&a, vals, sizeof a);
                 acc[t] = H::mfma(a, pb[kk], acc[t]);
             }
     };
 
-    // ---- main loop: one tile in LDS, the next one in flight to registers
-    uint64_t cur_lo = ~0ull, cur_hi = ~0ull, nxt_lo = ~0ull, nxt_hi = ~0ull;
-    int cur = find_tile(kbeg, cur_lo, cur_hi);
-    if (cur < wg_end) gload(cur);
+    // ---- main loop: a two-stage LDS ring; while the waves compute one tile
+    // the next one streams from HBM straight into the other stage
+    uint64_t lo0 = ~0ull, hi0 = ~0ull, lo1 = ~0ull, hi1 = ~0ull;
+    int cur = find_tile(kbeg, lo0, hi0);
+    if (cur < wg_end) issue(cur, sK0, sV0);
     while (cur < wg_end) {
-        __syncthreads();  // every wave is done reading the previous tile
-        lstore();
+        // stage 0 holds tile `cur`
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        const int nxt = find_tile(cur + BN, nxt_lo, nxt_hi);
-        if (nxt < wg_end) gload(nxt);
-        if (wave_active && cur < wave_end) compute(cur, cur_lo, cur_hi);
+        int nxt = find_tile(cur + BN, lo1, hi1);
+        if (nxt < wg_end) issue(nxt, sK1, sV1);
+        if (wave_active && cur < wave_end) compute(cur, lo0, hi0, sK0, sV0);
         cur = nxt;
-        cur_lo = nxt_lo;
-        cur_hi = nxt_hi;
+        if (cur >= wg_end) break;
+        // stage 1 holds tile `cur`
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        nxt = find_tile(cur + BN, lo0, hi0);
+        if (nxt < wg_end) issue(nxt, sK0, sV0);
+        if (wave_active && cur < wave_end) compute(cur, lo1, hi1, sK1, sV1);
+        cur = nxt;
     }
 
     // ---- epilogue: normalise and store (no barrier below this point)

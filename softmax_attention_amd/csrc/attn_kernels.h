@@ -39,7 +39,8 @@ struct FwdParams {
     int n_splits;    // key-range splits per (batch, KV head)
     int split_len;   // keys per split, a multiple of the key tile
     int causal;
-    float scale_log2;  // alpha * log2(e)
+    float scale_log2;  // |alpha| * log2(e)
+    int q_mode;        // 0: q as given; 1: q negated (alpha < 0); 2: q zeroed (alpha == 0)
     int xcd_units;     // (batch*KV head, split) units per XCD, or 0 for linear order
 };
 

@@ -108,9 +108,9 @@ hipError_t timed_launch(int kind, hipStream_t stream, Launch &&launch) {
     if (e != hipSuccess) return e;
     e = hipEventCreate(&b);
     if (e != hipSuccess) return e;
-    hipEventRecord(a, stream);
+    (void)hipEventRecord(a, stream);
     e = launch();
-    hipEventRecord(b, stream);
+    (void)hipEventRecord(b, stream);
     std::lock_guard<std::mutex> lock(g_prof_mu);
     g_prof.ev[kind].push_back({a, b});
     return e;
@@ -148,6 +148,20 @@ miattn_status check_common(const void *q, const void *o, float *lse, int B, int 
 
 float resolve_scale(float scale, int D) {
     return isnan(scale) ? (float)(1.0 / sqrt((double)D)) : scale;
+}
+
+// The kernels take exp2 of scores scaled by a positive factor c = |alpha|
+// log2(e).  A negative alpha is applied by negating q inside the kernel (an
+// exact sign flip); alpha == 0 makes every visible score equal, which the
+// kernel reproduces exactly by zeroing q (and using c = 1).
+void set_scale(FwdParams &p, float alpha) {
+    if (alpha == 0.f) {
+        p.q_mode = 2;
+        p.scale_log2 = 1.f;
+    } else {
+        p.q_mode = alpha < 0.f ? 1 : 0;
+        p.scale_log2 = fabsf(alpha) * 1.4426950408889634f;
+    }
 }
 
 int env_int(const char *name, int dflt) {
@@ -280,7 +294,7 @@ miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B,
     p.Hkv = Hkv;
     p.Skv = Skv;
     p.causal = causal;
-    p.scale_log2 = resolve_scale(scale, D) * 1.4426950408889634f;
+    set_scale(p, resolve_scale(scale, D));
     return run(p, D, dtype == MIATTN_BF16, false, Skv, (hipStream_t)stream);
 }
 
@@ -361,7 +375,7 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
     p.page_shift = page_shift;
     p.max_pages = max_pages;
     p.causal = causal;
-    p.scale_log2 = resolve_scale(scale, D) * 1.4426950408889634f;
+    set_scale(p, resolve_scale(scale, D));
     return run(p, D, dtype == MIATTN_BF16, true, capacity, (hipStream_t)stream);
 }
 
@@ -388,8 +402,8 @@ void miattn_profile_start(void) {
     std::lock_guard<std::mutex> lock(g_prof_mu);
     for (auto &v : g_prof.ev)
         for (auto &pr : v) {
-            hipEventDestroy(pr.first);
-            hipEventDestroy(pr.second);
+            (void)hipEventDestroy(pr.first);
+            (void)hipEventDestroy(pr.second);
         }
     g_prof.ev[0].clear();
     g_prof.ev[1].clear();
@@ -414,8 +428,8 @@ miattn_status miattn_profile_stop(double *attn_ms, int *attn_launches, double *m
             if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
             if (e != hipSuccess && st == MIATTN_OK) st = hip_fail(e, "hipEventElapsedTime");
             tot[kind] += ms;
-            hipEventDestroy(pr.first);
-            hipEventDestroy(pr.second);
+            (void)hipEventDestroy(pr.first);
+            (void)hipEventDestroy(pr.second);
         }
     if (attn_ms) *attn_ms = tot[0];
     if (attn_launches) *attn_launches = (int)ev[0].size();
