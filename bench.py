@@ -142,6 +142,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one workload and print its line (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy 5 times and exit: the "
+                         "reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
@@ -157,6 +162,21 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     mi.lib()
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}), flush=True)
+        return
+    if args.only == "decode":
+        wd = workloads.make(3)
+        d = time_decode(mi, wd, max(args.steps, 10), args.warmup)
+        nbytes = kv_bytes(wd.kv_lengths(), wd.Hkv, wd.D)
+        print(json.dumps({"workload": wd.name, "kv_bytes": nbytes, **d}), flush=True)
+        return
 
     w = workloads.make(2)
     flops = 4.0 * w.D * visible_pairs(w.B, w.Hq, w.Sq, [w.Skv] * w.B, True)
@@ -190,6 +210,9 @@ def main():
                      "kernel_avg_us": ms_kernel * 1e3},
     }
     del w
+    if args.only == "prefill":
+        print(json.dumps(line), flush=True)
+        return
 
     if not args.no_decode:
         wd = workloads.make(3)

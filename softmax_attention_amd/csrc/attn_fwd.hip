@@ -40,6 +40,8 @@
 //     skipped before their K/V is loaded.
 #include "attn_kernels.h"
 
+#include <type_traits>
+
 namespace miattn {
 namespace {
 
@@ -95,12 +97,19 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // (chunk c sits at position c ^ swz(r)) so that both read patterns below hit
 // distinct LDS banks: the QK^T operand (16 rows, one chunk each) and the
 // transposing V read (4 consecutive rows, two adjacent chunks each).
+//
+// For D >= 128 the swizzle is a bit permutation of row & 15 (bits 0,1,2,3 of
+// the row go to bits 2,3,1,0 of the chunk mask): any 16 consecutive rows get
+// 16 distinct masks (conflict-free K reads), and the four rows a transposing
+// read gathers differ in the mask's upper bits, so the two chunk pairs that
+// neighbouring 16-lane groups fetch never share a bank.  Measured on gfx950:
+// ~190 B/clk/CU for the K reads and ~124 B/clk/CU for the transposing reads.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (D == 64)
         return ((row >> 1) & 3) * 2 + ((row >> 3) & 1);
     else
-        return (row & 7) * 2 + ((row >> 3) & 1);
+        return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
 }
 
 template <int D>
@@ -132,6 +141,11 @@ constexpr float kLazy = 8.0f;
 
 template <int D>
 constexpr int waves_per_eu() { return D <= 128 ? 2 : 1; }
+
+#ifndef MIATTN_VALU_PER_MFMA
+#define MIATTN_VALU_PER_MFMA 6
+#endif
+constexpr int kValuPerMfma = MIATTN_VALU_PER_MFMA;
 
 template <int D, bool BF16, bool PAGED>
 __global__ __launch_bounds__(kThreadsPerBlock)
@@ -259,110 +273,127 @@ void attn_fwd_kernel(const FwdParams p) {
         return wg_end;
     };
 
-    // ---- element offset of key j's row for this KV head
-    const int64_t hstride = (int64_t)p.Hkv * D;
-    auto key_row = [&](int j) -> int64_t {
-        int64_t row;
-        if (PAGED) {
-            const int page = p.block_table[(int64_t)b * p.max_pages + (j >> p.page_shift)];
-            row = ((int64_t)page << p.page_shift) + (j & ((1 << p.page_shift) - 1));
-        } else {
-            row = (int64_t)b * p.Skv + j;
-        }
-        return row * hstride + (int64_t)kvh * D;
-    };
-
     // ---- HBM -> LDS, no registers: each of the tile's 16 1-KB pieces is one
     // global_load_lds_dwordx4 (lane l fills bytes [16l, 16l+16) of its piece);
     // piece e*4 + wave is this wave's e-th.  Lane l therefore always fills the
     // same (row, chunk) of every tile: fetch the chunk the swizzle puts there.
-    int ld_row[4], ld_chunk[4];
+    const int64_t hstride = (int64_t)p.Hkv * D;  // elements between consecutive keys
+    int ld_row[4];
+    int64_t ld_base[4];  // element offset of this lane's chunk, key row 0
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int byte = (e * 4 + wave) * 1024 + 16 * lane;
         const int row = byte / (2 * D);
         const int pos = (byte % (2 * D)) / 16;
         ld_row[e] = row;
-        ld_chunk[e] = pos ^ swz<D>(row);
+        ld_base[e] = (int64_t)kvh * D + 8 * (pos ^ swz<D>(row)) +
+                     (PAGED ? 0 : (int64_t)b * p.Skv * hstride);
     }
-    auto issue = [&](int j0, uint8_t *dk, uint8_t *dv) {
+    // a page holds whole tiles when page_size >= BN: one page per tile
+    const bool page_per_tile = PAGED && p.page_shift >= __builtin_ctz(BN);
+    const int32_t *bt_row = PAGED ? p.block_table + (int64_t)b * p.max_pages : nullptr;
+    auto issue = [&](int j0, const uint16_t *src, uint8_t *dst) {
+        int64_t tile_page_row = 0;
+        if (page_per_tile) tile_page_row = (int64_t)bt_row[j0 >> p.page_shift] << p.page_shift;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // keys past the end load the last key (finite data, masked below)
+            // keys past the end load the last key (finite data, masked later)
             const int j = min(j0 + ld_row[e], kv_len - 1);
-            const int64_t off = key_row(j) + 8 * ld_chunk[e];
-            const int piece = (e * 4 + wave) * 1024;
-            __builtin_amdgcn_global_load_lds((const void *)(p.k + off), (lds_void *)(dk + piece),
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(p.v + off), (lds_void *)(dv + piece),
-                                             16, 0, 0);
+            int64_t row;
+            if (!PAGED)
+                row = j;
+            else if (page_per_tile)
+                row = tile_page_row + (j & ((1 << p.page_shift) - 1));
+            else
+                row = ((int64_t)bt_row[j >> p.page_shift] << p.page_shift) +
+                      (j & ((1 << p.page_shift) - 1));
+            const int64_t off = ld_base[e] + row * hstride;
+            __builtin_amdgcn_global_load_lds((const void *)(src + off),
+                                             (lds_void *)(dst + (e * 4 + wave) * 1024), 16, 0, 0);
         }
     };
+    auto issue_k = [&](int j0, uint8_t *dst) { issue(j0, p.k, dst); };
+    auto issue_v = [&](int j0, uint8_t *dst) { issue(j0, p.v, dst); };
 
     const float c = p.scale_log2;  // > 0
 
-    // per-lane constants of the transposing V read: in each 16-lane group,
-    // lane 4r+q points at row r (of 4) and d-columns 4q..4q+3 of its block
+    // ---- LDS read addresses, fixed per lane for the whole kernel.  With the
+    // swizzle depending on row & 15 only, the 32-key block t and the 16-key
+    // step kk move a read by whole rows (an immediate offset); only the chunk
+    // index varies with the swizzle, so one byte offset per chunk position is
+    // kept in a register.
+    //   K (QK^T A operand): lane reads row 32t + l32, chunk 2ks + hl.
+    //   V (transposing read): in each 16-lane group g, lane 4r+q reads row
+    //   4*(g/2) + r (+8 for k-slots 4..7) of the 16-key step, d-columns
+    //   32t + 16*(g%2) + 4q .. +3.
+    int k_addr[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) k_addr[ks] = tile_off<D>(l32, 2 * ks + hl);
     const int tr_g = lane >> 4;
     const int tr_row = 4 * (tr_g >> 1) + ((lane & 15) >> 2);
     const int tr_col = 16 * (tr_g & 1) + 4 * (lane & 3);
+    int v_addr[DT][2];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int col = 32 * t + tr_col;
+            v_addr[t][h] = tile_off<D>(tr_row + 8 * h, col >> 3) + (col & 7) * 2;
+        }
 
-    // ---- one tile of scores, online softmax and P.V for this wave's rows
-    auto compute = [&](int j0, uint64_t mlo, uint64_t mhi, const uint8_t *sk,
-                       const uint8_t *sv) {
-        f32x16 s[NT];
+    // ---- S^T = K Q^T for one tile (K from an LDS stage)
+    auto qk = [&](const uint8_t *sk, f32x16 (&sc)[NT]) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
+            for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
                 const vec8 a = __builtin_bit_cast(
-                    vec8, *(const u32x4 *)(sk + tile_off<D>(32 * t + l32, 2 * ks + hl)));
-                s[t] = H::mfma(a, qf[ks], s[t]);
+                    vec8, *(const u32x4 *)(sk + k_addr[ks] + 32 * t * (2 * D)));
+                sc[t] = H::mfma(a, qf[ks], sc[t]);
             }
         }
+    };
 
-        bool full = j0 + BN <= wave_full_end;
-        if (has_mask) full = full && (mlo == kLoMask) && (BN <= 64 || mhi == ~0ull);
-        if (!full) {
+    // ---- online softmax of one tile's scores: masks (MASKED tiles only), the
+    // lazy max update, P rounded to 16 bits as the B operand of P.V, and the
+    // running denominator.  Branch-free, so that the scheduler can interleave
+    // it with the next tile's QK^T MFMAs.  Returns the factor the output
+    // accumulator must be multiplied by (1 when the max did not move).
+    auto softmax = [&](auto masked_tag, int j0, uint64_t mlo, uint64_t mhi, f32x16 (&sc)[NT],
+                       vec8 (&pb)[PSTEPS]) -> float {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        if constexpr (MASKED) {
+            // S^T layout: register r of lane half hl holds key
+            // 32t + 8*(r/4) + 4*hl + r%4 of the tile
+            const int lim = my_last - j0 - 4 * hl;
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT; ++t) {
+                uint32_t w = ~0u;
+                if (has_mask) w = (uint32_t)((t < 2 ? mlo : mhi) >> (32 * (t & 1) + 4 * hl));
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    // S^T layout: register r of lane half hl holds key
-                    // 8*(r/4) + 4*hl + r%4 of the 32-key block
-                    const int kk = 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    bool vis = j0 + kk <= my_last;
-                    if (has_mask)
-                        vis = vis && (((kk < 64 ? mlo >> kk : mhi >> (kk - 64)) & 1ull) != 0);
-                    if (!vis) s[t][r] = -INFINITY;
+                    const int kc = 32 * t + 8 * (r >> 2) + (r & 3);
+                    const bool vis = (kc <= lim) && ((w >> (8 * (r >> 2) + (r & 3))) & 1u);
+                    sc[t][r] = vis ? sc[t][r] : -INFINITY;
                 }
+            }
         }
-
-        // row max of the raw scores (scaling by c >= 0 keeps the order)
+        // row max of the raw scores (scaling by c > 0 keeps the order)
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float tile_max = (mx == -INFINITY) ? -INFINITY : mx * c;
-        if (__any(tile_max > m_run + kLazy)) {
-            const float m_new = fmaxf(m_run, tile_max);
-            const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-            l_run *= corr;
-#pragma unroll
-            for (int t = 0; t < DT; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[t][r] *= corr;
-            m_run = m_new;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        const bool raise = __any(tile_max > m_run + kLazy);
+        const float m_new = raise ? fmaxf(m_run, tile_max) : m_run;
+        const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
 
-        // P = exp2(c*s - m) rounded to 16 bits: the B operand of P.V; the row
-        // sum adds the rounded values, the ones P.V actually uses
-        vec8 pb[PSTEPS];
         float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
         for (int kk = 0; kk < PSTEPS; ++kk) {
@@ -370,8 +401,8 @@ void attn_fwd_kernel(const FwdParams p) {
             u32x4 packed;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float e0 = fast_exp2(__builtin_fmaf(s[t][8 * u + 2 * e], c, -m_use));
-                const float e1 = fast_exp2(__builtin_fmaf(s[t][8 * u + 2 * e + 1], c, -m_use));
+                const float e0 = fast_exp2(__builtin_fmaf(sc[t][8 * u + 2 * e], c, -m_use));
+                const float e1 = fast_exp2(__builtin_fmaf(sc[t][8 * u + 2 * e + 1], c, -m_use));
                 packed[e] = pack_half2<BF16>(e0, e1);
                 if (e & 1)
                     rs1 = add_pair<BF16>(packed[e], rs1);
@@ -380,49 +411,114 @@ void attn_fwd_kernel(const FwdParams p) {
             }
             pb[kk] = __builtin_bit_cast(vec8, packed);
         }
-        l_run += rs0 + rs1;
+        l_run = __builtin_fmaf(l_run, corr, rs0 + rs1);
+        return corr;
+    };
 
-        // O^T += V^T P^T; the V^T operand comes from two transposing reads of
-        // 4 keys each (k-slots 0..3 and 4..7 of this lane half)
+    // ---- O^T += V^T P^T; the V^T operand comes from two transposing reads of
+    // 4 keys each (k-slots 0..3 and 4..7 of this lane half)
+    auto pv = [&](const uint8_t *sv, const vec8 (&pb)[PSTEPS]) {
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
             for (int kk = 0; kk < PSTEPS; ++kk) {
-                const int row = 16 * kk + tr_row;
-                const int col = 32 * t + tr_col;
-                const int within = (col & 7) * 2;
-                const s16x4 lo =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(sv + tile_off<D>(row, col >> 3) + within));
-                const s16x4 hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(sv + tile_off<D>(row + 8, col >> 3) + within));
-                const short vals[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                vec8 a;
-                __builtin_memcpy(&a, vals, sizeof a);
+                const int step = 16 * kk * (2 * D);
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(sv + v_addr[t][0] + step));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(sv + v_addr[t][1] + step));
+                const vec8 a = __builtin_bit_cast(
+                    vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 acc[t] = H::mfma(a, pb[kk], acc[t]);
             }
     };
 
-    // ---- main loop: a two-stage LDS ring; while the waves compute one tile
-    // the next one streams from HBM straight into the other stage
-    uint64_t lo0 = ~0ull, hi0 = ~0ull, lo1 = ~0ull, hi1 = ~0ull;
-    int cur = find_tile(kbeg, lo0, hi0);
-    if (cur < wg_end) issue(cur, sK0, sV0);
+    // ---- scheduling hint for a block holding the next tile's QK^T and this
+    // tile's softmax: alternate one K read, one MFMA and a few VALU
+    // (transcendental included) instructions, so the MFMA pipe is fed while
+    // the softmax runs
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < NT * KSTEPS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x402, kValuPerMfma, 0);  // VALU + TRANS
+        }
+    };
+
+    // ---- one pipeline step for this wave: softmax and P.V of tile `cur`
+    // (scores already in sc_cur, V in stage sv), overlapped with QK^T of tile
+    // `nxt` (K in stage sk) into sc_nxt
+    auto step = [&](int cur, uint64_t mlo, uint64_t mhi, int nxt, f32x16 (&sc_cur)[NT],
+                    f32x16 (&sc_nxt)[NT], const uint8_t *sk, const uint8_t *sv) {
+        if (!(wave_active && cur < wave_end)) return;  // nothing for this wave any more
+        bool full = cur + BN <= wave_full_end;
+        if (has_mask) full = full && (mlo == kLoMask) && (BN <= 64 || mhi == ~0ull);
+        vec8 pb[PSTEPS];
+        float corr;
+        if (nxt < wave_end) {
+            if (full) {
+                qk(sk, sc_nxt);
+                corr = softmax(std::false_type{}, cur, mlo, mhi, sc_cur, pb);
+                interleave();
+            } else {
+                qk(sk, sc_nxt);
+                corr = softmax(std::true_type{}, cur, mlo, mhi, sc_cur, pb);
+                interleave();
+            }
+        } else {
+            if (full)
+                corr = softmax(std::false_type{}, cur, mlo, mhi, sc_cur, pb);
+            else
+                corr = softmax(std::true_type{}, cur, mlo, mhi, sc_cur, pb);
+        }
+        if (corr != 1.f) {
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[t][r] *= corr;
+        }
+        pv(sv, pb);
+    };
+
+    // ---- main loop.  K and V have rings of two stages each.  At the start of
+    // the step for tile `cur`: its scores are in registers, its V is in one V
+    // stage and the next tile's K in one K stage; the step streams the K of
+    // the tile after next and the V of the next tile into the free stages
+    // (straight from HBM, no registers) while the waves compute.
+    uint64_t mc_lo = ~0ull, mc_hi = ~0ull, mn_lo = ~0ull, mn_hi = ~0ull, m2_lo = ~0ull,
+             m2_hi = ~0ull;
+    f32x16 scA[NT], scB[NT];
+    int cur = find_tile(kbeg, mc_lo, mc_hi);
+    int nxt = cur < wg_end ? find_tile(cur + BN, mn_lo, mn_hi) : wg_end;
+    if (cur < wg_end) {
+        issue_k(cur, sK0);
+        issue_v(cur, sV0);
+    }
+    if (nxt < wg_end) issue_k(nxt, sK1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (wave_active && cur < wave_end) qk(sK0, scA);
     while (cur < wg_end) {
-        // stage 0 holds tile `cur`
+        // tile cur: scores in scA, V in sV0; tile nxt: K in sK1
+        int nxt2 = nxt < wg_end ? find_tile(nxt + BN, m2_lo, m2_hi) : wg_end;
+        if (nxt2 < wg_end) issue_k(nxt2, sK0);
+        if (nxt < wg_end) issue_v(nxt, sV1);
+        step(cur, mc_lo, mc_hi, nxt, scA, scB, sK1, sV0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        int nxt = find_tile(cur + BN, lo1, hi1);
-        if (nxt < wg_end) issue(nxt, sK1, sV1);
-        if (wave_active && cur < wave_end) compute(cur, lo0, hi0, sK0, sV0);
-        cur = nxt;
+        cur = nxt; mc_lo = mn_lo; mc_hi = mn_hi;
+        nxt = nxt2; mn_lo = m2_lo; mn_hi = m2_hi;
         if (cur >= wg_end) break;
-        // stage 1 holds tile `cur`
+        // tile cur: scores in scB, V in sV1; tile nxt: K in sK0
+        nxt2 = nxt < wg_end ? find_tile(nxt + BN, m2_lo, m2_hi) : wg_end;
+        if (nxt2 < wg_end) issue_k(nxt2, sK1);
+        if (nxt < wg_end) issue_v(nxt, sV0);
+        step(cur, mc_lo, mc_hi, nxt, scB, scA, sK0, sV1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        nxt = find_tile(cur + BN, lo0, hi0);
-        if (nxt < wg_end) issue(nxt, sK0, sV0);
-        if (wave_active && cur < wave_end) compute(cur, lo1, hi1, sK1, sV1);
-        cur = nxt;
+        cur = nxt; mc_lo = mn_lo; mc_hi = mn_hi;
+        nxt = nxt2; mn_lo = m2_lo; mn_hi = m2_hi;
     }
 
     // ---- epilogue: normalise and store (no barrier below this point)
