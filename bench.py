@@ -47,6 +47,26 @@ def visible_pairs(B, Hq, Sq, kv_lens, causal, keep_counts=None):
     return total * Hq
 
 
+def measured_traffic(kind):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    record (profiles/traffic.json), or None when the kernel sources changed
+    since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    for src, digest in rec.get("kernel_sources_sha256", {}).items():
+        full = os.path.join(ROOT, src)
+        if not os.path.exists(full):
+            return None
+        with open(full, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return rec.get(kind, {}).get("hbm_bytes")
+
+
 def kv_bytes(kv_lens, Hkv, D, elem_bytes=2):
     return sum(kv_lens) * Hkv * D * elem_bytes * 2
 
@@ -138,8 +158,8 @@ def cpu_baseline(w, target_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
@@ -205,7 +225,8 @@ def main():
                    "Skv": w.Skv, "D": w.D, "causal": True, "scale": w.scale,
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic("prefill"),
                      "kernel": "attn_fwd_kernel<128, bf16, dense>",
                      "kernel_avg_us": ms_kernel * 1e3},
     }
@@ -227,7 +248,8 @@ def main():
             "workload": wd.name, "value": call_gbs, "unit": "GB/s", "kv_bytes": nbytes,
             "median_call_us": d["median_call_ms"] * 1e3, "min_call_us": d["min_call_ms"] * 1e3,
             "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": kern_gbs / PEAK_HBM_GBS, "traffic": None,
+                         "unit": "GB/s", "frac": kern_gbs / PEAK_HBM_GBS,
+                         "traffic": measured_traffic("decode"),
                          "kernel": "attn_fwd_kernel<128, bf16, paged>",
                          "kernel_avg_us": d["attn_kernel_ms"] * 1e3,
                          "merge_kernel_avg_us": d["merge_kernel_ms"] * 1e3}}
