@@ -1,0 +1,118 @@
+// attn_device.h -- device-side helpers shared by the attention kernels of
+// libmiattn (internal): vector types, the 32x32x16 MFMA per input type,
+// 16-bit packing, the LDS tile swizzle and the lazy-max threshold.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miattn {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <bool BF16>
+struct Half;
+
+template <>
+struct Half<true> {
+    using vec8 = bf16x8;
+    using scalar = __bf16;
+    static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Half<false> {
+    using vec8 = f16x8;
+    using scalar = _Float16;
+    static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Round-to-nearest-even conversion of two floats into one packed dword (a
+// single v_cvt_pk_{bf16,f16}_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    if constexpr (BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- LDS tiles.  A K or V tile is stored row-major (one key per row, D
+// contiguous) without padding; the 16-byte chunks of row r are XOR-swizzled
+// (chunk c sits at position c ^ swz(r)) so that both read patterns below hit
+// distinct LDS banks: the QK^T operand (16 rows, one chunk each) and the
+// transposing V read (4 consecutive rows, two adjacent chunks each).
+//
+// For D >= 128 the swizzle is a bit permutation of row & 15 (bits 0,1,2,3 of
+// the row go to bits 2,3,1,0 of the chunk mask): any 16 consecutive rows get
+// 16 distinct masks (conflict-free K reads), and the four rows a transposing
+// read gathers differ in the mask's upper bits, so the two chunk pairs that
+// neighbouring 16-lane groups fetch never share a bank.  Measured on gfx950:
+// ~190 B/clk/CU for the K reads and ~124 B/clk/CU for the transposing reads.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 64)
+        return ((row >> 1) & 3) * 2 + ((row >> 3) & 1);
+    else
+        return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
+}
+
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {  // bytes
+    return row * (2 * D) + 16 * (chunk ^ swz<D>(row));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Sum of the two 16-bit values packed in `pk`, accumulated into acc in FP32.
+template <bool BF16>
+__device__ __forceinline__ float add_pair(uint32_t pk, float acc) {
+    if constexpr (BF16)
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
+                                               false);
+    else
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk),
+                                      __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+}
+
+// The running max is only raised when a tile's max exceeds it by more than
+// this many powers of two; until then exponentials are taken against the
+// stale max (bounded by 2^kLazy), which leaves the result unchanged in exact
+// arithmetic and saves rescaling O for almost every tile.
+constexpr float kLazy = 8.0f;
+
+// Workgroup barrier for the K/V rings.  __syncthreads() is a workgroup-scope
+// release/acquire fence around s_barrier, and the release half waits for every
+// outstanding global load (vmcnt(0)) -- which would drain the whole ring at
+// each barrier.  The rings order their loads with explicit, counted vmcnt
+// waits instead; the barrier itself only needs this wave's LDS reads done
+// (so a stage can be refilled) and must keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace dev
+}  // namespace miattn

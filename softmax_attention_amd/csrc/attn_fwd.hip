@@ -42,124 +42,60 @@
 
 #include <type_traits>
 
+#include "attn_device.h"
+
 namespace miattn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace dev;
 
-constexpr float kLn2 = 0.6931471805599453f;
 
-template <bool BF16>
-struct Half;
-
-template <>
-struct Half<true> {
-    using vec8 = bf16x8;
-    using scalar = __bf16;
-    static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-};
-
-template <>
-struct Half<false> {
-    using vec8 = f16x8;
-    using scalar = _Float16;
-    static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-};
-
-// Round-to-nearest-even conversion of two floats into one packed dword (a
-// single v_cvt_pk_{bf16,f16}_f32).
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-template <bool BF16>
-__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
-    const f32x2 v = {lo, hi};
-    if constexpr (BF16)
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-    else
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// ---- LDS tiles.  A K or V tile is stored row-major (one key per row, D
-// contiguous) without padding; the 16-byte chunks of row r are XOR-swizzled
-// (chunk c sits at position c ^ swz(r)) so that both read patterns below hit
-// distinct LDS banks: the QK^T operand (16 rows, one chunk each) and the
-// transposing V read (4 consecutive rows, two adjacent chunks each).
-//
-// For D >= 128 the swizzle is a bit permutation of row & 15 (bits 0,1,2,3 of
-// the row go to bits 2,3,1,0 of the chunk mask): any 16 consecutive rows get
-// 16 distinct masks (conflict-free K reads), and the four rows a transposing
-// read gathers differ in the mask's upper bits, so the two chunk pairs that
-// neighbouring 16-lane groups fetch never share a bank.  Measured on gfx950:
-// ~190 B/clk/CU for the K reads and ~124 B/clk/CU for the transposing reads.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (D == 64)
-        return ((row >> 1) & 3) * 2 + ((row >> 3) & 1);
-    else
-        return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
-}
-
-template <int D>
-__device__ __forceinline__ int tile_off(int row, int chunk) {  // bytes
-    return row * (2 * D) + 16 * (chunk ^ swz<D>(row));
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Sum of the two 16-bit values packed in `pk`, accumulated into acc in FP32.
-template <bool BF16>
-__device__ __forceinline__ float add_pair(uint32_t pk, float acc) {
-    if constexpr (BF16)
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
-                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
-                                               false);
-    else
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk),
-                                      __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
-}
-
-// The running max is only raised when a tile's max exceeds it by more than
-// this many powers of two; until then exponentials are taken against the
-// stale max (bounded by 2^kLazy), which leaves the result unchanged in exact
-// arithmetic and saves rescaling O for almost every tile.
-constexpr float kLazy = 8.0f;
-
-template <int D>
-constexpr int waves_per_eu() { return D <= 128 ? 2 : 1; }
+// Waves per SIMD the register budget is sized for: the 8-wave schedule needs
+// its two waves per SIMD; the 4-wave one runs two workgroups per CU for
+// D <= 128 and one for D = 256 (whose accumulators alone take 128 registers).
+template <int D, int WAVES>
+constexpr int waves_per_eu() { return (WAVES == 8 || D <= 128) ? 2 : 1; }
 
 #ifndef MIATTN_VALU_PER_MFMA
 #define MIATTN_VALU_PER_MFMA 6
 #endif
 constexpr int kValuPerMfma = MIATTN_VALU_PER_MFMA;
 
-template <int D, bool BF16, bool PAGED>
-__global__ __launch_bounds__(kThreadsPerBlock)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu<D>(), waves_per_eu<D>())))
+#ifndef MIATTN_READ_AHEAD
+#define MIATTN_READ_AHEAD 6
+#endif
+constexpr int kReadAhead = MIATTN_READ_AHEAD;
+
+// Scheduling hint for a block of LDS operand reads feeding MFMAs: issue
+// kReadAhead reads first, then keep about that many in flight ahead of the
+// MFMAs that consume them, so the matrix core does not wait out each read.
+template <int N_READS, int N_MFMA>
+__device__ __forceinline__ void sched_read_ahead() {
+    constexpr int per = (N_READS - kReadAhead + N_MFMA - 1) / N_MFMA;
+    __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);  // DS read
+#pragma unroll
+    for (int i = 0; i < N_MFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, per, 0);  // DS read
+    }
+}
+
+template <int D, bool BF16, bool PAGED, int WAVES>
+__global__ __launch_bounds__(64 * WAVES)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<D, WAVES>(), waves_per_eu<D, WAVES>())))
 void attn_fwd_kernel(const FwdParams p) {
     using H = Half<BF16>;
     using vec8 = typename H::vec8;
-    constexpr int BN = keys_per_tile(D);   // keys per tile
-    constexpr int TILE_BYTES = BN * D * 2; // 16 KB for K, the same for V
-    constexpr int NT = BN / 32;            // 32-key score blocks per tile
-    constexpr int KSTEPS = D / 16;         // MFMA k-steps over D
-    constexpr int DT = D / 32;             // 32-wide d blocks of O^T
-    constexpr int PSTEPS = BN / 16;        // MFMA k-steps over the tile's keys
-    static_assert(TILE_BYTES == 16 * 1024, "one tile = 16 direct 1 KB loads");
+    constexpr int BM = rows_per_workgroup(WAVES);  // packed rows per workgroup
+    constexpr int BN = keys_per_tile(D, WAVES);    // keys per tile
+    constexpr int TILE_BYTES = BN * D * 2;         // one K (or V) tile
+    constexpr int PIECES = TILE_BYTES / 1024;      // 1 KB direct loads per tile
+    constexpr int PPW = PIECES / WAVES;            // of them per wave
+    constexpr int NT = BN / 32;                    // 32-key score blocks per tile
+    constexpr int KSTEPS = D / 16;                 // MFMA k-steps over D
+    constexpr int DT = D / 32;                     // 32-wide d blocks of O^T
+    constexpr int PSTEPS = BN / 16;                // MFMA k-steps over the tile's keys
+    static_assert(PIECES % WAVES == 0, "whole 1 KB pieces per wave");
 
     // two stages of (K tile, V tile); separate arrays so the compiler can
     // tell a load into one stage from reads of the other
@@ -180,7 +116,13 @@ void attn_fwd_kernel(const FwdParams p) {
     // so its K/V stays in that XCD's L2.  Causal row blocks run heaviest first.
     const int units = p.B * p.Hkv * p.n_splits;
     int rank, unit;
-    if (p.xcd_units > 0) {
+    if (p.xcd_units > 0 && p.xcd_unit_major) {
+        // each XCD finishes the row blocks of one unit before the next, so its
+        // L2 holds one (batch, KV head)'s K/V at a time
+        const int s = blockIdx.x >> 3;
+        unit = (blockIdx.x & 7) * p.xcd_units + s / p.n_mblocks;
+        rank = s % p.n_mblocks;
+    } else if (p.xcd_units > 0) {
         const int s = blockIdx.x >> 3;
         unit = (blockIdx.x & 7) * p.xcd_units + s % p.xcd_units;
         rank = s / p.xcd_units;
@@ -202,8 +144,8 @@ void attn_fwd_kernel(const FwdParams p) {
     const int kend = min(kv_len, kbeg + p.split_len);
     const int delta = kv_len - p.Sq;  // query i sits at key position i + delta
 
-    const int row0 = mblock * kRowsPerBlock;
-    const int row_last = min(p.rows, row0 + kRowsPerBlock) - 1;
+    const int row0 = mblock * BM;
+    const int row_last = min(p.rows, row0 + BM) - 1;
     const int wg_end = p.causal ? min(kend, row_last / p.G + delta + 1) : kend;
 
     const int wrow0 = row0 + wave * kRowsPerWave;
@@ -252,7 +194,7 @@ void attn_fwd_kernel(const FwdParams p) {
     // ---- key padding mask: one bit per key of a tile, wave-uniform
     const bool has_mask = !PAGED && p.mask != nullptr;
     const uint8_t *mrow = has_mask ? p.mask + (int64_t)b * p.Skv : nullptr;
-    constexpr uint64_t kLoMask = BN >= 64 ? ~0ull : ((1ull << BN) - 1);
+    constexpr uint64_t kLoMask = BN >= 64 ? ~0ull : ((1ull << (BN & 63)) - 1);
     auto tile_bits = [&](int j0, uint64_t &lo, uint64_t &hi) {
         const int j = j0 + lane;
         const bool keep0 = (lane < BN) && j < kv_len && mrow[j] != 0;
@@ -273,16 +215,16 @@ void attn_fwd_kernel(const FwdParams p) {
         return wg_end;
     };
 
-    // ---- HBM -> LDS, no registers: each of the tile's 16 1-KB pieces is one
+    // ---- HBM -> LDS, no registers: each of the tile's 1 KB pieces is one
     // global_load_lds_dwordx4 (lane l fills bytes [16l, 16l+16) of its piece);
-    // piece e*4 + wave is this wave's e-th.  Lane l therefore always fills the
-    // same (row, chunk) of every tile: fetch the chunk the swizzle puts there.
+    // piece e*WAVES + wave is this wave's e-th.  Lane l therefore always fills
+    // the same (row, chunk) of every tile: fetch the chunk the swizzle puts there.
     const int64_t hstride = (int64_t)p.Hkv * D;  // elements between consecutive keys
-    int ld_row[4];
-    int64_t ld_base[4];  // element offset of this lane's chunk, key row 0
+    int ld_row[PPW];
+    int64_t ld_base[PPW];  // element offset of this lane's chunk, key row 0
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int byte = (e * 4 + wave) * 1024 + 16 * lane;
+    for (int e = 0; e < PPW; ++e) {
+        const int byte = (e * WAVES + wave) * 1024 + 16 * lane;
         const int row = byte / (2 * D);
         const int pos = (byte % (2 * D)) / 16;
         ld_row[e] = row;
@@ -296,7 +238,7 @@ void attn_fwd_kernel(const FwdParams p) {
         int64_t tile_page_row = 0;
         if (page_per_tile) tile_page_row = (int64_t)bt_row[j0 >> p.page_shift] << p.page_shift;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < PPW; ++e) {
             // keys past the end load the last key (finite data, masked later)
             const int j = min(j0 + ld_row[e], kv_len - 1);
             int64_t row;
@@ -309,7 +251,8 @@ void attn_fwd_kernel(const FwdParams p) {
                       (j & ((1 << p.page_shift) - 1));
             const int64_t off = ld_base[e] + row * hstride;
             __builtin_amdgcn_global_load_lds((const void *)(src + off),
-                                             (lds_void *)(dst + (e * 4 + wave) * 1024), 16, 0, 0);
+                                             (lds_void *)(dst + (e * WAVES + wave) * 1024), 16,
+                                             0, 0);
         }
     };
     auto issue_k = [&](int j0, uint8_t *dst) { issue(j0, p.k, dst); };
@@ -481,44 +424,173 @@ void attn_fwd_kernel(const FwdParams p) {
         pv(sv, pb);
     };
 
-    // ---- main loop.  K and V have rings of two stages each.  At the start of
-    // the step for tile `cur`: its scores are in registers, its V is in one V
-    // stage and the next tile's K in one K stage; the step streams the K of
-    // the tile after next and the V of the next tile into the free stages
-    // (straight from HBM, no registers) while the waves compute.
-    uint64_t mc_lo = ~0ull, mc_hi = ~0ull, mn_lo = ~0ull, mn_hi = ~0ull, m2_lo = ~0ull,
-             m2_hi = ~0ull;
-    f32x16 scA[NT], scB[NT];
-    int cur = find_tile(kbeg, mc_lo, mc_hi);
-    int nxt = cur < wg_end ? find_tile(cur + BN, mn_lo, mn_hi) : wg_end;
-    if (cur < wg_end) {
-        issue_k(cur, sK0);
-        issue_v(cur, sV0);
-    }
-    if (nxt < wg_end) issue_k(nxt, sK1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (wave_active && cur < wave_end) qk(sK0, scA);
-    while (cur < wg_end) {
-        // tile cur: scores in scA, V in sV0; tile nxt: K in sK1
-        int nxt2 = nxt < wg_end ? find_tile(nxt + BN, m2_lo, m2_hi) : wg_end;
-        if (nxt2 < wg_end) issue_k(nxt2, sK0);
-        if (nxt < wg_end) issue_v(nxt, sV1);
-        step(cur, mc_lo, mc_hi, nxt, scA, scB, sK1, sV0);
+    if constexpr (WAVES == 8) {
+        // ---- ping-pong main loop.  Waves 0-3 (group 0) and 4-7 (group 1)
+        // sit on the four SIMDs in pairs.  Each tile k takes one step of two
+        // phases, each ending in a workgroup barrier:
+        //   phase A: group 0 runs its MFMA phase (QK^T of tile k, P.V of
+        //            tile k-1); group 1 its softmax of tile k-1;
+        //   phase B: group 0 runs the softmax of tile k; group 1 its MFMA
+        //            phase (QK^T of tile k, P.V of tile k-1).
+        // A wave's scores go from its MFMA phase to its next softmax phase,
+        // its probabilities from there to its next MFMA phase.
+        //
+        // K and V have rings of four stages (128 KB of LDS at D = 128, one
+        // workgroup per CU).  Step k reads K(k) and V(k-1) and issues the
+        // loads of K(k+3) and V(k+2) into the stages step k-1 freed, so a load
+        // has three steps to land: the L2/MALL round trip stays hidden.  Every
+        // step issues the same number of loads (a step past the last tile
+        // reloads a valid tile into a stage nobody reads), so one counted
+        // wait -- all but the two youngest steps' loads -- orders the ring.
+        __shared__ __attribute__((aligned(1024))) uint8_t sK2[TILE_BYTES];
+        __shared__ __attribute__((aligned(1024))) uint8_t sV2[TILE_BYTES];
+        __shared__ __attribute__((aligned(1024))) uint8_t sK3[TILE_BYTES];
+        __shared__ __attribute__((aligned(1024))) uint8_t sV3[TILE_BYTES];
+        static_assert(PPW == 1 || PPW == 2, "counted waits below assume 1 or 2 loads per tile");
+
+        const int group = wave >> 2;
+        f32x16 sc[NT];
+        vec8 pb[PSTEPS];
+        float corr_pending = 1.f;
+        auto mma_phase = [&](int cur, int prev, const uint8_t *sk, const uint8_t *sv) {
+            const bool do_qk = wave_active && cur < wave_end;
+            const bool do_pv = wave_active && prev >= 0 && prev < wave_end;
+            if (do_pv && corr_pending != 1.f) {
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[t][r] *= corr_pending;
+            }
+            if (do_qk && do_pv) {
+                qk(sk, sc);
+                pv(sv, pb);
+                sched_read_ahead<NT * KSTEPS + 2 * DT * PSTEPS, NT * KSTEPS + DT * PSTEPS>();
+            } else if (do_qk) {
+                qk(sk, sc);
+                sched_read_ahead<NT * KSTEPS, NT * KSTEPS>();
+            } else if (do_pv) {
+                pv(sv, pb);
+                sched_read_ahead<2 * DT * PSTEPS, DT * PSTEPS>();
+            }
+        };
+        auto softmax_phase = [&](int tile, uint64_t lo, uint64_t hi) {
+            if (!(wave_active && tile >= 0 && tile < wave_end)) return;
+            bool full = tile + BN <= wave_full_end;
+            if (has_mask) full = full && (lo == kLoMask) && (BN <= 64 || hi == ~0ull);
+            if (full)
+                corr_pending = softmax(std::false_type{}, tile, lo, hi, sc, pb);
+            else
+                corr_pending = softmax(std::true_type{}, tile, lo, hi, sc, pb);
+        };
+
+        // upcoming tiles t0 (current), t1, t2, t3 with their mask bits;
+        // tiles past the workgroup's range read as wg_end
+        uint64_t lo0 = ~0ull, hi0 = ~0ull, lo1 = ~0ull, hi1 = ~0ull, lo2 = ~0ull, hi2 = ~0ull,
+                 lo3 = ~0ull, hi3 = ~0ull, plo = ~0ull, phi = ~0ull;
+        int t0 = find_tile(kbeg, lo0, hi0);
+        int t1 = t0 < wg_end ? find_tile(t0 + BN, lo1, hi1) : wg_end;
+        int t2 = t1 < wg_end ? find_tile(t1 + BN, lo2, hi2) : wg_end;
+        int t3 = wg_end;
+        int prev = -1;
+        const bool any_tile = t0 < wg_end;
+        const int spare = t0;  // a valid tile to reload when a step has none
+        auto issue_step = [&](int kt, uint8_t *dk, int vt, uint8_t *dv) {
+            issue_k(kt < wg_end ? kt : spare, dk);
+            issue_v(vt < wg_end ? vt : spare, dv);
+        };
+        // one step: K(t0) in K_CUR, V(prev) in V_PREV; K(t3) -> K_NEW, V(t2) -> V_NEW.
+        // (A macro, expanded in the loop below: the step holds the workgroup
+        // barriers and the loop exit, which the compiler mishandles when they
+        // sit in a lambda -- it deleted the whole computation.)
+#define MIATTN_PP_STEP(K_CUR, V_PREV, K_NEW, V_NEW)                                     \
+        {                                                                               \
+            t3 = t2 < wg_end ? find_tile(t2 + BN, lo3, hi3) : wg_end;                   \
+            if (any_tile) issue_step(t3, K_NEW, t2, V_NEW);                             \
+            if (group == 0) /* phase A */                                               \
+                mma_phase(t0, prev, K_CUR, V_PREV);                                     \
+            else                                                                        \
+                softmax_phase(prev, plo, phi);                                          \
+            ring_barrier();                                                            \
+            if (group == 0) /* phase B */                                               \
+                softmax_phase(t0 < wg_end ? t0 : -1, lo0, hi0);                         \
+            else                                                                        \
+                mma_phase(t0, prev, K_CUR, V_PREV);                                     \
+            /* the loads issued two steps ago hold K(t1) and V(t0) */                   \
+            if constexpr (PPW == 1)                                                     \
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");                        \
+            else                                                                        \
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");                        \
+            ring_barrier();                                                            \
+            if (t0 >= wg_end) break;                                                    \
+            prev = t0; plo = lo0; phi = hi0;                                            \
+            t0 = t1; lo0 = lo1; hi0 = hi1;                                              \
+            t1 = t2; lo1 = lo2; hi1 = hi2;                                              \
+            t2 = t3; lo2 = lo3; hi2 = hi3;                                              \
+        }
+
+        // prologue: steps -3, -2, -1 of loads (K(t0) with a spare V; K(t1),
+        // V(t0); K(t2), V(t1)), then wait for the first
+        if (any_tile) {
+            issue_step(t0, sK0, t0, sV3);
+            issue_step(t1, sK1, t0, sV0);
+            issue_step(t2, sK2, t1, sV1);
+        }
+        if constexpr (PPW == 1)
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        ring_barrier();
+        // The shared arrays are named only here, in the kernel body, and handed
+        // to the helpers as pointers.
+        for (;;) {
+            MIATTN_PP_STEP(sK0, sV3, sK3, sV2)  // k % 4 == 0
+            MIATTN_PP_STEP(sK1, sV0, sK0, sV3)  // k % 4 == 1
+            MIATTN_PP_STEP(sK2, sV1, sK1, sV0)  // k % 4 == 2
+            MIATTN_PP_STEP(sK3, sV2, sK2, sV1)  // k % 4 == 3
+        }
+#undef MIATTN_PP_STEP
+        // no load may still be writing this workgroup's LDS when it exits
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        // ---- main loop.  K and V have rings of two stages each.  At the start of
+        // the step for tile `cur`: its scores are in registers, its V is in one V
+        // stage and the next tile's K in one K stage; the step streams the K of
+        // the tile after next and the V of the next tile into the free stages
+        // (straight from HBM, no registers) while the waves compute.
+        uint64_t mc_lo = ~0ull, mc_hi = ~0ull, mn_lo = ~0ull, mn_hi = ~0ull, m2_lo = ~0ull,
+                 m2_hi = ~0ull;
+        f32x16 scA[NT], scB[NT];
+        int cur = find_tile(kbeg, mc_lo, mc_hi);
+        int nxt = cur < wg_end ? find_tile(cur + BN, mn_lo, mn_hi) : wg_end;
+        if (cur < wg_end) {
+            issue_k(cur, sK0);
+            issue_v(cur, sV0);
+        }
+        if (nxt < wg_end) issue_k(nxt, sK1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        cur = nxt; mc_lo = mn_lo; mc_hi = mn_hi;
-        nxt = nxt2; mn_lo = m2_lo; mn_hi = m2_hi;
-        if (cur >= wg_end) break;
-        // tile cur: scores in scB, V in sV1; tile nxt: K in sK0
-        nxt2 = nxt < wg_end ? find_tile(nxt + BN, m2_lo, m2_hi) : wg_end;
-        if (nxt2 < wg_end) issue_k(nxt2, sK1);
-        if (nxt < wg_end) issue_v(nxt, sV0);
-        step(cur, mc_lo, mc_hi, nxt, scB, scA, sK0, sV1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        cur = nxt; mc_lo = mn_lo; mc_hi = mn_hi;
-        nxt = nxt2; mn_lo = m2_lo; mn_hi = m2_hi;
+        if (wave_active && cur < wave_end) qk(sK0, scA);
+        while (cur < wg_end) {
+            // tile cur: scores in scA, V in sV0; tile nxt: K in sK1
+            int nxt2 = nxt < wg_end ? find_tile(nxt + BN, m2_lo, m2_hi) : wg_end;
+            if (nxt2 < wg_end) issue_k(nxt2, sK0);
+            if (nxt < wg_end) issue_v(nxt, sV1);
+            step(cur, mc_lo, mc_hi, nxt, scA, scB, sK1, sV0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            cur = nxt; mc_lo = mn_lo; mc_hi = mn_hi;
+            nxt = nxt2; mn_lo = m2_lo; mn_hi = m2_hi;
+            if (cur >= wg_end) break;
+            // tile cur: scores in scB, V in sV1; tile nxt: K in sK0
+            nxt2 = nxt < wg_end ? find_tile(nxt + BN, m2_lo, m2_hi) : wg_end;
+            if (nxt2 < wg_end) issue_k(nxt2, sK1);
+            if (nxt < wg_end) issue_v(nxt, sV0);
+            step(cur, mc_lo, mc_hi, nxt, scB, scA, sK0, sV1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            cur = nxt; mc_lo = mn_lo; mc_hi = mn_hi;
+            nxt = nxt2; mn_lo = m2_lo; mn_hi = m2_hi;
+        }
     }
 
     // ---- epilogue: normalise and store (no barrier below this point)
@@ -560,30 +632,37 @@ void attn_fwd_kernel(const FwdParams p) {
     }
 }
 
-template <int D, bool BF16, bool PAGED>
+template <int D, bool BF16, bool PAGED, int WAVES>
 hipError_t launch_one(const FwdParams &p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, PAGED>), dim3(grid), dim3(kThreadsPerBlock), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, PAGED, WAVES>), dim3(grid), dim3(64 * WAVES), 0,
                        stream, p);
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_d(const FwdParams &p, bool bf16, bool paged, int grid, hipStream_t stream) {
+template <int D, int WAVES>
+hipError_t launch_w(const FwdParams &p, bool bf16, bool paged, int grid, hipStream_t stream) {
     if (bf16)
-        return paged ? launch_one<D, true, true>(p, grid, stream)
-                     : launch_one<D, true, false>(p, grid, stream);
-    return paged ? launch_one<D, false, true>(p, grid, stream)
-                 : launch_one<D, false, false>(p, grid, stream);
+        return paged ? launch_one<D, true, true, WAVES>(p, grid, stream)
+                     : launch_one<D, true, false, WAVES>(p, grid, stream);
+    return paged ? launch_one<D, false, true, WAVES>(p, grid, stream)
+                 : launch_one<D, false, false, WAVES>(p, grid, stream);
 }
 
 }  // namespace
 
-hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int grid,
-                           hipStream_t stream) {
+hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int waves,
+                           int grid, hipStream_t stream) {
+    if (waves == 8) {
+        switch (D) {
+            case 64: return launch_w<64, 8>(p, bf16, paged, grid, stream);
+            case 128: return launch_w<128, 8>(p, bf16, paged, grid, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (D) {
-        case 64: return launch_d<64>(p, bf16, paged, grid, stream);
-        case 128: return launch_d<128>(p, bf16, paged, grid, stream);
-        case 256: return launch_d<256>(p, bf16, paged, grid, stream);
+        case 64: return launch_w<64, 4>(p, bf16, paged, grid, stream);
+        case 128: return launch_w<128, 4>(p, bf16, paged, grid, stream);
+        case 256: return launch_w<256, 4>(p, bf16, paged, grid, stream);
         default: return hipErrorInvalidValue;
     }
 }

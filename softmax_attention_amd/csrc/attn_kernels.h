@@ -13,13 +13,21 @@ namespace miattn {
 // heads that read this KV head sit next to each other: packed row r holds
 // query i = r / g of head kvh * g + r % g.  Every packed row reads the same
 // keys, so one K/V tile staged in LDS serves the whole group.
-constexpr int kRowsPerWave = 32;                       // one 32x32 MFMA column block
-constexpr int kWavesPerBlock = 4;
-constexpr int kRowsPerBlock = kRowsPerWave * kWavesPerBlock;  // 128
-constexpr int kThreadsPerBlock = 64 * kWavesPerBlock;         // 256
+constexpr int kRowsPerWave = 32;  // one 32x32 MFMA column block
 
-// Keys per KV tile: the tile holds 8192 elements of K and of V for every D.
-constexpr int keys_per_tile(int D) { return 8192 / D; }
+// Two schedules share one kernel template:
+//   4 waves (256 threads): each wave pipelines the next tile's QK^T under the
+//     current tile's softmax; used for D = 256 and decode-shaped calls.
+//   8 waves (512 threads, two per SIMD): the waves form two groups that
+//     alternate, phase by phase, between an MFMA phase (QK^T of one tile and
+//     P.V of the previous one) and a softmax phase, so each SIMD always has
+//     one wave feeding the matrix core while the other runs VALU work
+//     ("ping-pong"); used for D <= 128 prefill.
+constexpr int rows_per_workgroup(int waves) { return kRowsPerWave * waves; }
+
+// Keys per KV tile.  4 waves: 8192 / D keys (a 16 KB K or V tile, 4 KB per
+// wave of direct loads).  8 waves: 64 keys (8 KB at D = 64, 16 KB at D = 128).
+constexpr int keys_per_tile(int D, int waves) { return waves == 8 ? 64 : 8192 / D; }
 
 struct FwdParams {
     const uint16_t *q;   // [B, Sq, Hq, D]
@@ -35,13 +43,14 @@ struct FwdParams {
     int B, Sq, Hq, Hkv, G, Skv;
     int page_shift, max_pages;
     int rows;        // Sq * G packed rows per (batch, KV head)
-    int n_mblocks;   // ceil(rows / kRowsPerBlock)
+    int n_mblocks;   // ceil(rows / rows_per_workgroup(waves))
     int n_splits;    // key-range splits per (batch, KV head)
     int split_len;   // keys per split, a multiple of the key tile
     int causal;
     float scale_log2;  // |alpha| * log2(e)
     int q_mode;        // 0: q as given; 1: q negated (alpha < 0); 2: q zeroed (alpha == 0)
     int xcd_units;     // (batch*KV head, split) units per XCD, or 0 for linear order
+    int xcd_unit_major;  // with xcd_units: an XCD runs all row blocks of a unit, then the next
 };
 
 struct MergeParams {
@@ -55,8 +64,8 @@ struct MergeParams {
 };
 
 // Launchers: return the hipGetLastError() status of the launch.
-hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int grid,
-                           hipStream_t stream);
+hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int waves,
+                           int grid, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams &p, int D, bool bf16, hipStream_t stream);
 
 }  // namespace miattn

@@ -179,10 +179,16 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (dev < 0 || dev >= kMaxDevices) return fail(MIATTN_ERR_UNSUPPORTED, "device %d", dev);
 
-    const int BN = miattn::keys_per_tile(D);
     p.G = p.Hq / p.Hkv;
     p.rows = p.Sq * p.G;
-    p.n_mblocks = (p.rows + miattn::kRowsPerBlock - 1) / miattn::kRowsPerBlock;
+    // 8-wave ping-pong schedule for D <= 128 prefill; the 4-wave pipelined
+    // schedule for D = 256 and for decode-shaped calls (a few packed rows)
+    int waves = (D <= 128 && p.rows > miattn::kRowsPerWave) ? 8 : 4;
+    const int forced = env_int("MIATTN_WAVES", 0);
+    if ((forced == 4 || forced == 8) && (forced == 4 || D <= 128)) waves = forced;
+    const int BN = miattn::keys_per_tile(D, waves);
+    const int BM = miattn::rows_per_workgroup(waves);
+    p.n_mblocks = (p.rows + BM - 1) / BM;
     const int64_t bhs = (int64_t)p.B * p.Hkv;
     const int64_t cap_tiles = capacity > 0 ? (capacity + BN - 1) / BN : 1;
 
@@ -218,6 +224,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
                     (long long)grid, INT_MAX);
     const int64_t units = bhs * n_splits;
     p.xcd_units = (units % 8 == 0) ? (int)(units / 8) : 0;
+    p.xcd_unit_major = env_int("MIATTN_XCD_ORDER", 0);
 
     if (n_splits > 1) {
         const int64_t nrow = n_splits * bhs * p.rows;
@@ -229,7 +236,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
     }
 
     e = timed_launch(0, stream, [&] {
-        return miattn::launch_attn_fwd(p, D, bf16, paged, (int)grid, stream);
+        return miattn::launch_attn_fwd(p, D, bf16, paged, waves, (int)grid, stream);
     });
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
 
