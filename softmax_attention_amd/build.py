@@ -4,6 +4,7 @@ Usage: ``python -m softmax_attention_amd.build`` or ``build()`` from Python.
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import subprocess
 import sys
@@ -47,6 +48,12 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+    # every symbol must resolve (a kernel whose host-side launch stub was not
+    # emitted only shows up here, as an undefined symbol)
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    except OSError as e:
+        raise RuntimeError(f"built library does not load: {e}") from None
     os.replace(tmp, LIB)
     return LIB
 

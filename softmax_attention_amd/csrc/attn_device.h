@@ -81,9 +81,27 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {  // bytes
     return row * (2 * D) + 16 * (chunk ^ swz<D>(row));
 }
 
+// Word 3 of a raw buffer resource (stride 0): a 32-bit data format, without
+// which gfx9 buffer loads return zeros.
+constexpr int kBufferFlags = 0x00020000;
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+
+// One buffer_load_dwordx4 ... lds: lane l copies the 16 bytes at
+// base + voffset(l) to dst + 16 l, bypassing registers; offsets at or past
+// num_bytes read as zero.  (The body exists in the device pass only: the host
+// pass has no buffer-resource type and would otherwise drop the kernels'
+// launch stubs.)
+__device__ __forceinline__ void buffer_load_lds16(const void *base, int num_bytes, lds_void *dst,
+                                                  int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, num_bytes, kBufferFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voffset, 0, 0, 0);
+#endif
+}
 
 // Sum of the two 16-bit values packed in `pk`, accumulated into acc in FP32.
 template <bool BF16>
@@ -103,6 +121,24 @@ __device__ __forceinline__ float add_pair(uint32_t pk, float acc) {
 // arithmetic and saves rescaling O for almost every tile.
 constexpr float kLazy = 8.0f;
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in bits 6:4, lgkmcnt in bits 11:8; a field at its maximum does not wait).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// Waits are issued through the s_waitcnt builtin rather than inline assembly
+// because the compiler tracks which LDS array each direct-to-LDS load writes
+// and inserts a wait of its own before any LDS read that might still be in
+// flight; an assembly wait is opaque to it, so it would drain the whole ring
+// (vmcnt(0)) before reads that the counted waits already cover.  The empty
+// assembly statements keep memory accesses from moving across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
+    asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier for the K/V rings.  __syncthreads() is a workgroup-scope
 // release/acquire fence around s_barrier, and the release half waits for every
 // outstanding global load (vmcnt(0)) -- which would drain the whole ring at
@@ -111,7 +147,10 @@ constexpr float kLazy = 8.0f;
 // (so a stage can be refilled) and must keep the compiler from moving memory
 // accesses across it.
 __device__ __forceinline__ void ring_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 }  // namespace dev

@@ -136,7 +136,12 @@ void attn_fwd_kernel(const FwdParams p) {
     const int b = bh / p.Hkv;
     const int kvh = bh - b * p.Hkv;
 
-    const int kv_len = PAGED ? p.seqlen[b] : p.Skv;
+    // (a paged length is clamped to the table's capacity, and an empty cache
+    // holds no keys, so that malformed lengths cannot address memory
+    // outside the table or the cache)
+    const int kv_len =
+        !PAGED ? p.Skv
+               : (p.num_pages > 0 ? min(max(p.seqlen[b], 0), p.max_pages << p.page_shift) : 0);
     const int kbeg = split * p.split_len;
     // Splits past the end are never read by the merge, which counts the
     // splits that hold keys from the same length.
@@ -215,48 +220,86 @@ void attn_fwd_kernel(const FwdParams p) {
         return wg_end;
     };
 
-    // ---- HBM -> LDS, no registers: each of the tile's 1 KB pieces is one
-    // global_load_lds_dwordx4 (lane l fills bytes [16l, 16l+16) of its piece);
-    // piece e*WAVES + wave is this wave's e-th.  Lane l therefore always fills
-    // the same (row, chunk) of every tile: fetch the chunk the swizzle puts there.
+    // ---- HBM -> LDS, no registers: each 1 KB piece of a tile is one
+    // buffer_load_dwordx4 ... lds (lane l fills bytes [16l, 16l+16) of the
+    // piece); piece e*WAVES + wave is this wave's e-th.  A piece covers RPP
+    // consecutive keys, which never straddle a page (a page holds >= 16 keys
+    // and pieces start on multiples of RPP), so the piece's first key fixes a
+    // scalar base address -- one block-table entry, read through the scalar
+    // cache -- and each lane adds a small offset: its key within the piece and
+    // the chunk that the swizzle puts at its position.  Keys past the end load
+    // the last key (finite data, masked later).
+    //
+    // The buffer form, unlike global_load_lds, is not a FLAT instruction: the
+    // compiler then counts the LDS reads that follow (lgkmcnt(n)) instead of
+    // waiting for all of them whenever a direct load is in flight.
+    constexpr int RPP = 512 / D;                                // keys per piece
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);    // wave-uniform
+    const int l_dr = lane / (D / 8);   // this lane's key within a piece
+    const int l_pos = lane % (D / 8);  // this lane's 16-byte position in the row
     const int64_t hstride = (int64_t)p.Hkv * D;  // elements between consecutive keys
-    int ld_row[PPW];
-    int64_t ld_base[PPW];  // element offset of this lane's chunk, key row 0
+    const int row_bytes = p.Hkv * D * 2;
+    int l_chunk[PPW];  // byte offset, within its key row, of the chunk this lane fetches
 #pragma unroll
-    for (int e = 0; e < PPW; ++e) {
-        const int byte = (e * WAVES + wave) * 1024 + 16 * lane;
-        const int row = byte / (2 * D);
-        const int pos = (byte % (2 * D)) / 16;
-        ld_row[e] = row;
-        ld_base[e] = (int64_t)kvh * D + 8 * (pos ^ swz<D>(row)) +
-                     (PAGED ? 0 : (int64_t)b * p.Skv * hstride);
-    }
-    // a page holds whole tiles when page_size >= BN: one page per tile
-    const bool page_per_tile = PAGED && p.page_shift >= __builtin_ctz(BN);
-    const int32_t *bt_row = PAGED ? p.block_table + (int64_t)b * p.max_pages : nullptr;
-    auto issue = [&](int j0, const uint16_t *src, uint8_t *dst) {
-        int64_t tile_page_row = 0;
-        if (page_per_tile) tile_page_row = (int64_t)bt_row[j0 >> p.page_shift] << p.page_shift;
+    for (int e = 0; e < PPW; ++e)
+        l_chunk[e] = 16 * (l_pos ^ swz<D>((e * WAVES + wave_u) * RPP + l_dr));
+    const int64_t head_off = (int64_t)kvh * D + (PAGED ? 0 : (int64_t)b * p.Skv * hstride);
+    typedef __attribute__((address_space(4))) const int32_t const_i32;
+    const_i32 *bt_row =
+        PAGED ? (const_i32 *)(p.block_table + (int64_t)b * p.max_pages) : nullptr;
+    // first key and cache row of each of this wave's pieces of tile j0 (the
+    // block-table reads of a whole step are issued before any of them is
+    // waited for)
+    struct Pieces {
+        int jr[PPW];
+        int64_t row[PPW];
+    };
+    auto locate = [&](int j0, Pieces &pc) {
+        int32_t phys[PPW];
 #pragma unroll
         for (int e = 0; e < PPW; ++e) {
-            // keys past the end load the last key (finite data, masked later)
-            const int j = min(j0 + ld_row[e], kv_len - 1);
-            int64_t row;
-            if (!PAGED)
-                row = j;
-            else if (page_per_tile)
-                row = tile_page_row + (j & ((1 << p.page_shift) - 1));
-            else
-                row = ((int64_t)bt_row[j >> p.page_shift] << p.page_shift) +
-                      (j & ((1 << p.page_shift) - 1));
-            const int64_t off = ld_base[e] + row * hstride;
-            __builtin_amdgcn_global_load_lds((const void *)(src + off),
-                                             (lds_void *)(dst + (e * WAVES + wave) * 1024), 16,
-                                             0, 0);
+            pc.jr[e] = min(j0 + (e * WAVES + wave_u) * RPP, kv_len - 1);
+            if constexpr (PAGED) phys[e] = bt_row[pc.jr[e] >> p.page_shift];
+        }
+#pragma unroll
+        for (int e = 0; e < PPW; ++e) {
+            if constexpr (PAGED) {
+                // (indices clamped into the cache, so that a malformed table
+                // cannot address memory outside it)
+                pc.row[e] = ((int64_t)min(max(phys[e], 0), p.num_pages - 1) << p.page_shift) +
+                            (pc.jr[e] & ((1 << p.page_shift) - 1));
+            } else {
+                pc.row[e] = pc.jr[e];
+            }
         }
     };
-    auto issue_k = [&](int j0, uint8_t *dst) { issue(j0, p.k, dst); };
-    auto issue_v = [&](int j0, uint8_t *dst) { issue(j0, p.v, dst); };
+    auto fire = [&](const Pieces &pc, const uint16_t *src, uint8_t *dst) {
+#pragma unroll
+        for (int e = 0; e < PPW; ++e) {
+            const int piece = e * WAVES + wave_u;
+            const int dj = min(l_dr, kv_len - 1 - pc.jr[e]);
+            buffer_load_lds16(src + head_off + pc.row[e] * hstride, RPP * row_bytes,
+                              (lds_void *)(dst + piece * 1024), dj * row_bytes + l_chunk[e]);
+        }
+    };
+    // K of tile kt and V of tile vt
+    auto issue_kv = [&](int kt, uint8_t *dk, int vt, uint8_t *dv) {
+        Pieces pk, pv_;
+        locate(kt, pk);
+        locate(vt, pv_);
+        fire(pk, p.k, dk);
+        fire(pv_, p.v, dv);
+    };
+    auto issue_k = [&](int j0, uint8_t *dst) {
+        Pieces pc;
+        locate(j0, pc);
+        fire(pc, p.k, dst);
+    };
+    auto issue_v = [&](int j0, uint8_t *dst) {
+        Pieces pc;
+        locate(j0, pc);
+        fire(pc, p.v, dst);
+    };
 
     const float c = p.scale_log2;  // > 0
 
@@ -495,17 +538,17 @@ void attn_fwd_kernel(const FwdParams p) {
         const bool any_tile = t0 < wg_end;
         const int spare = t0;  // a valid tile to reload when a step has none
         auto issue_step = [&](int kt, uint8_t *dk, int vt, uint8_t *dv) {
-            issue_k(kt < wg_end ? kt : spare, dk);
-            issue_v(vt < wg_end ? vt : spare, dv);
+            issue_kv(kt < wg_end ? kt : spare, dk, vt < wg_end ? vt : spare, dv);
         };
         // one step: K(t0) in K_CUR, V(prev) in V_PREV; K(t3) -> K_NEW, V(t2) -> V_NEW.
-        // (A macro, expanded in the loop below: the step holds the workgroup
-        // barriers and the loop exit, which the compiler mishandles when they
-        // sit in a lambda -- it deleted the whole computation.)
+        // The step with t0 == wg_end only finishes P.V of the last tile; steps
+        // after it find no work and reload the spare tile.  (A macro, expanded
+        // in the loop below: the step holds the workgroup barriers, which the
+        // compiler mishandled inside a lambda -- it deleted the computation.)
 #define MIATTN_PP_STEP(K_CUR, V_PREV, K_NEW, V_NEW)                                     \
         {                                                                               \
             t3 = t2 < wg_end ? find_tile(t2 + BN, lo3, hi3) : wg_end;                   \
-            if (any_tile) issue_step(t3, K_NEW, t2, V_NEW);                             \
+            issue_step(t3, K_NEW, t2, V_NEW);                                           \
             if (group == 0) /* phase A */                                               \
                 mma_phase(t0, prev, K_CUR, V_PREV);                                     \
             else                                                                        \
@@ -516,41 +559,41 @@ void attn_fwd_kernel(const FwdParams p) {
             else                                                                        \
                 mma_phase(t0, prev, K_CUR, V_PREV);                                     \
             /* the loads issued two steps ago hold K(t1) and V(t0) */                   \
-            if constexpr (PPW == 1)                                                     \
-                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");                        \
-            else                                                                        \
-                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");                        \
-            ring_barrier();                                                            \
-            if (t0 >= wg_end) break;                                                    \
+            wait_vmcnt<4 * PPW>();                                                      \
+            ring_barrier();                                                             \
             prev = t0; plo = lo0; phi = hi0;                                            \
             t0 = t1; lo0 = lo1; hi0 = hi1;                                              \
             t1 = t2; lo1 = lo2; hi1 = hi2;                                              \
             t2 = t3; lo2 = lo3; hi2 = hi3;                                              \
         }
 
-        // prologue: steps -3, -2, -1 of loads (K(t0) with a spare V; K(t1),
-        // V(t0); K(t2), V(t1)), then wait for the first
+        // A workgroup without a visible tile skips the ring altogether.  Inside
+        // it every step issues its loads unconditionally: the compiler tracks
+        // which LDS array each direct load writes, and a load that might not
+        // have been issued would make it wait for all of them before each read.
         if (any_tile) {
+            // prologue: steps -3, -2, -1 of loads (K(t0) with a spare V; K(t1),
+            // V(t0); K(t2), V(t1)), then wait for the first
             issue_step(t0, sK0, t0, sV3);
             issue_step(t1, sK1, t0, sV0);
             issue_step(t2, sK2, t1, sV1);
-        }
-        if constexpr (PPW == 1)
-            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        ring_barrier();
-        // The shared arrays are named only here, in the kernel body, and handed
-        // to the helpers as pointers.
-        for (;;) {
-            MIATTN_PP_STEP(sK0, sV3, sK3, sV2)  // k % 4 == 0
-            MIATTN_PP_STEP(sK1, sV0, sK0, sV3)  // k % 4 == 1
-            MIATTN_PP_STEP(sK2, sV1, sK1, sV0)  // k % 4 == 2
-            MIATTN_PP_STEP(sK3, sV2, sK2, sV1)  // k % 4 == 3
+            wait_vmcnt<4 * PPW>();
+            ring_barrier();
+            // The shared arrays are named only here, in the kernel body, and
+            // handed to the helpers as pointers.  The loop leaves only after a
+            // whole round of four steps: an exit between steps makes the
+            // compiler merge the ring states of all four into the loop header
+            // and wait for every load there.
+            do {
+                MIATTN_PP_STEP(sK0, sV3, sK3, sV2)  // k % 4 == 0
+                MIATTN_PP_STEP(sK1, sV0, sK0, sV3)  // k % 4 == 1
+                MIATTN_PP_STEP(sK2, sV1, sK1, sV0)  // k % 4 == 2
+                MIATTN_PP_STEP(sK3, sV2, sK2, sV1)  // k % 4 == 3
+            } while (prev < wg_end);
+            // no load may still be writing this workgroup's LDS when it exits
+            wait_vmcnt<0>();
         }
 #undef MIATTN_PP_STEP
-        // no load may still be writing this workgroup's LDS when it exits
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
         // ---- main loop.  K and V have rings of two stages each.  At the start of
         // the step for tile `cur`: its scores are in registers, its V is in one V

@@ -41,7 +41,7 @@ struct FwdParams {
     const int32_t *seqlen;      // paged: [B]
     const int32_t *block_table; // paged: [B, max_pages]
     int B, Sq, Hq, Hkv, G, Skv;
-    int page_shift, max_pages;
+    int page_shift, max_pages, num_pages;  // paged: log2(page size), table width, cache pages
     int rows;        // Sq * G packed rows per (batch, KV head)
     int n_mblocks;   // ceil(rows / rows_per_workgroup(waves))
     int n_splits;    // key-range splits per (batch, KV head)

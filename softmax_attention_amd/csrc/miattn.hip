@@ -381,6 +381,7 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
     p.Hkv = Hkv;
     p.page_shift = page_shift;
     p.max_pages = max_pages;
+    p.num_pages = num_phys_pages;
     p.causal = causal;
     set_scale(p, resolve_scale(scale, D));
     return run(p, D, dtype == MIATTN_BF16, true, capacity, (hipStream_t)stream);
