@@ -103,6 +103,21 @@ __device__ __forceinline__ void buffer_load_lds16(const void *base, int num_byte
 #endif
 }
 
+// max(x, x of lane l ^ 32) in every lane: v_permlane32_swap exchanges the
+// two 32-lane halves without going through LDS.
+__device__ __forceinline__ float max_halves(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+// x + (x of lane l ^ 32) in every lane, as above.
+__device__ __forceinline__ float sum_halves(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
 // Sum of the two 16-bit values packed in `pk`, accumulated into acc in FP32.
 template <bool BF16>
 __device__ __forceinline__ float add_pair(uint32_t pk, float acc) {

@@ -51,15 +51,11 @@ using namespace dev;
 
 
 // Waves per SIMD the register budget is sized for: the 8-wave schedule needs
-// its two waves per SIMD; the 4-wave one runs two workgroups per CU for
-// D <= 128 and one for D = 256 (whose accumulators alone take 128 registers).
+// its two waves per SIMD, and so do three two-wave decode workgroups (48 KB
+// of LDS each) on one CU; the 4-wave D = 256 schedule runs one workgroup per
+// CU.
 template <int D, int WAVES>
-constexpr int waves_per_eu() { return (WAVES == 8 || D <= 128) ? 2 : 1; }
-
-#ifndef MIATTN_VALU_PER_MFMA
-#define MIATTN_VALU_PER_MFMA 6
-#endif
-constexpr int kValuPerMfma = MIATTN_VALU_PER_MFMA;
+constexpr int waves_per_eu() { return (WAVES == 8 || WAVES == 2) ? 2 : 1; }
 
 #ifndef MIATTN_READ_AHEAD
 #define MIATTN_READ_AHEAD 6
@@ -80,29 +76,47 @@ __device__ __forceinline__ void sched_read_ahead() {
     }
 }
 
-template <int D, bool BF16, bool PAGED, int WAVES>
+// (The kernel's helper lambdas are marked always_inline: an outlined one
+// would take the parameter block by address and push it to scratch.)
+//
+// K/V source: dense tensors, a paged cache whose pages hold whole key tiles,
+// or a paged cache with pages smaller than a tile (each 1 KB piece then
+// looks up its own page).
+enum KvMode { kDense = 0, kPagedTile = 1, kPagedPiece = 2 };
+
+template <int D, bool BF16, int KV, int WAVES>
 __global__ __launch_bounds__(64 * WAVES)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, WAVES>(), waves_per_eu<D, WAVES>())))
 void attn_fwd_kernel(const FwdParams p) {
+    constexpr bool PAGED = KV != kDense;
     using H = Half<BF16>;
     using vec8 = typename H::vec8;
     constexpr int BM = rows_per_workgroup(WAVES);  // packed rows per workgroup
     constexpr int BN = keys_per_tile(D, WAVES);    // keys per tile
     constexpr int TILE_BYTES = BN * D * 2;         // one K (or V) tile
     constexpr int PIECES = TILE_BYTES / 1024;      // 1 KB direct loads per tile
-    constexpr int PPW = PIECES / WAVES;            // of them per wave
+    // The two-wave (decode) schedule splits the roles: wave 0 computes, wave 1
+    // issues every load.  Otherwise each wave issues an equal share.
+    constexpr bool SPLIT_ROLES = WAVES == 2;
+    constexpr int LOADERS = SPLIT_ROLES ? 1 : WAVES;
+    constexpr int PPW = PIECES / LOADERS;          // 1 KB pieces per loading wave
     constexpr int NT = BN / 32;                    // 32-key score blocks per tile
     constexpr int KSTEPS = D / 16;                 // MFMA k-steps over D
     constexpr int DT = D / 32;                     // 32-wide d blocks of O^T
     constexpr int PSTEPS = BN / 16;                // MFMA k-steps over the tile's keys
-    static_assert(PIECES % WAVES == 0, "whole 1 KB pieces per wave");
+    static_assert(PIECES % LOADERS == 0, "whole 1 KB pieces per loading wave");
 
-    // two stages of (K tile, V tile); separate arrays so the compiler can
-    // tell a load into one stage from reads of the other
+    // K and V rings of four stages each (128 KB of LDS with 16 KB tiles, one
+    // workgroup per CU); separate arrays so that the compiler can tell a load
+    // into one stage from reads of another
     __shared__ __attribute__((aligned(1024))) uint8_t sK0[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sV0[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sK1[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sV1[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK2[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV2[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK3[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV3[TILE_BYTES];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -110,11 +124,11 @@ void attn_fwd_kernel(const FwdParams p) {
     const int l32 = lane & 31;
     const int hl = lane >> 5;
 
+    const int units = p.B * p.Hkv * p.n_splits;
     // ---- which (row block, batch, KV head, split) this workgroup owns.
     // Workgroups are dispatched round-robin over the 8 XCDs; when the unit
     // count allows, consecutive workgroups of one XCD share a (batch, KV head)
     // so its K/V stays in that XCD's L2.  Causal row blocks run heaviest first.
-    const int units = p.B * p.Hkv * p.n_splits;
     int rank, unit;
     if (p.xcd_units > 0 && p.xcd_unit_major) {
         // each XCD finishes the row blocks of one unit before the next, so its
@@ -131,10 +145,23 @@ void attn_fwd_kernel(const FwdParams p) {
         unit = blockIdx.x - rank * units;
     }
     const int mblock = p.causal ? (p.n_mblocks - 1 - rank) : rank;
-    const int bh = unit / p.n_splits;
-    const int split = unit - bh * p.n_splits;
-    const int b = bh / p.Hkv;
-    const int kvh = bh - b * p.Hkv;
+    // Units are (batch, KV head, split) with the split fastest, or -- with
+    // heads_inner, for split decode -- (batch, split, KV head) with the head
+    // fastest: the KV heads of one position share the cache rows, so
+    // workgroups that run together then read whole rows of the same pages.
+    int b, kvh, split;
+    if (p.heads_inner) {
+        const int bs = unit / p.Hkv;
+        kvh = unit - bs * p.Hkv;
+        b = bs / p.n_splits;
+        split = bs - b * p.n_splits;
+    } else {
+        const int bh_ = unit / p.n_splits;
+        split = unit - bh_ * p.n_splits;
+        b = bh_ / p.Hkv;
+        kvh = bh_ - b * p.Hkv;
+    }
+    const int bh = b * p.Hkv + kvh;
 
     // (a paged length is clamped to the table's capacity, and an empty cache
     // holds no keys, so that malformed lengths cannot address memory
@@ -153,8 +180,8 @@ void attn_fwd_kernel(const FwdParams p) {
     const int row_last = min(p.rows, row0 + BM) - 1;
     const int wg_end = p.causal ? min(kend, row_last / p.G + delta + 1) : kend;
 
-    const int wrow0 = row0 + wave * kRowsPerWave;
-    const bool wave_active = wrow0 < p.rows;
+    const int wrow0 = row0 + (SPLIT_ROLES ? 0 : wave * kRowsPerWave);
+    const bool wave_active = (!SPLIT_ROLES || wave == 0) && wrow0 < p.rows;
     const int wrow_last = min(p.rows, wrow0 + kRowsPerWave) - 1;
     // keys < wave_full_end are visible to every row of this wave; keys >=
     // wave_end to none of them
@@ -200,7 +227,7 @@ void attn_fwd_kernel(const FwdParams p) {
     const bool has_mask = !PAGED && p.mask != nullptr;
     const uint8_t *mrow = has_mask ? p.mask + (int64_t)b * p.Skv : nullptr;
     constexpr uint64_t kLoMask = BN >= 64 ? ~0ull : ((1ull << (BN & 63)) - 1);
-    auto tile_bits = [&](int j0, uint64_t &lo, uint64_t &hi) {
+    auto tile_bits = [&](int j0, uint64_t &lo, uint64_t &hi) __attribute__((always_inline)) {
         const int j = j0 + lane;
         const bool keep0 = (lane < BN) && j < kv_len && mrow[j] != 0;
         lo = __ballot(keep0) & kLoMask;
@@ -211,7 +238,7 @@ void attn_fwd_kernel(const FwdParams p) {
         }
     };
     // first tile start >= j that holds a kept key (or wg_end)
-    auto find_tile = [&](int j, uint64_t &lo, uint64_t &hi) -> int {
+    auto find_tile = [&](int j, uint64_t &lo, uint64_t &hi) __attribute__((always_inline)) -> int {
         if (!has_mask) return j;
         for (; j < wg_end; j += BN) {
             tile_bits(j, lo, hi);
@@ -222,19 +249,19 @@ void attn_fwd_kernel(const FwdParams p) {
 
     // ---- HBM -> LDS, no registers: each 1 KB piece of a tile is one
     // buffer_load_dwordx4 ... lds (lane l fills bytes [16l, 16l+16) of the
-    // piece); piece e*WAVES + wave is this wave's e-th.  A piece covers RPP
-    // consecutive keys, which never straddle a page (a page holds >= 16 keys
-    // and pieces start on multiples of RPP), so the piece's first key fixes a
-    // scalar base address -- one block-table entry, read through the scalar
-    // cache -- and each lane adds a small offset: its key within the piece and
-    // the chunk that the swizzle puts at its position.  Keys past the end load
-    // the last key (finite data, masked later).
+    // piece); piece e*WAVES + wave is this wave's e-th and covers RPP
+    // consecutive keys.  The load's base address is scalar (block-table
+    // entries are read through the scalar cache) and each lane adds a small
+    // offset: its key, and the chunk that the swizzle puts at its position.
+    // Keys past the end load the last key (finite data, masked later).
     //
     // The buffer form, unlike global_load_lds, is not a FLAT instruction: the
     // compiler then counts the LDS reads that follow (lgkmcnt(n)) instead of
     // waiting for all of them whenever a direct load is in flight.
     constexpr int RPP = 512 / D;                                // keys per piece
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);    // wave-uniform
+    const int loader = SPLIT_ROLES ? 0 : wave_u;  // this wave's index among the loaders
+    const bool loads = !SPLIT_ROLES || wave_u == 1;
     const int l_dr = lane / (D / 8);   // this lane's key within a piece
     const int l_pos = lane % (D / 8);  // this lane's 16-byte position in the row
     const int64_t hstride = (int64_t)p.Hkv * D;  // elements between consecutive keys
@@ -242,63 +269,84 @@ void attn_fwd_kernel(const FwdParams p) {
     int l_chunk[PPW];  // byte offset, within its key row, of the chunk this lane fetches
 #pragma unroll
     for (int e = 0; e < PPW; ++e)
-        l_chunk[e] = 16 * (l_pos ^ swz<D>((e * WAVES + wave_u) * RPP + l_dr));
+        l_chunk[e] = 16 * (l_pos ^ swz<D>((e * LOADERS + loader) * RPP + l_dr));
     const int64_t head_off = (int64_t)kvh * D + (PAGED ? 0 : (int64_t)b * p.Skv * hstride);
     typedef __attribute__((address_space(4))) const int32_t const_i32;
     const_i32 *bt_row =
         PAGED ? (const_i32 *)(p.block_table + (int64_t)b * p.max_pages) : nullptr;
-    // first key and cache row of each of this wave's pieces of tile j0 (the
-    // block-table reads of a whole step are issued before any of them is
-    // waited for)
-    struct Pieces {
-        int jr[PPW];
-        int64_t row[PPW];
+    // Where a tile lies in one page (always, for dense K/V) a single buffer
+    // descriptor based at the tile's first key serves all pieces and each
+    // lane clamps its own key; with smaller pages each piece gets its own
+    // base.  (The scalar unit is shared by the CU's waves, so the per-step
+    // scalar address arithmetic is kept small.)
+    constexpr bool tile_in_page = KV != kPagedPiece;
+    int l_key[PPW];  // this lane's key row within the tile, per piece
+#pragma unroll
+    for (int e = 0; e < PPW; ++e) l_key[e] = (e * LOADERS + loader) * RPP + l_dr;
+    auto cache_row = [&](int32_t phys, int j) __attribute__((always_inline)) -> int64_t {
+        // (page ids clamped into the cache, so that a malformed table cannot
+        // address memory outside it)
+        return ((int64_t)min(max(phys, 0), p.num_pages - 1) << p.page_shift) +
+               (j & ((1 << p.page_shift) - 1));
     };
-    auto locate = [&](int j0, Pieces &pc) {
-        int32_t phys[PPW];
+    // first tile holding a visible key (wg_end if none), with its mask bits
+    uint64_t first_lo = ~0ull, first_hi = ~0ull;
+    const int first_tile = find_tile(kbeg, first_lo, first_hi);
+    // Block-table entry of the page holding tile j (of the first tile for a
+    // tile past the range).  With whole-tile pages the schedules read it a
+    // step before the tile's loads are issued, so that the scalar load's
+    // latency stays off the issue path.
+    auto tile_page = [&](int j) __attribute__((always_inline)) -> int32_t {
+        if constexpr (KV == kPagedTile)
+            return bt_row[(j < wg_end ? j : first_tile) >> p.page_shift];
+        else
+            return 0;
+    };
+    // Loads of tile j0 into stage dst; `phys` is tile_page(j0).
+    auto issue = [&](int j0, int32_t phys, const uint16_t *src, uint8_t *dst) __attribute__((always_inline)) {
+        // A tile past the range keeps the ring's load count but fetches almost
+        // nothing: every lane reads the same 16 bytes of the first tile.
+        const bool pad = j0 >= wg_end;
+        const int keep = pad ? 0 : -1;  // lane offsets are and-ed with this (no branch)
+        if (pad) j0 = first_tile;
+        if constexpr (tile_in_page) {
+            int64_t row = j0;
+            if constexpr (PAGED) row = cache_row(phys, j0);
+            const uint16_t *base = src + head_off + row * hstride;
+            const int last = kv_len - 1 - j0;  // last valid key row of the tile
 #pragma unroll
-        for (int e = 0; e < PPW; ++e) {
-            pc.jr[e] = min(j0 + (e * WAVES + wave_u) * RPP, kv_len - 1);
-            if constexpr (PAGED) phys[e] = bt_row[pc.jr[e] >> p.page_shift];
-        }
+            for (int e = 0; e < PPW; ++e)
+                buffer_load_lds16(base, BN * row_bytes,
+                                  (lds_void *)(dst + (e * LOADERS + loader) * 1024),
+                                  (min(l_key[e], last) * row_bytes + l_chunk[e]) & keep);
+        } else {
+            // pages smaller than a tile: each of the tile's pages (at most
+            // BN / 16) is looked up once -- all reads issued before any is
+            // waited for -- and each piece picks its own
+            constexpr int kTilePages = BN / 16;
+            const int pg0 = j0 >> p.page_shift;
+            const int pg_last = (kv_len - 1) >> p.page_shift;
+            int32_t phys[kTilePages];
 #pragma unroll
-        for (int e = 0; e < PPW; ++e) {
-            if constexpr (PAGED) {
-                // (indices clamped into the cache, so that a malformed table
-                // cannot address memory outside it)
-                pc.row[e] = ((int64_t)min(max(phys[e], 0), p.num_pages - 1) << p.page_shift) +
-                            (pc.jr[e] & ((1 << p.page_shift) - 1));
-            } else {
-                pc.row[e] = pc.jr[e];
+            for (int q = 0; q < kTilePages; ++q) phys[q] = bt_row[min(pg0 + q, pg_last)];
+#pragma unroll
+            for (int e = 0; e < PPW; ++e) {
+                const int jr = min(j0 + (e * LOADERS + loader) * RPP, kv_len - 1);
+                const int qi = (jr >> p.page_shift) - pg0;
+                int32_t pe = phys[0];
+#pragma unroll
+                for (int q = 1; q < kTilePages; ++q) pe = qi == q ? phys[q] : pe;
+                buffer_load_lds16(src + head_off + cache_row(pe, jr) * hstride, RPP * row_bytes,
+                                  (lds_void *)(dst + (e * LOADERS + loader) * 1024),
+                                  (min(l_dr, kv_len - 1 - jr) * row_bytes + l_chunk[e]) & keep);
             }
         }
     };
-    auto fire = [&](const Pieces &pc, const uint16_t *src, uint8_t *dst) {
-#pragma unroll
-        for (int e = 0; e < PPW; ++e) {
-            const int piece = e * WAVES + wave_u;
-            const int dj = min(l_dr, kv_len - 1 - pc.jr[e]);
-            buffer_load_lds16(src + head_off + pc.row[e] * hstride, RPP * row_bytes,
-                              (lds_void *)(dst + piece * 1024), dj * row_bytes + l_chunk[e]);
-        }
-    };
-    // K of tile kt and V of tile vt
-    auto issue_kv = [&](int kt, uint8_t *dk, int vt, uint8_t *dv) {
-        Pieces pk, pv_;
-        locate(kt, pk);
-        locate(vt, pv_);
-        fire(pk, p.k, dk);
-        fire(pv_, p.v, dv);
-    };
-    auto issue_k = [&](int j0, uint8_t *dst) {
-        Pieces pc;
-        locate(j0, pc);
-        fire(pc, p.k, dst);
-    };
-    auto issue_v = [&](int j0, uint8_t *dst) {
-        Pieces pc;
-        locate(j0, pc);
-        fire(pc, p.v, dst);
+    // K of tile kt and V of tile vt (page entries pk and pv_)
+    auto issue_kv = [&](int kt, int32_t pk, uint8_t *dk, int vt, int32_t pv_, uint8_t *dv) __attribute__((always_inline)) {
+        if (!loads) return;
+        issue(kt, pk, p.k, dk);
+        issue(vt, pv_, p.v, dv);
     };
 
     const float c = p.scale_log2;  // > 0
@@ -328,7 +376,7 @@ void attn_fwd_kernel(const FwdParams p) {
         }
 
     // ---- S^T = K Q^T for one tile (K from an LDS stage)
-    auto qk = [&](const uint8_t *sk, f32x16 (&sc)[NT]) {
+    auto qk = [&](const uint8_t *sk, f32x16 (&sc)[NT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -348,7 +396,7 @@ void attn_fwd_kernel(const FwdParams p) {
     // it with the next tile's QK^T MFMAs.  Returns the factor the output
     // accumulator must be multiplied by (1 when the max did not move).
     auto softmax = [&](auto masked_tag, int j0, uint64_t mlo, uint64_t mhi, f32x16 (&sc)[NT],
-                       vec8 (&pb)[PSTEPS]) -> float {
+                       vec8 (&pb)[PSTEPS]) __attribute__((always_inline)) -> float {
         constexpr bool MASKED = decltype(masked_tag)::value;
         if constexpr (MASKED) {
             // S^T layout: register r of lane half hl holds key
@@ -372,7 +420,7 @@ void attn_fwd_kernel(const FwdParams p) {
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_halves(mx);
         const float tile_max = (mx == -INFINITY) ? -INFINITY : mx * c;
         const bool raise = __any(tile_max > m_run + kLazy);
         const float m_new = raise ? fmaxf(m_run, tile_max) : m_run;
@@ -403,7 +451,7 @@ void attn_fwd_kernel(const FwdParams p) {
 
     // ---- O^T += V^T P^T; the V^T operand comes from two transposing reads of
     // 4 keys each (k-slots 0..3 and 4..7 of this lane half)
-    auto pv = [&](const uint8_t *sv, const vec8 (&pb)[PSTEPS]) {
+    auto pv = [&](const uint8_t *sv, const vec8 (&pb)[PSTEPS]) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -417,54 +465,6 @@ void attn_fwd_kernel(const FwdParams p) {
                     vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 acc[t] = H::mfma(a, pb[kk], acc[t]);
             }
-    };
-
-    // ---- scheduling hint for a block holding the next tile's QK^T and this
-    // tile's softmax: alternate one K read, one MFMA and a few VALU
-    // (transcendental included) instructions, so the MFMA pipe is fed while
-    // the softmax runs
-    auto interleave = [&]() {
-#pragma unroll
-        for (int i = 0; i < NT * KSTEPS; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x402, kValuPerMfma, 0);  // VALU + TRANS
-        }
-    };
-
-    // ---- one pipeline step for this wave: softmax and P.V of tile `cur`
-    // (scores already in sc_cur, V in stage sv), overlapped with QK^T of tile
-    // `nxt` (K in stage sk) into sc_nxt
-    auto step = [&](int cur, uint64_t mlo, uint64_t mhi, int nxt, f32x16 (&sc_cur)[NT],
-                    f32x16 (&sc_nxt)[NT], const uint8_t *sk, const uint8_t *sv) {
-        if (!(wave_active && cur < wave_end)) return;  // nothing for this wave any more
-        bool full = cur + BN <= wave_full_end;
-        if (has_mask) full = full && (mlo == kLoMask) && (BN <= 64 || mhi == ~0ull);
-        vec8 pb[PSTEPS];
-        float corr;
-        if (nxt < wave_end) {
-            if (full) {
-                qk(sk, sc_nxt);
-                corr = softmax(std::false_type{}, cur, mlo, mhi, sc_cur, pb);
-                interleave();
-            } else {
-                qk(sk, sc_nxt);
-                corr = softmax(std::true_type{}, cur, mlo, mhi, sc_cur, pb);
-                interleave();
-            }
-        } else {
-            if (full)
-                corr = softmax(std::false_type{}, cur, mlo, mhi, sc_cur, pb);
-            else
-                corr = softmax(std::true_type{}, cur, mlo, mhi, sc_cur, pb);
-        }
-        if (corr != 1.f) {
-#pragma unroll
-            for (int t = 0; t < DT; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[t][r] *= corr;
-        }
-        pv(sv, pb);
     };
 
     if constexpr (WAVES == 8) {
@@ -482,20 +482,16 @@ void attn_fwd_kernel(const FwdParams p) {
         // workgroup per CU).  Step k reads K(k) and V(k-1) and issues the
         // loads of K(k+3) and V(k+2) into the stages step k-1 freed, so a load
         // has three steps to land: the L2/MALL round trip stays hidden.  Every
-        // step issues the same number of loads (a step past the last tile
-        // reloads a valid tile into a stage nobody reads), so one counted
-        // wait -- all but the two youngest steps' loads -- orders the ring.
-        __shared__ __attribute__((aligned(1024))) uint8_t sK2[TILE_BYTES];
-        __shared__ __attribute__((aligned(1024))) uint8_t sV2[TILE_BYTES];
-        __shared__ __attribute__((aligned(1024))) uint8_t sK3[TILE_BYTES];
-        __shared__ __attribute__((aligned(1024))) uint8_t sV3[TILE_BYTES];
+        // step issues the same number of loads (pad loads for tiles past the
+        // range), so one counted wait -- all but the two youngest steps'
+        // loads -- orders the ring.
         static_assert(PPW == 1 || PPW == 2, "counted waits below assume 1 or 2 loads per tile");
 
         const int group = wave >> 2;
         f32x16 sc[NT];
         vec8 pb[PSTEPS];
         float corr_pending = 1.f;
-        auto mma_phase = [&](int cur, int prev, const uint8_t *sk, const uint8_t *sv) {
+        auto mma_phase = [&](int cur, int prev, const uint8_t *sk, const uint8_t *sv) __attribute__((always_inline)) {
             const bool do_qk = wave_active && cur < wave_end;
             const bool do_pv = wave_active && prev >= 0 && prev < wave_end;
             if (do_pv && corr_pending != 1.f) {
@@ -516,7 +512,7 @@ void attn_fwd_kernel(const FwdParams p) {
                 sched_read_ahead<2 * DT * PSTEPS, DT * PSTEPS>();
             }
         };
-        auto softmax_phase = [&](int tile, uint64_t lo, uint64_t hi) {
+        auto softmax_phase = [&](int tile, uint64_t lo, uint64_t hi) __attribute__((always_inline)) {
             if (!(wave_active && tile >= 0 && tile < wave_end)) return;
             bool full = tile + BN <= wave_full_end;
             if (has_mask) full = full && (lo == kLoMask) && (BN <= 64 || hi == ~0ull);
@@ -530,30 +526,31 @@ void attn_fwd_kernel(const FwdParams p) {
         // tiles past the workgroup's range read as wg_end
         uint64_t lo0 = ~0ull, hi0 = ~0ull, lo1 = ~0ull, hi1 = ~0ull, lo2 = ~0ull, hi2 = ~0ull,
                  lo3 = ~0ull, hi3 = ~0ull, plo = ~0ull, phi = ~0ull;
-        int t0 = find_tile(kbeg, lo0, hi0);
+        int t0 = first_tile;
+        lo0 = first_lo;
+        hi0 = first_hi;
         int t1 = t0 < wg_end ? find_tile(t0 + BN, lo1, hi1) : wg_end;
         int t2 = t1 < wg_end ? find_tile(t1 + BN, lo2, hi2) : wg_end;
         int t3 = wg_end;
         int prev = -1;
         const bool any_tile = t0 < wg_end;
-        const int spare = t0;  // a valid tile to reload when a step has none
-        auto issue_step = [&](int kt, uint8_t *dk, int vt, uint8_t *dv) {
-            issue_kv(kt < wg_end ? kt : spare, dk, vt < wg_end ? vt : spare, dv);
-        };
+        int32_t pg_next = 0, pg_t2 = 0;  // page entries of the next K tile and of t2
         // one step: K(t0) in K_CUR, V(prev) in V_PREV; K(t3) -> K_NEW, V(t2) -> V_NEW.
         // The step with t0 == wg_end only finishes P.V of the last tile; steps
-        // after it find no work and reload the spare tile.  (A macro, expanded
+        // after it find no blockIdx.x and issue pad loads.  (A macro, expanded
         // in the loop below: the step holds the workgroup barriers, which the
         // compiler mishandled inside a lambda -- it deleted the computation.)
 #define MIATTN_PP_STEP(K_CUR, V_PREV, K_NEW, V_NEW)                                     \
         {                                                                               \
             t3 = t2 < wg_end ? find_tile(t2 + BN, lo3, hi3) : wg_end;                   \
-            issue_step(t3, K_NEW, t2, V_NEW);                                           \
+            issue_kv(t3, pg_next, K_NEW, t2, pg_t2, V_NEW);                             \
+            pg_t2 = pg_next;                                                            \
+            pg_next = tile_page(t3 + BN);                                               \
             if (group == 0) /* phase A */                                               \
                 mma_phase(t0, prev, K_CUR, V_PREV);                                     \
             else                                                                        \
                 softmax_phase(prev, plo, phi);                                          \
-            ring_barrier();                                                            \
+            ring_barrier();                                                             \
             if (group == 0) /* phase B */                                               \
                 softmax_phase(t0 < wg_end ? t0 : -1, lo0, hi0);                         \
             else                                                                        \
@@ -572,11 +569,16 @@ void attn_fwd_kernel(const FwdParams p) {
         // which LDS array each direct load writes, and a load that might not
         // have been issued would make it wait for all of them before each read.
         if (any_tile) {
-            // prologue: steps -3, -2, -1 of loads (K(t0) with a spare V; K(t1),
+            // prologue: steps -3, -2, -1 of loads (K(t0) with a pad V; K(t1),
             // V(t0); K(t2), V(t1)), then wait for the first
-            issue_step(t0, sK0, t0, sV3);
-            issue_step(t1, sK1, t0, sV0);
-            issue_step(t2, sK2, t1, sV1);
+            {
+                const int32_t g0 = tile_page(t0), g1 = tile_page(t1), g2 = tile_page(t2);
+                issue_kv(t0, g0, sK0, wg_end, g0, sV3);
+                issue_kv(t1, g1, sK1, t0, g0, sV0);
+                issue_kv(t2, g2, sK2, t1, g1, sV1);
+                pg_t2 = g2;
+                pg_next = tile_page(t2 + BN);
+            }
             wait_vmcnt<4 * PPW>();
             ring_barrier();
             // The shared arrays are named only here, in the kernel body, and
@@ -595,50 +597,106 @@ void attn_fwd_kernel(const FwdParams p) {
         }
 #undef MIATTN_PP_STEP
     } else {
-        // ---- main loop.  K and V have rings of two stages each.  At the start of
-        // the step for tile `cur`: its scores are in registers, its V is in one V
-        // stage and the next tile's K in one K stage; the step streams the K of
-        // the tile after next and the V of the next tile into the free stages
-        // (straight from HBM, no registers) while the waves compute.
-        uint64_t mc_lo = ~0ull, mc_hi = ~0ull, mn_lo = ~0ull, mn_hi = ~0ull, m2_lo = ~0ull,
-                 m2_hi = ~0ull;
-        f32x16 scA[NT], scB[NT];
-        int cur = find_tile(kbeg, mc_lo, mc_hi);
-        int nxt = cur < wg_end ? find_tile(cur + BN, mn_lo, mn_hi) : wg_end;
-        if (cur < wg_end) {
-            issue_k(cur, sK0);
-            issue_v(cur, sV0);
+        // ---- streaming loop (decode-shaped calls and D = 256).  Each step
+        // computes one tile (QK^T, softmax, P.V) from LDS while the loads of
+        // the tile three steps ahead land in the stage the previous step
+        // freed; the same counted wait as above (all but the two youngest
+        // steps' loads) and one barrier per step order the ring.
+        // ring depth: three stages for the two-wave decode workgroup, four
+        // otherwise
+        constexpr int kStages = SPLIT_ROLES ? 3 : 4;
+        f32x16 sc[NT];
+        vec8 pb[PSTEPS];
+        uint64_t lo0 = first_lo, hi0 = first_hi, lo1 = ~0ull, hi1 = ~0ull, lo2 = ~0ull,
+                 hi2 = ~0ull, lo3 = ~0ull, hi3 = ~0ull;
+        int t0 = first_tile;
+        int t1 = t0 < wg_end ? find_tile(t0 + BN, lo1, hi1) : wg_end;
+        int t2 = (kStages == 4 && t1 < wg_end) ? find_tile(t1 + BN, lo2, hi2) : wg_end;
+        int t3 = wg_end;
+        int32_t pg_next = 0;  // page entry of the next tile to load
+        auto compute = [&](const uint8_t *sk, const uint8_t *sv) __attribute__((always_inline)) {
+            if (!(wave_active && t0 < wave_end)) return;
+            bool full = t0 + BN <= wave_full_end;
+            if (has_mask) full = full && (lo0 == kLoMask) && (BN <= 64 || hi0 == ~0ull);
+            qk(sk, sc);
+            const float corr = full ? softmax(std::false_type{}, t0, lo0, hi0, sc, pb)
+                                    : softmax(std::true_type{}, t0, lo0, hi0, sc, pb);
+            if (corr != 1.f) {
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[t][r] *= corr;
+            }
+            pv(sv, pb);
+        };
+#define MIATTN_ST_STEP(K_CUR, V_CUR, K_NEW, V_NEW)                                      \
+        {                                                                               \
+            t3 = t2 < wg_end ? find_tile(t2 + BN, lo3, hi3) : wg_end;                   \
+            issue_kv(t3, pg_next, K_NEW, t3, pg_next, V_NEW);                           \
+            pg_next = tile_page(t3 + BN);                                               \
+            compute(K_CUR, V_CUR);                                                      \
+            /* the loads issued two steps ago hold tile t1 */                          \
+            wait_vmcnt<4 * PPW>();                                                      \
+            ring_barrier();                                                             \
+            t0 = t1; lo0 = lo1; hi0 = hi1;                                              \
+            t1 = t2; lo1 = lo2; hi1 = hi2;                                              \
+            t2 = t3; lo2 = lo3; hi2 = hi3;                                              \
         }
-        if (nxt < wg_end) issue_k(nxt, sK1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (wave_active && cur < wave_end) qk(sK0, scA);
-        while (cur < wg_end) {
-            // tile cur: scores in scA, V in sV0; tile nxt: K in sK1
-            int nxt2 = nxt < wg_end ? find_tile(nxt + BN, m2_lo, m2_hi) : wg_end;
-            if (nxt2 < wg_end) issue_k(nxt2, sK0);
-            if (nxt < wg_end) issue_v(nxt, sV1);
-            step(cur, mc_lo, mc_hi, nxt, scA, scB, sK1, sV0);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            cur = nxt; mc_lo = mn_lo; mc_hi = mn_hi;
-            nxt = nxt2; mn_lo = m2_lo; mn_hi = m2_hi;
-            if (cur >= wg_end) break;
-            // tile cur: scores in scB, V in sV1; tile nxt: K in sK0
-            nxt2 = nxt < wg_end ? find_tile(nxt + BN, m2_lo, m2_hi) : wg_end;
-            if (nxt2 < wg_end) issue_k(nxt2, sK1);
-            if (nxt < wg_end) issue_v(nxt, sV0);
-            step(cur, mc_lo, mc_hi, nxt, scB, scA, sK0, sV1);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            cur = nxt; mc_lo = mn_lo; mc_hi = mn_hi;
-            nxt = nxt2; mn_lo = m2_lo; mn_hi = m2_hi;
+        if (t0 < wg_end && kStages == 4) {
+            {
+                const int32_t g0 = tile_page(t0), g1 = tile_page(t1), g2 = tile_page(t2);
+                issue_kv(t0, g0, sK0, t0, g0, sV0);
+                issue_kv(t1, g1, sK1, t1, g1, sV1);
+                issue_kv(t2, g2, sK2, t2, g2, sV2);
+                pg_next = tile_page(t2 + BN);
+            }
+            wait_vmcnt<4 * PPW>();
+            ring_barrier();
+            do {
+                MIATTN_ST_STEP(sK0, sV0, sK3, sV3)
+                MIATTN_ST_STEP(sK1, sV1, sK0, sV0)
+                MIATTN_ST_STEP(sK2, sV2, sK1, sV1)
+                MIATTN_ST_STEP(sK3, sV3, sK2, sV2)
+            } while (t0 < wg_end);
+            wait_vmcnt<0>();
         }
+#undef MIATTN_ST_STEP
+        // three stages (decode: 48 KB of LDS, three workgroups per CU): step k
+        // computes t0 while t2 loads; at its end the loads of the previous
+        // step (tile t1) must have landed -- all but this step's.
+#define MIATTN_ST3_STEP(K_CUR, V_CUR, K_NEW, V_NEW)                                     \
+        {                                                                               \
+            t2 = t1 < wg_end ? find_tile(t1 + BN, lo2, hi2) : wg_end;                   \
+            issue_kv(t2, pg_next, K_NEW, t2, pg_next, V_NEW);                           \
+            pg_next = tile_page(t2 + BN);                                               \
+            compute(K_CUR, V_CUR);                                                      \
+            wait_vmcnt<2 * PPW>();                                                      \
+            ring_barrier();                                                             \
+            t0 = t1; lo0 = lo1; hi0 = hi1;                                              \
+            t1 = t2; lo1 = lo2; hi1 = hi2;                                              \
+        }
+        if (t0 < wg_end && kStages == 3) {
+            {
+                const int32_t g0 = tile_page(t0), g1 = tile_page(t1);
+                issue_kv(t0, g0, sK0, t0, g0, sV0);
+                issue_kv(t1, g1, sK1, t1, g1, sV1);
+                pg_next = tile_page(t1 + BN);
+            }
+            wait_vmcnt<2 * PPW>();
+            ring_barrier();
+            do {
+                MIATTN_ST3_STEP(sK0, sV0, sK2, sV2)
+                MIATTN_ST3_STEP(sK1, sV1, sK0, sV0)
+                MIATTN_ST3_STEP(sK2, sV2, sK1, sV1)
+            } while (t0 < wg_end);
+            wait_vmcnt<0>();
+        }
+#undef MIATTN_ST3_STEP
     }
 
     // ---- epilogue: normalise and store (no barrier below this point)
     if (!wave_active) return;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = sum_halves(l_run);
     if (!row_ok) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
@@ -673,41 +731,42 @@ void attn_fwd_kernel(const FwdParams p) {
             }
         if (hl == 0) p.lse_part[part] = lse_v;
     }
+
 }
 
-template <int D, bool BF16, bool PAGED, int WAVES>
+template <int D, bool BF16, int KV, int WAVES>
 hipError_t launch_one(const FwdParams &p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, PAGED, WAVES>), dim3(grid), dim3(64 * WAVES), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, KV, WAVES>), dim3(grid), dim3(64 * WAVES), 0,
                        stream, p);
     return hipGetLastError();
 }
 
+template <int D, int WAVES, int KV>
+hipError_t launch_kv(const FwdParams &p, bool bf16, int grid, hipStream_t stream) {
+    return bf16 ? launch_one<D, true, KV, WAVES>(p, grid, stream)
+                : launch_one<D, false, KV, WAVES>(p, grid, stream);
+}
+
 template <int D, int WAVES>
 hipError_t launch_w(const FwdParams &p, bool bf16, bool paged, int grid, hipStream_t stream) {
-    if (bf16)
-        return paged ? launch_one<D, true, true, WAVES>(p, grid, stream)
-                     : launch_one<D, true, false, WAVES>(p, grid, stream);
-    return paged ? launch_one<D, false, true, WAVES>(p, grid, stream)
-                 : launch_one<D, false, false, WAVES>(p, grid, stream);
+    if (!paged) return launch_kv<D, WAVES, kDense>(p, bf16, grid, stream);
+    if (p.page_shift >= __builtin_ctz(keys_per_tile(D, WAVES)))
+        return launch_kv<D, WAVES, kPagedTile>(p, bf16, grid, stream);
+    return launch_kv<D, WAVES, kPagedPiece>(p, bf16, grid, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int waves,
                            int grid, hipStream_t stream) {
-    if (waves == 8) {
-        switch (D) {
-            case 64: return launch_w<64, 8>(p, bf16, paged, grid, stream);
-            case 128: return launch_w<128, 8>(p, bf16, paged, grid, stream);
-            default: return hipErrorInvalidValue;
-        }
-    }
-    switch (D) {
-        case 64: return launch_w<64, 4>(p, bf16, paged, grid, stream);
-        case 128: return launch_w<128, 4>(p, bf16, paged, grid, stream);
-        case 256: return launch_w<256, 4>(p, bf16, paged, grid, stream);
-        default: return hipErrorInvalidValue;
-    }
+    if (waves == 8 && D == 64) return launch_w<64, 8>(p, bf16, paged, grid, stream);
+    if (waves == 8 && D == 128) return launch_w<128, 8>(p, bf16, paged, grid, stream);
+    if (waves == 1 && D == 64) return launch_w<64, 1>(p, bf16, paged, grid, stream);
+    if (waves == 1 && D == 128) return launch_w<128, 1>(p, bf16, paged, grid, stream);
+    if (waves == 2 && D == 64) return launch_w<64, 2>(p, bf16, paged, grid, stream);
+    if (waves == 2 && D == 128) return launch_w<128, 2>(p, bf16, paged, grid, stream);
+    if (waves == 4 && D == 256) return launch_w<256, 4>(p, bf16, paged, grid, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace miattn

@@ -16,18 +16,23 @@ namespace miattn {
 constexpr int kRowsPerWave = 32;  // one 32x32 MFMA column block
 
 // Two schedules share one kernel template:
-//   4 waves (256 threads): each wave pipelines the next tile's QK^T under the
-//     current tile's softmax; used for D = 256 and decode-shaped calls.
 //   8 waves (512 threads, two per SIMD): the waves form two groups that
 //     alternate, phase by phase, between an MFMA phase (QK^T of one tile and
 //     P.V of the previous one) and a softmax phase, so each SIMD always has
 //     one wave feeding the matrix core while the other runs VALU work
 //     ("ping-pong"); used for D <= 128 prefill.
-constexpr int rows_per_workgroup(int waves) { return kRowsPerWave * waves; }
+//   streaming (2 waves for decode-shaped calls with D <= 128 -- wave 0
+//     computes, wave 1 issues all loads -- and 4 waves for D = 256): each
+//     step computes one tile while later tiles load.
+constexpr int rows_per_workgroup(int waves) { return waves == 2 ? kRowsPerWave : kRowsPerWave * waves; }
 
-// Keys per KV tile.  4 waves: 8192 / D keys (a 16 KB K or V tile, 4 KB per
-// wave of direct loads).  8 waves: 64 keys (8 KB at D = 64, 16 KB at D = 128).
-constexpr int keys_per_tile(int D, int waves) { return waves == 8 ? 64 : 8192 / D; }
+// Keys per KV tile.  8 waves: 64 keys (8 KB at D = 64, 16 KB at D = 128).
+// Streaming: 8 KB tiles (4096 / D keys), at least one 32-key score block (16
+// KB at D = 256); with four-stage rings a decode workgroup then takes 64 KB of
+// LDS and two fit on a CU.
+constexpr int keys_per_tile(int D, int waves) {
+    return waves == 8 ? 64 : (4096 / D > 32 ? 4096 / D : 32);
+}
 
 struct FwdParams {
     const uint16_t *q;   // [B, Sq, Hq, D]
@@ -51,6 +56,7 @@ struct FwdParams {
     int q_mode;        // 0: q as given; 1: q negated (alpha < 0); 2: q zeroed (alpha == 0)
     int xcd_units;     // (batch*KV head, split) units per XCD, or 0 for linear order
     int xcd_unit_major;  // with xcd_units: an XCD runs all row blocks of a unit, then the next
+    int heads_inner;     // units ordered (batch, split, KV head) instead of (batch, KV head, split)
 };
 
 struct MergeParams {

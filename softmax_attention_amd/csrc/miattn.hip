@@ -181,11 +181,13 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
 
     p.G = p.Hq / p.Hkv;
     p.rows = p.Sq * p.G;
-    // 8-wave ping-pong schedule for D <= 128 prefill; the 4-wave pipelined
-    // schedule for D = 256 and for decode-shaped calls (a few packed rows)
-    int waves = (D <= 128 && p.rows > miattn::kRowsPerWave) ? 8 : 4;
+    // D <= 128: the 8-wave ping-pong schedule for prefill, a two-wave
+    // streaming workgroup (one computing, one loading) for decode-shaped calls
+    // (all packed rows in one MFMA column block); D = 256: the 4-wave
+    // streaming schedule.
+    int waves = D == 256 ? 4 : (p.rows > miattn::kRowsPerWave ? 8 : 2);
     const int forced = env_int("MIATTN_WAVES", 0);
-    if ((forced == 4 || forced == 8) && (forced == 4 || D <= 128)) waves = forced;
+    if (D <= 128 && (forced == 1 || forced == 2 || forced == 8)) waves = forced;
     const int BN = miattn::keys_per_tile(D, waves);
     const int BM = miattn::rows_per_workgroup(waves);
     p.n_mblocks = (p.rows + BM - 1) / BM;
@@ -225,6 +227,8 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
     const int64_t units = bhs * n_splits;
     p.xcd_units = (units % 8 == 0) ? (int)(units / 8) : 0;
     p.xcd_unit_major = env_int("MIATTN_XCD_ORDER", 0);
+    // split decode: the KV heads of one key range run side by side
+    p.heads_inner = env_int("MIATTN_HEADS_INNER", (n_splits > 1 && p.n_mblocks == 1) ? 1 : 0);
 
     if (n_splits > 1) {
         const int64_t nrow = n_splits * bhs * p.rows;
