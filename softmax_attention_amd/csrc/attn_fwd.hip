@@ -55,7 +55,7 @@ using namespace dev;
 // of LDS each) on one CU; the 4-wave D = 256 schedule runs one workgroup per
 // CU.
 template <int D, int WAVES>
-constexpr int waves_per_eu() { return (WAVES == 8 || WAVES == 2) ? 2 : 1; }
+constexpr int waves_per_eu() { return (WAVES == 8 || WAVES == 2 || WAVES == 3) ? 2 : 1; }
 
 #ifndef MIATTN_READ_AHEAD
 #define MIATTN_READ_AHEAD 6
@@ -95,10 +95,12 @@ void attn_fwd_kernel(const FwdParams p) {
     constexpr int BN = keys_per_tile(D, WAVES);    // keys per tile
     constexpr int TILE_BYTES = BN * D * 2;         // one K (or V) tile
     constexpr int PIECES = TILE_BYTES / 1024;      // 1 KB direct loads per tile
-    // The two-wave (decode) schedule splits the roles: wave 0 computes, wave 1
-    // issues every load.  Otherwise each wave issues an equal share.
-    constexpr bool SPLIT_ROLES = WAVES == 2;
-    constexpr int LOADERS = SPLIT_ROLES ? 1 : WAVES;
+    // The decode schedule (2 or 3 waves) splits the roles: wave 0 computes,
+    // the other waves issue every load (one loading wave streams only about
+    // half of what a CU's memory path takes).  Otherwise each wave issues an
+    // equal share.
+    constexpr bool SPLIT_ROLES = WAVES == 2 || WAVES == 3;
+    constexpr int LOADERS = SPLIT_ROLES ? WAVES - 1 : WAVES;
     constexpr int PPW = PIECES / LOADERS;          // 1 KB pieces per loading wave
     constexpr int NT = BN / 32;                    // 32-key score blocks per tile
     constexpr int KSTEPS = D / 16;                 // MFMA k-steps over D
@@ -124,56 +126,12 @@ void attn_fwd_kernel(const FwdParams p) {
     const int l32 = lane & 31;
     const int hl = lane >> 5;
 
-    const int units = p.B * p.Hkv * p.n_splits;
-    // ---- which (row block, batch, KV head, split) this workgroup owns.
-    // Workgroups are dispatched round-robin over the 8 XCDs; when the unit
-    // count allows, consecutive workgroups of one XCD share a (batch, KV head)
-    // so its K/V stays in that XCD's L2.  Causal row blocks run heaviest first.
-    int rank, unit;
-    if (p.xcd_units > 0 && p.xcd_unit_major) {
-        // each XCD finishes the row blocks of one unit before the next, so its
-        // L2 holds one (batch, KV head)'s K/V at a time
-        const int s = blockIdx.x >> 3;
-        unit = (blockIdx.x & 7) * p.xcd_units + s / p.n_mblocks;
-        rank = s % p.n_mblocks;
-    } else if (p.xcd_units > 0) {
-        const int s = blockIdx.x >> 3;
-        unit = (blockIdx.x & 7) * p.xcd_units + s % p.xcd_units;
-        rank = s / p.xcd_units;
-    } else {
-        rank = blockIdx.x / units;
-        unit = blockIdx.x - rank * units;
-    }
-    const int mblock = p.causal ? (p.n_mblocks - 1 - rank) : rank;
-    // Units are (batch, KV head, split) with the split fastest, or -- with
-    // heads_inner, for split decode -- (batch, split, KV head) with the head
-    // fastest: the KV heads of one position share the cache rows, so
-    // workgroups that run together then read whole rows of the same pages.
-    int b, kvh, split;
-    if (p.heads_inner) {
-        const int bs = unit / p.Hkv;
-        kvh = unit - bs * p.Hkv;
-        b = bs / p.n_splits;
-        split = bs - b * p.n_splits;
-    } else {
-        const int bh_ = unit / p.n_splits;
-        split = unit - bh_ * p.n_splits;
-        b = bh_ / p.Hkv;
-        kvh = bh_ - b * p.Hkv;
-    }
-    const int bh = b * p.Hkv + kvh;
-
-    // (a paged length is clamped to the table's capacity, and an empty cache
-    // holds no keys, so that malformed lengths cannot address memory
-    // outside the table or the cache)
-    const int kv_len =
-        !PAGED ? p.Skv
-               : (p.num_pages > 0 ? min(max(p.seqlen[b], 0), p.max_pages << p.page_shift) : 0);
-    const int kbeg = split * p.split_len;
-    // Splits past the end are never read by the merge, which counts the
-    // splits that hold keys from the same length.
-    if (p.n_splits > 1 && kbeg >= kv_len) return;
-    const int kend = min(kv_len, kbeg + p.split_len);
+    // ---- one unit of work: the key range [kbeg, kend) of row block `mblock`
+    // of (batch b, KV head kvh), whose length is kv_len; a split result goes
+    // to partial slot `slot`, a whole result straight to o and lse.
+    auto run = [&](const int mblock, const int b, const int kvh, const int kv_len,
+                   const int kbeg, const int kend, const int64_t slot,
+                   const bool partial) __attribute__((always_inline)) {
     const int delta = kv_len - p.Sq;  // query i sits at key position i + delta
 
     const int row0 = mblock * BM;
@@ -260,8 +218,8 @@ void attn_fwd_kernel(const FwdParams p) {
     // waiting for all of them whenever a direct load is in flight.
     constexpr int RPP = 512 / D;                                // keys per piece
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);    // wave-uniform
-    const int loader = SPLIT_ROLES ? 0 : wave_u;  // this wave's index among the loaders
-    const bool loads = !SPLIT_ROLES || wave_u == 1;
+    const int loader = SPLIT_ROLES ? wave_u - 1 : wave_u;  // this wave's index among the loaders
+    const bool loads = !SPLIT_ROLES || wave_u >= 1;
     const int l_dr = lane / (D / 8);   // this lane's key within a piece
     const int l_pos = lane % (D / 8);  // this lane's 16-byte position in the row
     const int64_t hstride = (int64_t)p.Hkv * D;  // elements between consecutive keys
@@ -701,7 +659,7 @@ void attn_fwd_kernel(const FwdParams p) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
 
-    if (p.n_splits == 1) {
+    if (!partial) {
         uint16_t *orow =
             p.o + (((int64_t)b * p.Sq + my_i) * p.Hq + (int64_t)kvh * p.G + my_gh) * D;
 #pragma unroll
@@ -718,7 +676,7 @@ void attn_fwd_kernel(const FwdParams p) {
         if (p.lse != nullptr && hl == 0)
             p.lse[((int64_t)b * p.Hq + (int64_t)kvh * p.G + my_gh) * p.Sq + my_i] = lse_v;
     } else {
-        const int64_t part = ((int64_t)bh * p.n_splits + split) * p.rows + my_row;
+        const int64_t part = slot * p.rows + my_row;
         float *op = p.o_part + part * D;
 #pragma unroll
         for (int t = 0; t < DT; ++t)
@@ -732,6 +690,90 @@ void attn_fwd_kernel(const FwdParams p) {
         if (hl == 0) p.lse_part[part] = lse_v;
     }
 
+    };
+
+    // ---- which work this workgroup owns
+    const int units = p.B * p.Hkv * p.n_splits;
+    if constexpr (SPLIT_ROLES) {
+        if (p.sk_grid > 0) {
+            // Stream-K decode: the (batch, KV head) key sequences, heads
+            // fastest, form one sequence of T key tiles; workgroup g takes
+            // tiles [g T / G, (g+1) T / G) -- an equal share, whatever the
+            // lengths -- and writes one partial per unit it touches, to slot
+            // unit + g (the plan kernel wrote T and each workgroup's first
+            // unit and tile; the merge kernel finds the slots the same way).
+            const int g = blockIdx.x;
+            const int64_t T = *(const int64_t *)p.sk_plan;
+            const int64_t s0 = (int64_t)g * T / p.sk_grid;
+            const int64_t s1 = (int64_t)(g + 1) * T / p.sk_grid;
+            if (s0 >= s1) return;
+            const int32_t *start = p.sk_plan + 2 + (p.B + 1);
+            int u = start[2 * g];
+            int off = start[2 * g + 1];
+            for (int64_t at = s0; at < s1; ++u, off = 0) {
+                const int b = u / p.Hkv;
+                const int kvh = u - b * p.Hkv;
+                const int len = PAGED ? (p.num_pages > 0 ? min(max(p.seqlen[b], 0),
+                                                               p.max_pages << p.page_shift)
+                                                         : 0)
+                                      : p.Skv;
+                const int tiles = (len + BN - 1) / BN;
+                const int n = (int)min((int64_t)(tiles - off), s1 - at);
+                if (n <= 0) continue;
+                run(0, b, kvh, len, off * BN, min(len, (off + n) * BN), (int64_t)u + g, true);
+                at += n;
+            }
+            return;
+        }
+    }
+    // Workgroups are dispatched round-robin over the 8 XCDs; when the unit
+    // count allows, consecutive workgroups of one XCD share a (batch, KV head)
+    // so its K/V stays in that XCD's L2.  Causal row blocks run heaviest first.
+    int rank, unit;
+    if (p.xcd_units > 0 && p.xcd_unit_major) {
+        // each XCD finishes the row blocks of one unit before the next, so its
+        // L2 holds one (batch, KV head)'s K/V at a time
+        const int s = blockIdx.x >> 3;
+        unit = (blockIdx.x & 7) * p.xcd_units + s / p.n_mblocks;
+        rank = s % p.n_mblocks;
+    } else if (p.xcd_units > 0) {
+        const int s = blockIdx.x >> 3;
+        unit = (blockIdx.x & 7) * p.xcd_units + s % p.xcd_units;
+        rank = s / p.xcd_units;
+    } else {
+        rank = blockIdx.x / units;
+        unit = blockIdx.x - rank * units;
+    }
+    const int mblock = p.causal ? (p.n_mblocks - 1 - rank) : rank;
+    // Units are (batch, KV head, split) with the split fastest, or -- with
+    // heads_inner -- (batch, split, KV head) with the head fastest: the KV
+    // heads of one position share the cache rows, so workgroups that run
+    // together then read whole rows of the same pages.
+    int b, kvh, split;
+    if (p.heads_inner) {
+        const int bs = unit / p.Hkv;
+        kvh = unit - bs * p.Hkv;
+        b = bs / p.n_splits;
+        split = bs - b * p.n_splits;
+    } else {
+        const int bh_ = unit / p.n_splits;
+        split = unit - bh_ * p.n_splits;
+        b = bh_ / p.Hkv;
+        kvh = bh_ - b * p.Hkv;
+    }
+    // (a paged length is clamped to the table's capacity, and an empty cache
+    // holds no keys, so that malformed lengths cannot address memory
+    // outside the table or the cache)
+    const int kv_len =
+        !PAGED ? p.Skv
+               : (p.num_pages > 0 ? min(max(p.seqlen[b], 0), p.max_pages << p.page_shift) : 0);
+    const int kbeg = split * p.split_len;
+    // Splits past the end are never read by the merge, which counts the
+    // splits that hold keys from the same length.
+    if (p.n_splits > 1 && kbeg >= kv_len) return;
+    const int kend = min(kv_len, kbeg + p.split_len);
+    run(mblock, b, kvh, kv_len, kbeg, kend, (int64_t)(b * p.Hkv + kvh) * p.n_splits + split,
+        p.n_splits > 1);
 }
 
 template <int D, bool BF16, int KV, int WAVES>
@@ -739,6 +781,23 @@ hipError_t launch_one(const FwdParams &p, int grid, hipStream_t stream) {
     hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, KV, WAVES>), dim3(grid), dim3(64 * WAVES), 0,
                        stream, p);
     return hipGetLastError();
+}
+
+template <int D, bool BF16, int KV, int WAVES>
+int blocks_per_cu() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel<D, BF16, KV, WAVES>,
+                                                     64 * WAVES, 0) != hipSuccess)
+        return 0;
+    return n;
+}
+
+template <int D, int W>
+int decode_blocks(const FwdParams &p, bool bf16, bool paged) {
+    const bool tile = p.page_shift >= __builtin_ctz(keys_per_tile(D, W));
+    if (!paged) return bf16 ? blocks_per_cu<D, true, kDense, W>() : blocks_per_cu<D, false, kDense, W>();
+    if (tile) return bf16 ? blocks_per_cu<D, true, kPagedTile, W>() : blocks_per_cu<D, false, kPagedTile, W>();
+    return bf16 ? blocks_per_cu<D, true, kPagedPiece, W>() : blocks_per_cu<D, false, kPagedPiece, W>();
 }
 
 template <int D, int WAVES, int KV>
@@ -757,14 +816,22 @@ hipError_t launch_w(const FwdParams &p, bool bf16, bool paged, int grid, hipStre
 
 }  // namespace
 
+int attn_fwd_decode_blocks_per_cu(const FwdParams &p, int D, bool bf16, bool paged, int waves) {
+    if (waves == 2 && D == 64) return decode_blocks<64, 2>(p, bf16, paged);
+    if (waves == 2 && D == 128) return decode_blocks<128, 2>(p, bf16, paged);
+    if (waves == 3 && D == 64) return decode_blocks<64, 3>(p, bf16, paged);
+    if (waves == 3 && D == 128) return decode_blocks<128, 3>(p, bf16, paged);
+    return 0;
+}
+
 hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int waves,
                            int grid, hipStream_t stream) {
     if (waves == 8 && D == 64) return launch_w<64, 8>(p, bf16, paged, grid, stream);
     if (waves == 8 && D == 128) return launch_w<128, 8>(p, bf16, paged, grid, stream);
-    if (waves == 1 && D == 64) return launch_w<64, 1>(p, bf16, paged, grid, stream);
-    if (waves == 1 && D == 128) return launch_w<128, 1>(p, bf16, paged, grid, stream);
     if (waves == 2 && D == 64) return launch_w<64, 2>(p, bf16, paged, grid, stream);
     if (waves == 2 && D == 128) return launch_w<128, 2>(p, bf16, paged, grid, stream);
+    if (waves == 3 && D == 64) return launch_w<64, 3>(p, bf16, paged, grid, stream);
+    if (waves == 3 && D == 128) return launch_w<128, 3>(p, bf16, paged, grid, stream);
     if (waves == 4 && D == 256) return launch_w<256, 4>(p, bf16, paged, grid, stream);
     return hipErrorInvalidValue;
 }

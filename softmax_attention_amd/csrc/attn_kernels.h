@@ -21,10 +21,12 @@ constexpr int kRowsPerWave = 32;  // one 32x32 MFMA column block
 //     P.V of the previous one) and a softmax phase, so each SIMD always has
 //     one wave feeding the matrix core while the other runs VALU work
 //     ("ping-pong"); used for D <= 128 prefill.
-//   streaming (2 waves for decode-shaped calls with D <= 128 -- wave 0
-//     computes, wave 1 issues all loads -- and 4 waves for D = 256): each
-//     step computes one tile while later tiles load.
-constexpr int rows_per_workgroup(int waves) { return waves == 2 ? kRowsPerWave : kRowsPerWave * waves; }
+//   streaming (3 waves for decode-shaped calls with D <= 128 -- wave 0
+//     computes, waves 1 and 2 issue all loads -- and 4 waves for D = 256):
+//     each step computes one tile while later tiles load.
+constexpr int rows_per_workgroup(int waves) {
+    return (waves == 2 || waves == 3) ? kRowsPerWave : kRowsPerWave * waves;
+}
 
 // Keys per KV tile.  8 waves: 64 keys (8 KB at D = 64, 16 KB at D = 128).
 // Streaming: 8 KB tiles (4096 / D keys), at least one 32-key score block (16
@@ -57,6 +59,11 @@ struct FwdParams {
     int xcd_units;     // (batch*KV head, split) units per XCD, or 0 for linear order
     int xcd_unit_major;  // with xcd_units: an XCD runs all row blocks of a unit, then the next
     int heads_inner;     // units ordered (batch, split, KV head) instead of (batch, KV head, split)
+    // stream-K decode (two-wave schedule): grid size G, or 0; the plan (int64
+    // T, then the tile prefix over batches [B+1], then per workgroup its first
+    // unit and tile [G][2]) written by the plan kernel
+    int sk_grid;
+    const int32_t *sk_plan;
 };
 
 struct MergeParams {
@@ -67,11 +74,28 @@ struct MergeParams {
     const int32_t *seqlen;  // paged lengths, or nullptr for dense
     int Skv;
     int B, Sq, Hq, Hkv, G, rows, n_splits, split_len;
+    // stream-K decode: grid size (0 otherwise), the plan, keys per tile and
+    // the length clamps the attention kernel applies
+    int sk_grid;
+    const int32_t *sk_plan;
+    int sk_bn, max_pages, page_shift, num_pages;
 };
+
+// Stream-K plan: the kernel's workgroups split the (batch, KV head) key
+// sequences into equal shares of tiles.
+struct PlanParams {
+    const int32_t *seqlen;  // paged lengths, or nullptr for dense (Skv)
+    int Skv, B, Hkv, bn, max_pages, page_shift, num_pages, grid;
+    int32_t *plan;          // out: int64 T, prefix [B+1], starts [grid][2]
+};
+constexpr int kPlanMaxBatch = 16384;  // batch entries the one-workgroup plan kernel handles
 
 // Launchers: return the hipGetLastError() status of the launch.
 hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int waves,
                            int grid, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams &p, int D, bool bf16, hipStream_t stream);
+hipError_t launch_sk_plan(const PlanParams &p, hipStream_t stream);
+// Workgroups of the two-wave (decode) attention kernel one CU runs at once (0 if unknown).
+int attn_fwd_decode_blocks_per_cu(const FwdParams &p, int D, bool bf16, bool paged, int waves);
 
 }  // namespace miattn

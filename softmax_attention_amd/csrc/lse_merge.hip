@@ -39,14 +39,50 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     const int i = r / p.G;
     const int gh = r - i * p.G;
 
-    const int kv_len = p.seqlen ? p.seqlen[b] : p.Skv;
-    // the splits that hold keys of this request (the attention kernel writes
-    // every row of each of them and nothing for the others)
-    const int n_valid = min(p.n_splits, (kv_len + p.split_len - 1) / p.split_len);
-    const int64_t base = (int64_t)bh * p.n_splits * p.rows + r;
+    // The partial results of this (batch, KV head): n_valid slots, `stride`
+    // rows apart, from row `base` on.
+    int n_valid;
+    int64_t base, stride = p.rows;
+    int64_t g_first = 0;  // stream-K: the first workgroup (slot = unit + workgroup)
+    int64_t T = 0;
+    if (p.sk_grid > 0) {
+        // Stream-K: the workgroups that touched this unit's tiles, [P, P +
+        // tiles) of the T-tile sequence; workgroup g held [g T / G, (g+1) T / G).
+        const int len = p.seqlen ? (p.num_pages > 0 ? min(max(p.seqlen[b], 0),
+                                                          p.max_pages << p.page_shift)
+                                                    : 0)
+                                 : p.Skv;
+        const int tiles = (len + p.sk_bn - 1) / p.sk_bn;
+        T = *(const int64_t *)p.sk_plan;
+        const int64_t P = (int64_t)p.Hkv * p.sk_plan[2 + b] + (int64_t)kvh * tiles;
+        if (tiles == 0 || T == 0) {
+            n_valid = 0;
+            g_first = 0;
+        } else {
+            const int G = p.sk_grid;
+            // the workgroup holding tile s is the largest g with g T / G <= s
+            g_first = ((P + 1) * G - 1) / T;
+            const int64_t g_last = ((P + tiles) * G - 1) / T;
+            n_valid = (int)(g_last - g_first + 1);
+        }
+        base = ((int64_t)bh + g_first) * p.rows + r;
+    } else {
+        const int kv_len = p.seqlen ? p.seqlen[b] : p.Skv;
+        // the splits that hold keys of this request (the attention kernel
+        // writes every row of each of them and nothing for the others)
+        n_valid = min(p.n_splits, (kv_len + p.split_len - 1) / p.split_len);
+        base = (int64_t)bh * p.n_splits * p.rows + r;
+    }
+    // stream-K: a workgroup whose share is empty (T < G) wrote nothing
+    auto skip = [&](int s) -> bool {
+        if (p.sk_grid == 0) return false;
+        const int64_t g = g_first + s;
+        return g * T / p.sk_grid == (g + 1) * T / p.sk_grid;
+    };
 
     float M = -INFINITY;
-    for (int s = lane; s < n_valid; s += 64) M = fmaxf(M, p.lse_part[base + (int64_t)s * p.rows]);
+    for (int s = lane; s < n_valid; s += 64)
+        if (!skip(s)) M = fmaxf(M, p.lse_part[base + (int64_t)s * stride]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
@@ -56,7 +92,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     float den = 0.f;
     if (M != -INFINITY) {
         for (int s = 0; s < n_valid; ++s) {
-            const int64_t idx = base + (int64_t)s * p.rows;
+            if (skip(s)) continue;
+            const int64_t idx = base + (int64_t)s * stride;
             const float ls = p.lse_part[idx];
             if (ls == -INFINITY) continue;
             const float w = __expf(ls - M);
@@ -76,6 +113,66 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
             den > 0.f ? M + __logf(den) : -INFINITY;
 }
 
+// Stream-K plan (one workgroup): tiles per batch entry, their exclusive
+// prefix over the batch, T = Hkv * (sum of tiles) key tiles in all, and for
+// each attention workgroup g the unit (batch * Hkv + KV head, heads fastest)
+// and tile within it where its share [g T / G, (g+1) T / G) begins.
+__global__ __launch_bounds__(1024) void sk_plan_kernel(const PlanParams p) {
+    __shared__ int32_t pre[kPlanMaxBatch + 1];
+    __shared__ int32_t part[1024];
+    const int tid = threadIdx.x;
+    auto tiles_of = [&](int b) -> int {
+        const int len = p.seqlen ? (p.num_pages > 0 ? min(max(p.seqlen[b], 0),
+                                                          p.max_pages << p.page_shift)
+                                                    : 0)
+                                 : p.Skv;
+        return (len + p.bn - 1) / p.bn;
+    };
+    // each thread scans a contiguous chunk, then the chunk totals are scanned
+    const int chunk = (p.B + 1023) / 1024;
+    const int lo = min(p.B, tid * chunk), hi = min(p.B, lo + chunk);
+    int sum = 0;
+    for (int b = lo; b < hi; ++b) {
+        pre[b] = sum;  // exclusive within the chunk
+        sum += tiles_of(b);
+    }
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int v = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    const int carry = tid > 0 ? part[tid - 1] : 0;
+    for (int b = lo; b < hi; ++b) pre[b] += carry;
+    if (tid == 0) pre[p.B] = part[1023];
+    __syncthreads();
+    const int64_t T = (int64_t)p.Hkv * pre[p.B];
+    if (tid == 0) *(int64_t *)p.plan = T;
+    for (int b = tid; b <= p.B; b += 1024) p.plan[2 + b] = pre[b];
+    int32_t *start = p.plan + 2 + (p.B + 1);
+    for (int g = tid; g < p.grid; g += 1024) {
+        const int64_t s = (int64_t)g * T / p.grid;
+        int u = p.B * p.Hkv, off = 0;
+        if (s < T) {
+            // the batch entry whose tiles hold s: the last b with Hkv*pre[b] <= s
+            int l = 0, h = p.B - 1;
+            while (l < h) {
+                const int m = (l + h + 1) >> 1;
+                if ((int64_t)p.Hkv * pre[m] <= s) l = m; else h = m - 1;
+            }
+            const int t = pre[l + 1] - pre[l];
+            const int64_t rem = s - (int64_t)p.Hkv * pre[l];
+            const int kvh = (int)(rem / t);
+            u = l * p.Hkv + kvh;
+            off = (int)(rem - (int64_t)kvh * t);
+        }
+        start[2 * g] = u;
+        start[2 * g + 1] = off;
+    }
+}
+
 template <int D, bool BF16>
 hipError_t launch_one(const MergeParams &p, hipStream_t stream) {
     const int64_t rows = (int64_t)p.B * p.Hkv * p.rows;
@@ -93,6 +190,11 @@ hipError_t launch_lse_merge(const MergeParams &p, int D, bool bf16, hipStream_t 
         case 256: return bf16 ? launch_one<256, true>(p, stream) : launch_one<256, false>(p, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_sk_plan(const PlanParams &p, hipStream_t stream) {
+    hipLaunchKernelGGL(sk_plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace miattn

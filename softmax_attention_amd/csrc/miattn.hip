@@ -42,9 +42,10 @@ bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 constexpr int kMaxDevices = 64;
 
 struct DeviceState {
-    void *ws = nullptr;  // split-KV partials
+    void *ws = nullptr;  // split-KV partials (and the stream-K plan)
     size_t ws_bytes = 0;
     int cus = 0;
+    int decode_per_cu[2][2][2][2] = {};  // decode kernel occupancy: [3 waves][D 128][bf16][paged]
 };
 
 std::mutex g_mu;
@@ -61,6 +62,17 @@ int compute_units(int dev) {
         g_dev[dev].cus = n;
     }
     return g_dev[dev].cus;
+}
+
+// Decode workgroups one CU runs at once (occupancy API, cached).
+int decode_per_cu(int dev, const miattn::FwdParams &p, int D, bool bf16, bool paged, int waves) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    int &slot = g_dev[dev].decode_per_cu[waves == 3][D == 128][bf16][paged];
+    if (slot == 0) {
+        const int n = miattn::attn_fwd_decode_blocks_per_cu(p, D, bf16, paged, waves);
+        slot = n > 0 ? n : -1;
+    }
+    return slot > 0 ? slot : 1;
 }
 
 miattn_status workspace(int dev, size_t bytes, void **out) {
@@ -181,23 +193,97 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
 
     p.G = p.Hq / p.Hkv;
     p.rows = p.Sq * p.G;
-    // D <= 128: the 8-wave ping-pong schedule for prefill, a two-wave
-    // streaming workgroup (one computing, one loading) for decode-shaped calls
+    // D <= 128: the 8-wave ping-pong schedule for prefill, a three-wave
+    // streaming workgroup (one computing, two loading) for decode-shaped calls
     // (all packed rows in one MFMA column block); D = 256: the 4-wave
     // streaming schedule.
-    int waves = D == 256 ? 4 : (p.rows > miattn::kRowsPerWave ? 8 : 2);
+    int waves = D == 256 ? 4 : (p.rows > miattn::kRowsPerWave ? 8 : 3);
     const int forced = env_int("MIATTN_WAVES", 0);
-    if (D <= 128 && (forced == 1 || forced == 2 || forced == 8)) waves = forced;
+    if (D <= 128 && (forced == 2 || forced == 3 || forced == 8)) waves = forced;
     const int BN = miattn::keys_per_tile(D, waves);
     const int BM = miattn::rows_per_workgroup(waves);
     p.n_mblocks = (p.rows + BM - 1) / BM;
     const int64_t bhs = (int64_t)p.B * p.Hkv;
     const int64_t cap_tiles = capacity > 0 ? (capacity + BN - 1) / BN : 1;
+    int split_keys = g_split_keys > 0 ? g_split_keys : env_int("MIATTN_SPLIT_KEYS", 0);
+    p.sk_grid = 0;
+    p.sk_plan = nullptr;
+
+    // Decode-shaped calls run stream-K: a grid of what the GPU holds at once,
+    // each workgroup an equal share of all (batch, KV head) key tiles, so no
+    // workgroup waits on a long request or for a dispatch slot.  A forced
+    // split length selects the split plan below instead.
+    if ((waves == 2 || waves == 3) && split_keys <= 0 && p.B <= miattn::kPlanMaxBatch &&
+        env_int("MIATTN_STREAMK", 1)) {
+        int per_cu = decode_per_cu(dev, p, D, bf16, paged, waves);
+        const int want = env_int("MIATTN_SK_PER_CU", 0);  // tuning override
+        if (want > 0 && want < per_cu) per_cu = want;
+        const int G = compute_units(dev) * per_cu;
+        p.n_mblocks = 1;
+        p.n_splits = 1;
+        p.split_len = 0;
+        p.xcd_units = 0;
+        p.xcd_unit_major = 0;
+        p.heads_inner = 0;
+        const int64_t slots = bhs + G;  // partial slot of (unit u, workgroup g): u + g
+        const size_t part_bytes = (size_t)slots * p.rows * (D + 1) * sizeof(float);
+        const size_t plan_off = (part_bytes + 255) / 256 * 256;
+        const size_t plan_bytes = (2 + (size_t)(p.B + 1) + 2 * (size_t)G) * sizeof(int32_t);
+        void *ws = nullptr;
+        miattn_status st = workspace(dev, plan_off + plan_bytes, &ws);
+        if (st != MIATTN_OK) return st;
+        p.o_part = (float *)ws;
+        p.lse_part = p.o_part + slots * p.rows * D;
+        int32_t *plan = (int32_t *)((char *)ws + plan_off);
+        p.sk_grid = G;
+        p.sk_plan = plan;
+
+        miattn::PlanParams q;
+        q.seqlen = paged ? p.seqlen : nullptr;
+        q.Skv = p.Skv;
+        q.B = p.B;
+        q.Hkv = p.Hkv;
+        q.bn = BN;
+        q.max_pages = p.max_pages;
+        q.page_shift = p.page_shift;
+        q.num_pages = p.num_pages;
+        q.grid = G;
+        q.plan = plan;
+        e = timed_launch(1, stream, [&] { return miattn::launch_sk_plan(q, stream); });
+        if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+        e = timed_launch(0, stream, [&] {
+            return miattn::launch_attn_fwd(p, D, bf16, paged, waves, G, stream);
+        });
+        if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+        MergeParams m = {};
+        m.o_part = p.o_part;
+        m.lse_part = p.lse_part;
+        m.o = p.o;
+        m.lse = p.lse;
+        m.seqlen = paged ? p.seqlen : nullptr;
+        m.Skv = p.Skv;
+        m.B = p.B;
+        m.Sq = p.Sq;
+        m.Hq = p.Hq;
+        m.Hkv = p.Hkv;
+        m.G = p.G;
+        m.rows = p.rows;
+        m.n_splits = 1;
+        m.split_len = 0;
+        m.sk_grid = G;
+        m.sk_plan = plan;
+        m.sk_bn = BN;
+        m.max_pages = p.max_pages;
+        m.page_shift = p.page_shift;
+        m.num_pages = p.num_pages;
+        e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
+        if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+        return MIATTN_OK;
+    }
 
     // Split the key axis when the (row block, batch, KV head) units alone
     // cannot fill the chip, or for decode-shaped calls, whose per-request
     // lengths vary and are only known on the device.
-    int split_keys = g_split_keys > 0 ? g_split_keys : env_int("MIATTN_SPLIT_KEYS", 0);
     int64_t tiles_per;
     if (split_keys > 0) {
         tiles_per = (split_keys + BN - 1) / BN;
@@ -245,7 +331,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
 
     if (n_splits > 1) {
-        MergeParams m;
+        MergeParams m = {};
         m.o_part = p.o_part;
         m.lse_part = p.lse_part;
         m.o = p.o;

@@ -198,6 +198,34 @@ def test_paged_decode(page_size, split_keys):
                what="decode")
 
 
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_streamk_decode_fewer_tiles_than_workgroups(page_size):
+    # 6 key tiles in all for several hundred workgroups: most workgroups get
+    # an empty share, and the merge must skip their slots
+    paged_case(3, 1, 4, 2, 128, [5, 0, 40], page_size, seed=31, what="sk_tiny")
+
+
+def test_streamk_decode_many_requests():
+    # more batch entries than the plan kernel's 1024 threads (chunked prefix),
+    # lengths 0..120 including zeros
+    g = torch.Generator().manual_seed(32)
+    lens = torch.randint(0, 121, (1500,), generator=g).tolist()
+    lens[7] = 0
+    lens[1499] = 0
+    paged_case(len(lens), 1, 4, 1, 64, lens, 32, dtype=torch.float16, seed=33, what="sk_many")
+
+
+def test_streamk_dense_decode():
+    say("dense decode-shaped call (stream-K over dense K/V)")
+    B, Sq, Skv, Hq, Hkv, D = 5, 1, 3000, 16, 4, 64
+    q, k, v = workloads.dense_inputs(B, Sq, Skv, Hq, Hkv, D, dtype=torch.float16, seed=34)
+    mi.set_split_keys(0)
+    o, lse = mi.attn_fwd_dense(q.to(DEV), k.to(DEV), v.to(DEV), causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_dense(q, k, v, causal=True)
+    check_full(o, lse, o_ref, lse_ref, "sk_dense")
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_paged_decode_head_dims(D):
     paged_case(4, 1, 16, 4, D, [700, 33, 1, 1500], 32, seed=22, what=f"decode_d{D}")
