@@ -118,6 +118,75 @@ __device__ __forceinline__ float sum_halves(float x) {
     return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// ---- stream-K decode plan, computed by each wave that needs it.  Batch entry
+// b holds ceil(len_b / bn) key tiles, len_b = seqlen[b] clamped into
+// [0, cap] (skv for every entry when seqlen is null); the (batch, KV head)
+// sequences, heads fastest, form one sequence of Hkv * (sum of tiles) tiles.
+struct SkBatch {
+    const int32_t *seqlen;
+    int skv, B, bn, cap;
+};
+
+__device__ __forceinline__ int sk_tiles(const SkBatch &s, int b) {
+    const int len = s.seqlen ? min(max(s.seqlen[b], 0), s.cap) : s.skv;
+    return (len + s.bn - 1) / s.bn;
+}
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+// tiles of the whole batch (returned) and of the entries before `upto`
+__device__ __forceinline__ int sk_sums(const SkBatch &s, int upto, int &before) {
+    const int lane = threadIdx.x & 63;
+    int total = 0, pre = 0;
+    for (int c = 0; c < s.B; c += 64) {
+        const int b = c + lane;
+        const int t = b < s.B ? sk_tiles(s, b) : 0;
+        const int incl = wave_incl_scan(t);
+        const int incl_before = wave_incl_scan(b < upto ? t : 0);
+        total += __shfl(incl, 63);
+        pre += __shfl(incl_before, 63);
+    }
+    before = pre;
+    return total;
+}
+
+// the entry b whose tiles hold tile `at` of the sequence (hkv * pre_b <= at <
+// hkv * (pre_b + t_b)), with pre_b (tiles before it) and t_b; `at` must be
+// below the sequence's length
+__device__ __forceinline__ void sk_find(const SkBatch &s, int hkv, int64_t at, int &b_out,
+                                        int &pre_out, int &t_out) {
+    const int lane = threadIdx.x & 63;
+    int carry = 0;
+    for (int c = 0; c < s.B; c += 64) {
+        const int b = c + lane;
+        const int t = b < s.B ? sk_tiles(s, b) : 0;
+        const int incl = carry + wave_incl_scan(t);
+        const int excl = incl - t;
+        const bool hit = b < s.B && (int64_t)hkv * excl <= at && at < (int64_t)hkv * incl;
+        const uint64_t m = __ballot(hit);
+        if (m) {
+            const int src = __builtin_ctzll(m);
+            b_out = c + src;
+            pre_out = __shfl(excl, src);
+            t_out = __shfl(t, src);
+            return;
+        }
+        carry = __shfl(incl, 63);
+    }
+    b_out = s.B;
+    pre_out = carry;
+    t_out = 0;
+}
+
 // Sum of the two 16-bit values packed in `pk`, accumulated into acc in FP32.
 template <bool BF16>
 __device__ __forceinline__ float add_pair(uint32_t pk, float acc) {

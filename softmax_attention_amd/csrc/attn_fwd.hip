@@ -700,16 +700,20 @@ void attn_fwd_kernel(const FwdParams p) {
             // fastest, form one sequence of T key tiles; workgroup g takes
             // tiles [g T / G, (g+1) T / G) -- an equal share, whatever the
             // lengths -- and writes one partial per unit it touches, to slot
-            // unit + g (the plan kernel wrote T and each workgroup's first
-            // unit and tile; the merge kernel finds the slots the same way).
+            // unit + g (the merge kernel finds the slots the same way).
             const int g = blockIdx.x;
-            const int64_t T = *(const int64_t *)p.sk_plan;
+            const SkBatch sb = {PAGED ? p.seqlen : nullptr, p.Skv, p.B, BN,
+                                (PAGED && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0};
+            int unused;
+            const int64_t T = (int64_t)p.Hkv * sk_sums(sb, 0, unused);
             const int64_t s0 = (int64_t)g * T / p.sk_grid;
             const int64_t s1 = (int64_t)(g + 1) * T / p.sk_grid;
             if (s0 >= s1) return;
-            const int32_t *start = p.sk_plan + 2 + (p.B + 1);
-            int u = start[2 * g];
-            int off = start[2 * g + 1];
+            int b0, pre0, t0;
+            sk_find(sb, p.Hkv, s0, b0, pre0, t0);
+            const int64_t rem = s0 - (int64_t)p.Hkv * pre0;
+            int u = b0 * p.Hkv + (int)(rem / t0);
+            int off = (int)(rem % t0);
             for (int64_t at = s0; at < s1; ++u, off = 0) {
                 const int b = u / p.Hkv;
                 const int kvh = u - b * p.Hkv;

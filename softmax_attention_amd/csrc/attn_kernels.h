@@ -59,11 +59,7 @@ struct FwdParams {
     int xcd_units;     // (batch*KV head, split) units per XCD, or 0 for linear order
     int xcd_unit_major;  // with xcd_units: an XCD runs all row blocks of a unit, then the next
     int heads_inner;     // units ordered (batch, split, KV head) instead of (batch, KV head, split)
-    // stream-K decode (two-wave schedule): grid size G, or 0; the plan (int64
-    // T, then the tile prefix over batches [B+1], then per workgroup its first
-    // unit and tile [G][2]) written by the plan kernel
-    int sk_grid;
-    const int32_t *sk_plan;
+    int sk_grid;  // stream-K decode (split-role schedule): grid size G, or 0
 };
 
 struct MergeParams {
@@ -74,27 +70,16 @@ struct MergeParams {
     const int32_t *seqlen;  // paged lengths, or nullptr for dense
     int Skv;
     int B, Sq, Hq, Hkv, G, rows, n_splits, split_len;
-    // stream-K decode: grid size (0 otherwise), the plan, keys per tile and
-    // the length clamps the attention kernel applies
-    int sk_grid;
-    const int32_t *sk_plan;
-    int sk_bn, max_pages, page_shift, num_pages;
+    // stream-K decode: grid size (0 otherwise), keys per tile and the length
+    // clamp the attention kernel applies (max_pages * page_size, 0 for an
+    // empty cache)
+    int sk_grid, sk_bn, sk_cap;
 };
-
-// Stream-K plan: the kernel's workgroups split the (batch, KV head) key
-// sequences into equal shares of tiles.
-struct PlanParams {
-    const int32_t *seqlen;  // paged lengths, or nullptr for dense (Skv)
-    int Skv, B, Hkv, bn, max_pages, page_shift, num_pages, grid;
-    int32_t *plan;          // out: int64 T, prefix [B+1], starts [grid][2]
-};
-constexpr int kPlanMaxBatch = 16384;  // batch entries the one-workgroup plan kernel handles
 
 // Launchers: return the hipGetLastError() status of the launch.
 hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int waves,
                            int grid, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams &p, int D, bool bf16, hipStream_t stream);
-hipError_t launch_sk_plan(const PlanParams &p, hipStream_t stream);
 // Workgroups of the two-wave (decode) attention kernel one CU runs at once (0 if unknown).
 int attn_fwd_decode_blocks_per_cu(const FwdParams &p, int D, bool bf16, bool paged, int waves);
 

@@ -13,8 +13,12 @@
 // One wave per packed row; lane l owns D/64 consecutive output elements.
 #include "attn_kernels.h"
 
+#include "attn_device.h"
+
 namespace miattn {
 namespace {
+
+using namespace dev;
 
 template <bool BF16>
 __device__ __forceinline__ uint16_t to_half_bits(float x) {
@@ -48,13 +52,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     if (p.sk_grid > 0) {
         // Stream-K: the workgroups that touched this unit's tiles, [P, P +
         // tiles) of the T-tile sequence; workgroup g held [g T / G, (g+1) T / G).
-        const int len = p.seqlen ? (p.num_pages > 0 ? min(max(p.seqlen[b], 0),
-                                                          p.max_pages << p.page_shift)
-                                                    : 0)
-                                 : p.Skv;
-        const int tiles = (len + p.sk_bn - 1) / p.sk_bn;
-        T = *(const int64_t *)p.sk_plan;
-        const int64_t P = (int64_t)p.Hkv * p.sk_plan[2 + b] + (int64_t)kvh * tiles;
+        const SkBatch sb = {p.seqlen, p.Skv, p.B, p.sk_bn, p.sk_cap};
+        int before;
+        T = (int64_t)p.Hkv * sk_sums(sb, b, before);
+        const int tiles = sk_tiles(sb, b);
+        const int64_t P = (int64_t)p.Hkv * before + (int64_t)kvh * tiles;
         if (tiles == 0 || T == 0) {
             n_valid = 0;
             g_first = 0;
@@ -113,66 +115,6 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
             den > 0.f ? M + __logf(den) : -INFINITY;
 }
 
-// Stream-K plan (one workgroup): tiles per batch entry, their exclusive
-// prefix over the batch, T = Hkv * (sum of tiles) key tiles in all, and for
-// each attention workgroup g the unit (batch * Hkv + KV head, heads fastest)
-// and tile within it where its share [g T / G, (g+1) T / G) begins.
-__global__ __launch_bounds__(1024) void sk_plan_kernel(const PlanParams p) {
-    __shared__ int32_t pre[kPlanMaxBatch + 1];
-    __shared__ int32_t part[1024];
-    const int tid = threadIdx.x;
-    auto tiles_of = [&](int b) -> int {
-        const int len = p.seqlen ? (p.num_pages > 0 ? min(max(p.seqlen[b], 0),
-                                                          p.max_pages << p.page_shift)
-                                                    : 0)
-                                 : p.Skv;
-        return (len + p.bn - 1) / p.bn;
-    };
-    // each thread scans a contiguous chunk, then the chunk totals are scanned
-    const int chunk = (p.B + 1023) / 1024;
-    const int lo = min(p.B, tid * chunk), hi = min(p.B, lo + chunk);
-    int sum = 0;
-    for (int b = lo; b < hi; ++b) {
-        pre[b] = sum;  // exclusive within the chunk
-        sum += tiles_of(b);
-    }
-    part[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int v = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    const int carry = tid > 0 ? part[tid - 1] : 0;
-    for (int b = lo; b < hi; ++b) pre[b] += carry;
-    if (tid == 0) pre[p.B] = part[1023];
-    __syncthreads();
-    const int64_t T = (int64_t)p.Hkv * pre[p.B];
-    if (tid == 0) *(int64_t *)p.plan = T;
-    for (int b = tid; b <= p.B; b += 1024) p.plan[2 + b] = pre[b];
-    int32_t *start = p.plan + 2 + (p.B + 1);
-    for (int g = tid; g < p.grid; g += 1024) {
-        const int64_t s = (int64_t)g * T / p.grid;
-        int u = p.B * p.Hkv, off = 0;
-        if (s < T) {
-            // the batch entry whose tiles hold s: the last b with Hkv*pre[b] <= s
-            int l = 0, h = p.B - 1;
-            while (l < h) {
-                const int m = (l + h + 1) >> 1;
-                if ((int64_t)p.Hkv * pre[m] <= s) l = m; else h = m - 1;
-            }
-            const int t = pre[l + 1] - pre[l];
-            const int64_t rem = s - (int64_t)p.Hkv * pre[l];
-            const int kvh = (int)(rem / t);
-            u = l * p.Hkv + kvh;
-            off = (int)(rem - (int64_t)kvh * t);
-        }
-        start[2 * g] = u;
-        start[2 * g + 1] = off;
-    }
-}
-
 template <int D, bool BF16>
 hipError_t launch_one(const MergeParams &p, hipStream_t stream) {
     const int64_t rows = (int64_t)p.B * p.Hkv * p.rows;
@@ -190,11 +132,6 @@ hipError_t launch_lse_merge(const MergeParams &p, int D, bool bf16, hipStream_t 
         case 256: return bf16 ? launch_one<256, true>(p, stream) : launch_one<256, false>(p, stream);
         default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_sk_plan(const PlanParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL(sk_plan_kernel, dim3(1), dim3(1024), 0, stream, p);
-    return hipGetLastError();
 }
 
 }  // namespace miattn

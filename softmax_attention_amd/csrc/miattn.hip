@@ -42,7 +42,7 @@ bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 constexpr int kMaxDevices = 64;
 
 struct DeviceState {
-    void *ws = nullptr;  // split-KV partials (and the stream-K plan)
+    void *ws = nullptr;  // split-KV partials
     size_t ws_bytes = 0;
     int cus = 0;
     int decode_per_cu[2][2][2][2] = {};  // decode kernel occupancy: [3 waves][D 128][bf16][paged]
@@ -207,13 +207,13 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
     const int64_t cap_tiles = capacity > 0 ? (capacity + BN - 1) / BN : 1;
     int split_keys = g_split_keys > 0 ? g_split_keys : env_int("MIATTN_SPLIT_KEYS", 0);
     p.sk_grid = 0;
-    p.sk_plan = nullptr;
 
     // Decode-shaped calls run stream-K: a grid of what the GPU holds at once,
     // each workgroup an equal share of all (batch, KV head) key tiles, so no
     // workgroup waits on a long request or for a dispatch slot.  A forced
     // split length selects the split plan below instead.
-    if ((waves == 2 || waves == 3) && split_keys <= 0 && p.B <= miattn::kPlanMaxBatch &&
+    // (the plan's tile sums are 32-bit: Hkv * B * tiles of the capacity)
+    if ((waves == 2 || waves == 3) && split_keys <= 0 && bhs * cap_tiles < INT_MAX &&
         env_int("MIATTN_STREAMK", 1)) {
         int per_cu = decode_per_cu(dev, p, D, bf16, paged, waves);
         const int want = env_int("MIATTN_SK_PER_CU", 0);  // tuning override
@@ -226,31 +226,13 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
         p.xcd_unit_major = 0;
         p.heads_inner = 0;
         const int64_t slots = bhs + G;  // partial slot of (unit u, workgroup g): u + g
-        const size_t part_bytes = (size_t)slots * p.rows * (D + 1) * sizeof(float);
-        const size_t plan_off = (part_bytes + 255) / 256 * 256;
-        const size_t plan_bytes = (2 + (size_t)(p.B + 1) + 2 * (size_t)G) * sizeof(int32_t);
         void *ws = nullptr;
-        miattn_status st = workspace(dev, plan_off + plan_bytes, &ws);
+        miattn_status st =
+            workspace(dev, (size_t)slots * p.rows * (D + 1) * sizeof(float), &ws);
         if (st != MIATTN_OK) return st;
         p.o_part = (float *)ws;
         p.lse_part = p.o_part + slots * p.rows * D;
-        int32_t *plan = (int32_t *)((char *)ws + plan_off);
         p.sk_grid = G;
-        p.sk_plan = plan;
-
-        miattn::PlanParams q;
-        q.seqlen = paged ? p.seqlen : nullptr;
-        q.Skv = p.Skv;
-        q.B = p.B;
-        q.Hkv = p.Hkv;
-        q.bn = BN;
-        q.max_pages = p.max_pages;
-        q.page_shift = p.page_shift;
-        q.num_pages = p.num_pages;
-        q.grid = G;
-        q.plan = plan;
-        e = timed_launch(1, stream, [&] { return miattn::launch_sk_plan(q, stream); });
-        if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
         e = timed_launch(0, stream, [&] {
             return miattn::launch_attn_fwd(p, D, bf16, paged, waves, G, stream);
         });
@@ -271,11 +253,8 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
         m.n_splits = 1;
         m.split_len = 0;
         m.sk_grid = G;
-        m.sk_plan = plan;
         m.sk_bn = BN;
-        m.max_pages = p.max_pages;
-        m.page_shift = p.page_shift;
-        m.num_pages = p.num_pages;
+        m.sk_cap = (paged && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0;
         e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
         return MIATTN_OK;
