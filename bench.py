@@ -250,7 +250,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": kern_gbs / PEAK_HBM_GBS,
                          "traffic": measured_traffic("decode"),
-                         "kernel": "attn_fwd_kernel<128, true, 1, 2> (D, bf16, paged K/V, 2 waves)",
+                         "kernel": "attn_fwd_kernel<128, true, 1, 3> (D, bf16, paged K/V, 3 waves, stream-K)",
                          "kernel_avg_us": d["attn_kernel_ms"] * 1e3,
                          "merge_kernel_avg_us": d["merge_kernel_ms"] * 1e3}}
         del wd
