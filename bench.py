@@ -47,23 +47,34 @@ def visible_pairs(B, Hq, Sq, kv_lens, causal, keep_counts=None):
     return total * Hq
 
 
+def source_digest(path):
+    """sha256 of a kernel source with comments and whitespace removed, so a
+    change to comments alone keeps the recorded counters valid."""
+    import hashlib
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def measured_traffic(kind):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     record (profiles/traffic.json), or None when the kernel sources changed
     since those counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    for src, digest in rec.get("kernel_sources_sha256", {}).items():
+    for src, digest in rec.get("kernel_sources_digest", {}).items():
         full = os.path.join(ROOT, src)
-        if not os.path.exists(full):
+        if not os.path.exists(full) or source_digest(full) != digest:
             return None
-        with open(full, "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != digest:
-                return None
+    if not rec.get("kernel_sources_digest"):
+        return None
     return rec.get(kind, {}).get("hbm_bytes")
 
 

@@ -13,16 +13,19 @@
 // published online softmax (Milakov & Gimelshein 2018, as used by Dao et al.
 // 2022); it equals the plain definition in exact arithmetic.
 //
-// Work decomposition (one workgroup = 4 waves = 256 threads):
+// Work decomposition:
 //   * rows: the query rows of the G = Hq/Hkv heads that share a KV head are
-//     packed (row r = query r / G, head kvh*G + r % G); a workgroup owns 128
-//     packed rows, each wave 32 of them.  In decode (Sq = 1) the whole GQA
-//     group lands in one wave's MFMA tile.
-//   * keys: a workgroup walks its key range in tiles of 8192 / D keys.  All 256
-//     threads load the next K and V tile from HBM with 16-byte loads into
-//     registers while the waves compute on the current tile from LDS.  K is
-//     stored row-major; V is stored transposed (d-major) so that the P.V MFMA
-//     reads its key-contiguous operand with one 16-byte LDS read per lane.
+//     packed (row r = query r / G, head kvh*G + r % G), so one K/V tile
+//     serves the whole group; a computing wave owns 32 packed rows.  In
+//     decode (Sq = 1) the whole GQA group lands in one wave's MFMA tile.
+//   * keys: a workgroup walks its key range in tiles; K and V go from HBM
+//     straight into LDS ring stages with buffer_load ... lds (no registers),
+//     ordered by counted vmcnt waits and an LDS-only barrier.  Schedules
+//     (WAVES): 8 waves in two groups alternating MFMA and softmax phases over
+//     64-key tiles (prefill, D <= 128); 2 or 3 waves where wave 0 computes
+//     and the others only load (decode, D <= 128), optionally as a persistent
+//     stream-K grid that gives every workgroup an equal share of all key
+//     tiles; 4 waves that all load and compute (D = 256).
 //   * scores: S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}: K (from LDS) is
 //     the A operand, Q (held in registers for the whole kernel) the B operand.
 //     Each lane then holds 16 scores per 32-key block for ONE query row (its
@@ -30,7 +33,8 @@
 //     sum none until the end.
 //   * P.V: O^T = V^T P^T.  The exponentiated scores are already laid out as the
 //     B operand (row = lane's column, 8 keys per lane), so P goes from the
-//     score registers to the MFMA without any data movement; O^T accumulates in
+//     score registers to the MFMA without any data movement; V^T is read from
+//     the row-major V tile with the transposing LDS read; O^T accumulates in
 //     registers with each lane owning one row, which makes the per-row
 //     rescaling lane-local.
 //   * masking: a tile that is fully visible to every row of a wave takes no
