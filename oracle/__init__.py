@@ -9,7 +9,7 @@ integer arrays, results leave as float64 numpy arrays.
 The arithmetic lives in ``attn_oracle.c`` (plain C, fp64, fixed summation
 order); this module only compiles it with gcc and marshals arguments.  See the
 header of ``attn_oracle.c`` for the definition it follows and its sources on
-the pages (TileOPs "Attention Operators" GQADenseFwdOp stages 1, 4, 5 and 7 and
+the pages (TileOPs "Attention Operators" GQADenseFwdOp stages 1 and 4-7 and
 MHADecodePagedWithKVCacheFwdOp; RL-Kernel "Standard Softmax Attention";
 MATE "QSA" Core Attention for the natural-log LSE and empty rows).
 """
@@ -56,14 +56,15 @@ def _load():
         lib.oracle_decode.restype = ctypes.c_double
         lib.oracle_resolve_scale.argtypes = [f32, i32]
         lib.oracle_resolve_scale.restype = ctypes.c_double
+        win = [i32, i32, f32]  # window_left, window_right, softcap
         lib.oracle_attn_dense.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, f32, i32,
-                                          P, P, P]
+                                          *win, P, P, P]
         lib.oracle_attn_dense_rows.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
-                                               i32, P, P, i64, P, P]
-        lib.oracle_attn_paged.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32,
-                                          f32, i32, P, P]
-        lib.oracle_attn_paged_rows.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
-                                               i32, f32, i32, P, i64, P, P]
+                                               i32, *win, P, P, i64, P, P]
+        lib.oracle_attn_paged.argtypes = [P, P, P, P, P, i32, i32, *win, i32, i32, i32, i32, i32,
+                                          i32, f32, i32, P, P]
+        lib.oracle_attn_paged_rows.argtypes = [P, P, P, P, P, i32, i32, *win, i32, i32, i32, i32,
+                                               i32, i32, f32, i32, P, i64, P, P]
         for name in ("oracle_attn_dense", "oracle_attn_dense_rows", "oracle_attn_paged",
                      "oracle_attn_paged_rows", "oracle_num_threads"):
             getattr(lib, name).restype = i32
@@ -97,6 +98,13 @@ def _scale_arg(scale) -> float:
     return float("nan") if scale is None else float(scale)
 
 
+def _opt_args(window, softcap):
+    """(window_left, window_right, softcap) as the C entry points take them:
+    -1 for an unlimited side, 0.0 for no cap (None and 0 both disable it)."""
+    wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    return wl, wr, 0.0 if softcap is None else float(softcap)
+
+
 def decode(bits: int, dtype: int) -> float:
     """Exact value of one 16-bit pattern (BF16 or FP16 code)."""
     return _load().oracle_decode(bits, dtype)
@@ -122,11 +130,13 @@ def _as_mask(mask, B, Skv):
     return m
 
 
-def attn_dense(q, k, v, *, scale=None, causal=True, key_padding_mask=None, dtype=None):
+def attn_dense(q, k, v, *, scale=None, causal=True, key_padding_mask=None, dtype=None,
+               window=None, softcap=None):
     """o [B,Sq,Hq,D] float64, lse [B,Hq,Sq] float64 for a dense call.
 
     q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D]: bf16/fp16 torch tensors (or uint16 bit
-    arrays with ``dtype`` given)."""
+    arrays with ``dtype`` given).  window = (w_L, w_R), -1 = unlimited side;
+    softcap None or 0 = no cap."""
     dt = _dtype_code(q) if dtype is None else dtype
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
     B, Sq, Hq, D = qb.shape
@@ -136,6 +146,7 @@ def attn_dense(q, k, v, *, scale=None, causal=True, key_padding_mask=None, dtype
     lse = np.zeros((B, Hq, Sq), np.float64)
     rc = _load().oracle_attn_dense(_ptr(qb), _ptr(kb), _ptr(vb), dt, B, Hq, Hkv, Sq, Skv, D,
                                    _scale_arg(scale), int(bool(causal)),
+                                   *_opt_args(window, softcap),
                                    None if m is None else _ptr(m), _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle_attn_dense rejected the call (rc={rc})")
@@ -148,7 +159,7 @@ def _sel_array(rows) -> np.ndarray:
 
 
 def attn_dense_rows(q, k, v, rows, *, scale=None, causal=True, key_padding_mask=None,
-                    dtype=None):
+                    dtype=None, window=None, softcap=None):
     """Selected rows (b, i, h) of a dense call: o [n, D], lse [n]."""
     dt = _dtype_code(q) if dtype is None else dtype
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
@@ -161,6 +172,7 @@ def attn_dense_rows(q, k, v, rows, *, scale=None, causal=True, key_padding_mask=
     lse = np.zeros((n,), np.float64)
     rc = _load().oracle_attn_dense_rows(_ptr(qb), _ptr(kb), _ptr(vb), dt, B, Hq, Hkv, Sq, Skv,
                                         D, _scale_arg(scale), int(bool(causal)),
+                                        *_opt_args(window, softcap),
                                         None if m is None else _ptr(m), _ptr(sel), n, _ptr(o),
                                         _ptr(lse))
     if rc != 0:
@@ -184,7 +196,7 @@ def _paged_args(q, k_cache, v_cache, real_seqlen_kv, block_table):
 
 
 def attn_paged(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, *, causal=True,
-               scale=None, dtype=None):
+               scale=None, dtype=None, window=None, softcap=None):
     """o [B,Sq,Hq,D], lse [B,Hq,Sq] (float64) for a paged call.
 
     k_cache/v_cache: [pages*page_size, Hkv, D] or [pages, page_size, Hkv, D]."""
@@ -194,7 +206,8 @@ def attn_paged(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, *, c
     o = np.zeros((B, Sq, Hq, D), np.float64)
     lse = np.zeros((B, Hq, Sq), np.float64)
     rc = _load().oracle_attn_paged(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(lens), _ptr(bt),
-                                   int(page_size), int(bool(causal)), B, Sq, Hq, Hkv, D,
+                                   int(page_size), int(bool(causal)),
+                                   *_opt_args(window, softcap), B, Sq, Hq, Hkv, D,
                                    bt.shape[1], _scale_arg(scale), dt, _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle_attn_paged rejected the call (rc={rc})")
@@ -202,7 +215,7 @@ def attn_paged(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, *, c
 
 
 def attn_paged_rows(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, rows, *,
-                    causal=True, scale=None, dtype=None):
+                    causal=True, scale=None, dtype=None, window=None, softcap=None):
     """Selected rows (b, i, h) of a paged call: o [n, D], lse [n]."""
     dt = _dtype_code(q) if dtype is None else dtype
     qb, kb, vb, lens, bt, B, Sq, Hq, Hkv, D = _paged_args(q, k_cache, v_cache, real_seqlen_kv,
@@ -212,7 +225,8 @@ def attn_paged_rows(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size,
     o = np.zeros((n, D), np.float64)
     lse = np.zeros((n,), np.float64)
     rc = _load().oracle_attn_paged_rows(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(lens), _ptr(bt),
-                                        int(page_size), int(bool(causal)), B, Sq, Hq, Hkv, D,
+                                        int(page_size), int(bool(causal)),
+                                        *_opt_args(window, softcap), B, Sq, Hq, Hkv, D,
                                         bt.shape[1], _scale_arg(scale), dt, _ptr(sel), n,
                                         _ptr(o), _ptr(lse))
     if rc != 0:

@@ -9,9 +9,13 @@
  * What is computed, and where the pages define it:
  *   - TileOPs "Attention Operators", GQADenseFwdOp: stage 1 (query position
  *     p_i = i + S_kv - S_q), stage 4 (scores Z = alpha <Q, K_r(h)>), stage 5
- *     (visibility: not causal, or j <= p_i), stage 7 (softmax over the KV
- *     axis, then the value reduction); the head map r(h) = floor(h / g) with
- *     g = H / H_kv; BSHD layout with D contiguous.
+ *     (visibility: not causal or j <= p_i, and inside the sliding window
+ *     p_i - w_L <= j <= p_i + w_R, a bound of -1 being unlimited), stage 6
+ *     (logits: c tanh(Z / c) with softcap c > 0, Z itself with c = 0),
+ *     stage 7 (softmax over the KV axis, then the value reduction); the head
+ *     map r(h) = floor(h / g) with g = H / H_kv; BSHD layout with D
+ *     contiguous.  GQAPagedFwdOp and MHADecodePagedWithKVCacheFwdOp take the
+ *     same window and softcap parameters.
  *   - TileOPs "Attention Operators", MHADecodePagedWithKVCacheFwdOp: physical
  *     cache [rows, H_kv, D], real_seqlen_kv[B] (the cache length, its query
  *     tokens included), block_table[B, num_pages]; query i sees keys up to
@@ -26,7 +30,9 @@
  *
  * Readings where the pages leave a step open (each also listed in the design
  * notes): the scale multiplies the finished dot product; the LSE is
- * ln sum_j exp(alpha <q, k_j>) over the visible keys; a causal call with
+ * ln sum_j exp(L_j) over the visible keys, L_j being the logit of stage 6
+ * (alpha <q, k_j>, capped when a softcap is given); a paged request's window
+ * is placed at its own p_i; a causal call with
  * S_q > S_kv is accepted and its first S_q - S_kv rows are empty; a masked
  * key and a causally hidden key are combined with AND.
  *
@@ -99,6 +105,8 @@ typedef struct {
     int B, Sq, Hq, Hkv, D;
     int causal;
     double alpha;
+    int window_left, window_right; /* -1: unlimited */
+    double softcap;                /* 0: no cap */
     /* dense */
     int Skv;
     const uint8_t *mask; /* [B, Skv] or NULL */
@@ -131,12 +139,17 @@ static int64_t kv_row_offset(const call_t *c, int b, int64_t j, int r)
     return (row * c->Hkv + r) * c->D;
 }
 
-/* Key j is visible to query i iff (not causal or j <= p_i) and the padding
- * mask keeps column j. */
+/* Key j is visible to query i iff (not causal or j <= p_i), it lies inside
+ * the window (p_i - w_L <= j when w_L != -1, j <= p_i + w_R when w_R != -1)
+ * and the padding mask keeps column j. */
 static int visible(const call_t *c, int b, int i, int64_t j)
 {
     int64_t p = (int64_t)i + kv_length(c, b) - c->Sq;
     if (c->causal && j > p)
+        return 0;
+    if (c->window_left != -1 && j < p - c->window_left)
+        return 0;
+    if (c->window_right != -1 && j > p + c->window_right)
         return 0;
     if (c->mask && c->mask[(int64_t)b * c->Skv + j] == 0)
         return 0;
@@ -164,6 +177,8 @@ static void attend_row(const call_t *c, int b, int i, int h, double *o_row,
         for (int d = 0; d < D; ++d)
             dot += decode(c->q, q_off + d, c->dtype) * decode(c->k, k_off + d, c->dtype);
         s[j] = c->alpha * dot;
+        if (c->softcap > 0.0) /* stage 6: the logit is c tanh(Z / c) */
+            s[j] = c->softcap * tanh(s[j] / c->softcap);
         ++n_visible;
     }
 
@@ -174,7 +189,7 @@ static void attend_row(const call_t *c, int b, int i, int h, double *o_row,
         return;
     }
 
-    /* softmax over the visible keys, shifted by their maximum */
+    /* softmax of the logits over the visible keys, shifted by their maximum */
     double m = -INFINITY;
     for (int64_t j = 0; j < n; ++j)
         if (visible(c, b, i, j) && s[j] > m)
@@ -207,6 +222,20 @@ static int check_common(int B, int Sq, int Hq, int Hkv, int D, int dtype)
         return -1;
     if (dtype != ORACLE_BF16 && dtype != ORACLE_FP16)
         return -1;
+    return 0;
+}
+
+/* Window bounds are -1 (unlimited) or >= 0; the softcap is 0 (none) or a
+ * positive finite value (a negative cap is an error on the pages). */
+static int set_options(call_t *c, int window_left, int window_right, float softcap)
+{
+    if (window_left < -1 || window_right < -1)
+        return -1;
+    if (!(softcap >= 0.0f) || isinf(softcap))
+        return -1;
+    c->window_left = window_left;
+    c->window_right = window_right;
+    c->softcap = (double)softcap;
     return 0;
 }
 
@@ -282,7 +311,8 @@ static int run_all(const call_t *c, double *o, double *lse)
 
 static int make_dense(call_t *c, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                       int dtype, int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
-                      int causal, const uint8_t *mask)
+                      int causal, int window_left, int window_right, float softcap,
+                      const uint8_t *mask)
 {
     if (check_common(B, Sq, Hq, Hkv, D, dtype) || Skv < 0)
         return -1;
@@ -292,13 +322,14 @@ static int make_dense(call_t *c, const uint16_t *q, const uint16_t *k, const uin
     c->causal = causal != 0;
     c->alpha = oracle_resolve_scale(scale, D);
     c->mask = mask;
-    return 0;
+    return set_options(c, window_left, window_right, softcap);
 }
 
 static int make_paged(call_t *c, const uint16_t *q, const uint16_t *k_cache,
                       const uint16_t *v_cache, const int32_t *seqlen,
-                      const int32_t *block_table, int page_size, int causal, int B, int Sq,
-                      int Hq, int Hkv, int D, int max_pages, float scale, int dtype)
+                      const int32_t *block_table, int page_size, int causal, int window_left,
+                      int window_right, float softcap, int B, int Sq, int Hq, int Hkv, int D,
+                      int max_pages, float scale, int dtype)
 {
     if (check_common(B, Sq, Hq, Hkv, D, dtype) || page_size <= 0 || max_pages < 0)
         return -1;
@@ -315,18 +346,21 @@ static int make_paged(call_t *c, const uint16_t *q, const uint16_t *k_cache,
     c->block_table = block_table;
     c->page_size = page_size;
     c->max_pages = max_pages;
-    return 0;
+    return set_options(c, window_left, window_right, softcap);
 }
 
 /* Dense call: q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (16-bit bit patterns), mask
- * [B,Skv] or NULL.  Writes o [B,Sq,Hq,D] and lse [B,Hq,Sq] in double.
+ * [B,Skv] or NULL; window bounds -1 (unlimited) or >= 0; softcap 0 (none) or
+ * > 0.  Writes o [B,Sq,Hq,D] and lse [B,Hq,Sq] in double.
  * Returns 0, -1 on invalid arguments, -2 on allocation failure. */
 int oracle_attn_dense(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype,
                       int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                      int window_left, int window_right, float softcap,
                       const uint8_t *key_padding_mask, double *o, double *lse)
 {
     call_t c;
-    if (make_dense(&c, q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, scale, causal, key_padding_mask))
+    if (make_dense(&c, q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, scale, causal, window_left,
+                   window_right, softcap, key_padding_mask))
         return -1;
     return run_all(&c, o, lse);
 }
@@ -335,11 +369,13 @@ int oracle_attn_dense(const uint16_t *q, const uint16_t *k, const uint16_t *v, i
  * Writes o [nsel, D] and lse [nsel]. */
 int oracle_attn_dense_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype,
                            int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
-                           int causal, const uint8_t *key_padding_mask, const int32_t *sel,
-                           int64_t nsel, double *o, double *lse)
+                           int causal, int window_left, int window_right, float softcap,
+                           const uint8_t *key_padding_mask, const int32_t *sel, int64_t nsel,
+                           double *o, double *lse)
 {
     call_t c;
-    if (make_dense(&c, q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, scale, causal, key_padding_mask))
+    if (make_dense(&c, q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, scale, causal, window_left,
+                   window_right, softcap, key_padding_mask))
         return -1;
     for (int64_t t = 0; t < nsel; ++t)
         if (sel[3 * t] < 0 || sel[3 * t] >= B || sel[3 * t + 1] < 0 || sel[3 * t + 1] >= Sq ||
@@ -353,12 +389,14 @@ int oracle_attn_dense_rows(const uint16_t *q, const uint16_t *k, const uint16_t 
  * dense call does. */
 int oracle_attn_paged(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                       const int32_t *real_seqlen_kv, const int32_t *block_table, int page_size,
-                      int causal, int B, int Sq, int Hq, int Hkv, int D, int max_pages,
-                      float scale, int dtype, double *o, double *lse)
+                      int causal, int window_left, int window_right, float softcap, int B,
+                      int Sq, int Hq, int Hkv, int D, int max_pages, float scale, int dtype,
+                      double *o, double *lse)
 {
     call_t c;
-    if (make_paged(&c, q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, causal, B,
-                   Sq, Hq, Hkv, D, max_pages, scale, dtype))
+    if (make_paged(&c, q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, causal,
+                   window_left, window_right, softcap, B, Sq, Hq, Hkv, D, max_pages, scale,
+                   dtype))
         return -1;
     return run_all(&c, o, lse);
 }
@@ -366,13 +404,15 @@ int oracle_attn_paged(const uint16_t *q, const uint16_t *k_cache, const uint16_t
 /* Paged call, selected rows only (triples b, i, h). */
 int oracle_attn_paged_rows(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                            const int32_t *real_seqlen_kv, const int32_t *block_table,
-                           int page_size, int causal, int B, int Sq, int Hq, int Hkv, int D,
-                           int max_pages, float scale, int dtype, const int32_t *sel,
-                           int64_t nsel, double *o, double *lse)
+                           int page_size, int causal, int window_left, int window_right,
+                           float softcap, int B, int Sq, int Hq, int Hkv, int D, int max_pages,
+                           float scale, int dtype, const int32_t *sel, int64_t nsel, double *o,
+                           double *lse)
 {
     call_t c;
-    if (make_paged(&c, q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, causal, B,
-                   Sq, Hq, Hkv, D, max_pages, scale, dtype))
+    if (make_paged(&c, q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, causal,
+                   window_left, window_right, softcap, B, Sq, Hq, Hkv, D, max_pages, scale,
+                   dtype))
         return -1;
     for (int64_t t = 0; t < nsel; ++t)
         if (sel[3 * t] < 0 || sel[3 * t] >= B || sel[3 * t + 1] < 0 || sel[3 * t + 1] >= Sq ||

@@ -36,9 +36,21 @@ MUTANTS = {
     "score_sign": ("s[j] = c->alpha * dot;", "s[j] = -c->alpha * dot;"),
     "dot_drops_last_term": ("for (int d = 0; d < D; ++d)\n            dot +=",
                             "for (int d = 0; d < D - 1; ++d)\n            dot +="),
+    "window_left_off_by_one": ("j < p - c->window_left", "j <= p - c->window_left"),
+    "window_right_off_by_one": ("j > p + c->window_right", "j >= p + c->window_right"),
+    "window_left_ignored": ("if (c->window_left != -1 && j < p - c->window_left)", "if (0)"),
+    "window_sides_swapped": ("j < p - c->window_left", "j < p - c->window_right"),
+    "window_not_at_query_position": ("j > p + c->window_right", "j > i + c->window_right"),
+    "softcap_ignored": ("if (c->softcap > 0.0) /*", "if (0) /*"),
+    "softcap_outer_factor_dropped": ("s[j] = c->softcap * tanh(s[j] / c->softcap);",
+                                     "s[j] = tanh(s[j] / c->softcap);"),
+    "softcap_before_scale": ("s[j] = c->softcap * tanh(s[j] / c->softcap);",
+                             "s[j] = c->alpha * c->softcap * tanh(dot / c->softcap);"),
     "value_sum_skips_first_key": ("for (int64_t j = 0; j < n; ++j) {\n            if (!visible(c, b, i, j))\n                continue;\n            acc +=",
                                   "for (int64_t j = 1; j < n; ++j) {\n            if (!visible(c, b, i, j))\n                continue;\n            acc +="),
 }
+
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_pins_window_softcap.py"]
 
 PLUGIN = "import os, oracle\noracle._LIB = os.environ['ORACLE_MUTANT_LIB']\n"
 
@@ -66,7 +78,7 @@ def test_pins_reject_planted_mistake(name, workdir):
     env = dict(os.environ, ORACLE_MUTANT_LIB=lib,
                PYTHONPATH=os.pathsep.join([workdir, ROOT]), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "-p", "oracle_mutant_plugin", os.path.join(ROOT, "tests",
-                                                                   "test_oracle_pins.py")],
+                        "-p", "oracle_mutant_plugin",
+                        *[os.path.join(ROOT, "tests", f) for f in PIN_FILES]],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode == 1, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
