@@ -10,10 +10,12 @@
  *   - TileOPs "Attention Operators", GQADenseFwdOp: the equation with FP32
  *     accumulation and the output in the input dtype; stage 1 (query row i sits
  *     at KV position p_i = i + S_kv - S_q); stage 4 (Z = alpha <Q, K>, alpha
- *     defaulting to 1/sqrt(D)); stage 5 (causal visibility j <= p_i); stage 7
+ *     defaulting to 1/sqrt(D)); stage 5 (visibility: causal j <= p_i, and the
+ *     sliding window p_i - w_L <= j <= p_i + w_R, -1 leaving a side
+ *     unlimited); stage 6 (logit c tanh(Z / c) for a softcap c > 0); stage 7
  *     (softmax over keys, then the value sum); query head h reads KV head
  *     floor(h / (H_q / H_kv)); BSHD layout with D contiguous; a refusal names
- *     the limit it hit.
+ *     the limit it hit.  GQAPagedFwdOp takes the same window and softcap.
  *   - TileOPs "Attention Operators", MHADecodePagedWithKVCacheFwdOp: the paged
  *     layout (physical cache [rows, H_kv, D], real_seqlen_kv [B],
  *     block_table [B, num_pages]) and the per-request end-aligned causal rule;
@@ -78,13 +80,21 @@ typedef enum { MIATTN_BF16 = 0, MIATTN_FP16 = 1 } miattn_dtype;
  *                            D in {64, 128, 256}
  *   scale  alpha; NaN selects 1/sqrt(D) (rounded to float); any finite value,
  *          0.0 included, is used verbatim; +-inf is refused
- *   causal 0 or 1: key j is visible to query i iff j <= i + Skv - Sq.  Sq > Skv
- *          is accepted; its first Sq - Skv rows see no key
+ *   causal 0 or 1: key j is visible to query i iff j <= p_i = i + Skv - Sq.
+ *          Sq > Skv is accepted; its first Sq - Skv rows see no key
+ *   window_left, window_right  sliding window: key j is visible to query i
+ *          only if j >= p_i - window_left (when window_left != -1) and
+ *          j <= p_i + window_right (when window_right != -1); -1 is
+ *          unlimited, other negative values are refused (INVALID_ARG)
+ *   softcap 0 for plain logits; c > 0 (finite) replaces each logit z by
+ *          c * tanh(z / c); negative, infinite or NaN values are refused
  *   key_padding_mask  device, [B, Skv] bytes, nonzero = keep; NULL = no mask.
- *          Combined with the causal rule by AND
+ *          Combined with the causal rule and the window by AND
  *   o      device, [B, Sq, Hq, D] dtype, written in full
- *   lse    device, [B, Hq, Sq] float32 (natural log), or NULL to skip it.  A
- *          row that sees no key gets o = 0 and lse = -inf
+ *   lse    device, [B, Hq, Sq] float32, or NULL to skip it: the natural log of
+ *          the softmax denominator, ln sum_j exp(logit_j) over the visible
+ *          keys (with a softcap, of the capped logits).  A row that sees no
+ *          key gets o = 0 and lse = -inf
  *   dtype  MIATTN_BF16 or MIATTN_FP16, the type of q, k, v and o
  *   stream hipStream_t or NULL
  *
@@ -92,6 +102,7 @@ typedef enum { MIATTN_BF16 = 0, MIATTN_FP16 = 1 } miattn_dtype;
  */
 miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B, int Hq,
                              int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                             int window_left, int window_right, float softcap,
                              const uint8_t *key_padding_mask, void *o, float *lse,
                              miattn_dtype dtype, void *stream);
 
@@ -110,7 +121,9 @@ miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B,
  *            block_table[b, j / page_size] * page_size + j % page_size.  Entries
  *            at p >= ceil(len / page_size) are never read
  *   page_size a power of two >= 16 (others return MIATTN_ERR_UNSUPPORTED)
- *   causal   0 or 1: key j is visible to query i iff j <= i + len_b - Sq
+ *   causal   0 or 1: key j is visible to query i iff j <= p_i = i + len_b - Sq
+ *   window_left, window_right, softcap  as for attn_fwd_dense, with p_i the
+ *            position of query i in request b's own key range
  *   o, lse   as for attn_fwd_dense
  *   B, Sq, Hq, Hkv, D  as for attn_fwd_dense; max_pages > 0
  *   num_phys_pages  number of physical pages in each cache (only checked under
@@ -122,7 +135,8 @@ miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B,
  */
 miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *real_seqlen_kv, const int32_t *block_table,
-                             int page_size, int causal, void *o, float *lse, int B, int Sq,
+                             int page_size, int causal, int window_left, int window_right,
+                             float softcap, void *o, float *lse, int B, int Sq,
                              int Hq, int Hkv, int D, int max_pages, int num_phys_pages,
                              float scale, miattn_dtype dtype, void *stream);
 

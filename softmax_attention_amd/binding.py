@@ -40,11 +40,11 @@ def lib() -> ctypes.CDLL:
                 "(or __graft_entry__.build()) first")
         L = ctypes.CDLL(LIB_PATH)
         P, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-        L.attn_fwd_dense.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, P, P,
-                                     i32, P]
+        L.attn_fwd_dense.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f32, i32,
+                                     i32, i32, f32, P, P, P, i32, P]
         L.attn_fwd_dense.restype = i32
-        L.attn_fwd_paged.argtypes = [P, P, P, P, P, i32, i32, P, P, i32, i32, i32, i32, i32,
-                                     i32, i32, f32, i32, P]
+        L.attn_fwd_paged.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f32, P, P, i32, i32,
+                                     i32, i32, i32, i32, i32, f32, i32, P]
         L.attn_fwd_paged.restype = i32
         L.miattn_last_error.argtypes = []
         L.miattn_last_error.restype = ctypes.c_char_p
@@ -88,18 +88,32 @@ def _scale(scale) -> float:
     return math.nan if scale is None else float(scale)
 
 
+def _window(window) -> Tuple[int, int]:
+    if window is None:
+        return -1, -1
+    wl, wr = window
+    return int(wl), int(wr)
+
+
+def _softcap(softcap) -> float:
+    return 0.0 if softcap is None else float(softcap)
+
+
 def _stream() -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 def attn_fwd_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale=None,
-                   causal: bool = True, key_padding_mask: Optional[torch.Tensor] = None,
+                   causal: bool = True, window=None, softcap=None,
+                   key_padding_mask: Optional[torch.Tensor] = None,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Dense attention forward on the current stream.
 
-    q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (bf16 or fp16, CUDA); key_padding_mask
-    [B,Skv] bool (True = keep).  Returns (o [B,Sq,Hq,D], lse [B,Hq,Sq] fp32)."""
+    q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (bf16 or fp16, CUDA); window (w_L, w_R),
+    -1 = unlimited side, None = no window; softcap None or 0 = plain logits;
+    key_padding_mask [B,Skv] bool (True = keep).  Returns (o [B,Sq,Hq,D],
+    lse [B,Hq,Sq] fp32)."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be rank 4 (BSHD)")
     if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
@@ -123,7 +137,8 @@ def attn_fwd_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale=N
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     st = lib().attn_fwd_dense(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Sq, Skv, D, _scale(scale),
-                              int(bool(causal)), _ptr(mask), _ptr(o),
+                              int(bool(causal)), *_window(window), _softcap(softcap),
+                              _ptr(mask), _ptr(o),
                               _ptr(lse) if return_lse else None, code, _stream())
     _check(st)
     return o, (lse if return_lse else None)
@@ -131,14 +146,17 @@ def attn_fwd_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale=N
 
 def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    real_seqlen_kv: torch.Tensor, block_table: torch.Tensor, page_size: int, *,
-                   causal: bool = True, scale=None, out: Optional[torch.Tensor] = None,
+                   causal: bool = True, scale=None, window=None, softcap=None,
+                   out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, return_lse: bool = True
                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Paged attention forward on the current stream.
 
     q [B,Sq,Hq,D]; k_cache/v_cache [pages*page_size, Hkv, D] or
     [pages, page_size, Hkv, D]; real_seqlen_kv int32 [B] (cache length, the Sq
-    query tokens included); block_table int32 [B, max_pages]."""
+    query tokens included); block_table int32 [B, max_pages]; window and
+    softcap as for attn_fwd_dense, the window placed at each request's own
+    query positions."""
     if q.dim() != 4:
         raise ValueError("q must be rank 4 (BSHD)")
     if k_cache.shape != v_cache.shape:
@@ -174,7 +192,8 @@ def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     st = lib().attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(real_seqlen_kv),
-                              _ptr(block_table), int(page_size), int(bool(causal)), _ptr(o),
+                              _ptr(block_table), int(page_size), int(bool(causal)),
+                              *_window(window), _softcap(softcap), _ptr(o),
                               _ptr(lse) if return_lse else None, B, Sq, Hq, Hkv, D,
                               block_table.shape[1], n_pages, _scale(scale), code, _stream())
     _check(st)

@@ -13,7 +13,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmiattn.so")
-SOURCES = ["attn_fwd.hip", "lse_merge.hip", "miattn.hip"]
+# (source, extra defines): attn_fwd.hip is compiled once per (head dim,
+# logit kind) pair, each unit holding that pair's kernels, so the units build
+# in parallel
+UNITS = [("attn_fwd.hip", [f"-DMIATTN_KD={d}", f"-DMIATTN_KCAP={c}"])
+         for d in (64, 128, 256) for c in (0, 1)] + [("lse_merge.hip", []), ("miattn.hip", [])]
+SOURCES = sorted({u[0] for u in UNITS})
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -23,7 +28,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wno-unused-function",
     # keep the compiler from forming packed-FP32 instructions (v_pk_*_f32)
@@ -32,22 +36,42 @@ FLAGS = [
     f"-I{CSRC}",
 ]
 
+# the host pass warns that it does not know the GPU-only feature
+_NOISE = "'-packed-fp32-ops' is not a recognized feature"
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Always recompiles; returns the path of the library."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), *[os.path.join(CSRC, s) for s in SOURCES],
-           "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
-    # the host pass warns that it does not know the GPU-only feature: drop that line
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if _NOISE not in ln]
+    return r.returncode, msgs
+
+
+def build(verbose: bool = False, extra_flags=None, jobs: int = 0) -> str:
+    """Always recompiles (the units in parallel); returns the path of the library."""
+    import concurrent.futures
+    import tempfile
+
+    jobs = jobs or min(len(UNITS), os.cpu_count() or 1)
+    with tempfile.TemporaryDirectory(prefix="miattn_build_") as tmpdir:
+        cmds = []
+        for n, (src, defs) in enumerate(UNITS):
+            obj = os.path.join(tmpdir, f"{n}_{os.path.splitext(src)[0]}.o")
+            cmds.append([HIPCC, *FLAGS, *(extra_flags or []), *defs, "-c",
+                         os.path.join(CSRC, src), "-o", obj])
+        with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+            results = list(pool.map(_run, cmds))
+        for cmd, (rc, msgs) in zip(cmds, results):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+                if msgs:
+                    print("\n".join(msgs))
+            if rc != 0:
+                raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+        tmp = LIB + ".tmp"
+        link = [HIPCC, f"--offload-arch={ARCH}", "-shared", *[c[-1] for c in cmds], "-o", tmp]
+        rc, msgs = _run(link)
+        if rc != 0:
+            raise RuntimeError("link failed:\n" + "\n".join(msgs))
     # every symbol must resolve (a kernel whose host-side launch stub was not
     # emitted only shows up here, as an undefined symbol)
     try:

@@ -125,11 +125,23 @@ __device__ __forceinline__ float sum_halves(float x) {
 struct SkBatch {
     const int32_t *seqlen;
     int skv, B, bn, cap;
+    int sq, win_left;  // queries per request; left window bound (-1: none)
 };
 
+// keys of entry b (a paged length clamped into [0, cap])
+__device__ __forceinline__ int sk_len(const SkBatch &s, int b) {
+    return s.seqlen ? min(max(s.seqlen[b], 0), s.cap) : s.skv;
+}
+
+// first key tile any query of an entry of length len can see: with a left
+// window the first query (at position len - sq) sees keys from len - sq - w_L
+__device__ __forceinline__ int sk_first_tile(const SkBatch &s, int len) {
+    return s.win_left < 0 ? 0 : max(0, len - s.sq - s.win_left) / s.bn;
+}
+
 __device__ __forceinline__ int sk_tiles(const SkBatch &s, int b) {
-    const int len = s.seqlen ? min(max(s.seqlen[b], 0), s.cap) : s.skv;
-    return (len + s.bn - 1) / s.bn;
+    const int len = sk_len(s, b);
+    return (len + s.bn - 1) / s.bn - sk_first_tile(s, len);
 }
 
 // inclusive prefix sum over the 64 lanes of a wave

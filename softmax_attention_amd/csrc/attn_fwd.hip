@@ -88,7 +88,9 @@ __device__ __forceinline__ void sched_read_ahead() {
 // looks up its own page).
 enum KvMode { kDense = 0, kPagedTile = 1, kPagedPiece = 2 };
 
-template <int D, bool BF16, int KV, int WAVES>
+// CAP: logits are capped (c tanh(z / c), TileOPs "Attention Operators",
+// GQADenseFwdOp stage 6); otherwise the logit is the scaled score itself.
+template <int D, bool BF16, int KV, int WAVES, bool CAP>
 __global__ __launch_bounds__(64 * WAVES)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, WAVES>(), waves_per_eu<D, WAVES>())))
 void attn_fwd_kernel(const FwdParams p) {
@@ -136,28 +138,53 @@ void attn_fwd_kernel(const FwdParams p) {
     auto run = [&](const int mblock, const int b, const int kvh, const int kv_len,
                    const int kbeg, const int kend, const int64_t slot,
                    const bool partial) __attribute__((always_inline)) {
-    const int delta = kv_len - p.Sq;  // query i sits at key position i + delta
+    const int delta = kv_len - p.Sq;  // query i sits at key position p_i = i + delta
+
+    // Keys query i may see before the padding mask (TileOPs "Attention
+    // Operators", GQADenseFwdOp stage 5): [key_lo(i), key_hi(i)], both
+    // nondecreasing in i.  (The host keeps i + delta + win_right in range.)
+    auto key_hi = [&](int i) __attribute__((always_inline)) -> int {
+        int h = kv_len - 1;
+        if (p.causal) h = min(h, i + delta);
+        if (p.win_right >= 0) h = min(h, i + delta + p.win_right);
+        return h;
+    };
+    auto key_lo = [&](int i) __attribute__((always_inline)) -> int {
+        return p.win_left >= 0 ? max(0, i + delta - p.win_left) : 0;
+    };
 
     const int row0 = mblock * BM;
     const int row_last = min(p.rows, row0 + BM) - 1;
-    const int wg_end = p.causal ? min(kend, row_last / p.G + delta + 1) : kend;
+    const int wg_end = min(kend, key_hi(row_last / p.G) + 1);
+    // the first tile (on the kbeg + n BN grid) that holds a key this
+    // workgroup's rows may see
+    const int wg_begin = max(kbeg, key_lo(row0 / p.G));
+    const int tile_begin = wg_begin >= wg_end ? wg_end : kbeg + (wg_begin - kbeg) / BN * BN;
 
     const int wrow0 = row0 + (SPLIT_ROLES ? 0 : wave * kRowsPerWave);
     const bool wave_active = (!SPLIT_ROLES || wave == 0) && wrow0 < p.rows;
     const int wrow_last = min(p.rows, wrow0 + kRowsPerWave) - 1;
-    // keys < wave_full_end are visible to every row of this wave; keys >=
-    // wave_end to none of them
-    const int wave_end =
-        !wave_active ? kbeg : (p.causal ? min(kend, wrow_last / p.G + delta + 1) : kend);
-    const int wave_full_end =
-        !wave_active ? kbeg : (p.causal ? min(kend, wrow0 / p.G + delta + 1) : kend);
+    // keys in [wave_full_begin, wave_full_end) are visible to every row of
+    // this wave (mask aside); keys outside [wave_begin, wave_end) to none
+    const int wave_end = !wave_active ? kbeg : min(kend, key_hi(wrow_last / p.G) + 1);
+    const int wave_full_end = !wave_active ? kbeg : min(kend, key_hi(wrow0 / p.G) + 1);
+    const int wave_begin = key_lo(wrow0 / p.G);
+    const int wave_full_begin = key_lo(wrow_last / p.G);
+    // does this wave compute on the tile starting at key t?
+    auto sees = [&](int t) __attribute__((always_inline)) -> bool {
+        return wave_active && t < wave_end && t + BN > wave_begin;
+    };
+    auto full_tile = [&](int t) __attribute__((always_inline)) -> bool {
+        return t + BN <= wave_full_end && t >= wave_full_begin;
+    };
 
     // ---- this lane's query row (the column it holds in every MFMA tile)
     const int my_row = wrow0 + l32;
     const bool row_ok = my_row < p.rows;
     const int my_i = my_row / p.G;
     const int my_gh = my_row - my_i * p.G;
-    const int my_last = !row_ok ? -1 : (p.causal ? min(kv_len - 1, my_i + delta) : kv_len - 1);
+    const int my_last = !row_ok ? -1 : key_hi(my_i);
+    const int my_first = key_lo(my_i);
 
     // ---- Q for the whole kernel: B operand, lane = row, 8 d-values per k-step.
     // The host folds the sign of the scale into Q (an exact sign flip) and
@@ -253,7 +280,7 @@ void attn_fwd_kernel(const FwdParams p) {
     };
     // first tile holding a visible key (wg_end if none), with its mask bits
     uint64_t first_lo = ~0ull, first_hi = ~0ull;
-    const int first_tile = find_tile(kbeg, first_lo, first_hi);
+    const int first_tile = find_tile(tile_begin, first_lo, first_hi);
     // Block-table entry of the page holding tile j (of the first tile for a
     // tile past the range).  With whole-tile pages the schedules read it a
     // step before the tile's loads are issued, so that the scalar load's
@@ -312,6 +339,7 @@ void attn_fwd_kernel(const FwdParams p) {
     };
 
     const float c = p.scale_log2;  // > 0
+    const float cap_x = p.cap_x, cap_k2 = p.cap_k2;
 
     // ---- LDS read addresses, fixed per lane for the whole kernel.  With the
     // swizzle depending on row & 15 only, the 32-key block t and the 16-key
@@ -363,32 +391,60 @@ void attn_fwd_kernel(const FwdParams p) {
         if constexpr (MASKED) {
             // S^T layout: register r of lane half hl holds key
             // 32t + 8*(r/4) + 4*hl + r%4 of the tile
+            // this lane's keys of block t are 32t + 4hl + bit, bit = 8*(r/4) + r%4;
+            // one word per block holds the visible ones: the padding mask's
+            // bits and-ed with the row's key range [lim_lo, lim]
             const int lim = my_last - j0 - 4 * hl;
+            const int lim_lo = my_first - j0 - 4 * hl;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 uint32_t w = ~0u;
                 if (has_mask) w = (uint32_t)((t < 2 ? mlo : mhi) >> (32 * (t & 1) + 4 * hl));
+                const int hi_c = min(max(lim - 32 * t, -1), 31);
+                const int lo_c = min(max(lim_lo - 32 * t, 0), 32);
+                w &= (uint32_t)((1ull << (hi_c + 1)) - 1) & (uint32_t)(~0ull << lo_c);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int kc = 32 * t + 8 * (r >> 2) + (r & 3);
-                    const bool vis = (kc <= lim) && ((w >> (8 * (r >> 2) + (r & 3))) & 1u);
+                    const bool vis = (w >> (8 * (r >> 2) + (r & 3))) & 1u;
                     sc[t][r] = vis ? sc[t][r] : -INFINITY;
                 }
             }
         }
-        // row max of the raw scores (scaling by c > 0 keeps the order)
+        // row max of the raw scores (the logit is increasing in the raw
+        // score, capped or not, so the max logit is the logit of the max)
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
         mx = max_halves(mx);
-        const float tile_max = (mx == -INFINITY) ? -INFINITY : mx * c;
+        // capped logit in log2 units: cap_k2 tanh(x) with tanh(x) = 1 - 2 / (e^{2x} + 1),
+        // which needs no sign split (e^{2x} -> 0 gives -1, -> inf gives 1)
+        float tile_max;
+        if constexpr (CAP)
+            tile_max = (mx == -INFINITY)
+                           ? -INFINITY
+                           : cap_k2 - 2.f * cap_k2 *
+                                          __builtin_amdgcn_rcpf(fast_exp2(mx * cap_x) + 1.f);
+        else
+            tile_max = (mx == -INFINITY) ? -INFINITY : mx * c;
         const bool raise = __any(tile_max > m_run + kLazy);
         const float m_new = raise ? fmaxf(m_run, tile_max) : m_run;
         const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
         m_run = m_new;
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        // exp2 argument of raw score s: the logit minus the running max
+        const float cap_off = cap_k2 - m_use;
+        auto arg = [&](float s) __attribute__((always_inline)) -> float {
+            if constexpr (CAP) {
+                const float r = __builtin_amdgcn_rcpf(fast_exp2(s * cap_x) + 1.f);
+                const float a = __builtin_fmaf(r, -2.f * cap_k2, cap_off);
+                // a hidden key (s = -inf) would get r = 1, a finite logit
+                return (MASKED && s == -INFINITY) ? -INFINITY : a;
+            } else {
+                return __builtin_fmaf(s, c, -m_use);
+            }
+        };
 
         float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
@@ -397,8 +453,8 @@ void attn_fwd_kernel(const FwdParams p) {
             u32x4 packed;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float e0 = fast_exp2(__builtin_fmaf(sc[t][8 * u + 2 * e], c, -m_use));
-                const float e1 = fast_exp2(__builtin_fmaf(sc[t][8 * u + 2 * e + 1], c, -m_use));
+                const float e0 = fast_exp2(arg(sc[t][8 * u + 2 * e]));
+                const float e1 = fast_exp2(arg(sc[t][8 * u + 2 * e + 1]));
                 packed[e] = pack_half2<BF16>(e0, e1);
                 if (e & 1)
                     rs1 = add_pair<BF16>(packed[e], rs1);
@@ -454,8 +510,8 @@ void attn_fwd_kernel(const FwdParams p) {
         vec8 pb[PSTEPS];
         float corr_pending = 1.f;
         auto mma_phase = [&](int cur, int prev, const uint8_t *sk, const uint8_t *sv) __attribute__((always_inline)) {
-            const bool do_qk = wave_active && cur < wave_end;
-            const bool do_pv = wave_active && prev >= 0 && prev < wave_end;
+            const bool do_qk = sees(cur);
+            const bool do_pv = prev >= 0 && sees(prev);
             if (do_pv && corr_pending != 1.f) {
 #pragma unroll
                 for (int t = 0; t < DT; ++t)
@@ -475,8 +531,8 @@ void attn_fwd_kernel(const FwdParams p) {
             }
         };
         auto softmax_phase = [&](int tile, uint64_t lo, uint64_t hi) __attribute__((always_inline)) {
-            if (!(wave_active && tile >= 0 && tile < wave_end)) return;
-            bool full = tile + BN <= wave_full_end;
+            if (!(tile >= 0 && sees(tile))) return;
+            bool full = full_tile(tile);
             if (has_mask) full = full && (lo == kLoMask) && (BN <= 64 || hi == ~0ull);
             if (full)
                 corr_pending = softmax(std::false_type{}, tile, lo, hi, sc, pb);
@@ -577,8 +633,8 @@ void attn_fwd_kernel(const FwdParams p) {
         int t3 = wg_end;
         int32_t pg_next = 0;  // page entry of the next tile to load
         auto compute = [&](const uint8_t *sk, const uint8_t *sv) __attribute__((always_inline)) {
-            if (!(wave_active && t0 < wave_end)) return;
-            bool full = t0 + BN <= wave_full_end;
+            if (!sees(t0)) return;
+            bool full = full_tile(t0);
             if (has_mask) full = full && (lo0 == kLoMask) && (BN <= 64 || hi0 == ~0ull);
             qk(sk, sc);
             const float corr = full ? softmax(std::false_type{}, t0, lo0, hi0, sc, pb)
@@ -707,7 +763,8 @@ void attn_fwd_kernel(const FwdParams p) {
             // unit + g (the merge kernel finds the slots the same way).
             const int g = blockIdx.x;
             const SkBatch sb = {PAGED ? p.seqlen : nullptr, p.Skv, p.B, BN,
-                                (PAGED && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0};
+                                (PAGED && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0,
+                                p.Sq, p.win_left};
             int unused;
             const int64_t T = (int64_t)p.Hkv * sk_sums(sb, 0, unused);
             const int64_t s0 = (int64_t)g * T / p.sk_grid;
@@ -721,14 +778,14 @@ void attn_fwd_kernel(const FwdParams p) {
             for (int64_t at = s0; at < s1; ++u, off = 0) {
                 const int b = u / p.Hkv;
                 const int kvh = u - b * p.Hkv;
-                const int len = PAGED ? (p.num_pages > 0 ? min(max(p.seqlen[b], 0),
-                                                               p.max_pages << p.page_shift)
-                                                         : 0)
-                                      : p.Skv;
-                const int tiles = (len + BN - 1) / BN;
+                // (the unit's tiles start at the first one its window reaches)
+                const int len = sk_len(sb, b);
+                const int t_first = sk_first_tile(sb, len);
+                const int tiles = (len + BN - 1) / BN - t_first;
                 const int n = (int)min((int64_t)(tiles - off), s1 - at);
                 if (n <= 0) continue;
-                run(0, b, kvh, len, off * BN, min(len, (off + n) * BN), (int64_t)u + g, true);
+                run(0, b, kvh, len, (t_first + off) * BN, min(len, (t_first + off + n) * BN),
+                    (int64_t)u + g, true);
                 at += n;
             }
             return;
@@ -784,64 +841,87 @@ void attn_fwd_kernel(const FwdParams p) {
         p.n_splits > 1);
 }
 
-template <int D, bool BF16, int KV, int WAVES>
+template <int D, bool BF16, int KV, int WAVES, bool CAP>
 hipError_t launch_one(const FwdParams &p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, KV, WAVES>), dim3(grid), dim3(64 * WAVES), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, KV, WAVES, CAP>), dim3(grid), dim3(64 * WAVES),
+                       0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool BF16, int KV, int WAVES>
+template <int D, bool BF16, int KV, int WAVES, bool CAP>
 int blocks_per_cu() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_kernel<D, BF16, KV, WAVES>,
-                                                     64 * WAVES, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, attn_fwd_kernel<D, BF16, KV, WAVES, CAP>, 64 * WAVES, 0) != hipSuccess)
         return 0;
     return n;
 }
 
-template <int D, int W>
+template <int D, int W, bool CAP>
 int decode_blocks(const FwdParams &p, bool bf16, bool paged) {
     const bool tile = p.page_shift >= __builtin_ctz(keys_per_tile(D, W));
-    if (!paged) return bf16 ? blocks_per_cu<D, true, kDense, W>() : blocks_per_cu<D, false, kDense, W>();
-    if (tile) return bf16 ? blocks_per_cu<D, true, kPagedTile, W>() : blocks_per_cu<D, false, kPagedTile, W>();
-    return bf16 ? blocks_per_cu<D, true, kPagedPiece, W>() : blocks_per_cu<D, false, kPagedPiece, W>();
+    if (!paged)
+        return bf16 ? blocks_per_cu<D, true, kDense, W, CAP>()
+                    : blocks_per_cu<D, false, kDense, W, CAP>();
+    if (tile)
+        return bf16 ? blocks_per_cu<D, true, kPagedTile, W, CAP>()
+                    : blocks_per_cu<D, false, kPagedTile, W, CAP>();
+    return bf16 ? blocks_per_cu<D, true, kPagedPiece, W, CAP>()
+                : blocks_per_cu<D, false, kPagedPiece, W, CAP>();
 }
 
-template <int D, int WAVES, int KV>
+template <int D, int WAVES, int KV, bool CAP>
 hipError_t launch_kv(const FwdParams &p, bool bf16, int grid, hipStream_t stream) {
-    return bf16 ? launch_one<D, true, KV, WAVES>(p, grid, stream)
-                : launch_one<D, false, KV, WAVES>(p, grid, stream);
+    return bf16 ? launch_one<D, true, KV, WAVES, CAP>(p, grid, stream)
+                : launch_one<D, false, KV, WAVES, CAP>(p, grid, stream);
 }
 
-template <int D, int WAVES>
+template <int D, int WAVES, bool CAP>
 hipError_t launch_w(const FwdParams &p, bool bf16, bool paged, int grid, hipStream_t stream) {
-    if (!paged) return launch_kv<D, WAVES, kDense>(p, bf16, grid, stream);
+    if (!paged) return launch_kv<D, WAVES, kDense, CAP>(p, bf16, grid, stream);
     if (p.page_shift >= __builtin_ctz(keys_per_tile(D, WAVES)))
-        return launch_kv<D, WAVES, kPagedTile>(p, bf16, grid, stream);
-    return launch_kv<D, WAVES, kPagedPiece>(p, bf16, grid, stream);
+        return launch_kv<D, WAVES, kPagedTile, CAP>(p, bf16, grid, stream);
+    return launch_kv<D, WAVES, kPagedPiece, CAP>(p, bf16, grid, stream);
 }
 
 }  // namespace
 
-int attn_fwd_decode_blocks_per_cu(const FwdParams &p, int D, bool bf16, bool paged, int waves) {
-    if (waves == 2 && D == 64) return decode_blocks<64, 2>(p, bf16, paged);
-    if (waves == 2 && D == 128) return decode_blocks<128, 2>(p, bf16, paged);
-    if (waves == 3 && D == 64) return decode_blocks<64, 3>(p, bf16, paged);
-    if (waves == 3 && D == 128) return decode_blocks<128, 3>(p, bf16, paged);
+// Schedules per head dimension: D <= 128 has the 8-wave prefill schedule and
+// the 3-wave decode schedule (plus the 2-wave one, plain logits only, kept
+// for comparison); D = 256 the 4-wave streaming schedule.
+template <int D, bool CAP>
+hipError_t launch_attn_fwd_dc(const FwdParams &p, bool bf16, bool paged, int waves, int grid,
+                              hipStream_t stream) {
+    if constexpr (D == 256) {
+        if (waves == 4) return launch_w<256, 4, CAP>(p, bf16, paged, grid, stream);
+    } else {
+        if (waves == 8) return launch_w<D, 8, CAP>(p, bf16, paged, grid, stream);
+        if (waves == 3) return launch_w<D, 3, CAP>(p, bf16, paged, grid, stream);
+        if constexpr (!CAP)
+            if (waves == 2) return launch_w<D, 2, CAP>(p, bf16, paged, grid, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D, bool CAP>
+int decode_blocks_per_cu_dc(const FwdParams &p, bool bf16, bool paged, int waves) {
+    if constexpr (D <= 128) {
+        if (waves == 3) return decode_blocks<D, 3, CAP>(p, bf16, paged);
+        if constexpr (!CAP)
+            if (waves == 2) return decode_blocks<D, 2, CAP>(p, bf16, paged);
+    }
     return 0;
 }
 
-hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int waves,
-                           int grid, hipStream_t stream) {
-    if (waves == 8 && D == 64) return launch_w<64, 8>(p, bf16, paged, grid, stream);
-    if (waves == 8 && D == 128) return launch_w<128, 8>(p, bf16, paged, grid, stream);
-    if (waves == 2 && D == 64) return launch_w<64, 2>(p, bf16, paged, grid, stream);
-    if (waves == 2 && D == 128) return launch_w<128, 2>(p, bf16, paged, grid, stream);
-    if (waves == 3 && D == 64) return launch_w<64, 3>(p, bf16, paged, grid, stream);
-    if (waves == 3 && D == 128) return launch_w<128, 3>(p, bf16, paged, grid, stream);
-    if (waves == 4 && D == 256) return launch_w<256, 4>(p, bf16, paged, grid, stream);
-    return hipErrorInvalidValue;
-}
+// This translation unit holds the kernels of one (D, CAP) pair, chosen by the
+// build (-DMIATTN_KD=64|128|256 -DMIATTN_KCAP=0|1).
+#if !defined(MIATTN_KD) || !defined(MIATTN_KCAP)
+#error "build attn_fwd.hip with -DMIATTN_KD=<head dim> -DMIATTN_KCAP=<0|1>"
+#endif
+template hipError_t launch_attn_fwd_dc<MIATTN_KD, (MIATTN_KCAP != 0)>(const FwdParams &, bool,
+                                                                       bool, int, int,
+                                                                       hipStream_t);
+template int decode_blocks_per_cu_dc<MIATTN_KD, (MIATTN_KCAP != 0)>(const FwdParams &, bool,
+                                                                     bool, int);
 
 }  // namespace miattn

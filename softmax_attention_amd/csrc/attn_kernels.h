@@ -54,7 +54,15 @@ struct FwdParams {
     int n_splits;    // key-range splits per (batch, KV head)
     int split_len;   // keys per split, a multiple of the key tile
     int causal;
+    // sliding window: query i sees keys [p_i - win_left, p_i + win_right]
+    // (p_i = i + len - Sq), -1 = unlimited on that side; the host turns a
+    // bound that cannot exclude any key into -1
+    int win_left, win_right;
     float scale_log2;  // |alpha| * log2(e)
+    // logit softcap C (capped kernels only): L log2(e) = cap_k2 * tanh(z alpha / C)
+    // with cap_k2 = C log2(e) and tanh(x) = 1 - 2 / (2^(cap_x s) + 1),
+    // cap_x = 2 log2(e) |alpha| / C, s being the raw score q.k
+    float cap_x, cap_k2;
     int q_mode;        // 0: q as given; 1: q negated (alpha < 0); 2: q zeroed (alpha == 0)
     int xcd_units;     // (batch*KV head, split) units per XCD, or 0 for linear order
     int xcd_unit_major;  // with xcd_units: an XCD runs all row blocks of a unit, then the next
@@ -72,15 +80,29 @@ struct MergeParams {
     int B, Sq, Hq, Hkv, G, rows, n_splits, split_len;
     // stream-K decode: grid size (0 otherwise), keys per tile and the length
     // clamp the attention kernel applies (max_pages * page_size, 0 for an
-    // empty cache)
-    int sk_grid, sk_bn, sk_cap;
+    // empty cache), and the left window bound (-1: none)
+    int sk_grid, sk_bn, sk_cap, sk_win_left;
 };
 
-// Launchers: return the hipGetLastError() status of the launch.
+// Launchers: return the hipGetLastError() status of the launch.  The
+// attention kernels of one head dimension and logit kind (plain or capped)
+// are compiled in a translation unit of their own (attn_fwd.hip built once
+// per pair), which defines these two templates for its pair.
+template <int D, bool CAP>
+hipError_t launch_attn_fwd_dc(const FwdParams &p, bool bf16, bool paged, int waves, int grid,
+                              hipStream_t stream);
+// Workgroups of the decode-shaped (2 or 3 wave) attention kernel one CU runs
+// at once (0 if unknown).
+template <int D, bool CAP>
+int decode_blocks_per_cu_dc(const FwdParams &p, bool bf16, bool paged, int waves);
+
+// Dispatch over the (D, CAP) pairs (miattn.hip; kept out of this header so
+// that a kernel unit does not instantiate the other units' kernels).
 hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int waves,
-                           int grid, hipStream_t stream);
+                           bool cap, int grid, hipStream_t stream);
+int attn_fwd_decode_blocks_per_cu(const FwdParams &p, int D, bool bf16, bool paged, int waves,
+                                  bool cap);
+
 hipError_t launch_lse_merge(const MergeParams &p, int D, bool bf16, hipStream_t stream);
-// Workgroups of the two-wave (decode) attention kernel one CU runs at once (0 if unknown).
-int attn_fwd_decode_blocks_per_cu(const FwdParams &p, int D, bool bf16, bool paged, int waves);
 
 }  // namespace miattn

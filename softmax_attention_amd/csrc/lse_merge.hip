@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     if (p.sk_grid > 0) {
         // Stream-K: the workgroups that touched this unit's tiles, [P, P +
         // tiles) of the T-tile sequence; workgroup g held [g T / G, (g+1) T / G).
-        const SkBatch sb = {p.seqlen, p.Skv, p.B, p.sk_bn, p.sk_cap};
+        const SkBatch sb = {p.seqlen, p.Skv, p.B, p.sk_bn, p.sk_cap, p.Sq, p.sk_win_left};
         int before;
         T = (int64_t)p.Hkv * sk_sums(sb, b, before);
         const int tiles = sk_tiles(sb, b);

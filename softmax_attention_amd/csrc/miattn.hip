@@ -10,6 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -18,6 +19,34 @@
 
 using miattn::FwdParams;
 using miattn::MergeParams;
+
+namespace miattn {
+
+hipError_t launch_attn_fwd(const FwdParams &p, int D, bool bf16, bool paged, int waves,
+                           bool cap, int grid, hipStream_t stream) {
+    switch (D * 2 + (cap ? 1 : 0)) {
+        case 128: return launch_attn_fwd_dc<64, false>(p, bf16, paged, waves, grid, stream);
+        case 129: return launch_attn_fwd_dc<64, true>(p, bf16, paged, waves, grid, stream);
+        case 256: return launch_attn_fwd_dc<128, false>(p, bf16, paged, waves, grid, stream);
+        case 257: return launch_attn_fwd_dc<128, true>(p, bf16, paged, waves, grid, stream);
+        case 512: return launch_attn_fwd_dc<256, false>(p, bf16, paged, waves, grid, stream);
+        case 513: return launch_attn_fwd_dc<256, true>(p, bf16, paged, waves, grid, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+int attn_fwd_decode_blocks_per_cu(const FwdParams &p, int D, bool bf16, bool paged, int waves,
+                                  bool cap) {
+    switch (D * 2 + (cap ? 1 : 0)) {
+        case 128: return decode_blocks_per_cu_dc<64, false>(p, bf16, paged, waves);
+        case 129: return decode_blocks_per_cu_dc<64, true>(p, bf16, paged, waves);
+        case 256: return decode_blocks_per_cu_dc<128, false>(p, bf16, paged, waves);
+        case 257: return decode_blocks_per_cu_dc<128, true>(p, bf16, paged, waves);
+        default: return 0;
+    }
+}
+
+}  // namespace miattn
 
 namespace {
 
@@ -45,7 +74,8 @@ struct DeviceState {
     void *ws = nullptr;  // split-KV partials
     size_t ws_bytes = 0;
     int cus = 0;
-    int decode_per_cu[2][2][2][2] = {};  // decode kernel occupancy: [3 waves][D 128][bf16][paged]
+    // decode kernel occupancy: [3 waves][D 128][bf16][paged][capped logits]
+    int decode_per_cu[2][2][2][2][2] = {};
 };
 
 std::mutex g_mu;
@@ -65,11 +95,12 @@ int compute_units(int dev) {
 }
 
 // Decode workgroups one CU runs at once (occupancy API, cached).
-int decode_per_cu(int dev, const miattn::FwdParams &p, int D, bool bf16, bool paged, int waves) {
+int decode_per_cu(int dev, const miattn::FwdParams &p, int D, bool bf16, bool paged, int waves,
+                  bool cap) {
     std::lock_guard<std::mutex> lock(g_mu);
-    int &slot = g_dev[dev].decode_per_cu[waves == 3][D == 128][bf16][paged];
+    int &slot = g_dev[dev].decode_per_cu[waves == 3][D == 128][bf16][paged][cap];
     if (slot == 0) {
-        const int n = miattn::attn_fwd_decode_blocks_per_cu(p, D, bf16, paged, waves);
+        const int n = miattn::attn_fwd_decode_blocks_per_cu(p, D, bf16, paged, waves, cap);
         slot = n > 0 ? n : -1;
     }
     return slot > 0 ? slot : 1;
@@ -176,6 +207,42 @@ void set_scale(FwdParams &p, float alpha) {
     }
 }
 
+// Sliding window and logit softcap (TileOPs "Attention Operators",
+// GQADenseFwdOp stages 5 and 6; the init parameters: -1 = an unlimited window
+// side, a cap of 0 disables capping, a negative cap is an error).  max_len is
+// the longest key range a request can have.  A bound that cannot exclude any
+// key becomes -1, which also keeps p_i + w_R within int range in the kernel.
+miattn_status check_window_softcap(int window_left, int window_right, float softcap) {
+    if (window_left < -1 || window_right < -1)
+        return fail(MIATTN_ERR_INVALID_ARG,
+                    "window_left=%d, window_right=%d: each must be -1 (unlimited) or >= 0",
+                    window_left, window_right);
+    if (!(softcap >= 0.f) || isinf(softcap))
+        return fail(MIATTN_ERR_INVALID_ARG, "softcap must be 0 (none) or positive and finite");
+    return MIATTN_OK;
+}
+
+miattn_status set_window_softcap(FwdParams &p, int window_left, int window_right,
+                                 float softcap, int64_t max_len, float alpha) {
+    // p_i lies in [-Sq, max_len - 1]: w_L >= max_len admits every key j >= 0,
+    // w_R >= max_len + Sq every key j < max_len
+    p.win_left = (window_left >= 0 && window_left < max_len) ? window_left : -1;
+    p.win_right =
+        (window_right >= 0 && window_right < max_len + p.Sq) ? window_right : -1;
+    if (p.win_right >= 0 && 2 * max_len + p.Sq > INT_MAX)
+        return fail(MIATTN_ERR_UNSUPPORTED,
+                    "a right window needs 2 * keys + Sq <= %d (keys = %lld, Sq = %d)", INT_MAX,
+                    (long long)max_len, p.Sq);
+    p.cap_x = 0.f;
+    p.cap_k2 = 0.f;
+    if (softcap > 0.f) {
+        const double l2e = 1.4426950408889634;
+        p.cap_x = (float)(2.0 * l2e * fabs((double)alpha) / (double)softcap);
+        p.cap_k2 = (float)((double)softcap * l2e);
+    }
+    return MIATTN_OK;
+}
+
 int env_int(const char *name, int dflt) {
     const char *s = getenv(name);
     if (!s || !*s) return dflt;
@@ -184,7 +251,7 @@ int env_int(const char *name, int dflt) {
 
 // ---------------------------------------------------------------- plan + launch
 
-miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
+miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, bool cap,
                   hipStream_t stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -200,6 +267,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
     int waves = D == 256 ? 4 : (p.rows > miattn::kRowsPerWave ? 8 : 3);
     const int forced = env_int("MIATTN_WAVES", 0);
     if (D <= 128 && (forced == 2 || forced == 3 || forced == 8)) waves = forced;
+    if (waves == 2 && cap) waves = 3;  // the two-wave comparison schedule has no capped build
     const int BN = miattn::keys_per_tile(D, waves);
     const int BM = miattn::rows_per_workgroup(waves);
     p.n_mblocks = (p.rows + BM - 1) / BM;
@@ -215,7 +283,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
     // (the plan's tile sums are 32-bit: Hkv * B * tiles of the capacity)
     if ((waves == 2 || waves == 3) && split_keys <= 0 && bhs * cap_tiles < INT_MAX &&
         env_int("MIATTN_STREAMK", 1)) {
-        int per_cu = decode_per_cu(dev, p, D, bf16, paged, waves);
+        int per_cu = decode_per_cu(dev, p, D, bf16, paged, waves, cap);
         const int want = env_int("MIATTN_SK_PER_CU", 0);  // tuning override
         if (want > 0 && want < per_cu) per_cu = want;
         const int G = compute_units(dev) * per_cu;
@@ -234,7 +302,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
         p.lse_part = p.o_part + slots * p.rows * D;
         p.sk_grid = G;
         e = timed_launch(0, stream, [&] {
-            return miattn::launch_attn_fwd(p, D, bf16, paged, waves, G, stream);
+            return miattn::launch_attn_fwd(p, D, bf16, paged, waves, cap, G, stream);
         });
         if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
         MergeParams m = {};
@@ -255,6 +323,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
         m.sk_grid = G;
         m.sk_bn = BN;
         m.sk_cap = (paged && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0;
+        m.sk_win_left = p.win_left;
         e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
         return MIATTN_OK;
@@ -263,6 +332,14 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
     // Split the key axis when the (row block, batch, KV head) units alone
     // cannot fill the chip, or for decode-shaped calls, whose per-request
     // lengths vary and are only known on the device.
+    // With a left window a row block sees at most w_L + its own query span
+    // (+ w_R without the causal rule) keys: size the splits for that span.
+    int64_t span_tiles = cap_tiles;
+    if (p.win_left >= 0) {
+        int64_t span = (int64_t)p.win_left + (BM + p.G - 1) / p.G + 1;
+        if (!p.causal) span += p.win_right >= 0 ? (int64_t)p.win_right : capacity;
+        span_tiles = std::min(cap_tiles, (span + BN - 1) / BN + 1);
+    }
     int64_t tiles_per;
     if (split_keys > 0) {
         tiles_per = (split_keys + BN - 1) / BN;
@@ -275,7 +352,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
             tiles_per = cap_tiles;
         } else {
             const int64_t want = (3 * (int64_t)cus + units0 - 1) / units0;
-            tiles_per = (cap_tiles + want - 1) / want;
+            tiles_per = (span_tiles + want - 1) / want;
         }
     }
     if (tiles_per < 1) tiles_per = 1;
@@ -305,7 +382,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity,
     }
 
     e = timed_launch(0, stream, [&] {
-        return miattn::launch_attn_fwd(p, D, bf16, paged, waves, (int)grid, stream);
+        return miattn::launch_attn_fwd(p, D, bf16, paged, waves, cap, (int)grid, stream);
     });
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
 
@@ -339,10 +416,13 @@ const char *miattn_last_error(void) { return g_err; }
 
 miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B, int Hq,
                              int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                             int window_left, int window_right, float softcap,
                              const uint8_t *key_padding_mask, void *o, float *lse,
                              miattn_dtype dtype, void *stream) {
     g_err[0] = '\0';
     miattn_status st = check_common(q, o, lse, B, Sq, Hq, Hkv, D, scale, dtype);
+    if (st != MIATTN_OK) return st;
+    st = check_window_softcap(window_left, window_right, softcap);
     if (st != MIATTN_OK) return st;
     if (Skv < 0) return fail(MIATTN_ERR_INVALID_ARG, "negative dimension: Skv=%d", Skv);
     if (causal != 0 && causal != 1)
@@ -370,17 +450,23 @@ miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B,
     p.Hkv = Hkv;
     p.Skv = Skv;
     p.causal = causal;
-    set_scale(p, resolve_scale(scale, D));
-    return run(p, D, dtype == MIATTN_BF16, false, Skv, (hipStream_t)stream);
+    const float alpha = resolve_scale(scale, D);
+    set_scale(p, alpha);
+    st = set_window_softcap(p, window_left, window_right, softcap, Skv, alpha);
+    if (st != MIATTN_OK) return st;
+    return run(p, D, dtype == MIATTN_BF16, false, Skv, softcap > 0.f, (hipStream_t)stream);
 }
 
 miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *real_seqlen_kv, const int32_t *block_table,
-                             int page_size, int causal, void *o, float *lse, int B, int Sq,
+                             int page_size, int causal, int window_left, int window_right,
+                             float softcap, void *o, float *lse, int B, int Sq,
                              int Hq, int Hkv, int D, int max_pages, int num_phys_pages,
                              float scale, miattn_dtype dtype, void *stream) {
     g_err[0] = '\0';
     miattn_status st = check_common(q, o, lse, B, Sq, Hq, Hkv, D, scale, dtype);
+    if (st != MIATTN_OK) return st;
+    st = check_window_softcap(window_left, window_right, softcap);
     if (st != MIATTN_OK) return st;
     if (page_size <= 0) return fail(MIATTN_ERR_INVALID_ARG, "page_size must be > 0 (got %d)",
                                     page_size);
@@ -452,8 +538,11 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
     p.max_pages = max_pages;
     p.num_pages = num_phys_pages;
     p.causal = causal;
-    set_scale(p, resolve_scale(scale, D));
-    return run(p, D, dtype == MIATTN_BF16, true, capacity, (hipStream_t)stream);
+    const float alpha = resolve_scale(scale, D);
+    set_scale(p, alpha);
+    st = set_window_softcap(p, window_left, window_right, softcap, capacity, alpha);
+    if (st != MIATTN_OK) return st;
+    return run(p, D, dtype == MIATTN_BF16, true, capacity, softcap > 0.f, (hipStream_t)stream);
 }
 
 miattn_status miattn_release_workspace(void) {

@@ -36,23 +36,24 @@ def test_library_exports_every_declared_symbol():
 
 def dense(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, Hq=8, Hkv=2, Sq=4, Skv=4, D=128, scale=NAN, causal=1,
-             mask=None, o=FAKE, lse=None, dtype=0, stream=None)
+             wl=-1, wr=-1, softcap=0.0, mask=None, o=FAKE, lse=None, dtype=0, stream=None)
     a.update(kw)
     L = mi.lib()
     st = L.attn_fwd_dense(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Skv"],
-                          a["D"], a["scale"], a["causal"], a["mask"], a["o"], a["lse"],
-                          a["dtype"], a["stream"])
+                          a["D"], a["scale"], a["causal"], a["wl"], a["wr"], a["softcap"],
+                          a["mask"], a["o"], a["lse"], a["dtype"], a["stream"])
     return st, L.miattn_last_error().decode()
 
 
 def paged(**kw):
-    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, bt=FAKE, page_size=64, causal=1, o=FAKE,
-             lse=None, B=2, Sq=1, Hq=8, Hkv=2, D=128, max_pages=4, n_phys=8, scale=NAN, dtype=0,
-             stream=None)
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, bt=FAKE, page_size=64, causal=1, wl=-1,
+             wr=-1, softcap=0.0, o=FAKE, lse=None, B=2, Sq=1, Hq=8, Hkv=2, D=128, max_pages=4,
+             n_phys=8, scale=NAN, dtype=0, stream=None)
     a.update(kw)
     L = mi.lib()
     st = L.attn_fwd_paged(a["q"], a["kc"], a["vc"], a["lens"], a["bt"], a["page_size"],
-                          a["causal"], a["o"], a["lse"], a["B"], a["Sq"], a["Hq"], a["Hkv"],
+                          a["causal"], a["wl"], a["wr"], a["softcap"], a["o"], a["lse"], a["B"],
+                          a["Sq"], a["Hq"], a["Hkv"],
                           a["D"], a["max_pages"], a["n_phys"], a["scale"], a["dtype"],
                           a["stream"])
     return st, L.miattn_last_error().decode()
@@ -76,6 +77,12 @@ def paged(**kw):
     (dict(o=FAKE + 4), 1, "o not 16-byte aligned"),
     (dict(lse=FAKE + 2), 1, "lse not 4-byte aligned"),
     (dict(causal=2), 1, "causal=2"),
+    (dict(wl=-2), 1, "window_left=-2"),
+    (dict(wr=-5), 1, "window_right=-5"),
+    (dict(softcap=-1.0), 1, "softcap"),
+    (dict(softcap=NAN), 1, "softcap"),
+    (dict(softcap=math.inf), 1, "softcap"),
+    (dict(B=0, softcap=-1.0), 1, "softcap"),  # checked before the empty-call exit
 ])
 def test_dense_refusals(kw, status, needle):
     st, msg = dense(**kw)
@@ -100,6 +107,8 @@ def test_dense_empty_calls_are_ok_without_touching_the_device():
     (dict(Hq=12, Hkv=8), 1, "not divisible"),
     (dict(D=512), 2, "D=512 unsupported"),
     (dict(max_pages=1 << 30, page_size=64), 2, "exceeds"),
+    (dict(wl=-3), 1, "window_left=-3"),
+    (dict(softcap=-0.5), 1, "softcap"),
 ])
 def test_paged_refusals(kw, status, needle):
     st, msg = paged(**kw)

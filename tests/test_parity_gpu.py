@@ -32,21 +32,26 @@ def _reset_split():
     mi.set_split_keys(0)
 
 
-def run_dense(q, k, v, *, scale, causal, mask=None):
+def run_dense(q, k, v, *, scale, causal, mask=None, window=None, softcap=None):
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     md = None if mask is None else mask.to(DEV)
-    o, lse = mi.attn_fwd_dense(qd, kd, vd, scale=scale, causal=causal, key_padding_mask=md)
+    o, lse = mi.attn_fwd_dense(qd, kd, vd, scale=scale, causal=causal, key_padding_mask=md,
+                               window=window, softcap=softcap)
     torch.cuda.synchronize()
     return o, lse
 
 
 def dense_case(B, Sq, Skv, Hq, Hkv, D, *, dtype=torch.bfloat16, causal=True, scale=None,
-               mask=None, seed=0, sigma=1.0, what=""):
+               mask=None, seed=0, sigma=1.0, window=None, softcap=None, split_keys=0, what=""):
     say(f"dense {what} B={B} Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv} D={D} {dtype} "
-        f"causal={causal} scale={scale} mask={mask is not None}")
+        f"causal={causal} scale={scale} mask={mask is not None} window={window} "
+        f"softcap={softcap} split_keys={split_keys}")
     q, k, v = workloads.dense_inputs(B, Sq, Skv, Hq, Hkv, D, dtype=dtype, seed=seed, sigma=sigma)
-    o, lse = run_dense(q, k, v, scale=scale, causal=causal, mask=mask)
-    o_ref, lse_ref = oracle.attn_dense(q, k, v, scale=scale, causal=causal, key_padding_mask=mask)
+    mi.set_split_keys(split_keys)
+    o, lse = run_dense(q, k, v, scale=scale, causal=causal, mask=mask, window=window,
+                       softcap=softcap)
+    o_ref, lse_ref = oracle.attn_dense(q, k, v, scale=scale, causal=causal, key_padding_mask=mask,
+                                       window=window, softcap=softcap)
     return check_full(o, lse, o_ref, lse_ref, what)
 
 
@@ -162,9 +167,9 @@ def test_dense_is_deterministic():
 
 
 def paged_case(B, Sq, Hq, Hkv, D, lens, page_size, *, dtype=torch.bfloat16, causal=True,
-               scale=None, seed=0, split_keys=0, what=""):
+               scale=None, seed=0, split_keys=0, window=None, softcap=None, what=""):
     say(f"paged {what} B={B} Sq={Sq} Hq={Hq} Hkv={Hkv} D={D} page={page_size} lens={lens} "
-        f"split_keys={split_keys}")
+        f"split_keys={split_keys} window={window} softcap={softcap}")
     cap = max(max(lens), 1)
     max_pages = (cap + page_size - 1) // page_size + 1
     n_phys = B * max_pages + 3
@@ -183,10 +188,11 @@ def paged_case(B, Sq, Hq, Hkv, D, lens, page_size, *, dtype=torch.bfloat16, caus
     lens_t = torch.tensor(lens, dtype=torch.int32)
     mi.set_split_keys(split_keys)
     o, lse = mi.attn_fwd_paged(q.to(DEV), kc.to(DEV), vc.to(DEV), lens_t.to(DEV), bt.to(DEV),
-                               page_size, causal=causal, scale=scale)
+                               page_size, causal=causal, scale=scale, window=window,
+                               softcap=softcap)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attn_paged(q, kc, vc, lens_t, bt, page_size, causal=causal,
-                                       scale=scale)
+                                       scale=scale, window=window, softcap=softcap)
     return check_full(o, lse, o_ref, lse_ref, what)
 
 
