@@ -238,7 +238,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic("prefill"),
-                     "kernel": "attn_fwd_kernel<128, true, 0, 8> (D, bf16, dense K/V, 8 waves)",
+                     "kernel": "attn_fwd_kernel<128, true, 0, 8, false> (D, bf16, dense K/V, 8 waves, plain logits)",
                      "kernel_avg_us": ms_kernel * 1e3},
     }
     del w
@@ -261,7 +261,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": kern_gbs / PEAK_HBM_GBS,
                          "traffic": measured_traffic("decode"),
-                         "kernel": "attn_fwd_kernel<128, true, 1, 3> (D, bf16, paged K/V, 3 waves, stream-K)",
+                         "kernel": "attn_fwd_kernel<128, true, 1, 3, false> (D, bf16, paged K/V, 3 waves, plain logits, stream-K)",
                          "kernel_avg_us": d["attn_kernel_ms"] * 1e3,
                          "merge_kernel_avg_us": d["merge_kernel_ms"] * 1e3}}
         del wd
