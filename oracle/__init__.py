@@ -65,8 +65,13 @@ def _load():
                                           i32, f32, i32, P, P]
         lib.oracle_attn_paged_rows.argtypes = [P, P, P, P, P, i32, i32, *win, i32, i32, i32, i32,
                                                i32, i32, f32, i32, P, i64, P, P]
+        lib.oracle_attn_varlen.argtypes = [P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32,
+                                           i32, *win, P, P, P]
+        lib.oracle_attn_paged_varlen.argtypes = [P, P, P, P, P, i32, P, i32, *win, P, i32, i32,
+                                                 i32, i32, i32, i32, f32, i32, P, P]
         for name in ("oracle_attn_dense", "oracle_attn_dense_rows", "oracle_attn_paged",
-                     "oracle_attn_paged_rows", "oracle_num_threads"):
+                     "oracle_attn_paged_rows", "oracle_attn_varlen", "oracle_attn_paged_varlen",
+                     "oracle_num_threads"):
             getattr(lib, name).restype = i32
         _lib = lib
     return _lib
@@ -234,5 +239,75 @@ def attn_paged_rows(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size,
     return o, lse
 
 
+def _i32(x) -> np.ndarray:
+    import torch
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x).astype(np.int32))
+
+
+def _sinks(sinks, Hq):
+    if sinks is None:
+        return None
+    import torch
+    if isinstance(sinks, torch.Tensor):
+        sinks = sinks.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(sinks, dtype=np.float32))
+    assert a.shape == (Hq,), a.shape
+    return a
+
+
+def attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, scale=None, causal=True, window=None,
+                softcap=None, sinks=None, dtype=None):
+    """Packed (THD) call: q [total_q,Hq,D], k/v [total_kv,Hkv,D], cu_seqlens [B+1]
+    (int), sinks [Hq] float32 or None.  Returns o [total_q,Hq,D] and lse
+    [Hq,total_q] (float64)."""
+    dt = _dtype_code(q) if dtype is None else dtype
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    total_q, Hq, D = qb.shape
+    total_kv, Hkv, _ = kb.shape
+    cq, ck = _i32(cu_seqlens_q), _i32(cu_seqlens_kv)
+    B = cq.shape[0] - 1
+    sk = _sinks(sinks, Hq)
+    o = np.zeros((total_q, Hq, D), np.float64)
+    lse = np.zeros((Hq, total_q), np.float64)
+    rc = _load().oracle_attn_varlen(_ptr(qb), _ptr(kb), _ptr(vb), dt, _ptr(cq), _ptr(ck), B,
+                                    total_q, total_kv, Hq, Hkv, D, _scale_arg(scale),
+                                    int(bool(causal)), *_opt_args(window, softcap),
+                                    None if sk is None else _ptr(sk), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_varlen rejected the call (rc={rc})")
+    return o, lse
+
+
+def attn_paged_varlen(q, k_cache, v_cache, cache_seqlens, block_table, page_size, cu_seqlens_q,
+                      *, causal=True, scale=None, window=None, softcap=None, sinks=None,
+                      dtype=None):
+    """Packed-query paged call: q [total_q,Hq,D] delimited by cu_seqlens_q [B+1];
+    k_cache/v_cache [pages*page_size,Hkv,D] or [pages,page_size,Hkv,D];
+    cache_seqlens [B] (each request's keys, its queries included);
+    block_table [B,max_pages].  Returns o [total_q,Hq,D], lse [Hq,total_q]."""
+    dt = _dtype_code(q) if dtype is None else dtype
+    qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
+    total_q, Hq, D = qb.shape
+    Hkv = kb.shape[-2]
+    lens, bt, cq = _i32(cache_seqlens), _i32(block_table), _i32(cu_seqlens_q)
+    B = cq.shape[0] - 1
+    assert lens.shape == (B,) and bt.ndim == 2 and bt.shape[0] == B
+    sk = _sinks(sinks, Hq)
+    o = np.zeros((total_q, Hq, D), np.float64)
+    lse = np.zeros((Hq, total_q), np.float64)
+    rc = _load().oracle_attn_paged_varlen(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(lens), _ptr(bt),
+                                          int(page_size), _ptr(cq), int(bool(causal)),
+                                          *_opt_args(window, softcap),
+                                          None if sk is None else _ptr(sk), B, total_q, Hq, Hkv,
+                                          D, bt.shape[1], _scale_arg(scale), dt, _ptr(o),
+                                          _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_paged_varlen rejected the call (rc={rc})")
+    return o, lse
+
+
 __all__ = ["BF16", "FP16", "build", "decode", "resolve_scale", "num_threads", "attn_dense",
-           "attn_dense_rows", "attn_paged", "attn_paged_rows"]
+           "attn_dense_rows", "attn_paged", "attn_paged_rows", "attn_varlen",
+           "attn_paged_varlen"]

@@ -27,12 +27,21 @@
  *     key_padding_mask [B, S_kv], True = keep, False sets the column to -inf.
  *   - MATE "QSA", Core Attention: the log-sum-exp is natural-log and an empty
  *     selection returns zero output with -inf LSE.
+ *   - TileOPs "Attention Operators", GQAVarlenFwdOp and GQAPagedFwdOp: packed
+ *     THD tensors [total, heads, dim] whose requests are delimited by
+ *     cu_seqlens (request b holds rows cu[b] .. cu[b+1] - 1), the causal mask
+ *     bottom-right aligned per request, and optional float32 sinks: one logit
+ *     per query head added to the softmax denominator only (neither scaled
+ *     nor capped); -inf disables a sink, +inf makes the head's output zero,
+ *     and a row with no visible key returns zero whatever its sink.
  *
  * Readings where the pages leave a step open (each also listed in the design
  * notes): the scale multiplies the finished dot product; the LSE is
  * ln sum_j exp(L_j) over the visible keys, L_j being the logit of stage 6
  * (alpha <q, k_j>, capped when a softcap is given); a paged request's window
- * is placed at its own p_i; a causal call with
+ * is placed at its own p_i; with a sink the LSE is the log of the whole
+ * denominator, ln(sum_j exp(L_j) + exp(sink)), so a row with no visible key
+ * has lse = sink; packed (THD) calls store lse as [H, total_q]; a causal call with
  * S_q > S_kv is accepted and its first S_q - S_kv rows are empty; a masked
  * key and a causally hidden key are combined with AND.
  *
@@ -107,6 +116,10 @@ typedef struct {
     double alpha;
     int window_left, window_right; /* -1: unlimited */
     double softcap;                /* 0: no cap */
+    /* packed (THD) requests: row offsets [B + 1], or NULL for B equal blocks */
+    const int32_t *cu_q, *cu_kv;
+    int total_q;
+    const float *sinks; /* [Hq] or NULL */
     /* dense */
     int Skv;
     const uint8_t *mask; /* [B, Skv] or NULL */
@@ -120,7 +133,22 @@ typedef struct {
 /* Number of keys request b holds. */
 static int64_t kv_length(const call_t *c, int b)
 {
-    return c->paged ? (int64_t)c->seqlen[b] : (int64_t)c->Skv;
+    if (c->paged)
+        return (int64_t)c->seqlen[b];
+    if (c->cu_kv)
+        return (int64_t)c->cu_kv[b + 1] - c->cu_kv[b];
+    return (int64_t)c->Skv;
+}
+
+/* Number of queries request b holds, and the packed row of its query i. */
+static int64_t q_length(const call_t *c, int b)
+{
+    return c->cu_q ? (int64_t)c->cu_q[b + 1] - c->cu_q[b] : (int64_t)c->Sq;
+}
+
+static int64_t q_row(const call_t *c, int b, int i)
+{
+    return c->cu_q ? (int64_t)c->cu_q[b] + i : (int64_t)b * c->Sq + i;
 }
 
 /* Element offset of key/value row (b, j, r): dense BSHD, or the page-table
@@ -133,6 +161,8 @@ static int64_t kv_row_offset(const call_t *c, int b, int64_t j, int r)
         int64_t in_page = j % c->page_size;
         int64_t phys_page = c->block_table[(int64_t)b * c->max_pages + logical_page];
         row = phys_page * c->page_size + in_page;
+    } else if (c->cu_kv) {
+        row = (int64_t)c->cu_kv[b] + j;
     } else {
         row = (int64_t)b * c->Skv + j;
     }
@@ -144,7 +174,7 @@ static int64_t kv_row_offset(const call_t *c, int b, int64_t j, int r)
  * and the padding mask keeps column j. */
 static int visible(const call_t *c, int b, int i, int64_t j)
 {
-    int64_t p = (int64_t)i + kv_length(c, b) - c->Sq;
+    int64_t p = (int64_t)i + kv_length(c, b) - q_length(c, b);
     if (c->causal && j > p)
         return 0;
     if (c->window_left != -1 && j < p - c->window_left)
@@ -165,7 +195,9 @@ static void attend_row(const call_t *c, int b, int i, int h, double *o_row,
     const int g = c->Hq / c->Hkv;
     const int r = h / g; /* query head h reads KV head floor(h / g) */
     const int64_t n = kv_length(c, b);
-    const int64_t q_off = (((int64_t)b * c->Sq + i) * c->Hq + h) * D;
+    const int64_t q_off = (q_row(c, b, i) * c->Hq + h) * D;
+    /* the head's sink logit (-inf: none), used as given */
+    const double sink = c->sinks ? (double)c->sinks[h] : -INFINITY;
 
     /* scores of the visible keys; s[j] is left unused for hidden keys */
     int64_t n_visible = 0;
@@ -182,15 +214,18 @@ static void attend_row(const call_t *c, int b, int i, int h, double *o_row,
         ++n_visible;
     }
 
-    if (n_visible == 0) { /* no visible key: zero output, -inf LSE */
+    if (n_visible == 0 || sink == INFINITY) {
+        /* no visible key: zero output, and the LSE of what the denominator
+         * holds (-inf without a sink); a +inf sink takes all the weight */
         for (int d = 0; d < D; ++d)
             o_row[d] = 0.0;
-        *lse_out = -INFINITY;
+        *lse_out = n_visible == 0 ? sink : INFINITY;
         return;
     }
 
-    /* softmax of the logits over the visible keys, shifted by their maximum */
-    double m = -INFINITY;
+    /* softmax of the logits over the visible keys, shifted by their maximum
+     * (and the sink's); the sink adds to the denominator only */
+    double m = sink;
     for (int64_t j = 0; j < n; ++j)
         if (visible(c, b, i, j) && s[j] > m)
             m = s[j];
@@ -201,6 +236,7 @@ static void attend_row(const call_t *c, int b, int i, int h, double *o_row,
         w[j] = exp(s[j] - m);
         l += w[j];
     }
+    l += exp(sink - m);
 
     for (int d = 0; d < D; ++d) {
         double acc = 0.0;
@@ -278,7 +314,9 @@ static int run_rows(const call_t *c, const int32_t *sel, int64_t nsel, double *o
 /* Evaluate every row: o [B, Sq, Hq, D], lse [B, Hq, Sq]. */
 static int run_all(const call_t *c, double *o, double *lse)
 {
-    int64_t nrows = (int64_t)c->B * c->Sq * c->Hq;
+    int64_t nrows = 0;
+    for (int b = 0; b < c->B; ++b)
+        nrows += q_length(c, b) * c->Hq;
     if (nrows == 0)
         return 0;
     int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * 3 * (size_t)nrows);
@@ -288,10 +326,11 @@ static int run_all(const call_t *c, double *o, double *lse)
         free(lse_rows);
         return -2;
     }
-    /* row order b, i, h matches the BSHD output, so o can be written in place */
+    /* row order b, i, h matches the BSHD (or packed THD) output, so o can be
+     * written in place */
     int64_t t = 0;
     for (int b = 0; b < c->B; ++b)
-        for (int i = 0; i < c->Sq; ++i)
+        for (int i = 0; i < q_length(c, b); ++i)
             for (int h = 0; h < c->Hq; ++h) {
                 sel[3 * t] = b;
                 sel[3 * t + 1] = i;
@@ -301,9 +340,13 @@ static int run_all(const call_t *c, double *o, double *lse)
     int rc = run_rows(c, sel, nrows, o, lse_rows);
     t = 0;
     for (int b = 0; b < c->B; ++b)
-        for (int i = 0; i < c->Sq; ++i)
-            for (int h = 0; h < c->Hq; ++h)
-                lse[((int64_t)b * c->Hq + h) * c->Sq + i] = lse_rows[t++];
+        for (int i = 0; i < q_length(c, b); ++i)
+            for (int h = 0; h < c->Hq; ++h) {
+                if (c->cu_q) /* packed: lse [Hq, total_q] */
+                    lse[(int64_t)h * c->total_q + q_row(c, b, i)] = lse_rows[t++];
+                else /* lse [B, Hq, Sq] */
+                    lse[((int64_t)b * c->Hq + h) * c->Sq + i] = lse_rows[t++];
+            }
     free(sel);
     free(lse_rows);
     return rc;
@@ -419,6 +462,67 @@ int oracle_attn_paged_rows(const uint16_t *q, const uint16_t *k_cache, const uin
             sel[3 * t + 2] < 0 || sel[3 * t + 2] >= Hq)
             return -1;
     return run_rows(&c, sel, nsel, o, lse);
+}
+
+/* Packed offsets: cu[0] = 0, nondecreasing, cu[B] = total. */
+static int check_offsets(const int32_t *cu, int B, int total)
+{
+    if (!cu || cu[0] != 0 || cu[B] != total)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (cu[b + 1] < cu[b])
+            return -1;
+    return 0;
+}
+
+/* Packed (THD) dense call: q [total_q, Hq, D], k/v [total_kv, Hkv, D]; request
+ * b holds queries cu_q[b] .. cu_q[b+1]-1 and keys cu_kv[b] .. cu_kv[b+1]-1;
+ * sinks [Hq] float32 or NULL.  Writes o [total_q, Hq, D] and lse [Hq, total_q]. */
+int oracle_attn_varlen(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype,
+                       const int32_t *cu_q, const int32_t *cu_kv, int B, int total_q,
+                       int total_kv, int Hq, int Hkv, int D, float scale, int causal,
+                       int window_left, int window_right, float softcap, const float *sinks,
+                       double *o, double *lse)
+{
+    call_t c;
+    if (B < 0 || total_q < 0 || total_kv < 0)
+        return -1;
+    if (make_dense(&c, q, k, v, dtype, B, Hq, Hkv, 0, 0, D, scale, causal, window_left,
+                   window_right, softcap, NULL))
+        return -1;
+    if (check_offsets(cu_q, B, total_q) || check_offsets(cu_kv, B, total_kv))
+        return -1;
+    c.cu_q = cu_q;
+    c.cu_kv = cu_kv;
+    c.total_q = total_q;
+    c.sinks = sinks;
+    return run_all(&c, o, lse);
+}
+
+/* Packed-query paged call: q [total_q, Hq, D] delimited by cu_q [B+1]; caches
+ * and block_table as for oracle_attn_paged; cache_seqlens [B] counts each
+ * request's keys, its queries included.  Writes o [total_q, Hq, D] and lse
+ * [Hq, total_q]. */
+int oracle_attn_paged_varlen(const uint16_t *q, const uint16_t *k_cache,
+                             const uint16_t *v_cache, const int32_t *cache_seqlens,
+                             const int32_t *block_table, int page_size, const int32_t *cu_q,
+                             int causal, int window_left, int window_right, float softcap,
+                             const float *sinks, int B, int total_q, int Hq, int Hkv, int D,
+                             int max_pages, float scale, int dtype, double *o, double *lse)
+{
+    call_t c;
+    if (total_q < 0)
+        return -1;
+    if (make_paged(&c, q, k_cache, v_cache, cache_seqlens, block_table, page_size, causal,
+                   window_left, window_right, softcap, B, 0, Hq, Hkv, D, max_pages, scale,
+                   dtype))
+        return -1;
+    if (check_offsets(cu_q, B, total_q))
+        return -1;
+    c.cu_q = cu_q;
+    c.total_q = total_q;
+    c.sinks = sinks;
+    return run_all(&c, o, lse);
 }
 
 /* Number of threads an OpenMP parallel region uses here. */

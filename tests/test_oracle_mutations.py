@@ -17,7 +17,7 @@ SRC = os.path.join(ROOT, "oracle", "attn_oracle.c")
 
 MUTANTS = {
     "head_map_modulo": ("const int r = h / g;", "const int r = h % c->Hkv;"),
-    "causal_not_end_aligned": ("int64_t p = (int64_t)i + kv_length(c, b) - c->Sq;",
+    "causal_not_end_aligned": ("int64_t p = (int64_t)i + kv_length(c, b) - q_length(c, b);",
                                "int64_t p = (int64_t)i;"),
     "causal_off_by_one": ("if (c->causal && j > p)", "if (c->causal && j >= p)"),
     "mask_ignored": ("if (c->mask && c->mask[(int64_t)b * c->Skv + j] == 0)", "if (0)"),
@@ -46,11 +46,24 @@ MUTANTS = {
                                      "s[j] = tanh(s[j] / c->softcap);"),
     "softcap_before_scale": ("s[j] = c->softcap * tanh(s[j] / c->softcap);",
                              "s[j] = c->alpha * c->softcap * tanh(dot / c->softcap);"),
+    "sink_scaled": ("const double sink = c->sinks ? (double)c->sinks[h] : -INFINITY;",
+                    "const double sink = c->sinks ? c->alpha * (double)c->sinks[h] : -INFINITY;"),
+    "sink_capped": ("const double sink = c->sinks ? (double)c->sinks[h] : -INFINITY;",
+                    "const double sink = c->sinks ? (c->softcap > 0.0 ? c->softcap * tanh(c->sinks[h] / c->softcap) : c->sinks[h]) : -INFINITY;"),
+    "sink_left_out_of_denominator": ("l += exp(sink - m);", "l += 0.0;"),
+    "empty_row_lse_ignores_sink": ("*lse_out = n_visible == 0 ? sink : INFINITY;",
+                                   "*lse_out = n_visible == 0 ? -INFINITY : INFINITY;"),
+    "varlen_position_uses_request_0": ("int64_t p = (int64_t)i + kv_length(c, b) - q_length(c, b);",
+                                       "int64_t p = (int64_t)i + kv_length(c, b) - q_length(c, 0);"),
+    "varlen_keys_at_query_offsets": ("row = (int64_t)c->cu_kv[b] + j;", "row = (int64_t)c->cu_q[b] + j;"),
+    "varlen_lse_batched_layout": ("lse[(int64_t)h * c->total_q + q_row(c, b, i)] = lse_rows[t++];",
+                                  "lse[q_row(c, b, i) * c->Hq + h] = lse_rows[t++];"),
     "value_sum_skips_first_key": ("for (int64_t j = 0; j < n; ++j) {\n            if (!visible(c, b, i, j))\n                continue;\n            acc +=",
                                   "for (int64_t j = 1; j < n; ++j) {\n            if (!visible(c, b, i, j))\n                continue;\n            acc +="),
 }
 
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_pins_window_softcap.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_pins_window_softcap.py",
+             "test_oracle_pins_varlen_sinks.py"]
 
 PLUGIN = "import os, oracle\noracle._LIB = os.environ['ORACLE_MUTANT_LIB']\n"
 
