@@ -29,6 +29,13 @@
  *     gives zero output and -inf LSE, split-KV partials are merged in FP32
  *     without recomputing QK or PV, and wrappers check shapes and layout
  *     without reading device contents.
+ *   - TileOPs "Attention Operators", GQAVarlenFwdOp and GQAPagedFwdOp: packed
+ *     THD tensors [total, heads, dim] with requests delimited by cumulative
+ *     offsets, the causal mask bottom-right aligned per request, offsets not
+ *     checked unless asked, and optional float32 sinks (one logit per query
+ *     head in the softmax denominator only; not scaled or capped; -inf
+ *     disables a sink, +inf zeroes the head's output; a row with no visible
+ *     key returns zero whatever its sink).
  *
  * Conventions for every entry point:
  *   - Pointers marked "device" are HIP device pointers; the caller allocates and
@@ -139,6 +146,68 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
                              float softcap, void *o, float *lse, int B, int Sq,
                              int Hq, int Hkv, int D, int max_pages, int num_phys_pages,
                              float scale, miattn_dtype dtype, void *stream);
+
+/*
+ * Packed (THD) attention forward: requests of different lengths in one call.
+ *
+ *   q    device, [total_q, Hq, D] dtype; request b holds rows
+ *        cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1
+ *   k, v device, [total_kv, Hkv, D] dtype; request b holds rows
+ *        cu_seqlens_kv[b] .. cu_seqlens_kv[b+1] - 1 (k, v may be NULL when
+ *        total_kv == 0)
+ *   cu_seqlens_q, cu_seqlens_kv  device, int32 [B + 1]: 0, nondecreasing,
+ *        ending at total_q / total_kv.  Not read by the host (checked only
+ *        under MIATTN_VALIDATE=1); the kernels clamp offsets into [0, total]
+ *        and lengths into [0, max_seqlen], so malformed offsets give wrong
+ *        results but no access outside the tensors
+ *   max_seqlen_q, max_seqlen_kv  the most queries / keys one request holds
+ *        (they size the launch)
+ *   causal, window_left, window_right, softcap, scale  as for attn_fwd_dense,
+ *        with p_i = i + Skv_b - Sq_b inside request b
+ *   sinks device, float32 [Hq] sink logits, or NULL: the head's sink enters
+ *        the softmax denominator only, used as given; a +inf sink gives o = 0
+ *        and lse = +inf; a row with no visible key gets o = 0 and lse = its
+ *        sink (-inf without one)
+ *   o    device, [total_q, Hq, D] dtype, written in full
+ *   lse  device, [Hq, total_q] float32 (the log of the whole denominator,
+ *        sink included), or NULL
+ *   B, Hq, Hkv, D, dtype, stream  as for attn_fwd_dense
+ *
+ * B == 0, total_q == 0 or max_seqlen_q == 0 returns MIATTN_OK without
+ * enqueuing anything.
+ */
+miattn_status attn_fwd_varlen(const void *q, const void *k, const void *v,
+                              const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_kv, int B,
+                              int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv,
+                              int Hq, int Hkv, int D, float scale, int causal, int window_left,
+                              int window_right, float softcap, const float *sinks, void *o,
+                              float *lse, miattn_dtype dtype, void *stream);
+
+/*
+ * Paged attention forward over packed queries (requests with different query
+ * counts, prefill and decode mixed).
+ *
+ *   q        device, [total_q, Hq, D] dtype, delimited by cu_seqlens_q as for
+ *            attn_fwd_varlen
+ *   k_cache, v_cache, block_table, page_size, max_pages, num_phys_pages  as
+ *            for attn_fwd_paged
+ *   cache_seqlens device, int32 [B]: keys of request b, its Sq_b query tokens
+ *            included (they sit at the end); a request with no query is
+ *            skipped
+ *   max_seqlen_q  the most queries one request holds
+ *   causal, window_left, window_right, softcap, sinks, scale  as for
+ *            attn_fwd_varlen, with p_i = i + cache_seqlens[b] - Sq_b
+ *   o, lse   [total_q, Hq, D] and [Hq, total_q], as for attn_fwd_varlen
+ *   B, Hq, Hkv, D, dtype, stream  as for attn_fwd_paged
+ */
+miattn_status attn_fwd_paged_varlen(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *cache_seqlens, const int32_t *block_table,
+                                    const int32_t *cu_seqlens_q, int page_size, int causal,
+                                    int window_left, int window_right, float softcap,
+                                    const float *sinks, void *o, float *lse, int B,
+                                    int total_q, int max_seqlen_q, int Hq, int Hkv, int D,
+                                    int max_pages, int num_phys_pages, float scale,
+                                    miattn_dtype dtype, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *miattn_last_error(void);

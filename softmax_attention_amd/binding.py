@@ -20,8 +20,9 @@ MIATTN_OK, MIATTN_ERR_INVALID_ARG, MIATTN_ERR_UNSUPPORTED, MIATTN_ERR_HIP = 0, 1
 MIATTN_BF16, MIATTN_FP16 = 0, 1
 
 # every symbol include/miattn.h declares
-EXPORTS = ("attn_fwd_dense", "attn_fwd_paged", "miattn_last_error", "miattn_release_workspace",
-           "miattn_set_split_keys", "miattn_profile_start", "miattn_profile_stop")
+EXPORTS = ("attn_fwd_dense", "attn_fwd_paged", "attn_fwd_varlen", "attn_fwd_paged_varlen",
+           "miattn_last_error", "miattn_release_workspace", "miattn_set_split_keys",
+           "miattn_profile_start", "miattn_profile_stop")
 
 _lib = None
 
@@ -46,6 +47,12 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_paged.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f32, P, P, i32, i32,
                                      i32, i32, i32, i32, i32, f32, i32, P]
         L.attn_fwd_paged.restype = i32
+        L.attn_fwd_varlen.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                      i32, i32, i32, f32, P, P, P, i32, P]
+        L.attn_fwd_varlen.restype = i32
+        L.attn_fwd_paged_varlen.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, P, P, P,
+                                            i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, P]
+        L.attn_fwd_paged_varlen.restype = i32
         L.miattn_last_error.argtypes = []
         L.miattn_last_error.restype = ctypes.c_char_p
         L.miattn_release_workspace.argtypes = []
@@ -196,6 +203,135 @@ def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                               *_window(window), _softcap(softcap), _ptr(o),
                               _ptr(lse) if return_lse else None, B, Sq, Hq, Hkv, D,
                               block_table.shape[1], n_pages, _scale(scale), code, _stream())
+    _check(st)
+    return o, (lse if return_lse else None)
+
+
+def _offsets(cu: torch.Tensor, device, name: str) -> torch.Tensor:
+    if cu.dtype != torch.int32 or cu.dim() != 1 or cu.numel() < 1:
+        raise ValueError(f"{name} must be a 1-D int32 tensor [B + 1]")
+    if not (cu.is_cuda and cu.device == device):
+        raise ValueError(f"{name} must be on the queries' GPU device")
+    return cu.contiguous()
+
+
+def _max_len(cu: torch.Tensor) -> int:
+    # one device -> host read when the caller does not pass the maximum
+    return int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+
+
+def _sinks_arg(sinks, Hq: int, device):
+    if sinks is None:
+        return None
+    if sinks.dtype != torch.float32 or tuple(sinks.shape) != (Hq,):
+        raise ValueError(f"sinks must be float32 [Hq] = [{Hq}]")
+    if not (sinks.is_cuda and sinks.device == device):
+        raise ValueError("sinks must be on the queries' GPU device")
+    return sinks.contiguous()
+
+
+def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    cu_seqlens_q: torch.Tensor, cu_seqlens_kv: torch.Tensor, *,
+                    max_seqlen_q: Optional[int] = None, max_seqlen_kv: Optional[int] = None,
+                    scale=None, causal: bool = True, window=None, softcap=None,
+                    sinks: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, return_lse: bool = True
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Packed (THD) attention forward on the current stream.
+
+    q [total_q,Hq,D], k/v [total_kv,Hkv,D]; cu_seqlens_q/kv int32 [B+1];
+    sinks float32 [Hq] or None.  Returns (o [total_q,Hq,D], lse [Hq,total_q]).
+    Without max_seqlen_q/kv the maxima are read from the offsets (a sync)."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be rank 3 (THD)")
+    if k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} "
+                         f"v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    code = _dtype_code(q)
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one GPU device")
+    cq = _offsets(cu_seqlens_q, q.device, "cu_seqlens_q")
+    ck = _offsets(cu_seqlens_kv, q.device, "cu_seqlens_kv")
+    if cq.numel() != ck.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv must both be [B + 1]")
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    total_q, Hq, D = q.shape
+    total_kv, Hkv = k.shape[0], k.shape[1]
+    B = cq.numel() - 1
+    mq = _max_len(cq) if max_seqlen_q is None else int(max_seqlen_q)
+    mk = _max_len(ck) if max_seqlen_kv is None else int(max_seqlen_kv)
+    sk = _sinks_arg(sinks, Hq, q.device)
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cq), _ptr(ck), B, total_q,
+                               total_kv, mq, mk, Hq, Hkv, D, _scale(scale), int(bool(causal)),
+                               *_window(window), _softcap(softcap), _ptr(sk), _ptr(o),
+                               _ptr(lse) if return_lse else None, code, _stream())
+    _check(st)
+    return o, (lse if return_lse else None)
+
+
+def attn_fwd_paged_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          cache_seqlens: torch.Tensor, block_table: torch.Tensor,
+                          cu_seqlens_q: torch.Tensor, page_size: int, *,
+                          max_seqlen_q: Optional[int] = None, causal: bool = True, scale=None,
+                          window=None, softcap=None, sinks: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          return_lse: bool = True
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Paged attention over packed queries on the current stream.
+
+    q [total_q,Hq,D] delimited by cu_seqlens_q int32 [B+1]; caches, block_table
+    and page_size as for attn_fwd_paged; cache_seqlens int32 [B] (each
+    request's keys, its queries included).  Returns (o [total_q,Hq,D],
+    lse [Hq,total_q])."""
+    if q.dim() != 3:
+        raise ValueError("q must be rank 3 (THD)")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have one shape")
+    if k_cache.dim() == 4:
+        if k_cache.shape[1] != page_size:
+            raise ValueError("rank-4 caches must be [pages, page_size, Hkv, D]")
+        n_pages = k_cache.shape[0]
+    elif k_cache.dim() == 3:
+        if k_cache.shape[0] % page_size != 0:
+            raise ValueError("flat cache rows must be a multiple of page_size")
+        n_pages = k_cache.shape[0] // page_size
+    else:
+        raise ValueError("caches must be rank 3 or 4")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share one dtype")
+    if cache_seqlens.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise ValueError("cache_seqlens and block_table must be int32")
+    code = _dtype_code(q)
+    if not all(t.is_cuda and t.device == q.device
+               for t in (q, k_cache, v_cache, cache_seqlens, block_table)):
+        raise ValueError("q, the caches, cache_seqlens and block_table must be on one GPU device")
+    cq = _offsets(cu_seqlens_q, q.device, "cu_seqlens_q")
+    total_q, Hq, D = q.shape
+    Hkv = k_cache.shape[-2]
+    B = cq.numel() - 1
+    if k_cache.shape[-1] != D:
+        raise ValueError("head dim of the caches differs from q")
+    if block_table.dim() != 2 or block_table.shape[0] != B or cache_seqlens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and cache_seqlens [B]")
+    mq = _max_len(cq) if max_seqlen_q is None else int(max_seqlen_q)
+    sk = _sinks_arg(sinks, Hq, q.device)
+    q = q.contiguous()
+    k_cache, v_cache = k_cache.contiguous(), v_cache.contiguous()
+    cache_seqlens, block_table = cache_seqlens.contiguous(), block_table.contiguous()
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd_paged_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+                                     _ptr(block_table), _ptr(cq), int(page_size),
+                                     int(bool(causal)), *_window(window), _softcap(softcap),
+                                     _ptr(sk), _ptr(o), _ptr(lse) if return_lse else None, B,
+                                     total_q, mq, Hq, Hkv, D, block_table.shape[1], n_pages,
+                                     _scale(scale), code, _stream())
     _check(st)
     return o, (lse if return_lse else None)
 

@@ -17,6 +17,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <bool BF16>
 struct Half;
@@ -122,26 +123,56 @@ __device__ __forceinline__ float sum_halves(float x) {
 // b holds ceil(len_b / bn) key tiles, len_b = seqlen[b] clamped into
 // [0, cap] (skv for every entry when seqlen is null); the (batch, KV head)
 // sequences, heads fastest, form one sequence of Hkv * (sum of tiles) tiles.
+// Request extents, clamped so that malformed offsets or lengths cannot
+// address rows outside the tensors: packed offsets into [0, total], lengths
+// into [0, the per-request maximum], paged lengths into [0, cap].
+__device__ __forceinline__ void q_span(const SeqDesc &s, int b, int64_t &row0, int &len) {
+    if (!s.cu_q) {
+        row0 = (int64_t)b * s.sq;
+        len = s.sq;
+        return;
+    }
+    const int a = min(max(s.cu_q[b], 0), s.total_q);
+    const int e = min(max(s.cu_q[b + 1], a), s.total_q);
+    row0 = a;
+    len = min(e - a, s.sq);
+}
+
+__device__ __forceinline__ int seq_kv_len(const SeqDesc &s, int b) {
+    if (s.seqlen) return min(max(s.seqlen[b], 0), s.cap);
+    if (!s.cu_kv) return s.skv;
+    const int a = min(max(s.cu_kv[b], 0), s.total_kv);
+    const int e = min(max(s.cu_kv[b + 1], a), s.total_kv);
+    return min(e - a, s.skv);
+}
+
+// first key row of request b in a dense (possibly packed) K/V tensor
+__device__ __forceinline__ int64_t seq_kv_row0(const SeqDesc &s, int b) {
+    return s.cu_kv ? (int64_t)min(max(s.cu_kv[b], 0), s.total_kv) : (int64_t)b * s.skv;
+}
+
+// Stream-K plan over the key tiles of all requests.
 struct SkBatch {
-    const int32_t *seqlen;
-    int skv, B, bn, cap;
-    int sq, win_left;  // queries per request; left window bound (-1: none)
+    SeqDesc sd;
+    int bn;        // keys per tile
+    int win_left;  // left window bound (-1: none)
 };
 
-// keys of entry b (a paged length clamped into [0, cap])
-__device__ __forceinline__ int sk_len(const SkBatch &s, int b) {
-    return s.seqlen ? min(max(s.seqlen[b], 0), s.cap) : s.skv;
+// first key tile any query of request b (sq_b queries, len keys) can see:
+// with a left window the first query (at position len - sq_b) sees keys from
+// len - sq_b - w_L on
+__device__ __forceinline__ int sk_first_tile(const SkBatch &s, int len, int sq_b) {
+    return s.win_left < 0 ? 0 : max(0, len - sq_b - s.win_left) / s.bn;
 }
 
-// first key tile any query of an entry of length len can see: with a left
-// window the first query (at position len - sq) sees keys from len - sq - w_L
-__device__ __forceinline__ int sk_first_tile(const SkBatch &s, int len) {
-    return s.win_left < 0 ? 0 : max(0, len - s.sq - s.win_left) / s.bn;
-}
-
+// key tiles of request b (none when it has no query)
 __device__ __forceinline__ int sk_tiles(const SkBatch &s, int b) {
-    const int len = sk_len(s, b);
-    return (len + s.bn - 1) / s.bn - sk_first_tile(s, len);
+    int64_t row0;
+    int sq_b;
+    q_span(s.sd, b, row0, sq_b);
+    if (sq_b == 0) return 0;
+    const int len = seq_kv_len(s.sd, b);
+    return (len + s.bn - 1) / s.bn - sk_first_tile(s, len, sq_b);
 }
 
 // inclusive prefix sum over the 64 lanes of a wave
@@ -159,9 +190,9 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 __device__ __forceinline__ int sk_sums(const SkBatch &s, int upto, int &before) {
     const int lane = threadIdx.x & 63;
     int total = 0, pre = 0;
-    for (int c = 0; c < s.B; c += 64) {
+    for (int c = 0; c < s.sd.B; c += 64) {
         const int b = c + lane;
-        const int t = b < s.B ? sk_tiles(s, b) : 0;
+        const int t = b < s.sd.B ? sk_tiles(s, b) : 0;
         const int incl = wave_incl_scan(t);
         const int incl_before = wave_incl_scan(b < upto ? t : 0);
         total += __shfl(incl, 63);
@@ -178,12 +209,12 @@ __device__ __forceinline__ void sk_find(const SkBatch &s, int hkv, int64_t at, i
                                         int &pre_out, int &t_out) {
     const int lane = threadIdx.x & 63;
     int carry = 0;
-    for (int c = 0; c < s.B; c += 64) {
+    for (int c = 0; c < s.sd.B; c += 64) {
         const int b = c + lane;
-        const int t = b < s.B ? sk_tiles(s, b) : 0;
+        const int t = b < s.sd.B ? sk_tiles(s, b) : 0;
         const int incl = carry + wave_incl_scan(t);
         const int excl = incl - t;
-        const bool hit = b < s.B && (int64_t)hkv * excl <= at && at < (int64_t)hkv * incl;
+        const bool hit = b < s.sd.B && (int64_t)hkv * excl <= at && at < (int64_t)hkv * incl;
         const uint64_t m = __ballot(hit);
         if (m) {
             const int src = __builtin_ctzll(m);
@@ -194,7 +225,7 @@ __device__ __forceinline__ void sk_find(const SkBatch &s, int hkv, int64_t at, i
         }
         carry = __shfl(incl, 63);
     }
-    b_out = s.B;
+    b_out = s.sd.B;
     pre_out = carry;
     t_out = 0;
 }

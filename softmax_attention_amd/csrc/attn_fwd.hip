@@ -132,13 +132,25 @@ void attn_fwd_kernel(const FwdParams p) {
     const int l32 = lane & 31;
     const int hl = lane >> 5;
 
+    // request extents: uniform blocks, packed (THD) offsets or paged lengths,
+    // clamped so that malformed ones stay inside the tensors
+    const SeqDesc sd = {PAGED ? p.seqlen : nullptr, p.cu_q, PAGED ? nullptr : p.cu_kv, p.B,
+                        p.Sq, p.Skv, p.total_q, p.total_kv,
+                        (PAGED && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0};
+
     // ---- one unit of work: the key range [kbeg, kend) of row block `mblock`
     // of (batch b, KV head kvh), whose length is kv_len; a split result goes
     // to partial slot `slot`, a whole result straight to o and lse.
     auto run = [&](const int mblock, const int b, const int kvh, const int kv_len,
                    const int kbeg, const int kend, const int64_t slot,
                    const bool partial) __attribute__((always_inline)) {
-    const int delta = kv_len - p.Sq;  // query i sits at key position p_i = i + delta
+    // this request's queries: packed rows q_row0 .. q_row0 + sq_b - 1
+    int64_t q_row0;
+    int sq_b;
+    q_span(sd, b, q_row0, sq_b);
+    const int rows_b = sq_b * p.G;  // its packed rows
+    if (mblock * BM >= rows_b) return;  // a shorter request: no rows in this block
+    const int delta = kv_len - sq_b;  // query i sits at key position p_i = i + delta
 
     // Keys query i may see before the padding mask (TileOPs "Attention
     // Operators", GQADenseFwdOp stage 5): [key_lo(i), key_hi(i)], both
@@ -154,7 +166,7 @@ void attn_fwd_kernel(const FwdParams p) {
     };
 
     const int row0 = mblock * BM;
-    const int row_last = min(p.rows, row0 + BM) - 1;
+    const int row_last = min(rows_b, row0 + BM) - 1;
     const int wg_end = min(kend, key_hi(row_last / p.G) + 1);
     // the first tile (on the kbeg + n BN grid) that holds a key this
     // workgroup's rows may see
@@ -162,8 +174,8 @@ void attn_fwd_kernel(const FwdParams p) {
     const int tile_begin = wg_begin >= wg_end ? wg_end : kbeg + (wg_begin - kbeg) / BN * BN;
 
     const int wrow0 = row0 + (SPLIT_ROLES ? 0 : wave * kRowsPerWave);
-    const bool wave_active = (!SPLIT_ROLES || wave == 0) && wrow0 < p.rows;
-    const int wrow_last = min(p.rows, wrow0 + kRowsPerWave) - 1;
+    const bool wave_active = (!SPLIT_ROLES || wave == 0) && wrow0 < rows_b;
+    const int wrow_last = min(rows_b, wrow0 + kRowsPerWave) - 1;
     // keys in [wave_full_begin, wave_full_end) are visible to every row of
     // this wave (mask aside); keys outside [wave_begin, wave_end) to none
     const int wave_end = !wave_active ? kbeg : min(kend, key_hi(wrow_last / p.G) + 1);
@@ -180,7 +192,7 @@ void attn_fwd_kernel(const FwdParams p) {
 
     // ---- this lane's query row (the column it holds in every MFMA tile)
     const int my_row = wrow0 + l32;
-    const bool row_ok = my_row < p.rows;
+    const bool row_ok = my_row < rows_b;
     const int my_i = my_row / p.G;
     const int my_gh = my_row - my_i * p.G;
     const int my_last = !row_ok ? -1 : key_hi(my_i);
@@ -195,7 +207,7 @@ void attn_fwd_kernel(const FwdParams p) {
         const uint32_t flip = p.q_mode == 1 ? 0x80008000u : 0u;
         const bool load_q = row_ok && p.q_mode != 2;
         const uint16_t *qrow =
-            p.q + (((int64_t)b * p.Sq + my_i) * p.Hq + (int64_t)kvh * p.G + my_gh) * D;
+            p.q + ((q_row0 + my_i) * p.Hq + (int64_t)kvh * p.G + my_gh) * D;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4 raw = {0u, 0u, 0u, 0u};
@@ -259,7 +271,7 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int e = 0; e < PPW; ++e)
         l_chunk[e] = 16 * (l_pos ^ swz<D>((e * LOADERS + loader) * RPP + l_dr));
-    const int64_t head_off = (int64_t)kvh * D + (PAGED ? 0 : (int64_t)b * p.Skv * hstride);
+    const int64_t head_off = (int64_t)kvh * D + (PAGED ? 0 : seq_kv_row0(sd, b) * hstride);
     typedef __attribute__((address_space(4))) const int32_t const_i32;
     const_i32 *bt_row =
         PAGED ? (const_i32 *)(p.block_table + (int64_t)b * p.max_pages) : nullptr;
@@ -716,12 +728,31 @@ void attn_fwd_kernel(const FwdParams p) {
     if (!wave_active) return;
     const float l_tot = sum_halves(l_run);
     if (!row_ok) return;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse_v = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float lse_v = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    const int my_h = kvh * p.G + my_gh;
+    if (!partial && p.sinks != nullptr) {
+        // The head's sink logit joins the denominator only, used as given
+        // (TileOPs "Attention Operators", GQAVarlenFwdOp / GQAPagedFwdOp): a
+        // row without visible keys stays zero with lse = sink, and a +inf
+        // sink takes all the weight.  (A split result gets its sink in the
+        // merge.)
+        const float sk = p.sinks[my_h];
+        if (l_tot == 0.f || sk == INFINITY) {
+            inv = 0.f;
+            lse_v = l_tot == 0.f ? sk : INFINITY;
+        } else {
+            const float s2 = sk * kLog2e;
+            const float mx = fmaxf(m_run, s2);
+            const float a = fast_exp2(m_run - mx);
+            const float den = __builtin_fmaf(l_tot, a, fast_exp2(s2 - mx));
+            inv = a / den;
+            lse_v = (mx + __builtin_amdgcn_logf(den)) * kLn2;
+        }
+    }
 
     if (!partial) {
-        uint16_t *orow =
-            p.o + (((int64_t)b * p.Sq + my_i) * p.Hq + (int64_t)kvh * p.G + my_gh) * D;
+        uint16_t *orow = p.o + ((q_row0 + my_i) * p.Hq + my_h) * D;
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -733,8 +764,12 @@ void attn_fwd_kernel(const FwdParams p) {
                                                        acc[t][4 * w + 3] * inv)};
                 *(u32x2 *)(orow + d0) = packed;
             }
-        if (p.lse != nullptr && hl == 0)
-            p.lse[((int64_t)b * p.Hq + (int64_t)kvh * p.G + my_gh) * p.Sq + my_i] = lse_v;
+        if (p.lse != nullptr && hl == 0) {
+            if (p.cu_q)  // packed: [Hq, total_q]
+                p.lse[(int64_t)my_h * p.total_q + q_row0 + my_i] = lse_v;
+            else         // [B, Hq, Sq]
+                p.lse[((int64_t)b * p.Hq + my_h) * p.Sq + my_i] = lse_v;
+        }
     } else {
         const int64_t part = slot * p.rows + my_row;
         float *op = p.o_part + part * D;
@@ -762,9 +797,7 @@ void attn_fwd_kernel(const FwdParams p) {
             // lengths -- and writes one partial per unit it touches, to slot
             // unit + g (the merge kernel finds the slots the same way).
             const int g = blockIdx.x;
-            const SkBatch sb = {PAGED ? p.seqlen : nullptr, p.Skv, p.B, BN,
-                                (PAGED && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0,
-                                p.Sq, p.win_left};
+            const SkBatch sb = {sd, BN, p.win_left};
             int unused;
             const int64_t T = (int64_t)p.Hkv * sk_sums(sb, 0, unused);
             const int64_t s0 = (int64_t)g * T / p.sk_grid;
@@ -779,9 +812,12 @@ void attn_fwd_kernel(const FwdParams p) {
                 const int b = u / p.Hkv;
                 const int kvh = u - b * p.Hkv;
                 // (the unit's tiles start at the first one its window reaches)
-                const int len = sk_len(sb, b);
-                const int t_first = sk_first_tile(sb, len);
-                const int tiles = (len + BN - 1) / BN - t_first;
+                const int len = seq_kv_len(sd, b);
+                int64_t unused_row0;
+                int sq_u;
+                q_span(sd, b, unused_row0, sq_u);
+                const int t_first = sk_first_tile(sb, len, sq_u);
+                const int tiles = sk_tiles(sb, b);
                 const int n = (int)min((int64_t)(tiles - off), s1 - at);
                 if (n <= 0) continue;
                 run(0, b, kvh, len, (t_first + off) * BN, min(len, (t_first + off + n) * BN),
@@ -829,9 +865,7 @@ void attn_fwd_kernel(const FwdParams p) {
     // (a paged length is clamped to the table's capacity, and an empty cache
     // holds no keys, so that malformed lengths cannot address memory
     // outside the table or the cache)
-    const int kv_len =
-        !PAGED ? p.Skv
-               : (p.num_pages > 0 ? min(max(p.seqlen[b], 0), p.max_pages << p.page_shift) : 0);
+    const int kv_len = seq_kv_len(sd, b);
     const int kbeg = split * p.split_len;
     // Splits past the end are never read by the merge, which counts the
     // splits that hold keys from the same length.

@@ -36,6 +36,20 @@ constexpr int keys_per_tile(int D, int waves) {
     return waves == 8 ? 64 : (4096 / D > 32 ? 4096 / D : 32);
 }
 
+// Per-request extents of a call, as the attention kernel, its stream-K plan
+// and the merge kernel all read them (device helpers in attn_device.h clamp
+// them identically).
+struct SeqDesc {
+    const int32_t *seqlen;  // paged: keys of request b, its queries included; else nullptr
+    const int32_t *cu_q;    // packed queries: request b holds rows cu_q[b] .. cu_q[b+1]-1
+    const int32_t *cu_kv;   // packed dense keys, likewise; nullptr: B blocks of skv keys
+    int B;
+    int sq;                 // queries per request (packed: the most one may hold)
+    int skv;                // dense keys per request (packed: the most one may hold)
+    int total_q, total_kv;  // packed row counts
+    int cap;                // paged: max_pages * page_size (0 for an empty cache)
+};
+
 struct FwdParams {
     const uint16_t *q;   // [B, Sq, Hq, D]
     const uint16_t *k;   // dense [B, Skv, Hkv, D] or paged cache [rows, Hkv, D]
@@ -47,7 +61,11 @@ struct FwdParams {
     const uint8_t *mask; // dense key padding [B, Skv] or nullptr
     const int32_t *seqlen;      // paged: [B]
     const int32_t *block_table; // paged: [B, max_pages]
-    int B, Sq, Hq, Hkv, G, Skv;
+    const int32_t *cu_q;        // packed (THD) queries: offsets [B + 1], or nullptr
+    const int32_t *cu_kv;       // packed dense keys: offsets [B + 1], or nullptr
+    const float *sinks;         // [Hq] sink logits, or nullptr
+    int total_q, total_kv;      // packed row counts (lse of a packed call is [Hq, total_q])
+    int B, Sq, Hq, Hkv, G, Skv; // packed calls: Sq and Skv are the per-request maxima
     int page_shift, max_pages, num_pages;  // paged: log2(page size), table width, cache pages
     int rows;        // Sq * G packed rows per (batch, KV head)
     int n_mblocks;   // ceil(rows / rows_per_workgroup(waves))
@@ -76,6 +94,9 @@ struct MergeParams {
     uint16_t *o;
     float *lse;
     const int32_t *seqlen;  // paged lengths, or nullptr for dense
+    const int32_t *cu_q, *cu_kv;
+    const float *sinks;
+    int total_q, total_kv;
     int Skv;
     int B, Sq, Hq, Hkv, G, rows, n_splits, split_len;
     // stream-K decode: grid size (0 otherwise), keys per tile and the length

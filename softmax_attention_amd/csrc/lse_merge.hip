@@ -9,6 +9,8 @@
 // "QSA", Core Attention).  A row whose every split is empty gets o = 0 and
 // lse = -inf (TileOPs "Attention Operators", MHADecodePagedWithKVCacheFwdOp:
 // a query that sees no key outputs zeros; MATE "QSA": empty -> -inf LSE).
+// A head's sink logit, when given, joins the merged denominator once
+// (GQAVarlenFwdOp / GQAPagedFwdOp: denominator only, used as given).
 //
 // One wave per packed row; lane l owns D/64 consecutive output elements.
 #include "attn_kernels.h"
@@ -42,6 +44,13 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     const int kvh = bh - b * p.Hkv;
     const int i = r / p.G;
     const int gh = r - i * p.G;
+    // the same request extents as the attention kernel
+    const SeqDesc sd = {p.seqlen, p.cu_q, p.cu_kv, p.B, p.Sq, p.Skv, p.total_q, p.total_kv,
+                        p.sk_cap};
+    int64_t q_row0;
+    int sq_b;
+    q_span(sd, b, q_row0, sq_b);
+    if (r >= sq_b * p.G) return;  // a shorter request: no such row
 
     // The partial results of this (batch, KV head): n_valid slots, `stride`
     // rows apart, from row `base` on.
@@ -52,7 +61,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     if (p.sk_grid > 0) {
         // Stream-K: the workgroups that touched this unit's tiles, [P, P +
         // tiles) of the T-tile sequence; workgroup g held [g T / G, (g+1) T / G).
-        const SkBatch sb = {p.seqlen, p.Skv, p.B, p.sk_bn, p.sk_cap, p.Sq, p.sk_win_left};
+        const SkBatch sb = {sd, p.sk_bn, p.sk_win_left};
         int before;
         T = (int64_t)p.Hkv * sk_sums(sb, b, before);
         const int tiles = sk_tiles(sb, b);
@@ -69,7 +78,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
         }
         base = ((int64_t)bh + g_first) * p.rows + r;
     } else {
-        const int kv_len = p.seqlen ? p.seqlen[b] : p.Skv;
+        const int kv_len = seq_kv_len(sd, b);
         // the splits that hold keys of this request (the attention kernel
         // writes every row of each of them and nothing for the others)
         n_valid = min(p.n_splits, (kv_len + p.split_len - 1) / p.split_len);
@@ -105,14 +114,31 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
             for (int e = 0; e < PER; ++e) accv[e] += w * src[e];
         }
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    uint16_t *dst = p.o + (((int64_t)b * p.Sq + i) * p.Hq + (int64_t)kvh * p.G + gh) * D +
-                    lane * PER;
+    const int h = kvh * p.G + gh;
+    float inv = den > 0.f ? 1.f / den : 0.f;
+    float lse_out = den > 0.f ? M + __logf(den) : -INFINITY;
+    if (p.sinks != nullptr) {
+        const float sk = p.sinks[h];
+        if (den == 0.f || sk == INFINITY) {
+            inv = 0.f;
+            lse_out = den == 0.f ? sk : INFINITY;
+        } else {
+            const float mx = fmaxf(M, sk);
+            const float a = __expf(M - mx);
+            const float den2 = __builtin_fmaf(den, a, __expf(sk - mx));
+            inv = a / den2;
+            lse_out = mx + __logf(den2);
+        }
+    }
+    uint16_t *dst = p.o + ((q_row0 + i) * p.Hq + h) * D + lane * PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) dst[e] = to_half_bits<BF16>(accv[e] * inv);
-    if (p.lse != nullptr && lane == 0)
-        p.lse[((int64_t)b * p.Hq + (int64_t)kvh * p.G + gh) * p.Sq + i] =
-            den > 0.f ? M + __logf(den) : -INFINITY;
+    if (p.lse != nullptr && lane == 0) {
+        if (p.cu_q)  // packed: [Hq, total_q]
+            p.lse[(int64_t)h * p.total_q + q_row0 + i] = lse_out;
+        else
+            p.lse[((int64_t)b * p.Hq + h) * p.Sq + i] = lse_out;
+    }
 }
 
 template <int D, bool BF16>

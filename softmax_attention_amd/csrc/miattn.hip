@@ -251,6 +251,34 @@ int env_int(const char *name, int dflt) {
 
 // ---------------------------------------------------------------- plan + launch
 
+// What the merge kernel needs of a call: its extents (as the attention kernel
+// clamps them), the partials' layout and the sinks.
+MergeParams merge_params(const FwdParams &p, bool paged) {
+    MergeParams m = {};
+    m.o_part = p.o_part;
+    m.lse_part = p.lse_part;
+    m.o = p.o;
+    m.lse = p.lse;
+    m.seqlen = paged ? p.seqlen : nullptr;
+    m.cu_q = p.cu_q;
+    m.cu_kv = paged ? nullptr : p.cu_kv;
+    m.sinks = p.sinks;
+    m.total_q = p.total_q;
+    m.total_kv = p.total_kv;
+    m.Skv = p.Skv;
+    m.B = p.B;
+    m.Sq = p.Sq;
+    m.Hq = p.Hq;
+    m.Hkv = p.Hkv;
+    m.G = p.G;
+    m.rows = p.rows;
+    m.n_splits = p.n_splits;
+    m.split_len = p.split_len;
+    m.sk_cap = (paged && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0;
+    m.sk_win_left = -1;
+    return m;
+}
+
 miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, bool cap,
                   hipStream_t stream) {
     int dev = 0;
@@ -305,24 +333,9 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
             return miattn::launch_attn_fwd(p, D, bf16, paged, waves, cap, G, stream);
         });
         if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-        MergeParams m = {};
-        m.o_part = p.o_part;
-        m.lse_part = p.lse_part;
-        m.o = p.o;
-        m.lse = p.lse;
-        m.seqlen = paged ? p.seqlen : nullptr;
-        m.Skv = p.Skv;
-        m.B = p.B;
-        m.Sq = p.Sq;
-        m.Hq = p.Hq;
-        m.Hkv = p.Hkv;
-        m.G = p.G;
-        m.rows = p.rows;
-        m.n_splits = 1;
-        m.split_len = 0;
+        MergeParams m = merge_params(p, paged);
         m.sk_grid = G;
         m.sk_bn = BN;
-        m.sk_cap = (paged && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0;
         m.sk_win_left = p.win_left;
         e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -387,21 +400,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
 
     if (n_splits > 1) {
-        MergeParams m = {};
-        m.o_part = p.o_part;
-        m.lse_part = p.lse_part;
-        m.o = p.o;
-        m.lse = p.lse;
-        m.seqlen = paged ? p.seqlen : nullptr;
-        m.Skv = p.Skv;
-        m.B = p.B;
-        m.Sq = p.Sq;
-        m.Hq = p.Hq;
-        m.Hkv = p.Hkv;
-        m.G = p.G;
-        m.rows = p.rows;
-        m.n_splits = p.n_splits;
-        m.split_len = p.split_len;
+        MergeParams m = merge_params(p, paged);
         e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     }
@@ -414,28 +413,76 @@ extern "C" {
 
 const char *miattn_last_error(void) { return g_err; }
 
-miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B, int Hq,
-                             int Hkv, int Sq, int Skv, int D, float scale, int causal,
-                             int window_left, int window_right, float softcap,
-                             const uint8_t *key_padding_mask, void *o, float *lse,
-                             miattn_dtype dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Packed offsets (MIATTN_VALIDATE=1 only; synchronises the stream): cu[0] = 0,
+// nondecreasing, cu[B] = total, and no request longer than max_len.
+miattn_status validate_offsets(const int32_t *cu, int B, int total, int max_len,
+                               const char *name, hipStream_t s) {
+    std::vector<int32_t> h((size_t)B + 1);
+    hipError_t e = hipMemcpyAsync(h.data(), cu, sizeof(int32_t) * h.size(),
+                                  hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "MIATTN_VALIDATE offsets copy");
+    if (h[0] != 0 || h[B] != total)
+        return fail(MIATTN_ERR_INVALID_ARG, "%s must start at 0 and end at %d (got %d .. %d)",
+                    name, total, h[0], h[B]);
+    for (int b = 0; b < B; ++b)
+        if (h[b + 1] < h[b] || h[b + 1] - h[b] > max_len)
+            return fail(MIATTN_ERR_INVALID_ARG,
+                        "%s[%d..%d] = %d..%d: a request must hold 0..%d rows", name, b, b + 1,
+                        h[b], h[b + 1], max_len);
+    return MIATTN_OK;
+}
+
+// The dense call, uniform (cu_q == NULL: B blocks of Sq queries and Skv keys)
+// or packed (THD: Sq and Skv are the per-request maxima, cu_q / cu_kv the
+// request offsets, lse [Hq, total_q]).
+miattn_status dense_call(const void *q, const void *k, const void *v, int B, int Hq, int Hkv,
+                         int Sq, int Skv, int D, float scale, int causal, int window_left,
+                         int window_right, float softcap, const uint8_t *key_padding_mask,
+                         bool packed, const int32_t *cu_q, const int32_t *cu_kv, int total_q,
+                         int total_kv, const float *sinks, void *o, float *lse,
+                         miattn_dtype dtype, void *stream) {
     g_err[0] = '\0';
-    miattn_status st = check_common(q, o, lse, B, Sq, Hq, Hkv, D, scale, dtype);
+    // (a packed call without query rows has nothing to check q and o against)
+    miattn_status st = check_common(q, o, lse, B, (packed && total_q == 0) ? 0 : Sq, Hq, Hkv,
+                                    D, scale, dtype);
     if (st != MIATTN_OK) return st;
     st = check_window_softcap(window_left, window_right, softcap);
     if (st != MIATTN_OK) return st;
     if (Skv < 0) return fail(MIATTN_ERR_INVALID_ARG, "negative dimension: Skv=%d", Skv);
     if (causal != 0 && causal != 1)
         return fail(MIATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
-    if (B == 0 || Sq == 0) return MIATTN_OK;
-    if (Skv > 0) {
+    if (packed && (total_q < 0 || total_kv < 0))
+        return fail(MIATTN_ERR_INVALID_ARG, "total_q=%d, total_kv=%d must be >= 0", total_q,
+                    total_kv);
+    if (sinks && ((uintptr_t)sinks & 3u))
+        return fail(MIATTN_ERR_INVALID_ARG, "sinks not 4-byte aligned");
+    if (B == 0 || Sq == 0 || (packed && total_q == 0)) return MIATTN_OK;
+    if (packed) {
+        if (!cu_q || !cu_kv)
+            return fail(MIATTN_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_kv must not be NULL");
+        if (((uintptr_t)cu_q & 3u) || ((uintptr_t)cu_kv & 3u))
+            return fail(MIATTN_ERR_INVALID_ARG, "cu_seqlens_q/cu_seqlens_kv not 4-byte aligned");
+    }
+    const int64_t kv_rows = packed ? (int64_t)total_kv : (int64_t)B * Skv;
+    if (kv_rows > 0 && Skv > 0) {
         if (!k || !v) return fail(MIATTN_ERR_INVALID_ARG, "k and v must not be NULL");
         if (!aligned16(k)) return fail(MIATTN_ERR_INVALID_ARG, "k not 16-byte aligned");
         if (!aligned16(v)) return fail(MIATTN_ERR_INVALID_ARG, "v not 16-byte aligned");
     }
-    if ((int64_t)B * Skv > INT_MAX)
+    if (kv_rows > INT_MAX)
         return fail(MIATTN_ERR_UNSUPPORTED, "B*Skv = %lld exceeds %d key rows",
-                    (long long)B * Skv, INT_MAX);
+                    (long long)kv_rows, INT_MAX);
+    if (packed && env_int("MIATTN_VALIDATE", 0) == 1) {
+        st = validate_offsets(cu_q, B, total_q, Sq, "cu_seqlens_q", (hipStream_t)stream);
+        if (st == MIATTN_OK)
+            st = validate_offsets(cu_kv, B, total_kv, Skv, "cu_seqlens_kv", (hipStream_t)stream);
+        if (st != MIATTN_OK) return st;
+    }
 
     FwdParams p = {};
     p.q = (const uint16_t *)q;
@@ -444,6 +491,11 @@ miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B,
     p.o = (uint16_t *)o;
     p.lse = lse;
     p.mask = key_padding_mask;
+    p.cu_q = cu_q;
+    p.cu_kv = packed ? cu_kv : nullptr;
+    p.total_q = total_q;
+    p.total_kv = total_kv;
+    p.sinks = sinks;
     p.B = B;
     p.Sq = Sq;
     p.Hq = Hq;
@@ -457,14 +509,19 @@ miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B,
     return run(p, D, dtype == MIATTN_BF16, false, Skv, softcap > 0.f, (hipStream_t)stream);
 }
 
-miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
-                             const int32_t *real_seqlen_kv, const int32_t *block_table,
-                             int page_size, int causal, int window_left, int window_right,
-                             float softcap, void *o, float *lse, int B, int Sq,
-                             int Hq, int Hkv, int D, int max_pages, int num_phys_pages,
-                             float scale, miattn_dtype dtype, void *stream) {
+// The paged call, uniform (cu_q == NULL: B blocks of Sq queries) or with
+// packed queries (Sq the per-request maximum, lse [Hq, total_q]).
+miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache,
+                         const int32_t *real_seqlen_kv, const int32_t *block_table,
+                         int page_size, int causal, int window_left, int window_right,
+                         float softcap, bool packed, const int32_t *cu_q, int total_q,
+                         const float *sinks, void *o, float *lse, int B, int Sq, int Hq, int Hkv,
+                         int D, int max_pages, int num_phys_pages, float scale,
+                         miattn_dtype dtype, void *stream) {
     g_err[0] = '\0';
-    miattn_status st = check_common(q, o, lse, B, Sq, Hq, Hkv, D, scale, dtype);
+    // (a packed call without query rows has nothing to check q and o against)
+    miattn_status st = check_common(q, o, lse, B, (packed && total_q == 0) ? 0 : Sq, Hq, Hkv,
+                                    D, scale, dtype);
     if (st != MIATTN_OK) return st;
     st = check_window_softcap(window_left, window_right, softcap);
     if (st != MIATTN_OK) return st;
@@ -479,11 +536,15 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
         return fail(MIATTN_ERR_INVALID_ARG, "num_phys_pages=%d is negative", num_phys_pages);
     if (causal != 0 && causal != 1)
         return fail(MIATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
+    if (packed && total_q < 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "total_q=%d must be >= 0", total_q);
+    if (sinks && ((uintptr_t)sinks & 3u))
+        return fail(MIATTN_ERR_INVALID_ARG, "sinks not 4-byte aligned");
     const int64_t capacity = (int64_t)max_pages * page_size;
     if (capacity > INT_MAX / 2)
         return fail(MIATTN_ERR_UNSUPPORTED, "max_pages*page_size = %lld exceeds %d keys",
                     (long long)capacity, INT_MAX / 2);
-    if (B == 0 || Sq == 0) return MIATTN_OK;
+    if (B == 0 || Sq == 0 || (packed && total_q == 0)) return MIATTN_OK;
     if (!k_cache || !v_cache || !real_seqlen_kv || !block_table)
         return fail(MIATTN_ERR_INVALID_ARG,
                     "k_cache, v_cache, real_seqlen_kv and block_table must not be NULL");
@@ -491,6 +552,9 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
     if (!aligned16(v_cache)) return fail(MIATTN_ERR_INVALID_ARG, "v_cache not 16-byte aligned");
     if (((uintptr_t)real_seqlen_kv & 3u) || ((uintptr_t)block_table & 3u))
         return fail(MIATTN_ERR_INVALID_ARG, "real_seqlen_kv/block_table not 4-byte aligned");
+    if (packed && !cu_q) return fail(MIATTN_ERR_INVALID_ARG, "cu_seqlens_q must not be NULL");
+    if (packed && ((uintptr_t)cu_q & 3u))
+        return fail(MIATTN_ERR_INVALID_ARG, "cu_seqlens_q not 4-byte aligned");
 
     int page_shift = 0;
     while ((1 << page_shift) < page_size) ++page_shift;
@@ -520,6 +584,10 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
                                 ph, num_phys_pages);
             }
         }
+        if (packed) {
+            st = validate_offsets(cu_q, B, total_q, Sq, "cu_seqlens_q", s);
+            if (st != MIATTN_OK) return st;
+        }
     }
 
     FwdParams p = {};
@@ -530,6 +598,9 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
     p.lse = lse;
     p.seqlen = real_seqlen_kv;
     p.block_table = block_table;
+    p.cu_q = cu_q;
+    p.total_q = total_q;
+    p.sinks = sinks;
     p.B = B;
     p.Sq = Sq;
     p.Hq = Hq;
@@ -543,6 +614,56 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
     st = set_window_softcap(p, window_left, window_right, softcap, capacity, alpha);
     if (st != MIATTN_OK) return st;
     return run(p, D, dtype == MIATTN_BF16, true, capacity, softcap > 0.f, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B, int Hq,
+                             int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                             int window_left, int window_right, float softcap,
+                             const uint8_t *key_padding_mask, void *o, float *lse,
+                             miattn_dtype dtype, void *stream) {
+    return dense_call(q, k, v, B, Hq, Hkv, Sq, Skv, D, scale, causal, window_left,
+                      window_right, softcap, key_padding_mask, false, nullptr, nullptr, 0, 0,
+                      nullptr, o, lse, dtype, stream);
+}
+
+miattn_status attn_fwd_varlen(const void *q, const void *k, const void *v,
+                              const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_kv, int B,
+                              int total_q, int total_kv, int max_seqlen_q, int max_seqlen_kv,
+                              int Hq, int Hkv, int D, float scale, int causal, int window_left,
+                              int window_right, float softcap, const float *sinks, void *o,
+                              float *lse, miattn_dtype dtype, void *stream) {
+    return dense_call(q, k, v, B, Hq, Hkv, max_seqlen_q, max_seqlen_kv, D, scale, causal,
+                      window_left, window_right, softcap, nullptr, true, cu_seqlens_q,
+                      cu_seqlens_kv, total_q, total_kv, sinks, o, lse, dtype, stream);
+}
+
+miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *real_seqlen_kv, const int32_t *block_table,
+                             int page_size, int causal, int window_left, int window_right,
+                             float softcap, void *o, float *lse, int B, int Sq,
+                             int Hq, int Hkv, int D, int max_pages, int num_phys_pages,
+                             float scale, miattn_dtype dtype, void *stream) {
+    return paged_call(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, causal,
+                      window_left, window_right, softcap, false, nullptr, 0, nullptr, o, lse, B,
+                      Sq, Hq, Hkv, D, max_pages, num_phys_pages, scale, dtype, stream);
+}
+
+miattn_status attn_fwd_paged_varlen(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *cache_seqlens, const int32_t *block_table,
+                                    const int32_t *cu_seqlens_q, int page_size, int causal,
+                                    int window_left, int window_right, float softcap,
+                                    const float *sinks, void *o, float *lse, int B,
+                                    int total_q, int max_seqlen_q, int Hq, int Hkv, int D,
+                                    int max_pages, int num_phys_pages, float scale,
+                                    miattn_dtype dtype, void *stream) {
+    return paged_call(q, k_cache, v_cache, cache_seqlens, block_table, page_size, causal,
+                      window_left, window_right, softcap, true, cu_seqlens_q, total_q, sinks, o,
+                      lse, B, max_seqlen_q, Hq, Hkv, D, max_pages, num_phys_pages, scale, dtype,
+                      stream);
 }
 
 miattn_status miattn_release_workspace(void) {

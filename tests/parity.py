@@ -3,7 +3,8 @@
 Floating point: |o - o_ref| <= 1e-2 + 1e-2 |o_ref| for the 16-bit output
 (converted exactly to double) and |lse - lse_ref| <= 2e-3.  Special values
 match exactly: where the oracle's row is empty (lse_ref = -inf) the HIP path
-must return lse = -inf and o = +-0; no NaN anywhere.
+must return lse = -inf and o = +-0, where a +inf sink takes the row (lse_ref =
++inf) lse = +inf and o = +-0; no NaN anywhere.
 """
 from __future__ import annotations
 
@@ -30,6 +31,10 @@ def check_rows(o: np.ndarray, lse: np.ndarray, o_ref: np.ndarray, lse_ref: np.nd
     assert np.array_equal(np.isneginf(lse), empty), \
         f"{what}: -inf LSE pattern differs ({int(np.isneginf(lse).sum())} vs {int(empty.sum())})"
     assert np.all(o[empty] == 0.0), f"{what}: empty rows must output zeros"
+    # a +inf sink takes all the weight: +inf LSE and zero output, exactly
+    full = np.isposinf(lse_ref)
+    assert np.array_equal(np.isposinf(lse), full), f"{what}: +inf LSE pattern differs"
+    assert np.all(o[full] == 0.0), f"{what}: rows with a +inf sink must output zeros"
     err_o = np.abs(o - o_ref)
     bound = O_ATOL + O_RTOL * np.abs(o_ref)
     bad = err_o > bound
@@ -37,7 +42,7 @@ def check_rows(o: np.ndarray, lse: np.ndarray, o_ref: np.ndarray, lse_ref: np.nd
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {int(bad.sum())} o elements out of tolerance; first "
                              f"{idx.tolist()}; max err {float(err_o.max()):.3e}")
-    fin = ~empty
+    fin = np.isfinite(lse_ref)
     err_l = np.abs(lse[fin] - lse_ref[fin])
     if err_l.size and err_l.max() > LSE_ATOL:
         raise AssertionError(f"{what}: lse max err {float(err_l.max()):.3e} > {LSE_ATOL}")

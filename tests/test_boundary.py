@@ -115,6 +115,70 @@ def test_paged_refusals(kw, status, needle):
     assert st == status and needle in msg, (st, msg)
 
 
+def varlen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cq=FAKE, ck=FAKE, B=2, tq=6, tk=9, mq=4, mk=5, Hq=8,
+             Hkv=2, D=128, scale=NAN, causal=1, wl=-1, wr=-1, softcap=0.0, sinks=None, o=FAKE,
+             lse=None, dtype=0, stream=None)
+    a.update(kw)
+    L = mi.lib()
+    st = L.attn_fwd_varlen(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["B"], a["tq"], a["tk"],
+                           a["mq"], a["mk"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"],
+                           a["wl"], a["wr"], a["softcap"], a["sinks"], a["o"], a["lse"],
+                           a["dtype"], a["stream"])
+    return st, L.miattn_last_error().decode()
+
+
+def paged_varlen(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, bt=FAKE, cq=FAKE, page_size=64, causal=1,
+             wl=-1, wr=-1, softcap=0.0, sinks=None, o=FAKE, lse=None, B=2, tq=5, mq=4, Hq=8,
+             Hkv=2, D=128, max_pages=4, n_phys=8, scale=NAN, dtype=0, stream=None)
+    a.update(kw)
+    L = mi.lib()
+    st = L.attn_fwd_paged_varlen(a["q"], a["kc"], a["vc"], a["lens"], a["bt"], a["cq"],
+                                 a["page_size"], a["causal"], a["wl"], a["wr"], a["softcap"],
+                                 a["sinks"], a["o"], a["lse"], a["B"], a["tq"], a["mq"], a["Hq"],
+                                 a["Hkv"], a["D"], a["max_pages"], a["n_phys"], a["scale"],
+                                 a["dtype"], a["stream"])
+    return st, L.miattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(cq=None), 1, "cu_seqlens_q and cu_seqlens_kv must not be NULL"),
+    (dict(ck=None), 1, "must not be NULL"),
+    (dict(cq=FAKE + 2), 1, "4-byte aligned"),
+    (dict(tq=-1), 1, "total_q=-1"),
+    (dict(mk=-1), 1, "Skv=-1"),
+    (dict(sinks=FAKE + 1), 1, "sinks not 4-byte aligned"),
+    (dict(Hq=6, Hkv=4), 1, "not divisible"),
+    (dict(softcap=-2.0), 1, "softcap"),
+    (dict(k=None), 1, "k and v"),
+    (dict(D=80), 2, "D=80"),
+])
+def test_varlen_refusals(kw, status, needle):
+    st, msg = varlen(**kw)
+    assert st == status and needle in msg, (st, msg)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(cq=None), 1, "cu_seqlens_q must not be NULL"),
+    (dict(cq=FAKE + 2), 1, "cu_seqlens_q not 4-byte aligned"),
+    (dict(tq=-3), 1, "total_q=-3"),
+    (dict(page_size=24), 2, "page_size=24"),
+    (dict(lens=None), 1, "must not be NULL"),
+    (dict(sinks=FAKE + 2), 1, "sinks not 4-byte aligned"),
+])
+def test_paged_varlen_refusals(kw, status, needle):
+    st, msg = paged_varlen(**kw)
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_varlen_empty_calls_are_ok_without_touching_the_device():
+    assert varlen(B=0, q=None, o=None, cq=None, ck=None)[0] == 0
+    assert varlen(tq=0, q=None, o=None)[0] == 0
+    assert varlen(mq=0, q=None, o=None)[0] == 0
+    assert paged_varlen(tq=0, q=None, o=None)[0] == 0
+
+
 def test_python_binding_maps_refusals_to_value_error():
     import torch
     st, _ = dense(Hq=5, Hkv=2)
