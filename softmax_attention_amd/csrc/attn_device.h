@@ -198,8 +198,11 @@ __device__ __forceinline__ int sk_sums(const SkBatch &s, int upto, int &before) 
         total += __shfl(incl, 63);
         pre += __shfl(incl_before, 63);
     }
-    before = pre;
-    return total;
+    // (wave-uniform values: scalar registers, so that addresses built from
+    // them stay scalar -- a buffer descriptor in vector registers costs a
+    // waterfall loop per load)
+    before = __builtin_amdgcn_readfirstlane(pre);
+    return __builtin_amdgcn_readfirstlane(total);
 }
 
 // the entry b whose tiles hold tile `at` of the sequence (hkv * pre_b <= at <
@@ -218,15 +221,15 @@ __device__ __forceinline__ void sk_find(const SkBatch &s, int hkv, int64_t at, i
         const uint64_t m = __ballot(hit);
         if (m) {
             const int src = __builtin_ctzll(m);
-            b_out = c + src;
-            pre_out = __shfl(excl, src);
-            t_out = __shfl(t, src);
+            b_out = __builtin_amdgcn_readfirstlane(c + src);
+            pre_out = __builtin_amdgcn_readfirstlane(__shfl(excl, src));
+            t_out = __builtin_amdgcn_readfirstlane(__shfl(t, src));
             return;
         }
         carry = __shfl(incl, 63);
     }
     b_out = s.sd.B;
-    pre_out = carry;
+    pre_out = __builtin_amdgcn_readfirstlane(carry);
     t_out = 0;
 }
 

@@ -497,6 +497,53 @@ void attn_fwd_kernel(const FwdParams p) {
             }
     };
 
+    // ---- the same two products with every operand read of a batch (up to
+    // 8 MFMAs) issued before its MFMAs: for the streaming schedules, where the
+    // scheduler otherwise waits out one LDS read before each MFMA
+    auto qk_batched = [&](const uint8_t *sk, f32x16 (&sc)[NT]) __attribute__((always_inline)) {
+        constexpr int CH = KSTEPS < 8 ? KSTEPS : 8;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+#pragma unroll
+            for (int k0 = 0; k0 < KSTEPS; k0 += CH) {
+                vec8 a[CH];
+#pragma unroll
+                for (int c = 0; c < CH; ++c)
+                    a[c] = __builtin_bit_cast(
+                        vec8, *(const u32x4 *)(sk + k_addr[k0 + c] + 32 * t * (2 * D)));
+                __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+                for (int c = 0; c < CH; ++c) sc[t] = H::mfma(a[c], qf[k0 + c], sc[t]);
+            }
+        }
+    };
+    auto pv_batched = [&](const uint8_t *sv, const vec8 (&pb)[PSTEPS]) __attribute__((always_inline)) {
+        constexpr int TB = (8 / PSTEPS) < DT ? (8 / PSTEPS) : DT;  // d blocks per batch
+#pragma unroll
+        for (int t0 = 0; t0 < DT; t0 += TB) {
+            vec8 a[TB][PSTEPS];
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+#pragma unroll
+                for (int kk = 0; kk < PSTEPS; ++kk) {
+                    const int step = 16 * kk * (2 * D);
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4 *)(sv + v_addr[t0 + t][0] + step));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4 *)(sv + v_addr[t0 + t][1] + step));
+                    a[t][kk] = __builtin_bit_cast(
+                        vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+#pragma unroll
+                for (int kk = 0; kk < PSTEPS; ++kk) acc[t0 + t] = H::mfma(a[t][kk], pb[kk], acc[t0 + t]);
+        }
+    };
+
     if constexpr (WAVES == 8) {
         // ---- ping-pong main loop.  Waves 0-3 (group 0) and 4-7 (group 1)
         // sit on the four SIMDs in pairs.  Each tile k takes one step of two
@@ -575,7 +622,6 @@ void attn_fwd_kernel(const FwdParams p) {
             t3 = t2 < wg_end ? find_tile(t2 + BN, lo3, hi3) : wg_end;                   \
             issue_kv(t3, pg_next, K_NEW, t2, pg_t2, V_NEW);                             \
             pg_t2 = pg_next;                                                            \
-            pg_next = tile_page(t3 + BN);                                               \
             if (group == 0) /* phase A */                                               \
                 mma_phase(t0, prev, K_CUR, V_PREV);                                     \
             else                                                                        \
@@ -585,6 +631,9 @@ void attn_fwd_kernel(const FwdParams p) {
                 softmax_phase(t0 < wg_end ? t0 : -1, lo0, hi0);                         \
             else                                                                        \
                 mma_phase(t0, prev, K_CUR, V_PREV);                                     \
+            /* (the next page entry is read here: a scalar load in flight during */    \
+            /* the phases would force every LDS wait there to lgkmcnt(0)) */            \
+            pg_next = tile_page(t3 + BN);                                               \
             /* the loads issued two steps ago hold K(t1) and V(t0) */                   \
             wait_vmcnt<4 * PPW>();                                                      \
             ring_barrier();                                                             \
@@ -648,7 +697,7 @@ void attn_fwd_kernel(const FwdParams p) {
             if (!sees(t0)) return;
             bool full = full_tile(t0);
             if (has_mask) full = full && (lo0 == kLoMask) && (BN <= 64 || hi0 == ~0ull);
-            qk(sk, sc);
+            qk_batched(sk, sc);
             const float corr = full ? softmax(std::false_type{}, t0, lo0, hi0, sc, pb)
                                     : softmax(std::true_type{}, t0, lo0, hi0, sc, pb);
             if (corr != 1.f) {
@@ -657,14 +706,14 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[t][r] *= corr;
             }
-            pv(sv, pb);
+            pv_batched(sv, pb);
         };
 #define MIATTN_ST_STEP(K_CUR, V_CUR, K_NEW, V_NEW)                                      \
         {                                                                               \
             t3 = t2 < wg_end ? find_tile(t2 + BN, lo3, hi3) : wg_end;                   \
             issue_kv(t3, pg_next, K_NEW, t3, pg_next, V_NEW);                           \
-            pg_next = tile_page(t3 + BN);                                               \
             compute(K_CUR, V_CUR);                                                      \
+            pg_next = tile_page(t3 + BN);                                               \
             /* the loads issued two steps ago hold tile t1 */                          \
             wait_vmcnt<4 * PPW>();                                                      \
             ring_barrier();                                                             \
@@ -698,8 +747,8 @@ void attn_fwd_kernel(const FwdParams p) {
         {                                                                               \
             t2 = t1 < wg_end ? find_tile(t1 + BN, lo2, hi2) : wg_end;                   \
             issue_kv(t2, pg_next, K_NEW, t2, pg_next, V_NEW);                           \
-            pg_next = tile_page(t2 + BN);                                               \
             compute(K_CUR, V_CUR);                                                      \
+            pg_next = tile_page(t2 + BN);                                               \
             wait_vmcnt<2 * PPW>();                                                      \
             ring_barrier();                                                             \
             t0 = t1; lo0 = lo1; hi0 = hi1;                                              \
