@@ -69,8 +69,15 @@ def _load():
                                            i32, *win, P, P, P]
         lib.oracle_attn_paged_varlen.argtypes = [P, P, P, P, P, i32, P, i32, *win, P, i32, i32,
                                                  i32, i32, i32, i32, f32, i32, P, P]
+        lib.oracle_e4m3_decode.argtypes = [i32]
+        lib.oracle_e4m3_decode.restype = ctypes.c_double
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.oracle_kv_write.argtypes = [P, P, i32, P, i32, i32, i32, i64, i32, f32, f32, P, P]
+        lib.oracle_attn_paged_append.argtypes = [P, P, P, P, P, P, P, i32, P, i32, f32, i32, i32,
+                                                 i32, i32, i32, i32, i32, f32, i32, P, P]
         for name in ("oracle_attn_dense", "oracle_attn_dense_rows", "oracle_attn_paged",
                      "oracle_attn_paged_rows", "oracle_attn_varlen", "oracle_attn_paged_varlen",
+                     "oracle_e4m3_encode", "oracle_kv_write", "oracle_attn_paged_append",
                      "oracle_num_threads"):
             getattr(lib, name).restype = i32
         _lib = lib
@@ -308,6 +315,71 @@ def attn_paged_varlen(q, k_cache, v_cache, cache_seqlens, block_table, page_size
     return o, lse
 
 
+def e4m3_encode(x: float) -> int:
+    """E4M3FN code of x (nearest, ties to even; NaN kept; |x| > 448 -> +-448)."""
+    return _load().oracle_e4m3_encode(float(x))
+
+
+def e4m3_decode(code: int) -> float:
+    return _load().oracle_e4m3_decode(int(code))
+
+
+def kv_write(k, v, k_pool, v_pool, slot_mapping, *, cache_fp8=False, k_scale=1.0,
+             v_scale=1.0, dtype=None):
+    """Scatter k/v [tokens,Hkv,D] into copies of the pools ([num_slots,Hkv,D] or
+    [pages,page_size,Hkv,D]: uint16 bit patterns, or uint8 E4M3FN codes when
+    cache_fp8); slot_mapping int64 [tokens], -1 skips.  Returns the new pools
+    as numpy arrays of the pools' shapes."""
+    dt = _dtype_code(k) if dtype is None else dtype
+    kb, vb = _bits(k), _bits(v)
+    tokens, Hkv, D = kb.shape
+    import torch
+    def pool_np(p):
+        if isinstance(p, torch.Tensor):
+            p = p.detach().cpu()
+            p = p.view(torch.uint8) if cache_fp8 else p.view(torch.int16)
+            p = p.numpy().view(np.uint8 if cache_fp8 else np.uint16)
+        return np.ascontiguousarray(np.array(p, copy=True))
+    kp, vp = pool_np(k_pool), pool_np(v_pool)
+    num_slots = kp.size // (Hkv * D)
+    sl = slot_mapping.detach().cpu().numpy() if isinstance(slot_mapping, torch.Tensor) \
+        else np.asarray(slot_mapping)
+    sl = np.ascontiguousarray(sl.astype(np.int64))
+    rc = _load().oracle_kv_write(_ptr(kb), _ptr(vb), dt, _ptr(sl), tokens, Hkv, D, num_slots,
+                                 int(bool(cache_fp8)), float(k_scale), float(v_scale), _ptr(kp),
+                                 _ptr(vp))
+    if rc != 0:
+        raise ValueError(f"oracle_kv_write rejected the call (rc={rc})")
+    return kp, vp
+
+
+def attn_paged_append(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, page_size,
+                      cu_seqlens_q, *, causal=True, softcap=None, scale=None, dtype=None):
+    """Prefill with append: writes k_new/v_new [total_q,Hkv,D] at each request's
+    positions cache_seqlens[b] + i (copies of the 16-bit pools), then attends the
+    packed queries to cache_seqlens[b] + Sq_b keys.  Returns o [total_q,Hq,D],
+    lse [Hq,total_q] and the two updated pools (uint16 numpy arrays)."""
+    dt = _dtype_code(q) if dtype is None else dtype
+    qb, kb, vb = _bits(q), _bits(k_new), _bits(v_new)
+    kc, vc = np.array(_bits(k_cache), copy=True), np.array(_bits(v_cache), copy=True)
+    total_q, Hq, D = qb.shape
+    Hkv = kb.shape[1]
+    lens, bt, cq = _i32(cache_seqlens), _i32(block_table), _i32(cu_seqlens_q)
+    B = cq.shape[0] - 1
+    num_pages = kc.size // (page_size * Hkv * D)
+    o = np.zeros((total_q, Hq, D), np.float64)
+    lse = np.zeros((Hq, total_q), np.float64)
+    rc = _load().oracle_attn_paged_append(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(kc), _ptr(vc),
+                                          _ptr(lens), _ptr(bt), int(page_size), _ptr(cq),
+                                          int(bool(causal)),
+                                          0.0 if softcap is None else float(softcap), B,
+                                          total_q, Hq, Hkv, D, bt.shape[1], num_pages,
+                                          _scale_arg(scale), dt, _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_paged_append rejected the call (rc={rc})")
+    return o, lse, kc, vc
+
+
 __all__ = ["BF16", "FP16", "build", "decode", "resolve_scale", "num_threads", "attn_dense",
            "attn_dense_rows", "attn_paged", "attn_paged_rows", "attn_varlen",
-           "attn_paged_varlen"]
+           "attn_paged_varlen", "e4m3_encode", "e4m3_decode", "kv_write", "attn_paged_append"]

@@ -27,6 +27,15 @@
  *     key_padding_mask [B, S_kv], True = keep, False sets the column to -inf.
  *   - MATE "QSA", Core Attention: the log-sum-exp is natural-log and an empty
  *     selection returns zero output with -inf LSE.
+ *   - TileOPs "Attention Operators", PagedKVCacheWriteFwdOp: each token's K
+ *     and V row goes to the pool row its slot names (page * page_size +
+ *     offset; -1 skips the token); an FP8 pool stores row / scale as
+ *     E4M3FN, NaN preserved, finite overflow and infinities saturated to the
+ *     largest finite magnitude of the same sign.
+ *   - TileOPs "Attention Operators", GQAPrefillPagedWithKVCacheFwdOp: the
+ *     packed chunk's keys and values are appended after each request's
+ *     cached ones (cache_seqlens counts them before the append), then the
+ *     chunk's queries attend to the cache.
  *   - TileOPs "Attention Operators", GQAVarlenFwdOp and GQAPagedFwdOp: packed
  *     THD tensors [total, heads, dim] whose requests are delimited by
  *     cu_seqlens (request b holds rows cu[b] .. cu[b+1] - 1), the causal mask
@@ -523,6 +532,138 @@ int oracle_attn_paged_varlen(const uint16_t *q, const uint16_t *k_cache,
     c.total_q = total_q;
     c.sinks = sinks;
     return run_all(&c, o, lse);
+}
+
+/* ---------------------------------------------------------------- FP8 E4M3FN
+ *
+ * OCP 8-bit E4M3FN: 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits; no
+ * infinities; S.1111.111 is NaN, so the largest finite magnitude is
+ * 1.110b * 2^8 = 448; exponent 0 holds zero and subnormals (fraction * 2^-9).
+ */
+static double e4m3_value(int code)
+{
+    int e = (code >> 3) & 15, f = code & 7;
+    double mag;
+    if (e == 15 && f == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)f, -9);
+    else
+        mag = ldexp((double)(8 + f), e - 10);
+    return (code & 0x80) ? -mag : mag;
+}
+
+double oracle_e4m3_decode(int code) { return e4m3_value(code & 0xff); }
+
+/* The E4M3FN code of x: the nearest finite value, ties to the even code (the
+ * one with fraction bit 0), found by checking every non-negative code; NaN
+ * stays NaN; magnitudes above 448, infinities included, saturate to 448. */
+int oracle_e4m3_encode(double x)
+{
+    if (isnan(x))
+        return signbit(x) ? 0xff : 0x7f;
+    int sign = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    if (a >= 448.0)
+        return sign | 0x7e;
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c <= 0x7e; ++c) {
+        double err = fabs(e4m3_value(c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return sign | best;
+}
+
+/* ---------------------------------------------------------------- KV write
+ *
+ * Write token n's rows k[n], v[n] ([Hkv, D] 16-bit patterns) into pool row
+ * slot[n] of k_pool / v_pool ([num_slots, Hkv, D]); slot -1 skips the token.
+ * cache_fp8 = 0: the pool holds the same 16-bit patterns; 1: E4M3FN codes of
+ * the value divided by k_scale / v_scale, the division done in float32 (the
+ * precision of the scale and of the device computation).  Returns -1 for a
+ * slot outside [-1, num_slots) or a non-positive scale. */
+int oracle_kv_write(const uint16_t *k, const uint16_t *v, int dtype, const int64_t *slot,
+                    int tokens, int Hkv, int D, int64_t num_slots, int cache_fp8,
+                    float k_scale, float v_scale, void *k_pool, void *v_pool)
+{
+    if (tokens < 0 || Hkv <= 0 || D <= 0 || num_slots < 0)
+        return -1;
+    if (cache_fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale)))
+        return -1;
+    for (int n = 0; n < tokens; ++n)
+        if (slot[n] < -1 || slot[n] >= num_slots)
+            return -1;
+    const int64_t row = (int64_t)Hkv * D;
+    for (int n = 0; n < tokens; ++n) {
+        if (slot[n] < 0)
+            continue;
+        for (int64_t e = 0; e < row; ++e) {
+            const int64_t src = (int64_t)n * row + e, dst = slot[n] * row + e;
+            if (!cache_fp8) {
+                ((uint16_t *)k_pool)[dst] = k[src];
+                ((uint16_t *)v_pool)[dst] = v[src];
+            } else {
+                float kq = (float)decode(k, src, dtype) / k_scale;
+                float vq = (float)decode(v, src, dtype) / v_scale;
+                ((uint8_t *)k_pool)[dst] = (uint8_t)oracle_e4m3_encode((double)kq);
+                ((uint8_t *)v_pool)[dst] = (uint8_t)oracle_e4m3_encode((double)vq);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Paged prefill with append (16-bit pools): request b's chunk (queries and
+ * new keys/values at packed rows cu_q[b] .. cu_q[b+1]-1) is written to its
+ * logical positions cache_seqlens[b] + i, i.e. pool row
+ * block_table[b, pos / page_size] * page_size + pos % page_size; then the
+ * chunk's queries attend to the request's cache_seqlens[b] + Sq_b keys.  The
+ * pools are updated in place; o [total_q, Hq, D], lse [Hq, total_q]. */
+int oracle_attn_paged_append(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                             uint16_t *k_cache, uint16_t *v_cache, const int32_t *cache_seqlens,
+                             const int32_t *block_table, int page_size, const int32_t *cu_q,
+                             int causal, float softcap, int B, int total_q, int Hq, int Hkv,
+                             int D, int max_pages, int num_pages, float scale, int dtype,
+                             double *o, double *lse)
+{
+    if (B < 0 || total_q < 0 || page_size <= 0 || max_pages <= 0 || num_pages < 0)
+        return -1;
+    if (check_offsets(cu_q, B, total_q))
+        return -1;
+    int64_t *slot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(total_q > 0 ? total_q : 1));
+    int32_t *lens = (int32_t *)malloc(sizeof(int32_t) * (size_t)(B > 0 ? B : 1));
+    if (!slot || !lens) {
+        free(slot);
+        free(lens);
+        return -2;
+    }
+    int rc = 0;
+    for (int b = 0; b < B && rc == 0; ++b) {
+        lens[b] = cache_seqlens[b] + (cu_q[b + 1] - cu_q[b]);
+        if (cache_seqlens[b] < 0 || (int64_t)lens[b] > (int64_t)max_pages * page_size)
+            rc = -1;
+        for (int i = cu_q[b]; i < cu_q[b + 1] && rc == 0; ++i) {
+            int64_t pos = (int64_t)cache_seqlens[b] + (i - cu_q[b]);
+            int32_t page = block_table[(int64_t)b * max_pages + pos / page_size];
+            if (page < 0 || page >= num_pages)
+                rc = -1;
+            slot[i] = (int64_t)page * page_size + pos % page_size;
+        }
+    }
+    if (rc == 0)
+        rc = oracle_kv_write(k_new, v_new, dtype, slot, total_q, Hkv, D,
+                             (int64_t)num_pages * page_size, 0, 1.0f, 1.0f, k_cache, v_cache);
+    if (rc == 0)
+        rc = oracle_attn_paged_varlen(q, k_cache, v_cache, lens, block_table, page_size, cu_q,
+                                      causal, -1, -1, softcap, NULL, B, total_q, Hq, Hkv, D,
+                                      max_pages, scale, dtype, o, lse);
+    free(slot);
+    free(lens);
+    return rc;
 }
 
 /* Number of threads an OpenMP parallel region uses here. */

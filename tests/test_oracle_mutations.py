@@ -58,12 +58,21 @@ MUTANTS = {
     "varlen_keys_at_query_offsets": ("row = (int64_t)c->cu_kv[b] + j;", "row = (int64_t)c->cu_q[b] + j;"),
     "varlen_lse_batched_layout": ("lse[(int64_t)h * c->total_q + q_row(c, b, i)] = lse_rows[t++];",
                                   "lse[q_row(c, b, i) * c->Hq + h] = lse_rows[t++];"),
+    "e4m3_ties_to_odd": ("(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
+    "e4m3_overflow_to_nan": ("    if (a >= 448.0)\n        return sign | 0x7e;", "    if (a > 448.0)\n        return sign | 0x7f;"),
+    "e4m3_subnormal_step": ("mag = ldexp((double)f, -9);", "mag = ldexp((double)f, -10);"),
+    "fp8_scale_multiplies": ("float kq = (float)decode(k, src, dtype) / k_scale;",
+                             "float kq = (float)decode(k, src, dtype) * k_scale;"),
+    "write_skips_slot_zero": ("        if (slot[n] < 0)\n            continue;", "        if (slot[n] <= 0)\n            continue;"),
+    "append_position_off_by_one": ("int64_t pos = (int64_t)cache_seqlens[b] + (i - cu_q[b]);",
+                                   "int64_t pos = (int64_t)cache_seqlens[b] + (i - cu_q[b]) + 1;"),
+    "append_lengths_not_grown": ("lens[b] = cache_seqlens[b] + (cu_q[b + 1] - cu_q[b]);", "lens[b] = cache_seqlens[b];"),
     "value_sum_skips_first_key": ("for (int64_t j = 0; j < n; ++j) {\n            if (!visible(c, b, i, j))\n                continue;\n            acc +=",
                                   "for (int64_t j = 1; j < n; ++j) {\n            if (!visible(c, b, i, j))\n                continue;\n            acc +="),
 }
 
 PIN_FILES = ["test_oracle_pins.py", "test_oracle_pins_window_softcap.py",
-             "test_oracle_pins_varlen_sinks.py"]
+             "test_oracle_pins_varlen_sinks.py", "test_oracle_pins_kv_write.py"]
 
 PLUGIN = "import os, oracle\noracle._LIB = os.environ['ORACLE_MUTANT_LIB']\n"
 
