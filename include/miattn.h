@@ -29,6 +29,13 @@
  *     gives zero output and -inf LSE, split-KV partials are merged in FP32
  *     without recomputing QK or PV, and wrappers check shapes and layout
  *     without reading device contents.
+ *   - TileOPs "Attention Operators", PagedKVCacheWriteFwdOp: each token's key
+ *     and value rows go to the pool row its slot names (page * page_size +
+ *     offset, -1 skipping the token); an FP8 pool stores row / scale as
+ *     E4M3FN, NaN preserved, finite overflow and infinities saturated to the
+ *     largest finite magnitude; GQAPrefillPagedWithKVCacheFwdOp: a packed
+ *     chunk's keys and values are appended after each request's cached ones
+ *     and its queries attend to the cache.
  *   - TileOPs "Attention Operators", GQAVarlenFwdOp and GQAPagedFwdOp: packed
  *     THD tensors [total, heads, dim] with requests delimited by cumulative
  *     offsets, the causal mask bottom-right aligned per request, offsets not
@@ -76,6 +83,13 @@ typedef enum {
 } miattn_status;
 
 typedef enum { MIATTN_BF16 = 0, MIATTN_FP16 = 1 } miattn_dtype;
+
+/* Element type of a KV-cache pool (the 16-bit ones equal the inputs' dtype). */
+typedef enum {
+    MIATTN_CACHE_BF16 = 0,
+    MIATTN_CACHE_FP16 = 1,
+    MIATTN_CACHE_FP8_E4M3 = 2 /* OCP E4M3FN bytes of value / scale */
+} miattn_cache_dtype;
 
 /*
  * Dense attention forward.
@@ -208,6 +222,57 @@ miattn_status attn_fwd_paged_varlen(const void *q, const void *k_cache, const vo
                                     int total_q, int max_seqlen_q, int Hq, int Hkv, int D,
                                     int max_pages, int num_phys_pages, float scale,
                                     miattn_dtype dtype, void *stream);
+
+/*
+ * Paged KV-cache write: scatter new key and value rows into the page pools.
+ *
+ *   k, v       device, [tokens, Hkv, D] dtype (16-byte aligned)
+ *   k_pages, v_pages  device pools [num_slots, Hkv, D] of cache_dtype (the same
+ *              bytes as [pages, page_size, Hkv, D], num_slots = pages *
+ *              page_size); written in place, nothing outside the named rows
+ *   slot_mapping device, int64 [tokens]: row of token n (page * page_size +
+ *              offset), or -1 to skip it.  Distinct slots are the caller's
+ *              obligation; slots outside [-1, num_slots) are skipped (refused
+ *              with INVALID_ARG under MIATTN_VALIDATE=1)
+ *   Hkv * D    a multiple of 8
+ *   dtype      MIATTN_BF16 or MIATTN_FP16, the type of k and v
+ *   cache_dtype  equal to dtype (rows copied), or MIATTN_CACHE_FP8_E4M3: each
+ *              value is divided by *k_scale / *v_scale in float32 and stored
+ *              as E4M3FN (nearest, ties to even; NaN kept; beyond +-448,
+ *              infinities included, saturated to +-448)
+ *   k_scale, v_scale  device float32 [1], required for an FP8 pool (finite and
+ *              positive; checked only under MIATTN_VALIDATE=1), else ignored
+ *   stream     hipStream_t or NULL
+ */
+miattn_status kv_cache_write(const void *k, const void *v, void *k_pages, void *v_pages,
+                             const int64_t *slot_mapping, int tokens, int Hkv, int D,
+                             int64_t num_slots, miattn_dtype dtype, miattn_cache_dtype cache_dtype,
+                             const float *k_scale, const float *v_scale, void *stream);
+
+/*
+ * Paged prefill with append (16-bit pools): request b's chunk -- queries,
+ * keys and values at packed rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 --
+ * is written to logical positions cache_seqlens[b] + i of its cache (pool
+ * row block_table[b, pos / page_size] * page_size + pos % page_size), then
+ * its queries attend to the request's cache_seqlens[b] + Sq_b keys.
+ *
+ *   q, k_new, v_new  device, [total_q, Hq, D] / [total_q, Hkv, D] dtype
+ *   k_cache, v_cache device pools as for attn_fwd_paged, written in place
+ *   cache_seqlens    device, int32 [B]: keys cached before the chunk
+ *   block_table      device, int32 [B, max_pages]; it must cover the appended
+ *                    positions (tokens it does not cover are not written)
+ *   cu_seqlens_q, max_seqlen_q  as for attn_fwd_paged_varlen
+ *   causal, softcap, scale, o, lse, dtype, stream  as for attn_fwd_paged_varlen
+ *                    (lse [Hq, total_q])
+ *   B, Hq, Hkv, D, page_size, max_pages, num_phys_pages  as for attn_fwd_paged
+ */
+miattn_status attn_fwd_paged_append(const void *q, const void *k_new, const void *v_new,
+                                    void *k_cache, void *v_cache, const int32_t *cache_seqlens,
+                                    const int32_t *block_table, const int32_t *cu_seqlens_q,
+                                    int page_size, int causal, float softcap, void *o,
+                                    float *lse, int B, int total_q, int max_seqlen_q, int Hq,
+                                    int Hkv, int D, int max_pages, int num_phys_pages,
+                                    float scale, miattn_dtype dtype, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *miattn_last_error(void);

@@ -18,10 +18,11 @@ LIB_PATH = os.path.join(_PKG, "libmiattn.so")
 
 MIATTN_OK, MIATTN_ERR_INVALID_ARG, MIATTN_ERR_UNSUPPORTED, MIATTN_ERR_HIP = 0, 1, 2, 3
 MIATTN_BF16, MIATTN_FP16 = 0, 1
+MIATTN_CACHE_BF16, MIATTN_CACHE_FP16, MIATTN_CACHE_FP8_E4M3 = 0, 1, 2
 
 # every symbol include/miattn.h declares
 EXPORTS = ("attn_fwd_dense", "attn_fwd_paged", "attn_fwd_varlen", "attn_fwd_paged_varlen",
-           "miattn_last_error", "miattn_release_workspace", "miattn_set_split_keys",
+           "kv_cache_write", "attn_fwd_paged_append", "miattn_last_error", "miattn_release_workspace", "miattn_set_split_keys",
            "miattn_profile_start", "miattn_profile_stop")
 
 _lib = None
@@ -53,6 +54,12 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_paged_varlen.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, P, P, P,
                                             i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, P]
         L.attn_fwd_paged_varlen.restype = i32
+        i64 = ctypes.c_int64
+        L.kv_cache_write.argtypes = [P, P, P, P, P, i32, i32, i32, i64, i32, i32, P, P, P]
+        L.kv_cache_write.restype = i32
+        L.attn_fwd_paged_append.argtypes = [P, P, P, P, P, P, P, P, i32, i32, f32, P, P, i32,
+                                            i32, i32, i32, i32, i32, i32, i32, f32, i32, P]
+        L.attn_fwd_paged_append.restype = i32
         L.miattn_last_error.argtypes = []
         L.miattn_last_error.restype = ctypes.c_char_p
         L.miattn_release_workspace.argtypes = []
@@ -333,6 +340,105 @@ def attn_fwd_paged_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                                      total_q, mq, Hq, Hkv, D, block_table.shape[1], n_pages,
                                      _scale(scale), code, _stream())
     _check(st)
+    return o, (lse if return_lse else None)
+
+
+def _pool_geometry(k_pages: torch.Tensor, Hkv: int, D: int) -> int:
+    """Rows (num_slots) of a pool [num_slots,Hkv,D] or [pages,page_size,Hkv,D]."""
+    if k_pages.dim() not in (3, 4) or tuple(k_pages.shape[-2:]) != (Hkv, D):
+        raise ValueError(f"pools must be [rows, {Hkv}, {D}] or [pages, page_size, {Hkv}, {D}]")
+    return k_pages.numel() // (Hkv * D)
+
+
+def kv_cache_write(k: torch.Tensor, v: torch.Tensor, k_pages: torch.Tensor,
+                   v_pages: torch.Tensor, slot_mapping: torch.Tensor, *,
+                   k_scale: Optional[torch.Tensor] = None,
+                   v_scale: Optional[torch.Tensor] = None) -> None:
+    """Scatter k/v [tokens,Hkv,D] into the pools at slot_mapping (int64 [tokens],
+    -1 skips), on the current stream.  Pools of torch.float8_e4m3fn store
+    value / scale (k_scale/v_scale float32 [1] on the device)."""
+    if k.dim() != 3 or k.shape != v.shape:
+        raise ValueError("k and v must be [tokens, Hkv, D] of one shape")
+    if k.dtype != v.dtype:
+        raise ValueError("k and v must share one dtype")
+    code = _dtype_code(k)
+    tokens, Hkv, D = k.shape
+    if k_pages.shape != v_pages.shape or k_pages.dtype != v_pages.dtype:
+        raise ValueError("k_pages and v_pages must have one shape and dtype")
+    fp8 = k_pages.dtype == torch.float8_e4m3fn
+    if not fp8 and k_pages.dtype != k.dtype:
+        raise ValueError("a 16-bit pool must have the dtype of k and v")
+    cache = MIATTN_CACHE_FP8_E4M3 if fp8 else code
+    if slot_mapping.dtype != torch.int64 or tuple(slot_mapping.shape) != (tokens,):
+        raise ValueError("slot_mapping must be int64 [tokens]")
+    dev = k.device
+    if not all(t.is_cuda and t.device == dev for t in (k, v, k_pages, v_pages, slot_mapping)):
+        raise ValueError("k, v, the pools and slot_mapping must be on one GPU device")
+    if not (k_pages.is_contiguous() and v_pages.is_contiguous()):
+        raise ValueError("the pools must be contiguous (they are written in place)")
+    if fp8:
+        for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if sc is None or sc.dtype != torch.float32 or sc.numel() != 1 or sc.device != dev:
+                raise ValueError(f"an FP8 pool needs {name}: float32 [1] on the GPU")
+    k, v, slot_mapping = k.contiguous(), v.contiguous(), slot_mapping.contiguous()
+    num_slots = _pool_geometry(k_pages, Hkv, D)
+    _check(lib().kv_cache_write(_ptr(k), _ptr(v), _ptr(k_pages), _ptr(v_pages),
+                                _ptr(slot_mapping), tokens, Hkv, D, num_slots, code, cache,
+                                _ptr(k_scale) if fp8 else None, _ptr(v_scale) if fp8 else None,
+                                _stream()))
+
+
+def attn_fwd_paged_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                          k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          cache_seqlens: torch.Tensor, block_table: torch.Tensor,
+                          cu_seqlens_q: torch.Tensor, page_size: int, *,
+                          max_seqlen_q: Optional[int] = None, causal: bool = True, scale=None,
+                          softcap=None, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None, return_lse: bool = True
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Paged prefill with append on the current stream: writes k_new/v_new
+    [total_q,Hkv,D] after each request's cache_seqlens[b] cached keys (16-bit
+    pools, in place), then attends the packed queries q [total_q,Hq,D] to
+    cache_seqlens[b] + Sq_b keys.  Returns (o [total_q,Hq,D], lse [Hq,total_q])."""
+    if q.dim() != 3 or k_new.dim() != 3 or k_new.shape != v_new.shape:
+        raise ValueError("q, k_new, v_new must be rank 3 (THD), k_new and v_new of one shape")
+    if k_new.shape[0] != q.shape[0] or k_new.shape[2] != q.shape[2]:
+        raise ValueError("k_new/v_new must have q's token count and head dim")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise ValueError("q, k_new, v_new must share one dtype")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("the pools must be 16-bit pools of q's dtype")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("the pools must be contiguous (they are written in place)")
+    code = _dtype_code(q)
+    dev = q.device
+    if not all(t.is_cuda and t.device == dev for t in (q, k_new, v_new, k_cache, v_cache,
+                                                       cache_seqlens, block_table)):
+        raise ValueError("all tensors must be on one GPU device")
+    if cache_seqlens.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise ValueError("cache_seqlens and block_table must be int32")
+    cq = _offsets(cu_seqlens_q, dev, "cu_seqlens_q")
+    total_q, Hq, D = q.shape
+    Hkv = k_new.shape[1]
+    B = cq.numel() - 1
+    if block_table.dim() != 2 or block_table.shape[0] != B or cache_seqlens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and cache_seqlens [B]")
+    num_slots = _pool_geometry(k_cache, Hkv, D)
+    if num_slots % page_size != 0:
+        raise ValueError("pool rows must be a multiple of page_size")
+    mq = _max_len(cq) if max_seqlen_q is None else int(max_seqlen_q)
+    q, k_new, v_new = q.contiguous(), k_new.contiguous(), v_new.contiguous()
+    cache_seqlens, block_table = cache_seqlens.contiguous(), block_table.contiguous()
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    _check(lib().attn_fwd_paged_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(cache_seqlens), _ptr(block_table),
+                                       _ptr(cq), int(page_size), int(bool(causal)),
+                                       _softcap(softcap), _ptr(o),
+                                       _ptr(lse) if return_lse else None, B, total_q, mq, Hq,
+                                       Hkv, D, block_table.shape[1], num_slots // page_size,
+                                       _scale(scale), code, _stream()))
     return o, (lse if return_lse else None)
 
 

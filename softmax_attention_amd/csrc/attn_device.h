@@ -139,7 +139,16 @@ __device__ __forceinline__ void q_span(const SeqDesc &s, int b, int64_t &row0, i
 }
 
 __device__ __forceinline__ int seq_kv_len(const SeqDesc &s, int b) {
-    if (s.seqlen) return min(max(s.seqlen[b], 0), s.cap);
+    if (s.seqlen) {
+        int64_t len = s.seqlen[b];
+        if (s.append) {  // the chunk's own keys follow the cached ones
+            int64_t row0;
+            int sq_b;
+            q_span(s, b, row0, sq_b);
+            len += sq_b;
+        }
+        return (int)min(max(len, (int64_t)0), (int64_t)s.cap);
+    }
     if (!s.cu_kv) return s.skv;
     const int a = min(max(s.cu_kv[b], 0), s.total_kv);
     const int e = min(max(s.cu_kv[b + 1], a), s.total_kv);

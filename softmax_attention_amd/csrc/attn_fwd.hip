@@ -136,7 +136,8 @@ void attn_fwd_kernel(const FwdParams p) {
     // clamped so that malformed ones stay inside the tensors
     const SeqDesc sd = {PAGED ? p.seqlen : nullptr, p.cu_q, PAGED ? nullptr : p.cu_kv, p.B,
                         p.Sq, p.Skv, p.total_q, p.total_kv,
-                        (PAGED && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0};
+                        (PAGED && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0,
+                        PAGED ? p.kv_append : 0};
 
     // ---- one unit of work: the key range [kbeg, kend) of row block `mblock`
     // of (batch b, KV head kvh), whose length is kv_len; a split result goes

@@ -48,6 +48,8 @@ struct SeqDesc {
     int skv;                // dense keys per request (packed: the most one may hold)
     int total_q, total_kv;  // packed row counts
     int cap;                // paged: max_pages * page_size (0 for an empty cache)
+    int append;             // paged: seqlen counts the keys before a chunk of Sq_b queries
+                            // whose keys were appended (the request holds seqlen + Sq_b)
 };
 
 struct FwdParams {
@@ -64,6 +66,7 @@ struct FwdParams {
     const int32_t *cu_q;        // packed (THD) queries: offsets [B + 1], or nullptr
     const int32_t *cu_kv;       // packed dense keys: offsets [B + 1], or nullptr
     const float *sinks;         // [Hq] sink logits, or nullptr
+    int kv_append;              // paged: seqlen excludes the appended chunk (see SeqDesc)
     int total_q, total_kv;      // packed row counts (lse of a packed call is [Hq, total_q])
     int B, Sq, Hq, Hkv, G, Skv; // packed calls: Sq and Skv are the per-request maxima
     int page_shift, max_pages, num_pages;  // paged: log2(page size), table width, cache pages
@@ -97,6 +100,7 @@ struct MergeParams {
     const int32_t *cu_q, *cu_kv;
     const float *sinks;
     int total_q, total_kv;
+    int kv_append;
     int Skv;
     int B, Sq, Hq, Hkv, G, rows, n_splits, split_len;
     // stream-K decode: grid size (0 otherwise), keys per tile and the length
@@ -125,5 +129,22 @@ int attn_fwd_decode_blocks_per_cu(const FwdParams &p, int D, bool bf16, bool pag
                                   bool cap);
 
 hipError_t launch_lse_merge(const MergeParams &p, int D, bool bf16, hipStream_t stream);
+
+// Paged KV-cache write (kv_write.hip): token n's K and V rows ([row_elems]
+// 16-bit values) go to pool row slot(n) -- slot_mapping[n], or in append mode
+// the position cache_seqlens[b] + i of the packed chunk's token i of request
+// b through the block table; slots outside [0, num_slots) are skipped.
+struct KvWriteParams {
+    const uint16_t *k, *v;             // [tokens, row_elems]
+    uint16_t *k_pool16, *v_pool16;     // 16-bit pools [num_slots, row_elems]
+    uint8_t *k_pool8, *v_pool8;        // FP8 E4M3FN pools [num_slots, row_elems]
+    const float *k_scale, *v_scale;    // FP8: device divisors [1]
+    const int64_t *slot_mapping;       // [tokens]
+    const int32_t *cu_q, *cache_seqlens, *block_table;  // append mode
+    int tokens, row_elems, B, page_size, max_pages;
+    int64_t num_slots;
+};
+hipError_t launch_kv_write(const KvWriteParams &p, bool bf16, bool fp8, bool append,
+                           hipStream_t stream);
 
 }  // namespace miattn

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     const int gh = r - i * p.G;
     // the same request extents as the attention kernel
     const SeqDesc sd = {p.seqlen, p.cu_q, p.cu_kv, p.B, p.Sq, p.Skv, p.total_q, p.total_kv,
-                        p.sk_cap};
+                        p.sk_cap, p.seqlen ? p.kv_append : 0};
     int64_t q_row0;
     int sq_b;
     q_span(sd, b, q_row0, sq_b);

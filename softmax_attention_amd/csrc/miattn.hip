@@ -265,6 +265,7 @@ MergeParams merge_params(const FwdParams &p, bool paged) {
     m.sinks = p.sinks;
     m.total_q = p.total_q;
     m.total_kv = p.total_kv;
+    m.kv_append = p.kv_append;
     m.Skv = p.Skv;
     m.B = p.B;
     m.Sq = p.Sq;
@@ -517,7 +518,8 @@ miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache
                          float softcap, bool packed, const int32_t *cu_q, int total_q,
                          const float *sinks, void *o, float *lse, int B, int Sq, int Hq, int Hkv,
                          int D, int max_pages, int num_phys_pages, float scale,
-                         miattn_dtype dtype, void *stream) {
+                         miattn_dtype dtype, void *stream,
+                         const miattn::KvWriteParams *append = nullptr) {
     g_err[0] = '\0';
     // (a packed call without query rows has nothing to check q and o against)
     miattn_status st = check_common(q, o, lse, B, (packed && total_q == 0) ? 0 : Sq, Hq, Hkv,
@@ -613,6 +615,25 @@ miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache
     set_scale(p, alpha);
     st = set_window_softcap(p, window_left, window_right, softcap, capacity, alpha);
     if (st != MIATTN_OK) return st;
+    if (append) {
+        // the chunk's keys and values go into the pools first (same stream)
+        miattn::KvWriteParams w = *append;
+        w.k_pool16 = (uint16_t *)k_cache;
+        w.v_pool16 = (uint16_t *)v_cache;
+        w.cu_q = cu_q;
+        w.cache_seqlens = real_seqlen_kv;
+        w.block_table = block_table;
+        w.B = B;
+        w.page_size = page_size;
+        w.max_pages = max_pages;
+        w.num_slots = (int64_t)num_phys_pages * page_size;
+        w.tokens = total_q;
+        w.row_elems = Hkv * D;
+        hipError_t e = miattn::launch_kv_write(w, dtype == MIATTN_BF16, false, true,
+                                               (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "KV write kernel launch");
+        p.kv_append = 1;
+    }
     return run(p, D, dtype == MIATTN_BF16, true, capacity, softcap > 0.f, (hipStream_t)stream);
 }
 
@@ -664,6 +685,109 @@ miattn_status attn_fwd_paged_varlen(const void *q, const void *k_cache, const vo
                       window_left, window_right, softcap, true, cu_seqlens_q, total_q, sinks, o,
                       lse, B, max_seqlen_q, Hq, Hkv, D, max_pages, num_phys_pages, scale, dtype,
                       stream);
+}
+
+miattn_status kv_cache_write(const void *k, const void *v, void *k_pages, void *v_pages,
+                             const int64_t *slot_mapping, int tokens, int Hkv, int D,
+                             int64_t num_slots, miattn_dtype dtype, miattn_cache_dtype cache_dtype,
+                             const float *k_scale, const float *v_scale, void *stream) {
+    g_err[0] = '\0';
+    if (tokens < 0) return fail(MIATTN_ERR_INVALID_ARG, "tokens=%d is negative", tokens);
+    if (Hkv <= 0 || D <= 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "Hkv=%d and D=%d must be positive", Hkv, D);
+    if (num_slots < 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "num_slots=%lld is negative", (long long)num_slots);
+    if (dtype != MIATTN_BF16 && dtype != MIATTN_FP16)
+        return fail(MIATTN_ERR_UNSUPPORTED, "dtype %d unsupported (MIATTN_BF16, MIATTN_FP16)",
+                    (int)dtype);
+    const bool fp8 = cache_dtype == MIATTN_CACHE_FP8_E4M3;
+    if (!fp8 && (int)cache_dtype != (int)dtype)
+        return fail(MIATTN_ERR_UNSUPPORTED,
+                    "cache_dtype %d must equal dtype %d or be MIATTN_CACHE_FP8_E4M3",
+                    (int)cache_dtype, (int)dtype);
+    if (((int64_t)Hkv * D) % 8 != 0 || (int64_t)Hkv * D > INT_MAX / 2)
+        return fail(MIATTN_ERR_UNSUPPORTED, "Hkv*D = %lld must be a multiple of 8 (and < %d)",
+                    (long long)Hkv * D, INT_MAX / 2);
+    if ((int64_t)tokens * (Hkv * D / 8) > (int64_t)INT_MAX * 256)
+        return fail(MIATTN_ERR_UNSUPPORTED, "tokens*Hkv*D too large for one launch");
+    if (tokens == 0) return MIATTN_OK;
+    if (!k || !v || !k_pages || !v_pages || !slot_mapping)
+        return fail(MIATTN_ERR_INVALID_ARG,
+                    "k, v, k_pages, v_pages and slot_mapping must not be NULL");
+    if (!aligned16(k) || !aligned16(v))
+        return fail(MIATTN_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+    const uintptr_t pool_align = fp8 ? 7u : 15u;
+    if (((uintptr_t)k_pages & pool_align) || ((uintptr_t)v_pages & pool_align))
+        return fail(MIATTN_ERR_INVALID_ARG, "k_pages/v_pages must be %d-byte aligned",
+                    fp8 ? 8 : 16);
+    if ((uintptr_t)slot_mapping & 7u)
+        return fail(MIATTN_ERR_INVALID_ARG, "slot_mapping not 8-byte aligned");
+    if (fp8 && (!k_scale || !v_scale || ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u)))
+        return fail(MIATTN_ERR_INVALID_ARG,
+                    "an FP8 cache needs 4-byte aligned k_scale and v_scale");
+    if (env_int("MIATTN_VALIDATE", 0) == 1) {
+        std::vector<int64_t> sl(tokens);
+        hipStream_t s = (hipStream_t)stream;
+        hipError_t e = hipMemcpyAsync(sl.data(), slot_mapping, sizeof(int64_t) * tokens,
+                                      hipMemcpyDeviceToHost, s);
+        float sc[2] = {1.f, 1.f};
+        if (e == hipSuccess && fp8)
+            e = hipMemcpyAsync(&sc[0], k_scale, sizeof(float), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess && fp8)
+            e = hipMemcpyAsync(&sc[1], v_scale, sizeof(float), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "MIATTN_VALIDATE metadata copy");
+        for (int n = 0; n < tokens; ++n)
+            if (sl[n] < -1 || sl[n] >= num_slots)
+                return fail(MIATTN_ERR_INVALID_ARG,
+                            "slot_mapping[%d]=%lld outside [-1, num_slots=%lld)", n,
+                            (long long)sl[n], (long long)num_slots);
+        if (!(sc[0] > 0.f) || !(sc[1] > 0.f) || isinf(sc[0]) || isinf(sc[1]))
+            return fail(MIATTN_ERR_INVALID_ARG, "FP8 scales must be finite and positive");
+    }
+    miattn::KvWriteParams w = {};
+    w.k = (const uint16_t *)k;
+    w.v = (const uint16_t *)v;
+    w.k_pool16 = (uint16_t *)k_pages;
+    w.v_pool16 = (uint16_t *)v_pages;
+    w.k_pool8 = (uint8_t *)k_pages;
+    w.v_pool8 = (uint8_t *)v_pages;
+    w.k_scale = k_scale;
+    w.v_scale = v_scale;
+    w.slot_mapping = slot_mapping;
+    w.tokens = tokens;
+    w.row_elems = Hkv * D;
+    w.num_slots = num_slots;
+    hipError_t e = miattn::launch_kv_write(w, dtype == MIATTN_BF16, fp8, false,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "KV write kernel launch");
+    return MIATTN_OK;
+}
+
+miattn_status attn_fwd_paged_append(const void *q, const void *k_new, const void *v_new,
+                                    void *k_cache, void *v_cache, const int32_t *cache_seqlens,
+                                    const int32_t *block_table, const int32_t *cu_seqlens_q,
+                                    int page_size, int causal, float softcap, void *o,
+                                    float *lse, int B, int total_q, int max_seqlen_q, int Hq,
+                                    int Hkv, int D, int max_pages, int num_phys_pages,
+                                    float scale, miattn_dtype dtype, void *stream) {
+    if (B > 0 && total_q > 0 && max_seqlen_q > 0) {
+        if (!k_new || !v_new) {
+            g_err[0] = '\0';
+            return fail(MIATTN_ERR_INVALID_ARG, "k_new and v_new must not be NULL");
+        }
+        if (!aligned16(k_new) || !aligned16(v_new)) {
+            g_err[0] = '\0';
+            return fail(MIATTN_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+        }
+    }
+    miattn::KvWriteParams w = {};
+    w.k = (const uint16_t *)k_new;
+    w.v = (const uint16_t *)v_new;
+    return paged_call(q, k_cache, v_cache, cache_seqlens, block_table, page_size, causal, -1,
+                      -1, softcap, true, cu_seqlens_q, total_q, nullptr, o, lse, B,
+                      max_seqlen_q, Hq, Hkv, D, max_pages, num_phys_pages, scale, dtype, stream,
+                      &w);
 }
 
 miattn_status miattn_release_workspace(void) {

@@ -179,6 +179,66 @@ def test_varlen_empty_calls_are_ok_without_touching_the_device():
     assert paged_varlen(tq=0, q=None, o=None)[0] == 0
 
 
+def kvw(**kw):
+    a = dict(k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, sl=FAKE, tokens=4, Hkv=2, D=128, num_slots=64,
+             dtype=0, cache=0, ks=None, vs=None, stream=None)
+    a.update(kw)
+    L = mi.lib()
+    st = L.kv_cache_write(a["k"], a["v"], a["kp"], a["vp"], a["sl"], a["tokens"], a["Hkv"],
+                          a["D"], a["num_slots"], a["dtype"], a["cache"], a["ks"], a["vs"],
+                          a["stream"])
+    return st, L.miattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(tokens=-1), 1, "tokens=-1"),
+    (dict(D=0), 1, "must be positive"),
+    (dict(num_slots=-5), 1, "num_slots"),
+    (dict(dtype=3), 2, "dtype 3"),
+    (dict(cache=1), 2, "cache_dtype 1 must equal dtype 0"),
+    (dict(Hkv=1, D=12), 2, "multiple of 8"),
+    (dict(sl=None), 1, "must not be NULL"),
+    (dict(k=FAKE + 8), 1, "16-byte aligned"),
+    (dict(kp=FAKE + 8), 1, "16-byte aligned"),
+    (dict(sl=FAKE + 4), 1, "8-byte aligned"),
+    (dict(cache=2), 1, "needs 4-byte aligned k_scale"),
+    (dict(cache=2, ks=FAKE, vs=FAKE, kp=FAKE + 4), 1, "8-byte aligned"),
+])
+def test_kv_write_refusals(kw, status, needle):
+    st, msg = kvw(**kw)
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_kv_write_without_tokens_is_ok_without_touching_the_device():
+    assert kvw(tokens=0, k=None, v=None, kp=None, vp=None, sl=None)[0] == 0
+
+
+def append_call(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, bt=FAKE, cq=FAKE,
+             page_size=64, causal=1, softcap=0.0, o=FAKE, lse=None, B=2, tq=5, mq=4, Hq=8,
+             Hkv=2, D=128, max_pages=4, n_phys=8, scale=NAN, dtype=0, stream=None)
+    a.update(kw)
+    L = mi.lib()
+    st = L.attn_fwd_paged_append(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["lens"],
+                                 a["bt"], a["cq"], a["page_size"], a["causal"], a["softcap"],
+                                 a["o"], a["lse"], a["B"], a["tq"], a["mq"], a["Hq"], a["Hkv"],
+                                 a["D"], a["max_pages"], a["n_phys"], a["scale"], a["dtype"],
+                                 a["stream"])
+    return st, L.miattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(kn=None), 1, "k_new and v_new must not be NULL"),
+    (dict(vn=FAKE + 2), 1, "16-byte aligned"),
+    (dict(cq=None), 1, "cu_seqlens_q must not be NULL"),
+    (dict(page_size=20), 2, "page_size=20"),
+    (dict(softcap=-3.0), 1, "softcap"),
+])
+def test_paged_append_refusals(kw, status, needle):
+    st, msg = append_call(**kw)
+    assert st == status and needle in msg, (st, msg)
+
+
 def test_python_binding_maps_refusals_to_value_error():
     import torch
     st, _ = dense(Hq=5, Hkv=2)
