@@ -69,6 +69,8 @@ def _load():
                                            i32, *win, P, P, P]
         lib.oracle_attn_paged_varlen.argtypes = [P, P, P, P, P, i32, P, i32, *win, P, i32, i32,
                                                  i32, i32, i32, i32, f32, i32, P, P]
+        lib.oracle_attn_bwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32,
+                                        i32, P, P, P]
         lib.oracle_e4m3_decode.argtypes = [i32]
         lib.oracle_e4m3_decode.restype = ctypes.c_double
         lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
@@ -78,6 +80,7 @@ def _load():
         for name in ("oracle_attn_dense", "oracle_attn_dense_rows", "oracle_attn_paged",
                      "oracle_attn_paged_rows", "oracle_attn_varlen", "oracle_attn_paged_varlen",
                      "oracle_e4m3_encode", "oracle_kv_write", "oracle_attn_paged_append",
+                     "oracle_attn_bwd",
                      "oracle_num_threads"):
             getattr(lib, name).restype = i32
         _lib = lib
@@ -315,6 +318,35 @@ def attn_paged_varlen(q, k_cache, v_cache, cache_seqlens, block_table, page_size
     return o, lse
 
 
+def _f64(x) -> np.ndarray:
+    import torch
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def attn_bwd(q, k, v, o, do, lse, *, scale=None, causal=True, dtype=None):
+    """Gradients of the dense call: q/do [B,Sq,Hq,D] and k/v [B,Skv,Hkv,D] as
+    bf16/fp16 tensors (or uint16 patterns with ``dtype``); o [B,Sq,Hq,D] and
+    lse [B,Hq,Sq] as any floats (taken exactly, as float64).  Returns dq, dk, dv
+    (float64)."""
+    dt = _dtype_code(q) if dtype is None else dtype
+    qb, kb, vb, dob = _bits(q), _bits(k), _bits(v), _bits(do)
+    B, Sq, Hq, D = qb.shape
+    _, Skv, Hkv, _ = kb.shape
+    of, lf = _f64(o), _f64(lse)
+    assert of.shape == (B, Sq, Hq, D) and lf.shape == (B, Hq, Sq)
+    dq = np.zeros((B, Sq, Hq, D), np.float64)
+    dk = np.zeros((B, Skv, Hkv, D), np.float64)
+    dv = np.zeros((B, Skv, Hkv, D), np.float64)
+    rc = _load().oracle_attn_bwd(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(of), _ptr(dob), _ptr(lf), dt,
+                                 B, Hq, Hkv, Sq, Skv, D, _scale_arg(scale), int(bool(causal)),
+                                 _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd rejected the call (rc={rc})")
+    return dq, dk, dv
+
+
 def e4m3_encode(x: float) -> int:
     """E4M3FN code of x (nearest, ties to even; NaN kept; |x| > 448 -> +-448)."""
     return _load().oracle_e4m3_encode(float(x))
@@ -382,4 +414,5 @@ def attn_paged_append(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_ta
 
 __all__ = ["BF16", "FP16", "build", "decode", "resolve_scale", "num_threads", "attn_dense",
            "attn_dense_rows", "attn_paged", "attn_paged_rows", "attn_varlen",
-           "attn_paged_varlen", "e4m3_encode", "e4m3_decode", "kv_write", "attn_paged_append"]
+           "attn_paged_varlen", "e4m3_encode", "e4m3_decode", "kv_write", "attn_paged_append",
+           "attn_bwd"]

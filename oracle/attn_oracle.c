@@ -27,6 +27,12 @@
  *     key_padding_mask [B, S_kv], True = keep, False sets the column to -inf.
  *   - MATE "QSA", Core Attention: the log-sum-exp is natural-log and an empty
  *     selection returns zero output with -inf LSE.
+ *   - TileOPs "Attention Operators", GQABwdOp: given q, k, v, o, do and lse,
+ *     the gradients dq, dk, dv of O = softmax(alpha Q K^T + M) V (the
+ *     standard softmax-attention backward, with P recomputed from the given
+ *     lse and D_i = sum_d dO_id O_id from the given o); RL-Kernel "Standard
+ *     Softmax Attention", Fixed Reduction Order: dK/dV of a KV head sum over
+ *     its query heads in group order, then over query positions.
  *   - TileOPs "Attention Operators", PagedKVCacheWriteFwdOp: each token's K
  *     and V row goes to the pool row its slot names (page * page_size +
  *     offset; -1 skips the token); an FP8 pool stores row / scale as
@@ -532,6 +538,69 @@ int oracle_attn_paged_varlen(const uint16_t *q, const uint16_t *k_cache,
     c.total_q = total_q;
     c.sinks = sinks;
     return run_all(&c, o, lse);
+}
+
+/* ---------------------------------------------------------------- backward
+ *
+ * Dense call, inputs as for oracle_attn_dense plus o [B,Sq,Hq,D] and lse
+ * [B,Hq,Sq] as doubles (exact copies of whatever the caller holds) and do
+ * [B,Sq,Hq,D] 16-bit patterns.  With s_ij = alpha <q_i, k_j> over visible keys,
+ *     P_ij = exp(s_ij - lse_i),  dP_ij = <dO_i, v_j>,  D_i = <dO_i, o_i>,
+ *     dS_ij = P_ij (dP_ij - D_i),
+ *     dq_i = alpha sum_j dS_ij k_j,  dk_j = alpha sum_i dS_ij q_i,
+ *     dv_j = sum_i P_ij dO_i,
+ * the sums over i running over the query heads of the KV head in group order,
+ * then over query positions.  A row with lse = -inf (no visible key)
+ * contributes nothing.  Writes dq [B,Sq,Hq,D], dk and dv [B,Skv,Hkv,D]. */
+int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const double *o,
+                    const uint16_t *dout, const double *lse, int dtype, int B, int Hq, int Hkv,
+                    int Sq, int Skv, int D, float scale, int causal, double *dq, double *dk,
+                    double *dv)
+{
+    call_t c;
+    if (make_dense(&c, q, k, v, dtype, B, Hq, Hkv, Sq, Skv, D, scale, causal, -1, -1, 0.0f,
+                   NULL))
+        return -1;
+    const int g = Hq / Hkv;
+    const double alpha = c.alpha;
+    memset(dq, 0, sizeof(double) * (size_t)B * Sq * Hq * D);
+    memset(dk, 0, sizeof(double) * (size_t)B * Skv * Hkv * D);
+    memset(dv, 0, sizeof(double) * (size_t)B * Skv * Hkv * D);
+    /* one KV head at a time: its dk/dv rows are only touched here, and each
+     * query row's dq only by its own head */
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b)
+        for (int r = 0; r < Hkv; ++r)
+            for (int local = 0; local < g; ++local) {
+                const int h = r * g + local;
+                for (int i = 0; i < Sq; ++i) {
+                    const double l_i = lse[((int64_t)b * Hq + h) * Sq + i];
+                    if (l_i == -INFINITY)
+                        continue;
+                    const int64_t qo = (((int64_t)b * Sq + i) * Hq + h) * D;
+                    double Di = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        Di += decode(dout, qo + d, dtype) * o[qo + d];
+                    for (int64_t j = 0; j < Skv; ++j) {
+                        if (!visible(&c, b, i, j))
+                            continue;
+                        const int64_t ko = kv_row_offset(&c, b, j, r);
+                        double s = 0.0, dp = 0.0;
+                        for (int d = 0; d < D; ++d) {
+                            s += decode(q, qo + d, dtype) * decode(k, ko + d, dtype);
+                            dp += decode(dout, qo + d, dtype) * decode(v, ko + d, dtype);
+                        }
+                        const double p = exp(alpha * s - l_i);
+                        const double ds = p * (dp - Di);
+                        for (int d = 0; d < D; ++d) {
+                            dq[qo + d] += alpha * ds * decode(k, ko + d, dtype);
+                            dk[ko + d] += alpha * ds * decode(q, qo + d, dtype);
+                            dv[ko + d] += p * decode(dout, qo + d, dtype);
+                        }
+                    }
+                }
+            }
+    return 0;
 }
 
 /* ---------------------------------------------------------------- FP8 E4M3FN

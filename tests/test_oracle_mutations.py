@@ -67,12 +67,23 @@ MUTANTS = {
     "append_position_off_by_one": ("int64_t pos = (int64_t)cache_seqlens[b] + (i - cu_q[b]);",
                                    "int64_t pos = (int64_t)cache_seqlens[b] + (i - cu_q[b]) + 1;"),
     "append_lengths_not_grown": ("lens[b] = cache_seqlens[b] + (cu_q[b + 1] - cu_q[b]);", "lens[b] = cache_seqlens[b];"),
+    "bwd_D_ignores_o": ("Di += decode(dout, qo + d, dtype) * o[qo + d];", "Di += 0.0 * o[qo + d];"),
+    "bwd_dq_unscaled": ("dq[qo + d] += alpha * ds * decode(k, ko + d, dtype);",
+                        "dq[qo + d] += ds * decode(k, ko + d, dtype);"),
+    "bwd_dv_uses_dS": ("dv[ko + d] += p * decode(dout, qo + d, dtype);",
+                       "dv[ko + d] += ds * decode(dout, qo + d, dtype);"),
+    "bwd_dk_reads_k": ("dk[ko + d] += alpha * ds * decode(q, qo + d, dtype);",
+                       "dk[ko + d] += alpha * ds * decode(k, ko + d, dtype);"),
+    "bwd_lse_unshifted": ("const double p = exp(alpha * s - l_i);", "const double p = exp(alpha * s);"),
+    "bwd_dp_uses_k": ("dp += decode(dout, qo + d, dtype) * decode(v, ko + d, dtype);",
+                      "dp += decode(dout, qo + d, dtype) * decode(k, ko + d, dtype);"),
     "value_sum_skips_first_key": ("for (int64_t j = 0; j < n; ++j) {\n            if (!visible(c, b, i, j))\n                continue;\n            acc +=",
                                   "for (int64_t j = 1; j < n; ++j) {\n            if (!visible(c, b, i, j))\n                continue;\n            acc +="),
 }
 
 PIN_FILES = ["test_oracle_pins.py", "test_oracle_pins_window_softcap.py",
-             "test_oracle_pins_varlen_sinks.py", "test_oracle_pins_kv_write.py"]
+             "test_oracle_pins_varlen_sinks.py", "test_oracle_pins_kv_write.py",
+             "test_oracle_pins_bwd.py"]
 
 PLUGIN = "import os, oracle\noracle._LIB = os.environ['ORACLE_MUTANT_LIB']\n"
 
