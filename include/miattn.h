@@ -29,6 +29,8 @@
  *     gives zero output and -inf LSE, split-KV partials are merged in FP32
  *     without recomputing QK or PV, and wrappers check shapes and layout
  *     without reading device contents.
+ *   - TileOPs "Attention Operators", GQABwdOp: the gradients dq, dk, dv from
+ *     q, k, v, o, do and lse, BSHD.
  *   - TileOPs "Attention Operators", PagedKVCacheWriteFwdOp: each token's key
  *     and value rows go to the pool row its slot names (page * page_size +
  *     offset, -1 skipping the token); an FP8 pool stores row / scale as
@@ -273,6 +275,34 @@ miattn_status attn_fwd_paged_append(const void *q, const void *k_new, const void
                                     float *lse, int B, int total_q, int max_seqlen_q, int Hq,
                                     int Hkv, int D, int max_pages, int num_phys_pages,
                                     float scale, miattn_dtype dtype, void *stream);
+
+/*
+ * Attention backward (TileOPs "Attention Operators", GQABwdOp): the gradients
+ * of the dense call's output with respect to q, k and v,
+ *     P = exp(alpha q.k - lse) on visible keys,  dS = P (dO.v - <dO, o>),
+ *     dq = alpha dS k,  dk = alpha dS^T q (summed over the g query heads of a
+ *     KV head),  dv = P^T dO,
+ * recomputing P from the forward's lse (no score matrix is stored).
+ *
+ *   q, o, dout device, [B, Sq, Hq, D] dtype (o: the forward's output, dout:
+ *              the gradient of the loss with respect to it)
+ *   k, v       device, [B, Skv, Hkv, D] dtype
+ *   lse        device, [B, Hq, Sq] float32, natural log, as attn_fwd_dense
+ *              writes it (-inf for a row that sees no key)
+ *   B, Hq, Hkv, Sq, Skv, scale, causal, dtype, stream  as for attn_fwd_dense
+ *              (no window, softcap or padding mask); D in {64, 128} (256
+ *              returns MIATTN_ERR_UNSUPPORTED)
+ *   dq         device, [B, Sq, Hq, D] dtype, written in full
+ *   dk, dv     device, [B, Skv, Hkv, D] dtype, written in full
+ *
+ * Accumulation is FP32; every output element has one writer (no atomics), so
+ * repeated calls give the same bits.  Uses the library workspace for
+ * 2 * B * Hq * Sq floats.
+ */
+miattn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                       const void *dout, const float *lse, int B, int Hq, int Hkv, int Sq, int Skv,
+                       int D, float scale, int causal, void *dq, void *dk, void *dv,
+                       miattn_dtype dtype, void *stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *miattn_last_error(void);

@@ -22,7 +22,7 @@ MIATTN_CACHE_BF16, MIATTN_CACHE_FP16, MIATTN_CACHE_FP8_E4M3 = 0, 1, 2
 
 # every symbol include/miattn.h declares
 EXPORTS = ("attn_fwd_dense", "attn_fwd_paged", "attn_fwd_varlen", "attn_fwd_paged_varlen",
-           "kv_cache_write", "attn_fwd_paged_append", "miattn_last_error", "miattn_release_workspace", "miattn_set_split_keys",
+           "kv_cache_write", "attn_fwd_paged_append", "attn_bwd", "miattn_last_error", "miattn_release_workspace", "miattn_set_split_keys",
            "miattn_profile_start", "miattn_profile_stop")
 
 _lib = None
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_paged_append.argtypes = [P, P, P, P, P, P, P, P, i32, i32, f32, P, P, i32,
                                             i32, i32, i32, i32, i32, i32, i32, f32, i32, P]
         L.attn_fwd_paged_append.restype = i32
+        L.attn_bwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, P, P,
+                               i32, P]
+        L.attn_bwd.restype = i32
         L.miattn_last_error.argtypes = []
         L.miattn_last_error.restype = ctypes.c_char_p
         L.miattn_release_workspace.argtypes = []
@@ -440,6 +443,37 @@ def attn_fwd_paged_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
                                        Hkv, D, block_table.shape[1], num_slots // page_size,
                                        _scale(scale), code, _stream()))
     return o, (lse if return_lse else None)
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+             do: torch.Tensor, lse: torch.Tensor, *, scale=None, causal: bool = True
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Attention backward on the current stream: q/o/do [B,Sq,Hq,D], k/v
+    [B,Skv,Hkv,D] (bf16 or fp16), lse [B,Hq,Sq] fp32 from attn_fwd_dense.
+    Returns (dq, dk, dv) in the input dtype."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be rank 4 (BSHD)")
+    if o.shape != q.shape or do.shape != q.shape or k.shape != v.shape:
+        raise ValueError("o and do must have q's shape, v k's shape")
+    if k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("q and k must agree on B and D")
+    if any(t.dtype != q.dtype for t in (k, v, o, do)):
+        raise ValueError("q, k, v, o, do must share one dtype")
+    code = _dtype_code(q)
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError(f"lse must be float32 [B, Hq, Sq] = [{B}, {Hq}, {Sq}]")
+    dev = q.device
+    if not all(t.is_cuda and t.device == dev for t in (q, k, v, o, do, lse)):
+        raise ValueError("all tensors must be on one GPU device")
+    q, k, v, o, do, lse = (t.contiguous() for t in (q, k, v, o, do, lse))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), B, Hq, Hkv,
+                          Sq, Skv, D, _scale(scale), int(bool(causal)), _ptr(dq), _ptr(dk),
+                          _ptr(dv), code, _stream()))
+    return dq, dk, dv
 
 
 def set_split_keys(keys_per_split: int) -> None:

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libmiattn.so")
 # in parallel
 UNITS = [("attn_fwd.hip", [f"-DMIATTN_KD={d}", f"-DMIATTN_KCAP={c}"])
          for d in (64, 128, 256) for c in (0, 1)] + [("lse_merge.hip", []), ("kv_write.hip", []),
-                                                  ("miattn.hip", [])]
+                                                  ("attn_bwd.hip", []), ("miattn.hip", [])]
 SOURCES = sorted({u[0] for u in UNITS})
 ARCH = "gfx950"
 

@@ -130,6 +130,23 @@ int attn_fwd_decode_blocks_per_cu(const FwdParams &p, int D, bool bf16, bool pag
 
 hipError_t launch_lse_merge(const MergeParams &p, int D, bool bf16, hipStream_t stream);
 
+// Attention backward (attn_bwd.hip): dq [B,Sq,Hq,D], dk and dv [B,Skv,Hkv,D]
+// from q, k, v, o, do (16-bit, BSHD) and lse [B,Hq,Sq]; d_rows and lse2_rows
+// ([B,Hq,Sq] fp32, library workspace) carry <dO_i, o_i> and lse_i log2(e).
+struct BwdParams {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float *lse;
+    uint16_t *dq, *dk, *dv;
+    float *d_rows, *lse2_rows;
+    int B, Sq, Skv, Hq, Hkv, G;
+    int rows;       // Sq * G packed rows per (batch, KV head)
+    int n_mblocks;  // ceil(rows / 128)
+    int causal;
+    float scale;       // alpha
+    float scale_log2;  // alpha log2(e)
+};
+hipError_t launch_attn_bwd(const BwdParams &p, int D, bool bf16, hipStream_t stream);
+
 // Paged KV-cache write (kv_write.hip): token n's K and V rows ([row_elems]
 // 16-bit values) go to pool row slot(n) -- slot_mapping[n], or in append mode
 // the position cache_seqlens[b] + i of the packed chunk's token i of request

@@ -790,6 +790,82 @@ miattn_status attn_fwd_paged_append(const void *q, const void *k_new, const void
                       &w);
 }
 
+miattn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                       const void *dout, const float *lse, int B, int Hq, int Hkv, int Sq, int Skv,
+                       int D, float scale, int causal, void *dq, void *dk, void *dv,
+                       miattn_dtype dtype, void *stream) {
+    g_err[0] = '\0';
+    miattn_status st = check_common(q, dq, const_cast<float *>(lse), B, Sq, Hq, Hkv, D, scale, dtype);
+    if (st != MIATTN_OK) return st;
+    if (D == 256) return fail(MIATTN_ERR_UNSUPPORTED, "D=256 unsupported by the backward (64, 128)");
+    if (Skv < 0) return fail(MIATTN_ERR_INVALID_ARG, "negative dimension: Skv=%d", Skv);
+    if (causal != 0 && causal != 1)
+        return fail(MIATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
+    if ((int64_t)B * Skv > INT_MAX || (int64_t)B * Sq * Hq > INT_MAX)
+        return fail(MIATTN_ERR_UNSUPPORTED, "B*Skv or B*Sq*Hq exceeds %d rows", INT_MAX);
+    if (B == 0 || (Sq == 0 && Skv == 0)) return MIATTN_OK;
+    if (Skv > 0) {
+        if (!k || !v || !dk || !dv)
+            return fail(MIATTN_ERR_INVALID_ARG, "k, v, dk and dv must not be NULL");
+        if (!aligned16(k) || !aligned16(v) || !aligned16(dk) || !aligned16(dv))
+            return fail(MIATTN_ERR_INVALID_ARG, "k, v, dk and dv must be 16-byte aligned");
+    }
+    if (Sq > 0) {
+        if (!o || !dout || !lse)
+            return fail(MIATTN_ERR_INVALID_ARG, "o, do and lse must not be NULL");
+        if (!aligned16(o) || !aligned16(dout))
+            return fail(MIATTN_ERR_INVALID_ARG, "o and do must be 16-byte aligned");
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MIATTN_ERR_UNSUPPORTED, "device %d", dev);
+    hipStream_t s = (hipStream_t)stream;
+    if (Sq == 0) {
+        // no query: every key gradient is zero
+        const size_t bytes = (size_t)B * Skv * Hkv * D * 2;
+        e = hipMemsetAsync(dk, 0, bytes, s);
+        if (e == hipSuccess) e = hipMemsetAsync(dv, 0, bytes, s);
+        return e == hipSuccess ? MIATTN_OK : hip_fail(e, "hipMemsetAsync");
+    }
+    miattn::BwdParams p = {};
+    p.q = (const uint16_t *)q;
+    p.k = (const uint16_t *)k;
+    p.v = (const uint16_t *)v;
+    p.o = (const uint16_t *)o;
+    p.dout = (const uint16_t *)dout;
+    p.lse = lse;
+    p.dq = (uint16_t *)dq;
+    p.dk = (uint16_t *)dk;
+    p.dv = (uint16_t *)dv;
+    p.B = B;
+    p.Sq = Sq;
+    p.Skv = Skv;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = Hq / Hkv;
+    p.rows = Sq * p.G;
+    p.n_mblocks = (p.rows + 127) / 128;
+    p.causal = causal;
+    const float alpha = resolve_scale(scale, D);
+    p.scale = alpha;
+    p.scale_log2 = alpha * 1.4426950408889634f;
+    const size_t nrows = (size_t)B * Hq * Sq;
+    void *ws = nullptr;
+    st = workspace(dev, nrows * 2 * sizeof(float), &ws);
+    if (st != MIATTN_OK) return st;
+    p.d_rows = (float *)ws;
+    p.lse2_rows = p.d_rows + nrows;
+    if (Skv == 0) {
+        // no key: every query gradient is zero
+        e = hipMemsetAsync(dq, 0, (size_t)B * Sq * Hq * D * 2, s);
+        return e == hipSuccess ? MIATTN_OK : hip_fail(e, "hipMemsetAsync");
+    }
+    e = timed_launch(0, s, [&] { return miattn::launch_attn_bwd(p, D, dtype == MIATTN_BF16, s); });
+    if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+    return MIATTN_OK;
+}
+
 miattn_status miattn_release_workspace(void) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
