@@ -11,6 +11,8 @@ with inputs resident in HBM.  The same line carries:
                 Hkv=8, D=128, page 64, lengths U[512, 8192]) against HBM peak,
                 timed per call, rotating over three copies of the caches so
                 that no call finds its data in the last-level cache;
+  backward      the attention backward (dq, dk, dv) of the same prefill,
+                TFLOP/s counting 10*D flops per visible triple;
   cpu_baseline  the fp64 CPU oracle on a bounded row sample of the prefill
                 workload, on this host's cores.
 
@@ -153,6 +155,34 @@ def time_decode(mi, w, steps, warmup, copies=3):
             "cache_copies": copies}
 
 
+def time_backward(mi, w, steps, warmup):
+    """Backward of the causal prefill: TFLOP/s counting 10 * D flops per
+    visible (query, key, query-head) triple (five products of 2 * D:
+    recomputed scores, dP, dV, dK, dQ)."""
+    import torch
+    dev = "cuda:0"
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    do = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
+    o, lse = mi.attn_fwd_dense(q, k, v, scale=w.scale, causal=True)
+    for _ in range(warmup):
+        mi.attn_bwd(q, k, v, o, do, lse, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        mi.attn_bwd(q, k, v, o, do, lse, scale=w.scale, causal=True)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    triples = visible_pairs(w.B, w.Hq, w.Sq, [w.Skv] * w.B, True)
+    tflops = 10 * w.D * triples / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "value": tflops, "unit": "TFLOP/s", "ms_per_call": ms,
+            "flops_per_call": 10 * w.D * triples, "counted": "10*D per visible triple",
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS}}
+
+
 def cpu_baseline(w, target_s=12.0):
     """The fp64 oracle on a bounded sample of the prefill workload's rows."""
     import numpy as np
@@ -188,6 +218,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="time one workload and print its line (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -281,6 +312,15 @@ def main():
                          "kernel_avg_us": d["attn_kernel_ms"] * 1e3,
                          "merge_kernel_avg_us": d["merge_kernel_ms"] * 1e3}}
         del wd
+
+    if not args.no_backward:
+        # the backward of the same prefill (dq, dk, dv from q, k, v, o, do, lse)
+        w = workloads.make(2)
+        bw = time_backward(mi, w, max(args.steps // 5, 5), 3)
+        line["backward"] = bw
+        print(f"[bench] backward {w.name}: {bw['ms_per_call'] * 1e3:.1f} us, "
+              f"{bw['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del w
 
     if not args.no_cpu_baseline:
         w = workloads.make(2)
