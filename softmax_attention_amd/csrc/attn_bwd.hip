@@ -26,6 +26,8 @@
 // with a two-buffer ring and one workgroup barrier per tile.
 #include "attn_kernels.h"
 
+#include <type_traits>
+
 #include "attn_device.h"
 
 namespace miattn {
@@ -353,82 +355,98 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams 
             adk[t][r] = 0.f;
         }
 
-    u32x4 rq[G::CPT], ro[G::CPT];
-    float rl = INFINITY, rd = 0.f;
-    auto fetch = [&](int r0) __attribute__((always_inline)) {
+    // Tiles are fetched two ahead into two register sets (tile n in set n & 1)
+    // so that a tile's global loads have two compute steps to arrive: with one
+    // wave per SIMD nothing else hides their latency.
+    u32x4 rq[2][G::CPT], ro[2][G::CPT];
+    float rl[2] = {INFINITY, INFINITY}, rd[2] = {0.f, 0.f};
+    auto fetch = [&](auto set_tag, int r0) __attribute__((always_inline)) {
+        constexpr int S = decltype(set_tag)::value;
 #pragma unroll
         for (int e = 0; e < G::CPT; ++e) {
             const int ch = tid + e * 64 * kBwdWaves;
             const int r = min(r0 + ch / (D / 8), p.rows - 1), cc = ch % (D / 8);
             const int i = r / p.G, h = kvh * p.G + (r - i * p.G);
             const int64_t off = (((int64_t)b * p.Sq + i) * p.Hq + h) * D + 8 * cc;
-            rq[e] = *(const u32x4 *)(p.q + off);
-            ro[e] = *(const u32x4 *)(p.dout + off);
+            rq[S][e] = *(const u32x4 *)(p.q + off);
+            ro[S][e] = *(const u32x4 *)(p.dout + off);
         }
         if (tid < kBwdRows) {
             const int r = r0 + tid;
             if (r < p.rows) {
                 const int i = r / p.G, h = kvh * p.G + (r - i * p.G);
                 const int64_t at = ((int64_t)b * p.Hq + h) * p.Sq + i;
-                rl = p.lse2_rows[at];
-                rd = p.d_rows[at];
+                rl[S] = p.lse2_rows[at];
+                rd[S] = p.d_rows[at];
             } else {
-                rl = INFINITY;  // a padding row: P = 0
-                rd = 0.f;
+                rl[S] = INFINITY;  // a padding row: P = 0
+                rd[S] = 0.f;
             }
         }
     };
-    auto stash = [&](int buf) __attribute__((always_inline)) {
+    auto stash = [&](auto set_tag, int buf) __attribute__((always_inline)) {
+        constexpr int S = decltype(set_tag)::value;
 #pragma unroll
         for (int e = 0; e < G::CPT; ++e) {
             const int ch = tid + e * 64 * kBwdWaves;
             const int r = ch / (D / 8), cc = ch % (D / 8);
-            *(u32x4 *)(&sQ[buf][tile_off<D>(r, cc)]) = rq[e];
-            *(u32x4 *)(&sO[buf][tile_off<D>(r, cc)]) = ro[e];
+            *(u32x4 *)(&sQ[buf][tile_off<D>(r, cc)]) = rq[S][e];
+            *(u32x4 *)(&sO[buf][tile_off<D>(r, cc)]) = ro[S][e];
         }
         if (tid < kBwdRows) {
-            sL[buf][tid] = rl;
-            sD[buf][tid] = rd;
+            sL[buf][tid] = rl[S];
+            sD[buf][tid] = rd[S];
         }
     };
+    auto compute = [&](int r0, int cur) __attribute__((always_inline)) {
+        // rows [r0, r0 + 32): skip when none of them sees any of the wave's keys
+        if (r0 + kBwdRows - 1 < wave_thr_lo) return;
+        const f32x16 s = tile_times_regs<D, BF16>(sQ[cur], la, kf);   // S
+        const f32x16 dp = tile_times_regs<D, BF16>(sO[cur], la, vf);  // dP
+        const bool full = r0 >= wave_thr_hi;
+        f32x16 pr, ds;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            // registers 4 q4 .. 4 q4 + 3 hold rows 8 q4 + 4 hl + 0..3
+            const f32x4 l4 = *(const f32x4 *)(&sL[cur][8 * q4 + 4 * hl]);
+            const f32x4 d4 = *(const f32x4 *)(&sD[cur][8 * q4 + 4 * hl]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q4 + e;
+                const bool vis = full || (r0 + 8 * q4 + 4 * hl + e >= my_thr);
+                const float x = vis ? fast_exp2(__builtin_fmaf(s[r], c, -l4[e])) : 0.f;
+                pr[r] = x;
+                ds[r] = x * (dp[r] - d4[e]);
+            }
+        }
+        vec8 pb[G::PSTEPS], dsb[G::PSTEPS];
+        pack_scores<BF16>(pr, pb);
+        pack_scores<BF16>(ds, dsb);
+        tileT_times_packed<D, BF16>(sO[cur], la, pb, adv);   // dV^T += dO^T P
+        tileT_times_packed<D, BF16>(sQ[cur], la, dsb, adk);  // dK^T += Q^T dS
+    };
+    // step on tile n (in LDS buffer n & 1, rows from r0): fetch tile n + 2
+    // into set n & 1, compute tile n, stash tile n + 1 from set (n + 1) & 1
+    using Z = std::integral_constant<int, 0>;
+    using O = std::integral_constant<int, 1>;
 
     if (key0 < p.Skv && wg_row0 < p.rows) {
-        fetch(wg_row0);
-        stash(0);
+        fetch(Z{}, wg_row0);
+        if (wg_row0 + kBwdRows < p.rows) fetch(O{}, wg_row0 + kBwdRows);
+        stash(Z{}, 0);
         __syncthreads();
-        int cur = 0;
-        for (int r0 = wg_row0; r0 < p.rows; r0 += kBwdRows) {
-            const bool more = r0 + kBwdRows < p.rows;
-            if (more) fetch(r0 + kBwdRows);
-            // rows [r0, r0 + 32): skip when none of them sees any of the wave's keys
-            if (r0 + kBwdRows - 1 >= wave_thr_lo) {
-                const f32x16 s = tile_times_regs<D, BF16>(sQ[cur], la, kf);   // S
-                const f32x16 dp = tile_times_regs<D, BF16>(sO[cur], la, vf);  // dP
-                const bool full = r0 >= wave_thr_hi;
-                f32x16 pr, ds;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    // registers 4 q4 .. 4 q4 + 3 hold rows 8 q4 + 4 hl + 0..3
-                    const f32x4 l4 = *(const f32x4 *)(&sL[cur][8 * q4 + 4 * hl]);
-                    const f32x4 d4 = *(const f32x4 *)(&sD[cur][8 * q4 + 4 * hl]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * q4 + e;
-                        const bool vis = full || (r0 + 8 * q4 + 4 * hl + e >= my_thr);
-                        const float x = vis ? fast_exp2(__builtin_fmaf(s[r], c, -l4[e])) : 0.f;
-                        pr[r] = x;
-                        ds[r] = x * (dp[r] - d4[e]);
-                    }
-                }
-                vec8 pb[G::PSTEPS], dsb[G::PSTEPS];
-                pack_scores<BF16>(pr, pb);
-                pack_scores<BF16>(ds, dsb);
-                tileT_times_packed<D, BF16>(sO[cur], la, pb, adv);   // dV^T += dO^T P
-                tileT_times_packed<D, BF16>(sQ[cur], la, dsb, adk);  // dK^T += Q^T dS
-            }
-            if (more) stash(cur ^ 1);
+        for (int r0 = wg_row0; r0 < p.rows; r0 += 2 * kBwdRows) {
+            // tile n even: set 0 is free, tile n + 1 waits in set 1
+            if (r0 + 2 * kBwdRows < p.rows) fetch(Z{}, r0 + 2 * kBwdRows);
+            compute(r0, 0);
+            if (r0 + kBwdRows < p.rows) stash(O{}, 1);
             __syncthreads();
-            cur ^= 1;
+            if (r0 + kBwdRows >= p.rows) break;
+            // tile n + 1 (odd): set 1 is free, tile n + 2 waits in set 0
+            if (r0 + 3 * kBwdRows < p.rows) fetch(O{}, r0 + 3 * kBwdRows);
+            compute(r0 + kBwdRows, 1);
+            if (r0 + 2 * kBwdRows < p.rows) stash(Z{}, 0);
+            __syncthreads();
         }
     }
     if (!key_ok) return;
