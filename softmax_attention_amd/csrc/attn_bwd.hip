@@ -252,54 +252,64 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const BwdParams p)
 
     // tile loads: thread chunk e of the tile -> row, 16-byte chunk
     const int64_t kv_base = ((int64_t)b * p.Skv * p.Hkv + kvh) * D;
-    u32x4 rk[G::CPT], rv[G::CPT];
-    auto fetch = [&](int j0) __attribute__((always_inline)) {
+    // key tiles fetched two ahead into two register sets (tile n in set n & 1)
+    u32x4 rk[2][G::CPT], rv[2][G::CPT];
+    auto fetch = [&](auto set_tag, int j0) __attribute__((always_inline)) {
+        constexpr int S = decltype(set_tag)::value;
 #pragma unroll
         for (int e = 0; e < G::CPT; ++e) {
             const int ch = tid + e * 64 * kBwdWaves;
             const int r = ch / (D / 8), cc = ch % (D / 8);
             const int key = min(j0 + r, p.Skv - 1);
             const int64_t off = kv_base + (int64_t)key * p.Hkv * D + 8 * cc;
-            rk[e] = *(const u32x4 *)(p.k + off);
-            rv[e] = *(const u32x4 *)(p.v + off);
+            rk[S][e] = *(const u32x4 *)(p.k + off);
+            rv[S][e] = *(const u32x4 *)(p.v + off);
         }
     };
-    auto stash = [&](int buf) __attribute__((always_inline)) {
+    auto stash = [&](auto set_tag, int buf) __attribute__((always_inline)) {
+        constexpr int S = decltype(set_tag)::value;
 #pragma unroll
         for (int e = 0; e < G::CPT; ++e) {
             const int ch = tid + e * 64 * kBwdWaves;
             const int r = ch / (D / 8), cc = ch % (D / 8);
-            *(u32x4 *)(&sK[buf][tile_off<D>(r, cc)]) = rk[e];
-            *(u32x4 *)(&sV[buf][tile_off<D>(r, cc)]) = rv[e];
+            *(u32x4 *)(&sK[buf][tile_off<D>(r, cc)]) = rk[S][e];
+            *(u32x4 *)(&sV[buf][tile_off<D>(r, cc)]) = rv[S][e];
         }
     };
+    auto compute = [&](int j0, int cur) __attribute__((always_inline)) {
+        if (j0 > wave_last) return;
+        const f32x16 s = tile_times_regs<D, BF16>(sK[cur], la, qf);   // S^T
+        const f32x16 dp = tile_times_regs<D, BF16>(sV[cur], la, df);  // dP^T
+        f32x16 ds;
+        const int lim = my_last - j0 - 4 * hl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kc = 8 * (r >> 2) + (r & 3);
+            const float pr = kc <= lim ? fast_exp2(__builtin_fmaf(s[r], c, -lse2)) : 0.f;
+            ds[r] = pr * (dp[r] - Di);
+        }
+        vec8 dsb[G::PSTEPS];
+        pack_scores<BF16>(ds, dsb);
+        tileT_times_packed<D, BF16>(sK[cur], la, dsb, acc);  // dQ^T += K^T dS^T
+    };
+    using Z = std::integral_constant<int, 0>;
+    using O = std::integral_constant<int, 1>;
 
     if (wg_end > 0) {
-        fetch(0);
-        stash(0);
+        fetch(Z{}, 0);
+        if (kBwdRows < wg_end) fetch(O{}, kBwdRows);
+        stash(Z{}, 0);
         __syncthreads();
-        int cur = 0;
-        for (int j0 = 0; j0 < wg_end; j0 += kBwdRows) {
-            const bool more = j0 + kBwdRows < wg_end;
-            if (more) fetch(j0 + kBwdRows);
-            if (j0 <= wave_last) {
-                const f32x16 s = tile_times_regs<D, BF16>(sK[cur], la, qf);   // S^T
-                const f32x16 dp = tile_times_regs<D, BF16>(sV[cur], la, df);  // dP^T
-                f32x16 ds;
-                const int lim = my_last - j0 - 4 * hl;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kc = 8 * (r >> 2) + (r & 3);
-                    const float pr = kc <= lim ? fast_exp2(__builtin_fmaf(s[r], c, -lse2)) : 0.f;
-                    ds[r] = pr * (dp[r] - Di);
-                }
-                vec8 dsb[G::PSTEPS];
-                pack_scores<BF16>(ds, dsb);
-                tileT_times_packed<D, BF16>(sK[cur], la, dsb, acc);  // dQ^T += K^T dS^T
-            }
-            if (more) stash(cur ^ 1);
+        for (int j0 = 0; j0 < wg_end; j0 += 2 * kBwdRows) {
+            if (j0 + 2 * kBwdRows < wg_end) fetch(Z{}, j0 + 2 * kBwdRows);
+            compute(j0, 0);
+            if (j0 + kBwdRows < wg_end) stash(O{}, 1);
             __syncthreads();
-            cur ^= 1;
+            if (j0 + kBwdRows >= wg_end) break;
+            if (j0 + 3 * kBwdRows < wg_end) fetch(O{}, j0 + 3 * kBwdRows);
+            compute(j0 + kBwdRows, 1);
+            if (j0 + 2 * kBwdRows < wg_end) stash(Z{}, 0);
+            __syncthreads();
         }
     }
     if (!row_ok) return;
