@@ -63,22 +63,22 @@ def source_digest(path):
     return hashlib.sha256(text.encode()).hexdigest()
 
 
-def measured_traffic(kind):
+def measured_traffic(kind, field="hbm_bytes"):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    record (profiles/traffic.json), or None when the kernel sources changed
-    since those counters were taken."""
+    record (profiles/traffic.json), or None when a kernel source that record
+    depends on changed since those counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f)
-    for src, digest in rec.get("kernel_sources_digest", {}).items():
+        entry = json.load(f).get(kind)
+    if not entry or not entry.get("sources"):
+        return None
+    for src, digest in entry["sources"].items():
         full = os.path.join(ROOT, src)
         if not os.path.exists(full) or source_digest(full) != digest:
             return None
-    if not rec.get("kernel_sources_digest"):
-        return None
-    return rec.get(kind, {}).get("hbm_bytes")
+    return entry.get(field)
 
 
 def kv_bytes(kv_lens, Hkv, D, elem_bytes=2):
@@ -180,7 +180,9 @@ def time_backward(mi, w, steps, warmup):
     return {"workload": w.name, "value": tflops, "unit": "TFLOP/s", "ms_per_call": ms,
             "flops_per_call": 10 * w.D * triples, "counted": "10*D per visible triple",
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS}}
+                         "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                         "traffic": measured_traffic("backward"),
+                         "traffic_per_kernel": measured_traffic("backward", "per_kernel")}}
 
 
 def cpu_baseline(w, target_s=12.0):
@@ -219,7 +221,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
                     help="time one workload and print its line (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy 5 times and exit: the "
@@ -253,6 +255,12 @@ def main():
         d = time_decode(mi, wd, max(args.steps, 10), args.warmup)
         nbytes = kv_bytes(wd.kv_lengths(), wd.Hkv, wd.D)
         print(json.dumps({"workload": wd.name, "kv_bytes": nbytes, **d}), flush=True)
+        return
+
+    if args.only == "backward":
+        w = workloads.make(2)
+        bw = time_backward(mi, w, args.steps, args.warmup)
+        print(json.dumps(bw), flush=True)
         return
 
     w = workloads.make(2)

@@ -207,7 +207,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const BwdParams p)
     __shared__ __attribute__((aligned(1024))) uint8_t sK[2][G::BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sV[2][G::BYTES];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int l32 = lane & 31, hl = lane >> 5;
     const int units = p.B * p.Hkv;
     const int rank = blockIdx.x / units;
@@ -230,6 +231,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const BwdParams p)
     const bool wave_rows = row0 + wave * 32 < p.rows;
     const int wave_last = !wave_rows ? -1
                           : (p.causal ? min(p.Skv - 1, wrow_last / p.G + delta) : p.Skv - 1);
+    // the last visible key of the wave's first row: no row of the wave sees
+    // fewer keys (rows past the end have lse2 = +inf, so their P is 0 anyway)
+    const int wave_first_last =
+        p.causal ? min(p.Skv - 1, (row0 + wave * 32) / p.G + delta) : p.Skv - 1;
     const int64_t qoff = (((int64_t)b * p.Sq + my_i) * p.Hq + my_h) * D;
     vec8 qf[G::KSTEPS], df[G::KSTEPS];
 #pragma unroll
@@ -281,13 +286,22 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const BwdParams p)
         const f32x16 s = tile_times_regs<D, BF16>(sK[cur], la, qf);   // S^T
         const f32x16 dp = tile_times_regs<D, BF16>(sV[cur], la, df);  // dP^T
         f32x16 ds;
-        const int lim = my_last - j0 - 4 * hl;
+        // dS; when every row of the wave sees all 32 keys (wave-uniform) the
+        // visibility test drops out
+        auto grads = [&](auto full_tag) __attribute__((always_inline)) {
+            const int lim = my_last - j0 - 4 * hl;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kc = 8 * (r >> 2) + (r & 3);
-            const float pr = kc <= lim ? fast_exp2(__builtin_fmaf(s[r], c, -lse2)) : 0.f;
-            ds[r] = pr * (dp[r] - Di);
-        }
+            for (int r = 0; r < 16; ++r) {
+                const int kc = 8 * (r >> 2) + (r & 3);
+                const bool vis = decltype(full_tag)::value || kc <= lim;
+                const float pr = vis ? fast_exp2(__builtin_fmaf(s[r], c, -lse2)) : 0.f;
+                ds[r] = pr * (dp[r] - Di);
+            }
+        };
+        if (j0 + kBwdRows - 1 <= wave_first_last)
+            grads(std::true_type{});
+        else
+            grads(std::false_type{});
         vec8 dsb[G::PSTEPS];
         pack_scores<BF16>(ds, dsb);
         tileT_times_packed<D, BF16>(sK[cur], la, dsb, acc);  // dQ^T += K^T dS^T
@@ -327,7 +341,8 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams 
     __shared__ __attribute__((aligned(16))) float sL[2][kBwdRows];      // lse2 of the rows
     __shared__ __attribute__((aligned(16))) float sD[2][kBwdRows];      // D of the rows
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int l32 = lane & 31, hl = lane >> 5;
     const int units = p.B * p.Hkv;
     const int rank = blockIdx.x / units;
@@ -367,25 +382,44 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams 
 
     // Tiles are fetched two ahead into two register sets (tile n in set n & 1)
     // so that a tile's global loads have two compute steps to arrive: with one
-    // wave per SIMD nothing else hides their latency.
+    // wave per SIMD nothing else hides their latency.  Tiles are fetched in
+    // order, so each thread keeps the (query, head-in-group) pair of its rows
+    // and steps it by kBwdRows packed rows per fetch instead of dividing.
     u32x4 rq[2][G::CPT], ro[2][G::CPT];
     float rl[2] = {INFINITY, INFINITY}, rd[2] = {0.f, 0.f};
-    auto fetch = [&](auto set_tag, int r0) __attribute__((always_inline)) {
+    const int step_i = kBwdRows / p.G, step_h = kBwdRows - step_i * p.G;
+    int ri[G::CPT], rh[G::CPT];  // chunk e's row: query ri[e], head kvh G + rh[e]
+#pragma unroll
+    for (int e = 0; e < G::CPT; ++e) {
+        const int r = wg_row0 + (tid + e * 64 * kBwdWaves) / (D / 8);
+        ri[e] = r / p.G;
+        rh[e] = r - ri[e] * p.G;
+    }
+    int li = (wg_row0 + tid) / p.G, lh = wg_row0 + tid - li * p.G;  // lse / D row (tid < 32)
+    const int64_t q_base = ((int64_t)b * p.Sq * p.Hq + (int64_t)kvh * p.G) * D + 8 * (tid % (D / 8));
+    const int64_t l_base = ((int64_t)b * p.Hq + (int64_t)kvh * p.G) * p.Sq;
+    const int hqd = p.Hq * D;
+    auto advance = [&](int &i, int &h) __attribute__((always_inline)) {
+        i += step_i;
+        h += step_h;
+        if (h >= p.G) {
+            h -= p.G;
+            ++i;
+        }
+    };
+    auto fetch = [&](auto set_tag) __attribute__((always_inline)) {
         constexpr int S = decltype(set_tag)::value;
 #pragma unroll
         for (int e = 0; e < G::CPT; ++e) {
-            const int ch = tid + e * 64 * kBwdWaves;
-            const int r = min(r0 + ch / (D / 8), p.rows - 1), cc = ch % (D / 8);
-            const int i = r / p.G, h = kvh * p.G + (r - i * p.G);
-            const int64_t off = (((int64_t)b * p.Sq + i) * p.Hq + h) * D + 8 * cc;
+            // rows past the end read the last query's row (their P is 0)
+            const int64_t off = q_base + (int64_t)min(ri[e], p.Sq - 1) * hqd + rh[e] * D;
             rq[S][e] = *(const u32x4 *)(p.q + off);
             ro[S][e] = *(const u32x4 *)(p.dout + off);
+            advance(ri[e], rh[e]);
         }
         if (tid < kBwdRows) {
-            const int r = r0 + tid;
-            if (r < p.rows) {
-                const int i = r / p.G, h = kvh * p.G + (r - i * p.G);
-                const int64_t at = ((int64_t)b * p.Hq + h) * p.Sq + i;
+            if (li < p.Sq) {
+                const int64_t at = l_base + (int64_t)lh * p.Sq + li;
                 rl[S] = p.lse2_rows[at];
                 rd[S] = p.d_rows[at];
             } else {
@@ -393,6 +427,7 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams 
                 rd[S] = 0.f;
             }
         }
+        advance(li, lh);
     };
     auto stash = [&](auto set_tag, int buf) __attribute__((always_inline)) {
         constexpr int S = decltype(set_tag)::value;
@@ -413,22 +448,30 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams 
         if (r0 + kBwdRows - 1 < wave_thr_lo) return;
         const f32x16 s = tile_times_regs<D, BF16>(sQ[cur], la, kf);   // S
         const f32x16 dp = tile_times_regs<D, BF16>(sO[cur], la, vf);  // dP
-        const bool full = r0 >= wave_thr_hi;
         f32x16 pr, ds;
+        // P and dS; in a tile every row of which sees all the wave's keys
+        // (wave-uniform) the visibility test drops out
+        auto probs = [&](auto full_tag) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            // registers 4 q4 .. 4 q4 + 3 hold rows 8 q4 + 4 hl + 0..3
-            const f32x4 l4 = *(const f32x4 *)(&sL[cur][8 * q4 + 4 * hl]);
-            const f32x4 d4 = *(const f32x4 *)(&sD[cur][8 * q4 + 4 * hl]);
+            for (int q4 = 0; q4 < 4; ++q4) {
+                // registers 4 q4 .. 4 q4 + 3 hold rows 8 q4 + 4 hl + 0..3
+                const f32x4 l4 = *(const f32x4 *)(&sL[cur][8 * q4 + 4 * hl]);
+                const f32x4 d4 = *(const f32x4 *)(&sD[cur][8 * q4 + 4 * hl]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * q4 + e;
-                const bool vis = full || (r0 + 8 * q4 + 4 * hl + e >= my_thr);
-                const float x = vis ? fast_exp2(__builtin_fmaf(s[r], c, -l4[e])) : 0.f;
-                pr[r] = x;
-                ds[r] = x * (dp[r] - d4[e]);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q4 + e;
+                    const bool vis =
+                        decltype(full_tag)::value || (r0 + 8 * q4 + 4 * hl + e >= my_thr);
+                    const float x = vis ? fast_exp2(__builtin_fmaf(s[r], c, -l4[e])) : 0.f;
+                    pr[r] = x;
+                    ds[r] = x * (dp[r] - d4[e]);
+                }
             }
-        }
+        };
+        if (r0 >= wave_thr_hi)
+            probs(std::true_type{});
+        else
+            probs(std::false_type{});
         vec8 pb[G::PSTEPS], dsb[G::PSTEPS];
         pack_scores<BF16>(pr, pb);
         pack_scores<BF16>(ds, dsb);
@@ -441,19 +484,19 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams 
     using O = std::integral_constant<int, 1>;
 
     if (key0 < p.Skv && wg_row0 < p.rows) {
-        fetch(Z{}, wg_row0);
-        if (wg_row0 + kBwdRows < p.rows) fetch(O{}, wg_row0 + kBwdRows);
+        fetch(Z{});
+        if (wg_row0 + kBwdRows < p.rows) fetch(O{});
         stash(Z{}, 0);
         __syncthreads();
         for (int r0 = wg_row0; r0 < p.rows; r0 += 2 * kBwdRows) {
             // tile n even: set 0 is free, tile n + 1 waits in set 1
-            if (r0 + 2 * kBwdRows < p.rows) fetch(Z{}, r0 + 2 * kBwdRows);
+            if (r0 + 2 * kBwdRows < p.rows) fetch(Z{});  // rows r0 + 2 kBwdRows ...
             compute(r0, 0);
             if (r0 + kBwdRows < p.rows) stash(O{}, 1);
             __syncthreads();
             if (r0 + kBwdRows >= p.rows) break;
             // tile n + 1 (odd): set 1 is free, tile n + 2 waits in set 0
-            if (r0 + 3 * kBwdRows < p.rows) fetch(O{}, r0 + 3 * kBwdRows);
+            if (r0 + 3 * kBwdRows < p.rows) fetch(O{});  // rows r0 + 3 kBwdRows ...
             compute(r0 + kBwdRows, 1);
             if (r0 + 2 * kBwdRows < p.rows) stash(Z{}, 0);
             __syncthreads();
