@@ -310,19 +310,21 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const BwdParams p)
     using O = std::integral_constant<int, 1>;
 
     if (wg_end > 0) {
+        // fetches and stashes run unconditionally (past the last tile they
+        // move clamped keys that nothing reads), keeping the load counts static
         fetch(Z{}, 0);
-        if (kBwdRows < wg_end) fetch(O{}, kBwdRows);
+        fetch(O{}, kBwdRows);
         stash(Z{}, 0);
         __syncthreads();
         for (int j0 = 0; j0 < wg_end; j0 += 2 * kBwdRows) {
-            if (j0 + 2 * kBwdRows < wg_end) fetch(Z{}, j0 + 2 * kBwdRows);
+            fetch(Z{}, j0 + 2 * kBwdRows);
             compute(j0, 0);
-            if (j0 + kBwdRows < wg_end) stash(O{}, 1);
+            stash(O{}, 1);
             __syncthreads();
             if (j0 + kBwdRows >= wg_end) break;
-            if (j0 + 3 * kBwdRows < wg_end) fetch(O{}, j0 + 3 * kBwdRows);
+            fetch(O{}, j0 + 3 * kBwdRows);
             compute(j0 + kBwdRows, 1);
-            if (j0 + 2 * kBwdRows < wg_end) stash(Z{}, 0);
+            stash(Z{}, 0);
             __syncthreads();
         }
     }
@@ -386,7 +388,8 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams 
     // order, so each thread keeps the (query, head-in-group) pair of its rows
     // and steps it by kBwdRows packed rows per fetch instead of dividing.
     u32x4 rq[2][G::CPT], ro[2][G::CPT];
-    float rl[2] = {INFINITY, INFINITY}, rd[2] = {0.f, 0.f};
+    float rl[2], rd[2];
+    bool rok[2];
     const int step_i = kBwdRows / p.G, step_h = kBwdRows - step_i * p.G;
     int ri[G::CPT], rh[G::CPT];  // chunk e's row: query ri[e], head kvh G + rh[e]
 #pragma unroll
@@ -417,16 +420,15 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams 
             ro[S][e] = *(const u32x4 *)(p.dout + off);
             advance(ri[e], rh[e]);
         }
-        if (tid < kBwdRows) {
-            if (li < p.Sq) {
-                const int64_t at = l_base + (int64_t)lh * p.Sq + li;
-                rl[S] = p.lse2_rows[at];
-                rd[S] = p.d_rows[at];
-            } else {
-                rl[S] = INFINITY;  // a padding row: P = 0
-                rd[S] = 0.f;
-            }
-        }
+        // every thread loads (threads past the tile's rows read a clamped row
+        // they never stash), so each fetch issues the same loads and the
+        // waits before a stash count exactly the fetch issued after it
+        // (the padding test is applied at the stash: a select here would wait
+        // for the load at once)
+        const int64_t at = l_base + (int64_t)lh * p.Sq + min(li, p.Sq - 1);
+        rl[S] = p.lse2_rows[at];
+        rd[S] = p.d_rows[at];
+        rok[S] = li < p.Sq;
         advance(li, lh);
     };
     auto stash = [&](auto set_tag, int buf) __attribute__((always_inline)) {
@@ -439,8 +441,8 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams 
             *(u32x4 *)(&sO[buf][tile_off<D>(r, cc)]) = ro[S][e];
         }
         if (tid < kBwdRows) {
-            sL[buf][tid] = rl[S];
-            sD[buf][tid] = rd[S];
+            sL[buf][tid] = rok[S] ? rl[S] : INFINITY;  // a padding row: P = 0
+            sD[buf][tid] = rok[S] ? rd[S] : 0.f;
         }
     };
     auto compute = [&](int r0, int cur) __attribute__((always_inline)) {
@@ -484,21 +486,23 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams 
     using O = std::integral_constant<int, 1>;
 
     if (key0 < p.Skv && wg_row0 < p.rows) {
+        // fetches and stashes run unconditionally (past the last tile they
+        // move clamped rows that nothing reads), keeping the load counts static
         fetch(Z{});
-        if (wg_row0 + kBwdRows < p.rows) fetch(O{});
+        fetch(O{});
         stash(Z{}, 0);
         __syncthreads();
         for (int r0 = wg_row0; r0 < p.rows; r0 += 2 * kBwdRows) {
             // tile n even: set 0 is free, tile n + 1 waits in set 1
-            if (r0 + 2 * kBwdRows < p.rows) fetch(Z{});  // rows r0 + 2 kBwdRows ...
+            fetch(Z{});  // rows r0 + 2 kBwdRows ...
             compute(r0, 0);
-            if (r0 + kBwdRows < p.rows) stash(O{}, 1);
+            stash(O{}, 1);
             __syncthreads();
             if (r0 + kBwdRows >= p.rows) break;
             // tile n + 1 (odd): set 1 is free, tile n + 2 waits in set 0
-            if (r0 + 3 * kBwdRows < p.rows) fetch(O{});  // rows r0 + 3 kBwdRows ...
+            fetch(O{});  // rows r0 + 3 kBwdRows ...
             compute(r0 + kBwdRows, 1);
-            if (r0 + 2 * kBwdRows < p.rows) stash(Z{}, 0);
+            stash(Z{}, 0);
             __syncthreads();
         }
     }
