@@ -13,6 +13,10 @@ with inputs resident in HBM.  The same line carries:
                 that no call finds its data in the last-level cache;
   backward      the attention backward (dq, dk, dv) of the same prefill,
                 TFLOP/s counting 10*D flops per visible triple;
+  other_configs median call time and TFLOP/s of the key-padding MHA (B=4,
+                H=16, S=2048, D=64, fp16) and of the wide-group chunked prefill
+                through the paged path (B=2, Hq=24, Hkv=2, D=256, 512 queries
+                after 16384 keys);
   cpu_baseline  the fp64 CPU oracle on a bounded row sample of the prefill
                 workload, on this host's cores.
 
@@ -185,6 +189,59 @@ def time_backward(mi, w, steps, warmup):
                          "traffic_per_kernel": measured_traffic("backward", "per_kernel")}}
 
 
+def time_calls(fn, steps, warmup):
+    """Median and minimum of per-call HIP-event times (ms) on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return ms[len(ms) // 2], ms[0]
+
+
+def time_other_configs(mi, steps):
+    """The key-padding MHA (fp16, D=64, non-causal) and the wide-group chunked
+    prefill through the paged path (D=256, G=12): TFLOP/s of whole calls at
+    4*D flops per visible triple, against the dense 16-bit MFMA peak."""
+    import torch
+
+    from softmax_attention_amd import workloads
+    dev = "cuda:0"
+    out = {}
+    w = workloads.make(4)
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    mask = w.key_padding_mask.to(dev)
+    triples = int(w.key_padding_mask.sum()) * w.Sq * w.Hq
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    med, mn = time_calls(lambda: mi.attn_fwd_dense(q, k, v, scale=w.scale, causal=False,
+                                                   key_padding_mask=mask, out=o, lse=lse),
+                         steps, 10)
+    out[w.name] = {"median_call_us": med * 1e3, "min_call_us": mn * 1e3, "dtype": "f16",
+                   "tflops": 4 * w.D * triples / (med * 1e-3) / 1e12, "triples": triples}
+    del q, k, v, o, lse, w
+    w = workloads.make(5)
+    q, kc, vc = w.q.to(dev), w.k_cache.to(dev), w.v_cache.to(dev)
+    lens, bt = w.real_seqlen_kv.to(dev), w.block_table.to(dev)
+    triples = visible_pairs(w.B, w.Hq, w.Sq, w.kv_lengths(), True)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    med, mn = time_calls(lambda: mi.attn_fwd_paged(q, kc, vc, lens, bt, w.page_size,
+                                                   scale=w.scale, out=o, lse=lse), steps, 10)
+    out[w.name] = {"median_call_us": med * 1e3, "min_call_us": mn * 1e3, "dtype": "bf16",
+                   "tflops": 4 * w.D * triples / (med * 1e-3) / 1e12, "triples": triples}
+    for rec in out.values():
+        rec["frac_of_peak"] = rec["tflops"] / PEAK_BF16_TFLOPS
+    return out
+
+
 def cpu_baseline(w, target_s=12.0):
     """The fp64 oracle on a bounded sample of the prefill workload's rows."""
     import numpy as np
@@ -221,6 +278,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the key-padding MHA and wide-group chunked prefill timings")
     ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
                     help="time one workload and print its line (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -329,6 +388,12 @@ def main():
         print(f"[bench] backward {w.name}: {bw['ms_per_call'] * 1e3:.1f} us, "
               f"{bw['value']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         del w
+
+    if not args.no_other:
+        line["other_configs"] = time_other_configs(mi, max(args.steps, 50))
+        for name, rec in line["other_configs"].items():
+            print(f"[bench] {name}: call {rec['median_call_us']:.1f} us, "
+                  f"{rec['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
         w = workloads.make(2)
