@@ -75,11 +75,16 @@ def _load():
         lib.oracle_e4m3_decode.restype = ctypes.c_double
         lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
         lib.oracle_kv_write.argtypes = [P, P, i32, P, i32, i32, i32, i64, i32, f32, f32, P, P]
-        lib.oracle_attn_paged_append.argtypes = [P, P, P, P, P, P, P, i32, P, i32, f32, i32, i32,
-                                                 i32, i32, i32, i32, i32, f32, i32, P, P]
+        lib.oracle_attn_paged_varlen_fp8.argtypes = [P, P, P, f32, f32, P, P, i32, P, i32, *win,
+                                                     P, i32, i32, i32, i32, i32, i32, f32, i32,
+                                                     P, P]
+        lib.oracle_attn_paged_append.argtypes = [P, P, P, P, P, i32, f32, f32, P, P, i32, P, i32,
+                                                 f32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                                 P, P]
         for name in ("oracle_attn_dense", "oracle_attn_dense_rows", "oracle_attn_paged",
                      "oracle_attn_paged_rows", "oracle_attn_varlen", "oracle_attn_paged_varlen",
                      "oracle_e4m3_encode", "oracle_kv_write", "oracle_attn_paged_append",
+                     "oracle_attn_paged_varlen_fp8",
                      "oracle_attn_bwd",
                      "oracle_num_threads"):
             getattr(lib, name).restype = i32
@@ -292,12 +297,17 @@ def attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, *, scale=None, causal=True
 
 def attn_paged_varlen(q, k_cache, v_cache, cache_seqlens, block_table, page_size, cu_seqlens_q,
                       *, causal=True, scale=None, window=None, softcap=None, sinks=None,
-                      dtype=None):
+                      cache_fp8=False, k_scale=1.0, v_scale=1.0, dtype=None):
     """Packed-query paged call: q [total_q,Hq,D] delimited by cu_seqlens_q [B+1];
-    k_cache/v_cache [pages*page_size,Hkv,D] or [pages,page_size,Hkv,D];
+    k_cache/v_cache [pages*page_size,Hkv,D] or [pages,page_size,Hkv,D] (16-bit,
+    or with cache_fp8 E4M3FN codes dequantized by k_scale / v_scale);
     cache_seqlens [B] (each request's keys, its queries included);
     block_table [B,max_pages].  Returns o [total_q,Hq,D], lse [Hq,total_q]."""
     dt = _dtype_code(q) if dtype is None else dtype
+    if cache_fp8:
+        return _attn_paged_varlen_fp8(q, k_cache, v_cache, cache_seqlens, block_table,
+                                      page_size, cu_seqlens_q, causal, scale, window, softcap,
+                                      sinks, float(k_scale), float(v_scale), dt)
     qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
     total_q, Hq, D = qb.shape
     Hkv = kb.shape[-2]
@@ -315,6 +325,38 @@ def attn_paged_varlen(q, k_cache, v_cache, cache_seqlens, block_table, page_size
                                           _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle_attn_paged_varlen rejected the call (rc={rc})")
+    return o, lse
+
+
+def _codes(x) -> np.ndarray:
+    """uint8 E4M3FN codes of a uint8 / float8_e4m3fn tensor or array."""
+    if isinstance(x, np.ndarray):
+        assert x.dtype == np.uint8
+        return np.ascontiguousarray(x)
+    import torch
+    return np.ascontiguousarray(x.detach().cpu().contiguous().view(torch.uint8).numpy())
+
+
+def _attn_paged_varlen_fp8(q, k_cache, v_cache, cache_seqlens, block_table, page_size,
+                           cu_seqlens_q, causal, scale, window, softcap, sinks, k_scale,
+                           v_scale, dt):
+    qb, kb, vb = _bits(q), _codes(k_cache), _codes(v_cache)
+    total_q, Hq, D = qb.shape
+    Hkv = kb.shape[-2]
+    lens, bt, cq = _i32(cache_seqlens), _i32(block_table), _i32(cu_seqlens_q)
+    B = cq.shape[0] - 1
+    assert lens.shape == (B,) and bt.ndim == 2 and bt.shape[0] == B
+    sk = _sinks(sinks, Hq)
+    o = np.zeros((total_q, Hq, D), np.float64)
+    lse = np.zeros((Hq, total_q), np.float64)
+    rc = _load().oracle_attn_paged_varlen_fp8(_ptr(qb), _ptr(kb), _ptr(vb), k_scale, v_scale,
+                                              _ptr(lens), _ptr(bt), int(page_size), _ptr(cq),
+                                              int(bool(causal)), *_opt_args(window, softcap),
+                                              None if sk is None else _ptr(sk), B, total_q, Hq,
+                                              Hkv, D, bt.shape[1], _scale_arg(scale), dt,
+                                              _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_paged_varlen_fp8 rejected the call (rc={rc})")
     return o, lse
 
 
@@ -386,14 +428,19 @@ def kv_write(k, v, k_pool, v_pool, slot_mapping, *, cache_fp8=False, k_scale=1.0
 
 
 def attn_paged_append(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, page_size,
-                      cu_seqlens_q, *, causal=True, softcap=None, scale=None, dtype=None):
+                      cu_seqlens_q, *, causal=True, softcap=None, scale=None, cache_fp8=False,
+                      k_scale=1.0, v_scale=1.0, dtype=None):
     """Prefill with append: writes k_new/v_new [total_q,Hkv,D] at each request's
-    positions cache_seqlens[b] + i (copies of the 16-bit pools), then attends the
-    packed queries to cache_seqlens[b] + Sq_b keys.  Returns o [total_q,Hq,D],
-    lse [Hq,total_q] and the two updated pools (uint16 numpy arrays)."""
+    positions cache_seqlens[b] + i (copies of the pools: 16-bit, or with cache_fp8
+    E4M3FN codes of value / scale), then attends the packed queries to
+    cache_seqlens[b] + Sq_b keys.  Returns o [total_q,Hq,D], lse [Hq,total_q] and
+    the two updated pools (uint16, or uint8 codes, numpy arrays)."""
     dt = _dtype_code(q) if dtype is None else dtype
     qb, kb, vb = _bits(q), _bits(k_new), _bits(v_new)
-    kc, vc = np.array(_bits(k_cache), copy=True), np.array(_bits(v_cache), copy=True)
+    if cache_fp8:
+        kc, vc = np.array(_codes(k_cache), copy=True), np.array(_codes(v_cache), copy=True)
+    else:
+        kc, vc = np.array(_bits(k_cache), copy=True), np.array(_bits(v_cache), copy=True)
     total_q, Hq, D = qb.shape
     Hkv = kb.shape[1]
     lens, bt, cq = _i32(cache_seqlens), _i32(block_table), _i32(cu_seqlens_q)
@@ -402,6 +449,7 @@ def attn_paged_append(q, k_new, v_new, k_cache, v_cache, cache_seqlens, block_ta
     o = np.zeros((total_q, Hq, D), np.float64)
     lse = np.zeros((Hq, total_q), np.float64)
     rc = _load().oracle_attn_paged_append(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(kc), _ptr(vc),
+                                          int(bool(cache_fp8)), float(k_scale), float(v_scale),
                                           _ptr(lens), _ptr(bt), int(page_size), _ptr(cq),
                                           int(bool(causal)),
                                           0.0 if softcap is None else float(softcap), B,

@@ -122,10 +122,16 @@ double oracle_resolve_scale(float scale, int D)
     return (double)scale;
 }
 
+static double e4m3_value(int code);
+
 /* Everything that locates a key or value row for one call. */
 typedef struct {
-    const uint16_t *q, *k, *v;
+    const uint16_t *q;
+    const void *k, *v; /* 16-bit patterns, or E4M3FN codes when cache_fp8 */
     int dtype;
+    /* an FP8 pool holds E4M3FN codes; element = decoded code * its scale */
+    int cache_fp8;
+    double k_scale, v_scale;
     int B, Sq, Hq, Hkv, D;
     int causal;
     double alpha;
@@ -184,6 +190,18 @@ static int64_t kv_row_offset(const call_t *c, int b, int64_t j, int r)
     return (row * c->Hkv + r) * c->D;
 }
 
+/* Element idx of the key (which = 0) or value (1) tensor: the 16-bit value,
+ * or for an FP8 pool the code's value times the pool's dequantization scale
+ * (TileOPs "Attention Operators", GQAPrefillPagedWithKVCacheFwdOp: k_scale and
+ * v_scale of an FP8 pool; GQAVarlenFwdOp: each scale multiplies its tensor). */
+static double kv_value(const call_t *c, int which, int64_t idx)
+{
+    const void *base = which ? c->v : c->k;
+    if (c->cache_fp8)
+        return e4m3_value(((const uint8_t *)base)[idx]) * (which ? c->v_scale : c->k_scale);
+    return decode((const uint16_t *)base, idx, c->dtype);
+}
+
 /* Key j is visible to query i iff (not causal or j <= p_i), it lies inside
  * the window (p_i - w_L <= j when w_L != -1, j <= p_i + w_R when w_R != -1)
  * and the padding mask keeps column j. */
@@ -222,7 +240,7 @@ static void attend_row(const call_t *c, int b, int i, int h, double *o_row,
         int64_t k_off = kv_row_offset(c, b, j, r);
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
-            dot += decode(c->q, q_off + d, c->dtype) * decode(c->k, k_off + d, c->dtype);
+            dot += decode(c->q, q_off + d, c->dtype) * kv_value(c, 0, k_off + d);
         s[j] = c->alpha * dot;
         if (c->softcap > 0.0) /* stage 6: the logit is c tanh(Z / c) */
             s[j] = c->softcap * tanh(s[j] / c->softcap);
@@ -258,7 +276,7 @@ static void attend_row(const call_t *c, int b, int i, int h, double *o_row,
         for (int64_t j = 0; j < n; ++j) {
             if (!visible(c, b, i, j))
                 continue;
-            acc += w[j] * decode(c->v, kv_row_offset(c, b, j, r) + d, c->dtype);
+            acc += w[j] * kv_value(c, 1, kv_row_offset(c, b, j, r) + d);
         }
         o_row[d] = acc / l;
     }
@@ -383,8 +401,8 @@ static int make_dense(call_t *c, const uint16_t *q, const uint16_t *k, const uin
     return set_options(c, window_left, window_right, softcap);
 }
 
-static int make_paged(call_t *c, const uint16_t *q, const uint16_t *k_cache,
-                      const uint16_t *v_cache, const int32_t *seqlen,
+static int make_paged(call_t *c, const uint16_t *q, const void *k_cache,
+                      const void *v_cache, const int32_t *seqlen,
                       const int32_t *block_table, int page_size, int causal, int window_left,
                       int window_right, float softcap, int B, int Sq, int Hq, int Hkv, int D,
                       int max_pages, float scale, int dtype)
@@ -540,6 +558,36 @@ int oracle_attn_paged_varlen(const uint16_t *q, const uint16_t *k_cache,
     return run_all(&c, o, lse);
 }
 
+/* As oracle_attn_paged_varlen over FP8 pools: k_cache / v_cache hold E4M3FN
+ * codes, dequantized by k_scale / v_scale (finite and positive, else -1). */
+int oracle_attn_paged_varlen_fp8(const uint16_t *q, const uint8_t *k_cache,
+                                 const uint8_t *v_cache, float k_scale, float v_scale,
+                                 const int32_t *cache_seqlens, const int32_t *block_table,
+                                 int page_size, const int32_t *cu_q, int causal,
+                                 int window_left, int window_right, float softcap,
+                                 const float *sinks, int B, int total_q, int Hq, int Hkv, int D,
+                                 int max_pages, float scale, int dtype, double *o, double *lse)
+{
+    call_t c;
+    if (total_q < 0)
+        return -1;
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale))
+        return -1;
+    if (make_paged(&c, q, k_cache, v_cache, cache_seqlens, block_table, page_size, causal,
+                   window_left, window_right, softcap, B, 0, Hq, Hkv, D, max_pages, scale,
+                   dtype))
+        return -1;
+    if (check_offsets(cu_q, B, total_q))
+        return -1;
+    c.cu_q = cu_q;
+    c.total_q = total_q;
+    c.sinks = sinks;
+    c.cache_fp8 = 1;
+    c.k_scale = (double)k_scale;
+    c.v_scale = (double)v_scale;
+    return run_all(&c, o, lse);
+}
+
 /* ---------------------------------------------------------------- backward
  *
  * Dense call, inputs as for oracle_attn_dense plus o [B,Sq,Hq,D] and lse
@@ -686,14 +734,17 @@ int oracle_kv_write(const uint16_t *k, const uint16_t *v, int dtype, const int64
     return 0;
 }
 
-/* Paged prefill with append (16-bit pools): request b's chunk (queries and
+/* Paged prefill with append: request b's chunk (queries and
  * new keys/values at packed rows cu_q[b] .. cu_q[b+1]-1) is written to its
  * logical positions cache_seqlens[b] + i, i.e. pool row
  * block_table[b, pos / page_size] * page_size + pos % page_size; then the
  * chunk's queries attend to the request's cache_seqlens[b] + Sq_b keys.  The
- * pools are updated in place; o [total_q, Hq, D], lse [Hq, total_q]. */
+ * pools (16-bit, or FP8 with cache_fp8 and its two scales: the chunk is
+ * written quantized and read back dequantized) are updated in place;
+ * o [total_q, Hq, D], lse [Hq, total_q]. */
 int oracle_attn_paged_append(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
-                             uint16_t *k_cache, uint16_t *v_cache, const int32_t *cache_seqlens,
+                             void *k_cache, void *v_cache, int cache_fp8, float k_scale,
+                             float v_scale, const int32_t *cache_seqlens,
                              const int32_t *block_table, int page_size, const int32_t *cu_q,
                              int causal, float softcap, int B, int total_q, int Hq, int Hkv,
                              int D, int max_pages, int num_pages, float scale, int dtype,
@@ -725,11 +776,18 @@ int oracle_attn_paged_append(const uint16_t *q, const uint16_t *k_new, const uin
     }
     if (rc == 0)
         rc = oracle_kv_write(k_new, v_new, dtype, slot, total_q, Hkv, D,
-                             (int64_t)num_pages * page_size, 0, 1.0f, 1.0f, k_cache, v_cache);
-    if (rc == 0)
-        rc = oracle_attn_paged_varlen(q, k_cache, v_cache, lens, block_table, page_size, cu_q,
-                                      causal, -1, -1, softcap, NULL, B, total_q, Hq, Hkv, D,
-                                      max_pages, scale, dtype, o, lse);
+                             (int64_t)num_pages * page_size, cache_fp8, k_scale, v_scale,
+                             k_cache, v_cache);
+    if (rc == 0 && cache_fp8)
+        rc = oracle_attn_paged_varlen_fp8(q, (const uint8_t *)k_cache, (const uint8_t *)v_cache,
+                                          k_scale, v_scale, lens, block_table, page_size, cu_q,
+                                          causal, -1, -1, softcap, NULL, B, total_q, Hq, Hkv, D,
+                                          max_pages, scale, dtype, o, lse);
+    else if (rc == 0)
+        rc = oracle_attn_paged_varlen(q, (const uint16_t *)k_cache, (const uint16_t *)v_cache,
+                                      lens, block_table, page_size, cu_q, causal, -1, -1,
+                                      softcap, NULL, B, total_q, Hq, Hkv, D, max_pages, scale,
+                                      dtype, o, lse);
     free(slot);
     free(lens);
     return rc;

@@ -28,7 +28,7 @@ MUTANTS = {
     "empty_row_nan": ("o_row[d] = 0.0;", "o_row[d] = NAN;"),
     "page_offset_unscaled": ("row = phys_page * c->page_size + in_page;",
                              "row = phys_page + in_page;"),
-    "scores_read_v": ("decode(c->k, k_off + d, c->dtype);", "decode(c->v, k_off + d, c->dtype);"),
+    "scores_read_v": ("kv_value(c, 0, k_off + d);", "kv_value(c, 1, k_off + d);"),
     "fp16_exponent_bias": ("mag = ldexp((double)(1024 + frac), e - 25);",
                            "mag = ldexp((double)(1024 + frac), e - 24);"),
     "bf16_low_bit": ("uint32_t u = (uint32_t)bits << 16;",
@@ -63,6 +63,13 @@ MUTANTS = {
     "e4m3_subnormal_step": ("mag = ldexp((double)f, -9);", "mag = ldexp((double)f, -10);"),
     "fp8_scale_multiplies": ("float kq = (float)decode(k, src, dtype) / k_scale;",
                              "float kq = (float)decode(k, src, dtype) * k_scale;"),
+    "fp8_read_scales_swapped": ("* (which ? c->v_scale : c->k_scale);",
+                                "* (which ? c->k_scale : c->v_scale);"),
+    "fp8_read_scale_dropped": ("* (which ? c->v_scale : c->k_scale);", "* 1.0;"),
+    "fp8_read_as_16bit": ("    if (c->cache_fp8)\n        return e4m3_value(",
+                          "    if (0)\n        return e4m3_value("),
+    "fp8_append_writes_v_with_k_scale": ("(int64_t)num_pages * page_size, cache_fp8, k_scale, v_scale,",
+                                         "(int64_t)num_pages * page_size, cache_fp8, k_scale, k_scale,"),
     "write_skips_slot_zero": ("        if (slot[n] < 0)\n            continue;", "        if (slot[n] <= 0)\n            continue;"),
     "append_position_off_by_one": ("int64_t pos = (int64_t)cache_seqlens[b] + (i - cu_q[b]);",
                                    "int64_t pos = (int64_t)cache_seqlens[b] + (i - cu_q[b]) + 1;"),
@@ -83,7 +90,7 @@ MUTANTS = {
 
 PIN_FILES = ["test_oracle_pins.py", "test_oracle_pins_window_softcap.py",
              "test_oracle_pins_varlen_sinks.py", "test_oracle_pins_kv_write.py",
-             "test_oracle_pins_bwd.py"]
+             "test_oracle_pins_bwd.py", "test_oracle_pins_fp8_cache.py"]
 
 PLUGIN = "import os, oracle\noracle._LIB = os.environ['ORACLE_MUTANT_LIB']\n"
 
