@@ -215,6 +215,16 @@ miattn_status attn_fwd_varlen(const void *q, const void *k, const void *v,
  *            attn_fwd_varlen, with p_i = i + cache_seqlens[b] - Sq_b
  *   o, lse   [total_q, Hq, D] and [Hq, total_q], as for attn_fwd_varlen
  *   B, Hq, Hkv, D, dtype, stream  as for attn_fwd_paged
+ *   cache_dtype  equal to dtype (16-bit pools), or MIATTN_CACHE_FP8_E4M3:
+ *            the pools hold E4M3FN codes and a key (value) element is the
+ *            code's value times *k_scale (*v_scale) (TileOPs "Attention
+ *            Operators", GQAPrefillPagedWithKVCacheFwdOp: the dequantization
+ *            scales of an FP8 pool; GQAVarlenFwdOp: each scale multiplies its
+ *            tensor).  FP8 pools are served for D = 64 and 128 (D = 256:
+ *            UNSUPPORTED); the pools must be 16-byte aligned
+ *   k_scale, v_scale  device float32 [1], required with an FP8 pool (finite
+ *            and positive, the caller's obligation: checked only under
+ *            MIATTN_VALIDATE=1), else ignored
  */
 miattn_status attn_fwd_paged_varlen(const void *q, const void *k_cache, const void *v_cache,
                                     const int32_t *cache_seqlens, const int32_t *block_table,
@@ -223,7 +233,8 @@ miattn_status attn_fwd_paged_varlen(const void *q, const void *k_cache, const vo
                                     const float *sinks, void *o, float *lse, int B,
                                     int total_q, int max_seqlen_q, int Hq, int Hkv, int D,
                                     int max_pages, int num_phys_pages, float scale,
-                                    miattn_dtype dtype, void *stream);
+                                    miattn_dtype dtype, miattn_cache_dtype cache_dtype,
+                                    const float *k_scale, const float *v_scale, void *stream);
 
 /*
  * Paged KV-cache write: scatter new key and value rows into the page pools.
@@ -252,7 +263,7 @@ miattn_status kv_cache_write(const void *k, const void *v, void *k_pages, void *
                              const float *k_scale, const float *v_scale, void *stream);
 
 /*
- * Paged prefill with append (16-bit pools): request b's chunk -- queries,
+ * Paged prefill with append: request b's chunk -- queries,
  * keys and values at packed rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 --
  * is written to logical positions cache_seqlens[b] + i of its cache (pool
  * row block_table[b, pos / page_size] * page_size + pos % page_size), then
@@ -267,6 +278,9 @@ miattn_status kv_cache_write(const void *k, const void *v, void *k_pages, void *
  *   causal, softcap, scale, o, lse, dtype, stream  as for attn_fwd_paged_varlen
  *                    (lse [Hq, total_q])
  *   B, Hq, Hkv, D, page_size, max_pages, num_phys_pages  as for attn_fwd_paged
+ *   cache_dtype, k_scale, v_scale  as for attn_fwd_paged_varlen; with an FP8
+ *                    pool the chunk is written as kv_cache_write writes it
+ *                    (value / scale as E4M3FN) and read back dequantized
  */
 miattn_status attn_fwd_paged_append(const void *q, const void *k_new, const void *v_new,
                                     void *k_cache, void *v_cache, const int32_t *cache_seqlens,
@@ -274,7 +288,9 @@ miattn_status attn_fwd_paged_append(const void *q, const void *k_new, const void
                                     int page_size, int causal, float softcap, void *o,
                                     float *lse, int B, int total_q, int max_seqlen_q, int Hq,
                                     int Hkv, int D, int max_pages, int num_phys_pages,
-                                    float scale, miattn_dtype dtype, void *stream);
+                                    float scale, miattn_dtype dtype,
+                                    miattn_cache_dtype cache_dtype, const float *k_scale,
+                                    const float *v_scale, void *stream);
 
 /*
  * Attention backward (TileOPs "Attention Operators", GQABwdOp): the gradients

@@ -52,13 +52,15 @@ def lib() -> ctypes.CDLL:
                                       i32, i32, i32, f32, P, P, P, i32, P]
         L.attn_fwd_varlen.restype = i32
         L.attn_fwd_paged_varlen.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, P, P, P,
-                                            i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, P]
+                                            i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                            i32, P, P, P]
         L.attn_fwd_paged_varlen.restype = i32
         i64 = ctypes.c_int64
         L.kv_cache_write.argtypes = [P, P, P, P, P, i32, i32, i32, i64, i32, i32, P, P, P]
         L.kv_cache_write.restype = i32
         L.attn_fwd_paged_append.argtypes = [P, P, P, P, P, P, P, P, i32, i32, f32, P, P, i32,
-                                            i32, i32, i32, i32, i32, i32, i32, f32, i32, P]
+                                            i32, i32, i32, i32, i32, i32, i32, f32, i32, i32, P,
+                                            P, P]
         L.attn_fwd_paged_append.restype = i32
         L.attn_bwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, P, P,
                                i32, P]
@@ -284,20 +286,38 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return o, (lse if return_lse else None)
 
 
+def _pool_kind(q, k_cache, v_cache, k_scale, v_scale):
+    """(cache dtype code, k_scale, v_scale) of a pool pair: 16-bit pools of q's
+    dtype, or torch.float8_e4m3fn pools with float32 [1] scales on q's device."""
+    if k_cache.dtype != v_cache.dtype:
+        raise ValueError("k and v pools must share one dtype")
+    if k_cache.dtype == torch.float8_e4m3fn:
+        for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if sc is None or sc.dtype != torch.float32 or sc.numel() != 1 or sc.device != q.device:
+                raise ValueError(f"an FP8 pool needs {name}: float32 [1] on the GPU")
+        return MIATTN_CACHE_FP8_E4M3, k_scale.contiguous(), v_scale.contiguous()
+    if k_cache.dtype != q.dtype:
+        raise ValueError("q and 16-bit pools must share one dtype")
+    return _dtype_code(q), None, None
+
+
 def attn_fwd_paged_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                           cache_seqlens: torch.Tensor, block_table: torch.Tensor,
                           cu_seqlens_q: torch.Tensor, page_size: int, *,
                           max_seqlen_q: Optional[int] = None, causal: bool = True, scale=None,
                           window=None, softcap=None, sinks: Optional[torch.Tensor] = None,
+                          k_scale: Optional[torch.Tensor] = None,
+                          v_scale: Optional[torch.Tensor] = None,
                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                           return_lse: bool = True
                           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Paged attention over packed queries on the current stream.
 
     q [total_q,Hq,D] delimited by cu_seqlens_q int32 [B+1]; caches, block_table
-    and page_size as for attn_fwd_paged; cache_seqlens int32 [B] (each
-    request's keys, its queries included).  Returns (o [total_q,Hq,D],
-    lse [Hq,total_q])."""
+    and page_size as for attn_fwd_paged (torch.float8_e4m3fn pools take
+    k_scale/v_scale float32 [1] on the device: element = code * scale);
+    cache_seqlens int32 [B] (each request's keys, its queries included).
+    Returns (o [total_q,Hq,D], lse [Hq,total_q])."""
     if q.dim() != 3:
         raise ValueError("q must be rank 3 (THD)")
     if k_cache.shape != v_cache.shape:
@@ -312,8 +332,7 @@ def attn_fwd_paged_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
         n_pages = k_cache.shape[0] // page_size
     else:
         raise ValueError("caches must be rank 3 or 4")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("q and the caches must share one dtype")
+    cache, k_scale, v_scale = _pool_kind(q, k_cache, v_cache, k_scale, v_scale)
     if cache_seqlens.dtype != torch.int32 or block_table.dtype != torch.int32:
         raise ValueError("cache_seqlens and block_table must be int32")
     code = _dtype_code(q)
@@ -341,7 +360,8 @@ def attn_fwd_paged_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                                      int(bool(causal)), *_window(window), _softcap(softcap),
                                      _ptr(sk), _ptr(o), _ptr(lse) if return_lse else None, B,
                                      total_q, mq, Hq, Hkv, D, block_table.shape[1], n_pages,
-                                     _scale(scale), code, _stream())
+                                     _scale(scale), code, cache, _ptr(k_scale), _ptr(v_scale),
+                                     _stream())
     _check(st)
     return o, (lse if return_lse else None)
 
@@ -396,21 +416,24 @@ def attn_fwd_paged_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
                           cache_seqlens: torch.Tensor, block_table: torch.Tensor,
                           cu_seqlens_q: torch.Tensor, page_size: int, *,
                           max_seqlen_q: Optional[int] = None, causal: bool = True, scale=None,
-                          softcap=None, out: Optional[torch.Tensor] = None,
+                          softcap=None, k_scale: Optional[torch.Tensor] = None,
+                          v_scale: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None,
                           lse: Optional[torch.Tensor] = None, return_lse: bool = True
                           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Paged prefill with append on the current stream: writes k_new/v_new
-    [total_q,Hkv,D] after each request's cache_seqlens[b] cached keys (16-bit
-    pools, in place), then attends the packed queries q [total_q,Hq,D] to
-    cache_seqlens[b] + Sq_b keys.  Returns (o [total_q,Hq,D], lse [Hq,total_q])."""
+    [total_q,Hkv,D] after each request's cache_seqlens[b] cached keys (pools
+    written in place: 16-bit, or torch.float8_e4m3fn storing value / scale with
+    k_scale/v_scale float32 [1]), then attends the packed queries q
+    [total_q,Hq,D] to cache_seqlens[b] + Sq_b keys.  Returns (o [total_q,Hq,D],
+    lse [Hq,total_q])."""
     if q.dim() != 3 or k_new.dim() != 3 or k_new.shape != v_new.shape:
         raise ValueError("q, k_new, v_new must be rank 3 (THD), k_new and v_new of one shape")
     if k_new.shape[0] != q.shape[0] or k_new.shape[2] != q.shape[2]:
         raise ValueError("k_new/v_new must have q's token count and head dim")
     if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
         raise ValueError("q, k_new, v_new must share one dtype")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("the pools must be 16-bit pools of q's dtype")
+    cache, k_scale, v_scale = _pool_kind(q, k_cache, v_cache, k_scale, v_scale)
     if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
         raise ValueError("the pools must be contiguous (they are written in place)")
     code = _dtype_code(q)
@@ -441,7 +464,8 @@ def attn_fwd_paged_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
                                        _softcap(softcap), _ptr(o),
                                        _ptr(lse) if return_lse else None, B, total_q, mq, Hq,
                                        Hkv, D, block_table.shape[1], num_slots // page_size,
-                                       _scale(scale), code, _stream()))
+                                       _scale(scale), code, cache, _ptr(k_scale),
+                                       _ptr(v_scale), _stream()))
     return o, (lse if return_lse else None)
 
 

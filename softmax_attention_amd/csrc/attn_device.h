@@ -57,6 +57,20 @@ __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Four E4M3FN codes (bytes 0..3 of w) -> four 16-bit values of the MFMA type,
+// packed in pairs (bytes 0, 1 and 2, 3; the lower byte in the lower half).
+// Exact: every E4M3FN value is both a bf16 and an fp16 value; NaN codes give
+// NaN.  (gfx950's scaled packed conversion, with scale 1.)
+template <bool BF16>
+__device__ __forceinline__ u32x2 fp8x4_to_half4(uint32_t w) {
+    if constexpr (BF16)
+        return {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true))};
+    else
+        return {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, true))};
+}
+
 // ---- LDS tiles.  A K or V tile is stored row-major (one key per row, D
 // contiguous) without padding; the 16-byte chunks of row r are XOR-swizzled
 // (chunk c sits at position c ^ swz(r)) so that both read patterns below hit

@@ -85,8 +85,8 @@ __device__ __forceinline__ void sched_read_ahead() {
 //
 // K/V source: dense tensors, a paged cache whose pages hold whole key tiles,
 // or a paged cache with pages smaller than a tile (each 1 KB piece then
-// looks up its own page).
-enum KvMode { kDense = 0, kPagedTile = 1, kPagedPiece = 2 };
+// looks up its own page); the last two again over FP8 E4M3FN pools.
+enum KvMode { kDense = 0, kPagedTile = 1, kPagedPiece = 2, kPagedTile8 = 3, kPagedPiece8 = 4 };
 
 // CAP: logits are capped (c tanh(z / c), TileOPs "Attention Operators",
 // GQADenseFwdOp stage 6); otherwise the logit is the scaled score itself.
@@ -95,6 +95,11 @@ __global__ __launch_bounds__(64 * WAVES)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, WAVES>(), waves_per_eu<D, WAVES>())))
 void attn_fwd_kernel(const FwdParams p) {
     constexpr bool PAGED = KV != kDense;
+    // FP8 pools: K and V hold E4M3FN codes (paging mode KV - 2), dequantized
+    // by one scale each (TileOPs "Attention Operators",
+    // GQAPrefillPagedWithKVCacheFwdOp: the k_scale and v_scale of an FP8 pool)
+    constexpr bool FP8 = KV == kPagedTile8 || KV == kPagedPiece8;
+    constexpr int KVP = FP8 ? KV - 2 : KV;
     using H = Half<BF16>;
     using vec8 = typename H::vec8;
     constexpr int BM = rows_per_workgroup(WAVES);  // packed rows per workgroup
@@ -113,6 +118,7 @@ void attn_fwd_kernel(const FwdParams p) {
     constexpr int DT = D / 32;                     // 32-wide d blocks of O^T
     constexpr int PSTEPS = BN / 16;                // MFMA k-steps over the tile's keys
     static_assert(PIECES % LOADERS == 0, "whole 1 KB pieces per loading wave");
+    static_assert(!FP8 || SPLIT_ROLES, "FP8 pools are read by the split-role schedule");
 
     // K and V rings of four stages each (128 KB of LDS with 16 KB tiles, one
     // workgroup per CU); separate arrays so that the compiler can tell a load
@@ -281,7 +287,7 @@ void attn_fwd_kernel(const FwdParams p) {
     // lane clamps its own key; with smaller pages each piece gets its own
     // base.  (The scalar unit is shared by the CU's waves, so the per-step
     // scalar address arithmetic is kept small.)
-    constexpr bool tile_in_page = KV != kPagedPiece;
+    constexpr bool tile_in_page = KVP != kPagedPiece;
     int l_key[PPW];  // this lane's key row within the tile, per piece
 #pragma unroll
     for (int e = 0; e < PPW; ++e) l_key[e] = (e * LOADERS + loader) * RPP + l_dr;
@@ -299,7 +305,7 @@ void attn_fwd_kernel(const FwdParams p) {
     // step before the tile's loads are issued, so that the scalar load's
     // latency stays off the issue path.
     auto tile_page = [&](int j) __attribute__((always_inline)) -> int32_t {
-        if constexpr (KV == kPagedTile)
+        if constexpr (KVP == kPagedTile)
             return bt_row[(j < wg_end ? j : first_tile) >> p.page_shift];
         else
             return 0;
@@ -351,8 +357,11 @@ void attn_fwd_kernel(const FwdParams p) {
         issue(vt, pv_, p.v, dv);
     };
 
-    const float c = p.scale_log2;  // > 0
-    const float cap_x = p.cap_x, cap_k2 = p.cap_k2;
+    // (an FP8 pool's key scale multiplies every raw score, so it joins the
+    // factors applied to the raw score)
+    const float k_deq = FP8 ? *p.k_scale : 1.f;
+    const float c = p.scale_log2 * k_deq;  // > 0
+    const float cap_x = p.cap_x * k_deq, cap_k2 = p.cap_k2;
 
     // ---- LDS read addresses, fixed per lane for the whole kernel.  With the
     // swizzle depending on row & 15 only, the 32-key block t and the 16-key
@@ -709,6 +718,120 @@ void attn_fwd_kernel(const FwdParams p) {
             }
             pv_batched(sv, pb);
         };
+        if constexpr (FP8) {
+        // ---- FP8 pools.  Wave 1 moves E4M3FN key and value tiles HBM -> LDS
+        // with direct loads into a four-stage FP8 ring; wave 2 converts each
+        // landed tile into the 16-bit MFMA type, written to one of two 16-bit
+        // stages in the swizzled layout of the 16-bit tiles, so wave 0 runs
+        // the 16-bit path unchanged.  (The roles stay apart because the
+        // compiler cannot tell the ring's stages apart for a wave that reads
+        // LDS while its own direct loads are in flight: it would wait for all
+        // of them.)  Step n: wave 0 computes tile n from 16-bit stage n & 1;
+        // wave 2 converts tile n + 1 (landed during step n - 1); wave 1 issues
+        // tile n + 4 into the FP8 stage tile n left, then waits for tile n + 2.
+        // A piece (1 KB) holds RPP8 whole key rows, lane l its 16 bytes (16
+        // d-values) at offset 16 l.  (Tiles of a paged call follow one
+        // another: there is no padding mask.)
+        constexpr int U16 = D / 16;          // 16-byte pieces per key row
+        constexpr int RPP8 = 1024 / D;       // key rows per 1 KB piece
+        constexpr int STAGE8 = BN * D;       // bytes of one FP8 K (or V) tile
+        constexpr int PC8 = STAGE8 / 1024;   // pieces per tensor and tile
+        __shared__ __attribute__((aligned(1024))) uint8_t fK0[STAGE8];
+        __shared__ __attribute__((aligned(1024))) uint8_t fV0[STAGE8];
+        __shared__ __attribute__((aligned(1024))) uint8_t fK1[STAGE8];
+        __shared__ __attribute__((aligned(1024))) uint8_t fV1[STAGE8];
+        __shared__ __attribute__((aligned(1024))) uint8_t fK2[STAGE8];
+        __shared__ __attribute__((aligned(1024))) uint8_t fV2[STAGE8];
+        __shared__ __attribute__((aligned(1024))) uint8_t fK3[STAGE8];
+        __shared__ __attribute__((aligned(1024))) uint8_t fV3[STAGE8];
+        const uint8_t *k8 = (const uint8_t *)p.k, *v8 = (const uint8_t *)p.v;
+        const int row8 = p.Hkv * D;  // bytes between consecutive keys
+        const int l_row8 = lane / U16, l_col8 = lane % U16;
+        const bool dma = wave_u == 1, conv = wave_u == 2;
+        auto issue8 = [&](int j0, uint8_t *dk, uint8_t *dv) __attribute__((always_inline)) {
+            if (!dma) return;
+            // a tile past the range keeps the load count, every lane reading
+            // the first tile's first 16 bytes
+            const bool pad = j0 >= wg_end;
+            const int keep = pad ? 0 : -1;
+            if (pad) j0 = first_tile;
+            const int last = kv_len - 1 - j0;  // last valid key row of the tile
+            if constexpr (KVP == kPagedTile) {
+                const int64_t off =
+                    cache_row(bt_row[j0 >> p.page_shift], j0) * row8 + (int64_t)kvh * D;
+#pragma unroll
+                for (int e = 0; e < PC8; ++e) {
+                    const int vo = (min(e * RPP8 + l_row8, last) * row8 + 16 * l_col8) & keep;
+                    buffer_load_lds16(k8 + off, BN * row8, (lds_void *)(dk + e * 1024), vo);
+                    buffer_load_lds16(v8 + off, BN * row8, (lds_void *)(dv + e * 1024), vo);
+                }
+            } else {
+                // pages smaller than a tile: a piece's rows lie in one page
+#pragma unroll
+                for (int e = 0; e < PC8; ++e) {
+                    const int jr = min(j0 + e * RPP8, kv_len - 1);
+                    const int64_t off =
+                        cache_row(bt_row[jr >> p.page_shift], jr) * row8 + (int64_t)kvh * D;
+                    const int vo = (min(l_row8, kv_len - 1 - jr) * row8 + 16 * l_col8) & keep;
+                    buffer_load_lds16(k8 + off, RPP8 * row8, (lds_void *)(dk + e * 1024), vo);
+                    buffer_load_lds16(v8 + off, RPP8 * row8, (lds_void *)(dv + e * 1024), vo);
+                }
+            }
+        };
+        // an FP8 stage -> a 16-bit stage: lane l's 16 bytes of piece e are
+        // chunks 2 l_col8 and 2 l_col8 + 1 (d 0..7 and 8..15 of the piece) of
+        // key row e RPP8 + l_row8
+        auto convert8 = [&](const uint8_t *fk, const uint8_t *fv, uint8_t *dk, uint8_t *dv) __attribute__((always_inline)) {
+            if (!conv) return;
+#pragma unroll
+            for (int e = 0; e < PC8; ++e) {
+                const u32x4 kw = *(const u32x4 *)(fk + e * 1024 + 16 * lane);
+                const u32x4 vw = *(const u32x4 *)(fv + e * 1024 + 16 * lane);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const u32x2 k01 = fp8x4_to_half4<BF16>(kw[2 * h]);
+                    const u32x2 k23 = fp8x4_to_half4<BF16>(kw[2 * h + 1]);
+                    const u32x2 v01 = fp8x4_to_half4<BF16>(vw[2 * h]);
+                    const u32x2 v23 = fp8x4_to_half4<BF16>(vw[2 * h + 1]);
+                    const int at = tile_off<D>(e * RPP8 + l_row8, 2 * l_col8 + h);
+                    *(u32x4 *)(dk + at) = u32x4{k01[0], k01[1], k23[0], k23[1]};
+                    *(u32x4 *)(dv + at) = u32x4{v01[0], v01[1], v23[0], v23[1]};
+                }
+            }
+        };
+        int n = 0;  // the tile computed next: key first_tile + n * BN
+#define MIATTN_F8_STEP(F_NEW_K, F_NEW_V, F_NXT_K, F_NXT_V, K_CUR, V_CUR, K_NXT, V_NXT)      \
+        {                                                                               \
+            t0 = first_tile + n * BN;                                                   \
+            issue8(t0 + 4 * BN, F_NEW_K, F_NEW_V);                                      \
+            compute(K_CUR, V_CUR);                                                      \
+            convert8(F_NXT_K, F_NXT_V, K_NXT, V_NXT);                                   \
+            /* tile n + 2 has landed when only the two younger tiles' loads remain */  \
+            wait_vmcnt<2 * 2 * PC8>();                                                  \
+            ring_barrier();                                                             \
+            ++n;                                                                        \
+        }
+        if (first_tile < wg_end) {
+            issue8(first_tile, fK0, fV0);
+            issue8(first_tile + BN, fK1, fV1);
+            issue8(first_tile + 2 * BN, fK2, fV2);
+            issue8(first_tile + 3 * BN, fK3, fV3);
+            wait_vmcnt<2 * 2 * PC8>();  // tiles 0 and 1
+            ring_barrier();
+            convert8(fK0, fV0, sK0, sV0);
+            ring_barrier();
+            // whole rounds of four steps (steps past the range compute nothing
+            // and issue pad loads), so that every step sees the same ring state
+            do {
+                MIATTN_F8_STEP(fK0, fV0, fK1, fV1, sK0, sV0, sK1, sV1)
+                MIATTN_F8_STEP(fK1, fV1, fK2, fV2, sK1, sV1, sK0, sV0)
+                MIATTN_F8_STEP(fK2, fV2, fK3, fV3, sK0, sV0, sK1, sV1)
+                MIATTN_F8_STEP(fK3, fV3, fK0, fV0, sK1, sV1, sK0, sV0)
+            } while (first_tile + n * BN < wg_end);
+            wait_vmcnt<0>();
+        }
+#undef MIATTN_F8_STEP
+        } else {
 #define MIATTN_ST_STEP(K_CUR, V_CUR, K_NEW, V_NEW)                                      \
         {                                                                               \
             t3 = t2 < wg_end ? find_tile(t2 + BN, lo3, hi3) : wg_end;                   \
@@ -772,14 +895,17 @@ void attn_fwd_kernel(const FwdParams p) {
             wait_vmcnt<0>();
         }
 #undef MIATTN_ST3_STEP
+        }
     }
 
     // ---- epilogue: normalise and store (no barrier below this point)
     if (!wave_active) return;
     const float l_tot = sum_halves(l_run);
     if (!row_ok) return;
-    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float lse_v = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    // (only a row without a visible key has l = 0; a NaN score -- a NaN in q
+    // or k -- makes l NaN, and the NaN goes on into o and lse)
+    float inv = l_tot != 0.f ? 1.f / l_tot : 0.f;
+    float lse_v = l_tot != 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     const int my_h = kvh * p.G + my_gh;
     if (!partial && p.sinks != nullptr) {
         // The head's sink logit joins the denominator only, used as given
@@ -800,6 +926,8 @@ void attn_fwd_kernel(const FwdParams p) {
             lse_v = (mx + __builtin_amdgcn_logf(den)) * kLn2;
         }
     }
+
+    if constexpr (FP8) inv *= *p.v_scale;  // the value pool's scale multiplies the output
 
     if (!partial) {
         uint16_t *orow = p.o + ((q_row0 + my_i) * p.Hq + my_h) * D;
@@ -944,6 +1072,16 @@ int blocks_per_cu() {
 template <int D, int W, bool CAP>
 int decode_blocks(const FwdParams &p, bool bf16, bool paged) {
     const bool tile = p.page_shift >= __builtin_ctz(keys_per_tile(D, W));
+    if constexpr (W == 3) {
+        if (paged && p.k_scale != nullptr) {
+            if (tile)
+                return bf16 ? blocks_per_cu<D, true, kPagedTile8, W, CAP>()
+                            : blocks_per_cu<D, false, kPagedTile8, W, CAP>();
+            return bf16 ? blocks_per_cu<D, true, kPagedPiece8, W, CAP>()
+                        : blocks_per_cu<D, false, kPagedPiece8, W, CAP>();
+        }
+    }
+    if (p.k_scale != nullptr) return 0;  // FP8 pools: the three-wave schedule only
     if (!paged)
         return bf16 ? blocks_per_cu<D, true, kDense, W, CAP>()
                     : blocks_per_cu<D, false, kDense, W, CAP>();
@@ -962,8 +1100,15 @@ hipError_t launch_kv(const FwdParams &p, bool bf16, int grid, hipStream_t stream
 
 template <int D, int WAVES, bool CAP>
 hipError_t launch_w(const FwdParams &p, bool bf16, bool paged, int grid, hipStream_t stream) {
+    const bool tile = p.page_shift >= __builtin_ctz(keys_per_tile(D, WAVES));
+    if constexpr (WAVES == 3) {
+        if (paged && p.k_scale != nullptr)
+            return tile ? launch_kv<D, WAVES, kPagedTile8, CAP>(p, bf16, grid, stream)
+                        : launch_kv<D, WAVES, kPagedPiece8, CAP>(p, bf16, grid, stream);
+    }
+    if (p.k_scale != nullptr) return hipErrorInvalidValue;  // FP8 pools: three waves only
     if (!paged) return launch_kv<D, WAVES, kDense, CAP>(p, bf16, grid, stream);
-    if (p.page_shift >= __builtin_ctz(keys_per_tile(D, WAVES)))
+    if (tile)
         return launch_kv<D, WAVES, kPagedTile, CAP>(p, bf16, grid, stream);
     return launch_kv<D, WAVES, kPagedPiece, CAP>(p, bf16, grid, stream);
 }

@@ -66,6 +66,9 @@ struct FwdParams {
     const int32_t *cu_q;        // packed (THD) queries: offsets [B + 1], or nullptr
     const int32_t *cu_kv;       // packed dense keys: offsets [B + 1], or nullptr
     const float *sinks;         // [Hq] sink logits, or nullptr
+    // FP8 E4M3FN pools (paged, 3-wave schedule): k/v point at codes, and the
+    // element is code * *k_scale (or *v_scale); nullptr for 16-bit K/V
+    const float *k_scale, *v_scale;
     int kv_append;              // paged: seqlen excludes the appended chunk (see SeqDesc)
     int total_q, total_kv;      // packed row counts (lse of a packed call is [Hq, total_q])
     int B, Sq, Hq, Hkv, G, Skv; // packed calls: Sq and Skv are the per-request maxima

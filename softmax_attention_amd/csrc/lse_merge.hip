@@ -91,11 +91,16 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
         return g * T / p.sk_grid == (g + 1) * T / p.sk_grid;
     };
 
+    // the largest partial LSE; a NaN one (a NaN score in its share) wins, so
+    // that the NaN reaches o and lse
+    auto max_nan = [](float a, float b) -> float {
+        return a != a ? a : (b != b ? b : fmaxf(a, b));
+    };
     float M = -INFINITY;
     for (int s = lane; s < n_valid; s += 64)
-        if (!skip(s)) M = fmaxf(M, p.lse_part[base + (int64_t)s * stride]);
+        if (!skip(s)) M = max_nan(M, p.lse_part[base + (int64_t)s * stride]);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    for (int off = 32; off >= 1; off >>= 1) M = max_nan(M, __shfl_xor(M, off));
 
     float accv[PER];
 #pragma unroll
@@ -115,8 +120,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
         }
     }
     const int h = kvh * p.G + gh;
-    float inv = den > 0.f ? 1.f / den : 0.f;
-    float lse_out = den > 0.f ? M + __logf(den) : -INFINITY;
+    float inv = den != 0.f ? 1.f / den : 0.f;
+    float lse_out = den != 0.f ? M + __logf(den) : -INFINITY;
     if (p.sinks != nullptr) {
         const float sk = p.sinks[h];
         if (den == 0.f || sk == INFINITY) {

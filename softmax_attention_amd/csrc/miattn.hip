@@ -74,8 +74,8 @@ struct DeviceState {
     void *ws = nullptr;  // split-KV partials
     size_t ws_bytes = 0;
     int cus = 0;
-    // decode kernel occupancy: [3 waves][D 128][bf16][paged][capped logits]
-    int decode_per_cu[2][2][2][2][2] = {};
+    // decode kernel occupancy: [3 waves][D 128][bf16][paged][capped logits][FP8 pools]
+    int decode_per_cu[2][2][2][2][2][2] = {};
 };
 
 std::mutex g_mu;
@@ -98,7 +98,8 @@ int compute_units(int dev) {
 int decode_per_cu(int dev, const miattn::FwdParams &p, int D, bool bf16, bool paged, int waves,
                   bool cap) {
     std::lock_guard<std::mutex> lock(g_mu);
-    int &slot = g_dev[dev].decode_per_cu[waves == 3][D == 128][bf16][paged][cap];
+    int &slot =
+        g_dev[dev].decode_per_cu[waves == 3][D == 128][bf16][paged][cap][p.k_scale != nullptr];
     if (slot == 0) {
         const int n = miattn::attn_fwd_decode_blocks_per_cu(p, D, bf16, paged, waves, cap);
         slot = n > 0 ? n : -1;
@@ -297,6 +298,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     const int forced = env_int("MIATTN_WAVES", 0);
     if (D <= 128 && (forced == 2 || forced == 3 || forced == 8)) waves = forced;
     if (waves == 2 && cap) waves = 3;  // the two-wave comparison schedule has no capped build
+    if (p.k_scale != nullptr) waves = 3;  // FP8 pools: the three-wave schedule reads them
     const int BN = miattn::keys_per_tile(D, waves);
     const int BM = miattn::rows_per_workgroup(waves);
     p.n_mblocks = (p.rows + BM - 1) / BM;
@@ -310,8 +312,8 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     // workgroup waits on a long request or for a dispatch slot.  A forced
     // split length selects the split plan below instead.
     // (the plan's tile sums are 32-bit: Hkv * B * tiles of the capacity)
-    if ((waves == 2 || waves == 3) && split_keys <= 0 && bhs * cap_tiles < INT_MAX &&
-        env_int("MIATTN_STREAMK", 1)) {
+    if ((waves == 2 || waves == 3) && p.rows <= miattn::kRowsPerWave && split_keys <= 0 &&
+        bhs * cap_tiles < INT_MAX && env_int("MIATTN_STREAMK", 1)) {
         int per_cu = decode_per_cu(dev, p, D, bf16, paged, waves, cap);
         const int want = env_int("MIATTN_SK_PER_CU", 0);  // tuning override
         if (want > 0 && want < per_cu) per_cu = want;
@@ -519,7 +521,9 @@ miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache
                          const float *sinks, void *o, float *lse, int B, int Sq, int Hq, int Hkv,
                          int D, int max_pages, int num_phys_pages, float scale,
                          miattn_dtype dtype, void *stream,
-                         const miattn::KvWriteParams *append = nullptr) {
+                         const miattn::KvWriteParams *append = nullptr,
+                         int cache_dtype = -1,  // -1: 16-bit pools of the inputs' dtype
+                         const float *k_scale = nullptr, const float *v_scale = nullptr) {
     g_err[0] = '\0';
     // (a packed call without query rows has nothing to check q and o against)
     miattn_status st = check_common(q, o, lse, B, (packed && total_q == 0) ? 0 : Sq, Hq, Hkv,
@@ -540,6 +544,17 @@ miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache
         return fail(MIATTN_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
     if (packed && total_q < 0)
         return fail(MIATTN_ERR_INVALID_ARG, "total_q=%d must be >= 0", total_q);
+    if (cache_dtype < 0) cache_dtype = (int)dtype;
+    const bool fp8 = cache_dtype == MIATTN_CACHE_FP8_E4M3;
+    if (!fp8 && cache_dtype != (int)dtype)
+        return fail(MIATTN_ERR_UNSUPPORTED,
+                    "cache_dtype %d must equal dtype %d or be MIATTN_CACHE_FP8_E4M3",
+                    cache_dtype, (int)dtype);
+    if (fp8 && D > 128)
+        return fail(MIATTN_ERR_UNSUPPORTED, "FP8 pools: D=%d unsupported (64, 128)", D);
+    if (fp8 && (!k_scale || !v_scale || ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u)))
+        return fail(MIATTN_ERR_INVALID_ARG,
+                    "an FP8 pool needs 4-byte aligned k_scale and v_scale");
     if (sinks && ((uintptr_t)sinks & 3u))
         return fail(MIATTN_ERR_INVALID_ARG, "sinks not 4-byte aligned");
     const int64_t capacity = (int64_t)max_pages * page_size;
@@ -590,6 +605,16 @@ miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache
             st = validate_offsets(cu_q, B, total_q, Sq, "cu_seqlens_q", s);
             if (st != MIATTN_OK) return st;
         }
+        if (fp8) {
+            float sc[2] = {1.f, 1.f};
+            e = hipMemcpyAsync(&sc[0], k_scale, sizeof(float), hipMemcpyDeviceToHost, s);
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(&sc[1], v_scale, sizeof(float), hipMemcpyDeviceToHost, s);
+            if (e == hipSuccess) e = hipStreamSynchronize(s);
+            if (e != hipSuccess) return hip_fail(e, "MIATTN_VALIDATE scale copy");
+            if (!(sc[0] > 0.f) || !(sc[1] > 0.f) || isinf(sc[0]) || isinf(sc[1]))
+                return fail(MIATTN_ERR_INVALID_ARG, "FP8 scales must be finite and positive");
+        }
     }
 
     FwdParams p = {};
@@ -603,6 +628,8 @@ miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache
     p.cu_q = cu_q;
     p.total_q = total_q;
     p.sinks = sinks;
+    p.k_scale = fp8 ? k_scale : nullptr;
+    p.v_scale = fp8 ? v_scale : nullptr;
     p.B = B;
     p.Sq = Sq;
     p.Hq = Hq;
@@ -620,6 +647,10 @@ miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache
         miattn::KvWriteParams w = *append;
         w.k_pool16 = (uint16_t *)k_cache;
         w.v_pool16 = (uint16_t *)v_cache;
+        w.k_pool8 = (uint8_t *)k_cache;
+        w.v_pool8 = (uint8_t *)v_cache;
+        w.k_scale = k_scale;
+        w.v_scale = v_scale;
         w.cu_q = cu_q;
         w.cache_seqlens = real_seqlen_kv;
         w.block_table = block_table;
@@ -629,7 +660,7 @@ miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache
         w.num_slots = (int64_t)num_phys_pages * page_size;
         w.tokens = total_q;
         w.row_elems = Hkv * D;
-        hipError_t e = miattn::launch_kv_write(w, dtype == MIATTN_BF16, false, true,
+        hipError_t e = miattn::launch_kv_write(w, dtype == MIATTN_BF16, fp8, true,
                                                (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "KV write kernel launch");
         p.kv_append = 1;
@@ -680,11 +711,16 @@ miattn_status attn_fwd_paged_varlen(const void *q, const void *k_cache, const vo
                                     const float *sinks, void *o, float *lse, int B,
                                     int total_q, int max_seqlen_q, int Hq, int Hkv, int D,
                                     int max_pages, int num_phys_pages, float scale,
-                                    miattn_dtype dtype, void *stream) {
+                                    miattn_dtype dtype, miattn_cache_dtype cache_dtype,
+                                    const float *k_scale, const float *v_scale, void *stream) {
+    if ((int)cache_dtype < 0 || (int)cache_dtype > MIATTN_CACHE_FP8_E4M3) {
+        g_err[0] = '\0';
+        return fail(MIATTN_ERR_INVALID_ARG, "cache_dtype %d unknown", (int)cache_dtype);
+    }
     return paged_call(q, k_cache, v_cache, cache_seqlens, block_table, page_size, causal,
                       window_left, window_right, softcap, true, cu_seqlens_q, total_q, sinks, o,
                       lse, B, max_seqlen_q, Hq, Hkv, D, max_pages, num_phys_pages, scale, dtype,
-                      stream);
+                      stream, nullptr, cache_dtype, k_scale, v_scale);
 }
 
 miattn_status kv_cache_write(const void *k, const void *v, void *k_pages, void *v_pages,
@@ -700,6 +736,8 @@ miattn_status kv_cache_write(const void *k, const void *v, void *k_pages, void *
     if (dtype != MIATTN_BF16 && dtype != MIATTN_FP16)
         return fail(MIATTN_ERR_UNSUPPORTED, "dtype %d unsupported (MIATTN_BF16, MIATTN_FP16)",
                     (int)dtype);
+    if ((int)cache_dtype < 0 || (int)cache_dtype > MIATTN_CACHE_FP8_E4M3)
+        return fail(MIATTN_ERR_INVALID_ARG, "cache_dtype %d unknown", (int)cache_dtype);
     const bool fp8 = cache_dtype == MIATTN_CACHE_FP8_E4M3;
     if (!fp8 && (int)cache_dtype != (int)dtype)
         return fail(MIATTN_ERR_UNSUPPORTED,
@@ -770,7 +808,13 @@ miattn_status attn_fwd_paged_append(const void *q, const void *k_new, const void
                                     int page_size, int causal, float softcap, void *o,
                                     float *lse, int B, int total_q, int max_seqlen_q, int Hq,
                                     int Hkv, int D, int max_pages, int num_phys_pages,
-                                    float scale, miattn_dtype dtype, void *stream) {
+                                    float scale, miattn_dtype dtype,
+                                    miattn_cache_dtype cache_dtype, const float *k_scale,
+                                    const float *v_scale, void *stream) {
+    if ((int)cache_dtype < 0 || (int)cache_dtype > MIATTN_CACHE_FP8_E4M3) {
+        g_err[0] = '\0';
+        return fail(MIATTN_ERR_INVALID_ARG, "cache_dtype %d unknown", (int)cache_dtype);
+    }
     if (B > 0 && total_q > 0 && max_seqlen_q > 0) {
         if (!k_new || !v_new) {
             g_err[0] = '\0';
@@ -787,7 +831,7 @@ miattn_status attn_fwd_paged_append(const void *q, const void *k_new, const void
     return paged_call(q, k_cache, v_cache, cache_seqlens, block_table, page_size, causal, -1,
                       -1, softcap, true, cu_seqlens_q, total_q, nullptr, o, lse, B,
                       max_seqlen_q, Hq, Hkv, D, max_pages, num_phys_pages, scale, dtype, stream,
-                      &w);
+                      &w, cache_dtype, k_scale, v_scale);
 }
 
 miattn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,

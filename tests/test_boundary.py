@@ -131,14 +131,15 @@ def varlen(**kw):
 def paged_varlen(**kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, bt=FAKE, cq=FAKE, page_size=64, causal=1,
              wl=-1, wr=-1, softcap=0.0, sinks=None, o=FAKE, lse=None, B=2, tq=5, mq=4, Hq=8,
-             Hkv=2, D=128, max_pages=4, n_phys=8, scale=NAN, dtype=0, stream=None)
+             Hkv=2, D=128, max_pages=4, n_phys=8, scale=NAN, dtype=0, cache=0, ks=None, vs=None,
+             stream=None)
     a.update(kw)
     L = mi.lib()
     st = L.attn_fwd_paged_varlen(a["q"], a["kc"], a["vc"], a["lens"], a["bt"], a["cq"],
                                  a["page_size"], a["causal"], a["wl"], a["wr"], a["softcap"],
                                  a["sinks"], a["o"], a["lse"], a["B"], a["tq"], a["mq"], a["Hq"],
                                  a["Hkv"], a["D"], a["max_pages"], a["n_phys"], a["scale"],
-                                 a["dtype"], a["stream"])
+                                 a["dtype"], a["cache"], a["ks"], a["vs"], a["stream"])
     return st, L.miattn_last_error().decode()
 
 
@@ -166,6 +167,12 @@ def test_varlen_refusals(kw, status, needle):
     (dict(page_size=24), 2, "page_size=24"),
     (dict(lens=None), 1, "must not be NULL"),
     (dict(sinks=FAKE + 2), 1, "sinks not 4-byte aligned"),
+    (dict(cache=1), 2, "cache_dtype 1 must equal dtype 0"),
+    (dict(cache=-1), 1, "cache_dtype -1 unknown"),
+    (dict(cache=7), 1, "cache_dtype 7 unknown"),
+    (dict(cache=2), 1, "an FP8 pool needs 4-byte aligned k_scale and v_scale"),
+    (dict(cache=2, ks=FAKE, vs=FAKE + 2), 1, "an FP8 pool needs"),
+    (dict(cache=2, ks=FAKE, vs=FAKE, D=256, Hq=8, Hkv=2), 2, "FP8 pools: D=256"),
 ])
 def test_paged_varlen_refusals(kw, status, needle):
     st, msg = paged_varlen(**kw)
@@ -196,6 +203,8 @@ def kvw(**kw):
     (dict(num_slots=-5), 1, "num_slots"),
     (dict(dtype=3), 2, "dtype 3"),
     (dict(cache=1), 2, "cache_dtype 1 must equal dtype 0"),
+    (dict(cache=-1), 1, "cache_dtype -1 unknown"),
+    (dict(cache=7), 1, "cache_dtype 7 unknown"),
     (dict(Hkv=1, D=12), 2, "multiple of 8"),
     (dict(sl=None), 1, "must not be NULL"),
     (dict(k=FAKE + 8), 1, "16-byte aligned"),
@@ -216,14 +225,15 @@ def test_kv_write_without_tokens_is_ok_without_touching_the_device():
 def append_call(**kw):
     a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, bt=FAKE, cq=FAKE,
              page_size=64, causal=1, softcap=0.0, o=FAKE, lse=None, B=2, tq=5, mq=4, Hq=8,
-             Hkv=2, D=128, max_pages=4, n_phys=8, scale=NAN, dtype=0, stream=None)
+             Hkv=2, D=128, max_pages=4, n_phys=8, scale=NAN, dtype=0, cache=0, ks=None, vs=None,
+             stream=None)
     a.update(kw)
     L = mi.lib()
     st = L.attn_fwd_paged_append(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["lens"],
                                  a["bt"], a["cq"], a["page_size"], a["causal"], a["softcap"],
                                  a["o"], a["lse"], a["B"], a["tq"], a["mq"], a["Hq"], a["Hkv"],
                                  a["D"], a["max_pages"], a["n_phys"], a["scale"], a["dtype"],
-                                 a["stream"])
+                                 a["cache"], a["ks"], a["vs"], a["stream"])
     return st, L.miattn_last_error().decode()
 
 
@@ -233,6 +243,7 @@ def append_call(**kw):
     (dict(cq=None), 1, "cu_seqlens_q must not be NULL"),
     (dict(page_size=20), 2, "page_size=20"),
     (dict(softcap=-3.0), 1, "softcap"),
+    (dict(cache=2, ks=None, vs=FAKE), 1, "an FP8 pool needs"),
 ])
 def test_paged_append_refusals(kw, status, needle):
     st, msg = append_call(**kw)

@@ -1,0 +1,178 @@
+"""GPU parity of paged attention over FP8 E4M3FN pools (TileOPs "Attention
+Operators", GQAPrefillPagedWithKVCacheFwdOp: an FP8 pool with one key and one
+value dequantization scale) against the fp64 oracle, with the comparison rule
+of tests/parity.py: stream-K decode, the split plan, packed prefill-shaped
+requests (several row blocks), pages smaller than a key tile, both 16-bit
+query types, window, softcap and sinks, the append that writes the chunk
+quantized and reads it back, NaN codes, and the full-size decode workload
+with its caches quantized."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import softmax_attention_amd as mi
+from softmax_attention_amd import workloads
+from tests.parity import check_rows
+from tests.test_parity_gpu import DEV, _reset_split, say
+from tests.test_parity_gpu_varlen_sinks import compare, make_sinks
+
+pytestmark = pytest.mark.gpu
+
+__all__ = ["_reset_split"]  # the autouse fixture that restores the split plan
+
+
+def fp8_codes(shape, seed):
+    """E4M3FN codes: quantized normal values (sigma 40, so codes span the range)
+    with one code in eight drawn uniformly (subnormals, zeros, both signs);
+    no NaN codes."""
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn(shape, generator=g) * 40).clamp(-440, 440)
+    codes = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    u = torch.randint(0, 256, shape, generator=g, dtype=torch.uint8)
+    pick = torch.randint(0, 8, shape, generator=g) == 0
+    codes = torch.where(pick, u, codes)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C
+    return codes.view(torch.float8_e4m3fn)
+
+
+def scales(ks, vs):
+    return (torch.tensor([ks], dtype=torch.float32), torch.tensor([vs], dtype=torch.float32))
+
+
+def fp8_case(sq, lens, Hq, Hkv, D, page_size, *, dtype=torch.bfloat16, causal=True, window=None,
+             softcap=None, sinks=None, split_keys=0, ks=0.02, vs=0.05, seed=0, what=""):
+    say(f"fp8 {what} sq={sq} lens={lens} Hq={Hq} Hkv={Hkv} D={D} page={page_size} {dtype} "
+        f"window={window} softcap={softcap} sinks={sinks is not None} split_keys={split_keys}")
+    B = len(lens)
+    max_pages = max(1, -(-max(lens) // page_size))
+    n_phys = B * max_pages + 3
+    g = torch.Generator().manual_seed(seed)
+    bt = torch.randperm(n_phys, generator=g)[:B * max_pages].view(B, max_pages).to(torch.int32)
+    kc = fp8_codes((n_phys * page_size, Hkv, D), seed + 1)
+    vc = fp8_codes((n_phys * page_size, Hkv, D), seed + 2)
+    q = workloads.dense_inputs(1, max(sum(sq), 1), 1, Hq, Hkv, D, dtype=dtype, seed=seed + 3)[0]
+    q = q[0, :sum(sq)]
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum(sq)]), dtype=torch.int32)
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    k_s, v_s = scales(ks, vs)
+    mi.set_split_keys(split_keys)
+    o, lse = mi.attn_fwd_paged_varlen(q.to(DEV), kc.to(DEV), vc.to(DEV), lens_t.to(DEV),
+                                      bt.to(DEV), cu_q.to(DEV), page_size, causal=causal,
+                                      window=window, softcap=softcap,
+                                      sinks=None if sinks is None else sinks.to(DEV),
+                                      k_scale=k_s.to(DEV), v_scale=v_s.to(DEV))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_paged_varlen(q, kc, vc, lens_t, bt, page_size, cu_q,
+                                              causal=causal, window=window, softcap=softcap,
+                                              sinks=sinks, cache_fp8=True, k_scale=ks,
+                                              v_scale=vs)
+    return compare(o, lse, o_ref, lse_ref, what)
+
+
+def test_fp8_decode_streamk():
+    lens = [1, 0, 64, 65, 1000, 513, 2047, 300]
+    fp8_case([1] * len(lens), lens, 32, 8, 128, 64, seed=300, what="decode")
+
+
+def test_fp8_decode_split_plan_d64_fp16_small_pages():
+    lens = [1, 0, 64, 65, 1000, 513, 2047, 300]
+    fp8_case([1] * len(lens), lens, 8, 2, 64, 16, dtype=torch.float16, split_keys=128,
+             ks=0.5, vs=2.0, seed=301, what="split")
+
+
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_fp8_packed_prefill_row_blocks_window_softcap_sinks(page_size):
+    # 37 queries x G = 4 packed rows: several 32-row blocks per request
+    fp8_case([37, 1, 0, 5], [900, 40, 20, 2000], 16, 4, 128, page_size, window=(300, -1),
+             softcap=25.0, sinks=make_sinks(16, 302), seed=302, what="prefill")
+
+
+def test_fp8_decode_non_causal_fp16():
+    lens = [130, 7, 4096]
+    fp8_case([1, 3, 2], lens, 8, 8, 128, 64, dtype=torch.float16, causal=False, ks=0.01,
+             vs=0.3, seed=303, what="mha")
+
+
+@pytest.mark.parametrize("split_keys", [0, 64])
+def test_fp8_nan_code_reaches_exactly_the_rows_that_see_it(split_keys):
+    say(f"fp8 NaN code split_keys={split_keys}")
+    mi.set_split_keys(split_keys)
+    page_size, Hq, Hkv, D = 64, 8, 2, 128
+    lens, sq = [200], [5]  # queries at keys 195..199 (causal)
+    bt = torch.tensor([[2, 0, 3, 1]], dtype=torch.int32)
+    kc = fp8_codes((4 * page_size, Hkv, D), 304)
+    vc = fp8_codes((4 * page_size, Hkv, D), 305)
+    kc.view(torch.uint8)[int(bt[0, 197 // page_size]) * page_size + 197 % page_size, 1, 7] = 0x7F
+    q = workloads.dense_inputs(1, 5, 1, Hq, Hkv, D, seed=306)[0][0]
+    cu = torch.tensor([0, 5], dtype=torch.int32)
+    k_s, v_s = scales(0.02, 0.05)
+    o, lse = mi.attn_fwd_paged_varlen(q.to(DEV), kc.to(DEV), vc.to(DEV),
+                                      torch.tensor(lens, dtype=torch.int32, device=DEV),
+                                      bt.to(DEV), cu.to(DEV), page_size, k_scale=k_s.to(DEV),
+                                      v_scale=v_s.to(DEV))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_paged_varlen(q, kc, vc, lens, bt, page_size, cu,
+                                              cache_fp8=True, k_scale=0.02, v_scale=0.05)
+    on = torch.isnan(o.cpu().float()).any(dim=-1).numpy()
+    ln = torch.isnan(lse.cpu()).numpy().T
+    ref = np.isnan(o_ref).any(axis=-1)
+    assert ref.sum() == 3 * (Hq // Hkv) and np.array_equal(on, ref) and np.array_equal(ln, ref)
+    fin = ~ref
+    check_rows(o.cpu().double().numpy()[fin], lse.cpu().double().numpy().T[fin], o_ref[fin],
+               lse_ref.T[fin], "fp8 rows without the NaN key")
+
+
+@pytest.mark.parametrize("causal,cap", [(True, None), (False, 10.0)])
+def test_fp8_append_writes_quantized_and_reads_back(causal, cap):
+    say(f"fp8 append causal={causal} softcap={cap}")
+    page_size, Hq, Hkv, D = 16, 8, 2, 128
+    sq, before = [3, 0, 40, 1], [5, 9, 30, 0]
+    B, max_pages = len(sq), 6
+    n_phys = B * max_pages + 2
+    g = torch.Generator().manual_seed(307)
+    bt = torch.randperm(n_phys, generator=g)[:B * max_pages].view(B, max_pages).to(torch.int32)
+    kp = fp8_codes((n_phys, page_size, Hkv, D), 308)
+    vp = fp8_codes((n_phys, page_size, Hkv, D), 309)
+    tq = sum(sq)
+    q, kn, vn = workloads.dense_inputs(1, tq, tq, Hq, Hkv, D, seed=310)
+    q, kn, vn = q[0], kn[0] * 3, vn[0] * 3
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(sq)]), dtype=torch.int32)
+    ks, vs = 0.05, 0.02
+    k_s, v_s = scales(ks, vs)
+    kd, vd = kp.to(DEV), vp.to(DEV)
+    o, lse = mi.attn_fwd_paged_append(q.to(DEV), kn.to(DEV), vn.to(DEV), kd, vd,
+                                      torch.tensor(before, dtype=torch.int32, device=DEV),
+                                      bt.to(DEV), cu.to(DEV), page_size, causal=causal,
+                                      softcap=cap, k_scale=k_s.to(DEV), v_scale=v_s.to(DEV))
+    torch.cuda.synchronize()
+    o_ref, lse_ref, nk, nv = oracle.attn_paged_append(q, kn, vn, kp, vp, before, bt, page_size,
+                                                      cu, causal=causal, softcap=cap,
+                                                      cache_fp8=True, k_scale=ks, v_scale=vs)
+    assert np.array_equal(kd.cpu().view(torch.uint8).numpy().reshape(-1), nk.reshape(-1))
+    assert np.array_equal(vd.cpu().view(torch.uint8).numpy().reshape(-1), nv.reshape(-1))
+    compare(o, lse, o_ref, lse_ref, "fp8 append")
+
+
+def test_full_size_decode_over_quantized_caches():
+    w = workloads.make(3)
+    say(f"{w.name} over FP8 pools")
+    ks = float(w.k_cache.float().abs().amax()) / 448.0
+    vs = float(w.v_cache.float().abs().amax()) / 448.0
+    k_s, v_s = scales(ks, vs)
+    k8 = torch.empty(w.k_cache.shape, dtype=torch.float8_e4m3fn, device=DEV)
+    v8 = torch.empty_like(k8)
+    rows = w.k_cache.shape[0]
+    mi.kv_cache_write(w.k_cache.to(DEV), w.v_cache.to(DEV), k8, v8,
+                      torch.arange(rows, dtype=torch.int64, device=DEV),
+                      k_scale=k_s.to(DEV), v_scale=v_s.to(DEV))
+    cu = torch.arange(0, w.B + 1, dtype=torch.int32)
+    q = w.q.reshape(w.B, w.Hq, w.D)
+    o, lse = mi.attn_fwd_paged_varlen(q.to(DEV), k8, v8, w.real_seqlen_kv.to(DEV),
+                                      w.block_table.to(DEV), cu.to(DEV), w.page_size,
+                                      k_scale=k_s.to(DEV), v_scale=v_s.to(DEV))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_paged_varlen(q, k8.cpu(), v8.cpu(), w.real_seqlen_kv,
+                                              w.block_table, w.page_size, cu, cache_fp8=True,
+                                              k_scale=float(k_s), v_scale=float(v_s))
+    compare(o, lse, o_ref, lse_ref, w.name + " fp8")
