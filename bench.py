@@ -11,6 +11,8 @@ with inputs resident in HBM.  The same line carries:
                 Hkv=8, D=128, page 64, lengths U[512, 8192]) against HBM peak,
                 timed per call, rotating over three copies of the caches so
                 that no call finds its data in the last-level cache;
+  paged_decode_fp8  the same decode with the caches quantized into FP8
+                E4M3FN pools (half the bytes), timed the same way;
   backward      the attention backward (dq, dk, dv) of the same prefill,
                 TFLOP/s counting 10*D flops per visible triple;
   other_configs median call time and TFLOP/s of the key-padding MHA (B=4,
@@ -110,25 +112,48 @@ def time_prefill(mi, w, steps, warmup):
     return total_ms / steps, prof["attn_ms"] / max(prof["attn_launches"], 1)
 
 
-def time_decode(mi, w, steps, warmup, copies=3):
+def time_decode(mi, w, steps, warmup, copies=3, fp8=False):
     """Paged decode timing.  The caches (1.08 GB of visible K/V against a 256 MB
     last-level cache) rotate over `copies` identical copies, so each call reads
     data that two other calls' 2 GB of reads have evicted since it was last
     touched.  (Overwriting a scratch buffer between calls instead leaves its
     dirty lines in the cache, and the timed kernel then pays for writing them
-    back: about 60 us more per call on MI355X.)"""
+    back: about 60 us more per call on MI355X.)  With fp8 the caches are first
+    quantized into FP8 E4M3FN pools (scale = max |x| / 448) by kv_cache_write
+    and read through attn_fwd_paged_varlen with one query per request."""
     import torch
     dev = "cuda:0"
     q = w.q.to(dev)
-    caches = [(w.k_cache.to(dev), w.v_cache.to(dev))]
+    lens, bt = w.real_seqlen_kv.to(dev), w.block_table.to(dev)
+    if fp8:
+        k16, v16 = w.k_cache.to(dev), w.v_cache.to(dev)
+        ks = torch.tensor([float(k16.float().abs().amax()) / 448.0], device=dev)
+        vs = torch.tensor([float(v16.float().abs().amax()) / 448.0], device=dev)
+        k8 = torch.empty(k16.shape, dtype=torch.float8_e4m3fn, device=dev)
+        v8 = torch.empty_like(k8)
+        mi.kv_cache_write(k16, v16, k8, v8, torch.arange(k16.shape[0], device=dev),
+                          k_scale=ks, v_scale=vs)
+        del k16, v16
+        caches = [(k8, v8)]
+        q3 = q.reshape(w.B, w.Hq, w.D)
+        cu = torch.arange(0, w.B + 1, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q3)
+        lse = torch.empty((w.Hq, w.B), dtype=torch.float32, device=dev)
+
+        def call(kc, vc):
+            mi.attn_fwd_paged_varlen(q3, kc, vc, lens, bt, cu, w.page_size, max_seqlen_q=1,
+                                     k_scale=ks, v_scale=vs, out=o, lse=lse)
+    else:
+        caches = [(w.k_cache.to(dev), w.v_cache.to(dev))]
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+
+        def call(kc, vc):
+            mi.attn_fwd_paged(q, kc, vc, lens, bt, w.page_size, out=o, lse=lse)
     for _ in range(copies - 1):
         caches.append((caches[0][0].clone(), caches[0][1].clone()))
-    lens, bt = w.real_seqlen_kv.to(dev), w.block_table.to(dev)
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     for i in range(warmup):
-        kc, vc = caches[i % copies]
-        mi.attn_fwd_paged(q, kc, vc, lens, bt, w.page_size, out=o, lse=lse)
+        call(*caches[i % copies])
     torch.cuda.synchronize()
     # whole calls (the library's own kernel timing off), then the kernels
     call_ms = []
@@ -136,7 +161,7 @@ def time_decode(mi, w, steps, warmup, copies=3):
         kc, vc = caches[(warmup + i) % copies]
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
-        mi.attn_fwd_paged(q, kc, vc, lens, bt, w.page_size, out=o, lse=lse)
+        call(kc, vc)
         e.record()
         torch.cuda.synchronize()
         call_ms.append(s.elapsed_time(e))
@@ -145,7 +170,7 @@ def time_decode(mi, w, steps, warmup, copies=3):
     for i in range(steps):
         kc, vc = caches[(warmup + steps + i) % copies]
         mi.profile_start()
-        mi.attn_fwd_paged(q, kc, vc, lens, bt, w.page_size, out=o, lse=lse)
+        call(kc, vc)
         torch.cuda.synchronize()
         prof = mi.profile_stop()
         a_ms += prof["attn_ms"]
@@ -280,7 +305,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the key-padding MHA and wide-group chunked prefill timings")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_fp8", "backward"], default=None,
                     help="time one workload and print its line (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy 5 times and exit: the "
@@ -309,11 +334,13 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}), flush=True)
         return
-    if args.only == "decode":
+    if args.only in ("decode", "decode_fp8"):
         wd = workloads.make(3)
-        d = time_decode(mi, wd, max(args.steps, 10), args.warmup)
-        nbytes = kv_bytes(wd.kv_lengths(), wd.Hkv, wd.D)
-        print(json.dumps({"workload": wd.name, "kv_bytes": nbytes, **d}), flush=True)
+        fp8 = args.only == "decode_fp8"
+        d = time_decode(mi, wd, max(args.steps, 10), args.warmup, fp8=fp8)
+        nbytes = kv_bytes(wd.kv_lengths(), wd.Hkv, wd.D) // (2 if fp8 else 1)
+        print(json.dumps({"workload": wd.name + ("_fp8_e4m3" if fp8 else ""), "kv_bytes": nbytes,
+                          **d}), flush=True)
         return
 
     if args.only == "backward":
@@ -378,6 +405,24 @@ def main():
                          "kernel": "attn_fwd_kernel<128, true, 1, 3, false> (D, bf16, paged K/V, 3 waves, plain logits, stream-K)",
                          "kernel_avg_us": d["attn_kernel_ms"] * 1e3,
                          "merge_kernel_avg_us": d["merge_kernel_ms"] * 1e3}}
+        # the same decode over FP8 E4M3FN pools (half the bytes)
+        d8 = time_decode(mi, wd, max(args.steps, 10), args.warmup, fp8=True)
+        nb8 = nbytes // 2
+        call8 = nb8 / (d8["median_call_ms"] * 1e-3) / 1e9
+        kern8 = nb8 / (d8["attn_kernel_ms"] * 1e-3) / 1e9
+        print(f"[bench] decode fp8 pools: call {d8['median_call_ms'] * 1e3:.1f} us "
+              f"({call8:.0f} GB/s of FP8 K/V), attention kernel "
+              f"{d8['attn_kernel_ms'] * 1e3:.1f} us, merge {d8['merge_kernel_ms'] * 1e3:.1f} us",
+              file=sys.stderr, flush=True)
+        line["paged_decode_fp8"] = {
+            "workload": wd.name + "_fp8_e4m3", "value": call8, "unit": "GB/s", "kv_bytes": nb8,
+            "median_call_us": d8["median_call_ms"] * 1e3, "min_call_us": d8["min_call_ms"] * 1e3,
+            "speedup_vs_16bit_call": d["median_call_ms"] / d8["median_call_ms"],
+            "roofline": {"bound": "hbm", "achieved": kern8, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": kern8 / PEAK_HBM_GBS,
+                         "kernel": "attn_fwd_kernel<128, true, 3, 3, false> (D, bf16, FP8 pages, 3 waves, plain logits, stream-K)",
+                         "kernel_avg_us": d8["attn_kernel_ms"] * 1e3,
+                         "merge_kernel_avg_us": d8["merge_kernel_ms"] * 1e3}}
         del wd
 
     if not args.no_backward:

@@ -720,36 +720,33 @@ void attn_fwd_kernel(const FwdParams p) {
         };
         if constexpr (FP8) {
         // ---- FP8 pools.  Wave 1 moves E4M3FN key and value tiles HBM -> LDS
-        // with direct loads into a four-stage FP8 ring; wave 2 converts each
+        // with direct loads into an S8-stage FP8 ring; wave 2 converts each
         // landed tile into the 16-bit MFMA type, written to one of two 16-bit
         // stages in the swizzled layout of the 16-bit tiles, so wave 0 runs
-        // the 16-bit path unchanged.  (The roles stay apart because the
-        // compiler cannot tell the ring's stages apart for a wave that reads
-        // LDS while its own direct loads are in flight: it would wait for all
-        // of them.)  Step n: wave 0 computes tile n from 16-bit stage n & 1;
+        // the 16-bit path unchanged.  The roles stay apart: no wave reads LDS
+        // while direct loads of its own are in flight (the compiler would
+        // make it wait for all of them), so the stages need not be separate
+        // arrays.  Step n: wave 0 computes tile n from 16-bit stage n & 1;
         // wave 2 converts tile n + 1 (landed during step n - 1); wave 1 issues
-        // tile n + 4 into the FP8 stage tile n left, then waits for tile n + 2.
-        // A piece (1 KB) holds RPP8 whole key rows, lane l its 16 bytes (16
-        // d-values) at offset 16 l.  (Tiles of a paged call follow one
-        // another: there is no padding mask.)
+        // tile n + S8 into the FP8 stage tile n left, then waits for tile
+        // n + 2 -- S8 - 2 tiles stay in flight.  A piece (1 KB) holds RPP8
+        // whole key rows, lane l its 16 bytes (16 d-values) at offset 16 l.
+        // (Tiles of a paged call follow one another: there is no padding mask.)
+        constexpr int S8 = 4;                // FP8 ring stages
         constexpr int U16 = D / 16;          // 16-byte pieces per key row
         constexpr int RPP8 = 1024 / D;       // key rows per 1 KB piece
         constexpr int STAGE8 = BN * D;       // bytes of one FP8 K (or V) tile
         constexpr int PC8 = STAGE8 / 1024;   // pieces per tensor and tile
-        __shared__ __attribute__((aligned(1024))) uint8_t fK0[STAGE8];
-        __shared__ __attribute__((aligned(1024))) uint8_t fV0[STAGE8];
-        __shared__ __attribute__((aligned(1024))) uint8_t fK1[STAGE8];
-        __shared__ __attribute__((aligned(1024))) uint8_t fV1[STAGE8];
-        __shared__ __attribute__((aligned(1024))) uint8_t fK2[STAGE8];
-        __shared__ __attribute__((aligned(1024))) uint8_t fV2[STAGE8];
-        __shared__ __attribute__((aligned(1024))) uint8_t fK3[STAGE8];
-        __shared__ __attribute__((aligned(1024))) uint8_t fV3[STAGE8];
+        static_assert((S8 - 2) * 2 * PC8 <= 63, "the counted wait fits vmcnt");
+        __shared__ __attribute__((aligned(1024))) uint8_t fK[S8][STAGE8];
+        __shared__ __attribute__((aligned(1024))) uint8_t fV[S8][STAGE8];
         const uint8_t *k8 = (const uint8_t *)p.k, *v8 = (const uint8_t *)p.v;
         const int row8 = p.Hkv * D;  // bytes between consecutive keys
         const int l_row8 = lane / U16, l_col8 = lane % U16;
         const bool dma = wave_u == 1, conv = wave_u == 2;
-        auto issue8 = [&](int j0, uint8_t *dk, uint8_t *dv) __attribute__((always_inline)) {
+        auto issue8 = [&](int j0, int stage) __attribute__((always_inline)) {
             if (!dma) return;
+            uint8_t *dk = fK[stage], *dv = fV[stage];
             // a tile past the range keeps the load count, every lane reading
             // the first tile's first 16 bytes
             const bool pad = j0 >= wg_end;
@@ -778,11 +775,12 @@ void attn_fwd_kernel(const FwdParams p) {
                 }
             }
         };
-        // an FP8 stage -> a 16-bit stage: lane l's 16 bytes of piece e are
-        // chunks 2 l_col8 and 2 l_col8 + 1 (d 0..7 and 8..15 of the piece) of
-        // key row e RPP8 + l_row8
-        auto convert8 = [&](const uint8_t *fk, const uint8_t *fv, uint8_t *dk, uint8_t *dv) __attribute__((always_inline)) {
+        // FP8 stage -> 16-bit stage: lane l's 16 bytes of piece e are chunks
+        // 2 l_col8 and 2 l_col8 + 1 (d 0..7 and 8..15 of the piece) of key row
+        // e RPP8 + l_row8
+        auto convert8 = [&](int stage, uint8_t *dk, uint8_t *dv) __attribute__((always_inline)) {
             if (!conv) return;
+            const uint8_t *fk = fK[stage], *fv = fV[stage];
 #pragma unroll
             for (int e = 0; e < PC8; ++e) {
                 const u32x4 kw = *(const u32x4 *)(fk + e * 1024 + 16 * lane);
@@ -799,38 +797,28 @@ void attn_fwd_kernel(const FwdParams p) {
                 }
             }
         };
-        int n = 0;  // the tile computed next: key first_tile + n * BN
-#define MIATTN_F8_STEP(F_NEW_K, F_NEW_V, F_NXT_K, F_NXT_V, K_CUR, V_CUR, K_NXT, V_NXT)      \
-        {                                                                               \
-            t0 = first_tile + n * BN;                                                   \
-            issue8(t0 + 4 * BN, F_NEW_K, F_NEW_V);                                      \
-            compute(K_CUR, V_CUR);                                                      \
-            convert8(F_NXT_K, F_NXT_V, K_NXT, V_NXT);                                   \
-            /* tile n + 2 has landed when only the two younger tiles' loads remain */  \
-            wait_vmcnt<2 * 2 * PC8>();                                                  \
-            ring_barrier();                                                             \
-            ++n;                                                                        \
-        }
         if (first_tile < wg_end) {
-            issue8(first_tile, fK0, fV0);
-            issue8(first_tile + BN, fK1, fV1);
-            issue8(first_tile + 2 * BN, fK2, fV2);
-            issue8(first_tile + 3 * BN, fK3, fV3);
-            wait_vmcnt<2 * 2 * PC8>();  // tiles 0 and 1
+#pragma unroll
+            for (int st = 0; st < S8; ++st) issue8(first_tile + st * BN, st);
+            wait_vmcnt<(S8 - 2) * 2 * PC8>();  // tiles 0 and 1
             ring_barrier();
-            convert8(fK0, fV0, sK0, sV0);
+            convert8(0, sK0, sV0);
             ring_barrier();
-            // whole rounds of four steps (steps past the range compute nothing
-            // and issue pad loads), so that every step sees the same ring state
-            do {
-                MIATTN_F8_STEP(fK0, fV0, fK1, fV1, sK0, sV0, sK1, sV1)
-                MIATTN_F8_STEP(fK1, fV1, fK2, fV2, sK1, sV1, sK0, sV0)
-                MIATTN_F8_STEP(fK2, fV2, fK3, fV3, sK0, sV0, sK1, sV1)
-                MIATTN_F8_STEP(fK3, fV3, fK0, fV0, sK1, sV1, sK0, sV0)
-            } while (first_tile + n * BN < wg_end);
+            int st_new = 0, st_nxt = 1;  // FP8 stages of tiles n (refilled) and n + 1
+            for (int n = 0; first_tile + n * BN < wg_end; ++n) {
+                t0 = first_tile + n * BN;
+                issue8(t0 + S8 * BN, st_new);
+                const bool odd = n & 1;
+                compute(odd ? sK1 : sK0, odd ? sV1 : sV0);
+                convert8(st_nxt, odd ? sK0 : sK1, odd ? sV0 : sV1);
+                // tile n + 2 has landed when only the S8 - 2 younger tiles' loads remain
+                wait_vmcnt<(S8 - 2) * 2 * PC8>();
+                ring_barrier();
+                st_new = st_nxt;
+                st_nxt = st_nxt + 1 == S8 ? 0 : st_nxt + 1;
+            }
             wait_vmcnt<0>();
         }
-#undef MIATTN_F8_STEP
         } else {
 #define MIATTN_ST_STEP(K_CUR, V_CUR, K_NEW, V_NEW)                                      \
         {                                                                               \
@@ -977,6 +965,33 @@ void attn_fwd_kernel(const FwdParams p) {
             const int g = blockIdx.x;
             const SkBatch sb = {sd, BN, p.win_left};
             int unused;
+            if (p.sk_heads) {
+                // by head: share c = g / Hkv of head g % Hkv's T1 tiles (one
+                // head's tiles of every request, in request order); partial
+                // slot kvh (B + G / Hkv) + b + c
+                const int kvh = g % p.Hkv, c = g / p.Hkv, shares = p.sk_grid / p.Hkv;
+                const int64_t T1 = sk_sums(sb, 0, unused);
+                const int64_t s0 = (int64_t)c * T1 / shares;
+                const int64_t s1 = (int64_t)(c + 1) * T1 / shares;
+                if (s0 >= s1) return;
+                int b, pre, tb;
+                sk_find(sb, 1, s0, b, pre, tb);
+                int off = (int)(s0 - pre);
+                for (int64_t at = s0; at < s1; ++b, off = 0) {
+                    const int len = seq_kv_len(sd, b);
+                    int64_t unused_row0;
+                    int sq_u;
+                    q_span(sd, b, unused_row0, sq_u);
+                    const int t_first = sk_first_tile(sb, len, sq_u);
+                    const int tiles = sk_tiles(sb, b);
+                    const int n = (int)min((int64_t)(tiles - off), s1 - at);
+                    if (n <= 0) continue;
+                    run(0, b, kvh, len, (t_first + off) * BN, min(len, (t_first + off + n) * BN),
+                        (int64_t)kvh * (p.B + shares) + b + c, true);
+                    at += n;
+                }
+                return;
+            }
             const int64_t T = (int64_t)p.Hkv * sk_sums(sb, 0, unused);
             const int64_t s0 = (int64_t)g * T / p.sk_grid;
             const int64_t s1 = (int64_t)(g + 1) * T / p.sk_grid;

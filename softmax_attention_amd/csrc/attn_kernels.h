@@ -92,6 +92,10 @@ struct FwdParams {
     int xcd_unit_major;  // with xcd_units: an XCD runs all row blocks of a unit, then the next
     int heads_inner;     // units ordered (batch, split, KV head) instead of (batch, KV head, split)
     int sk_grid;  // stream-K decode (split-role schedule): grid size G, or 0
+    // stream-K by head: workgroup g serves KV head g % Hkv, and the G / Hkv
+    // workgroups of one head split that head's key tiles, so the Hkv
+    // workgroups g, g + 1, ... read the same cache rows together
+    int sk_heads;
 };
 
 struct MergeParams {
@@ -109,7 +113,7 @@ struct MergeParams {
     // stream-K decode: grid size (0 otherwise), keys per tile and the length
     // clamp the attention kernel applies (max_pages * page_size, 0 for an
     // empty cache), and the left window bound (-1: none)
-    int sk_grid, sk_bn, sk_cap, sk_win_left;
+    int sk_grid, sk_bn, sk_cap, sk_win_left, sk_heads;
 };
 
 // Launchers: return the hipGetLastError() status of the launch.  The

@@ -58,25 +58,33 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     int64_t base, stride = p.rows;
     int64_t g_first = 0;  // stream-K: the first workgroup (slot = unit + workgroup)
     int64_t T = 0;
+    int64_t sk_g = 0;  // stream-K: workgroups sharing the sequence of T tiles
     if (p.sk_grid > 0) {
         // Stream-K: the workgroups that touched this unit's tiles, [P, P +
         // tiles) of the T-tile sequence; workgroup g held [g T / G, (g+1) T / G).
+        // (by head: the shares of head kvh over its own T tiles, slots
+        // kvh (B + G / Hkv) + b + share)
         const SkBatch sb = {sd, p.sk_bn, p.sk_win_left};
         int before;
-        T = (int64_t)p.Hkv * sk_sums(sb, b, before);
+        const int64_t T1 = sk_sums(sb, b, before);
+        T = p.sk_heads ? T1 : (int64_t)p.Hkv * T1;
         const int tiles = sk_tiles(sb, b);
-        const int64_t P = (int64_t)p.Hkv * before + (int64_t)kvh * tiles;
+        const int64_t P = p.sk_heads ? (int64_t)before
+                                     : (int64_t)p.Hkv * before + (int64_t)kvh * tiles;
+        const int G = p.sk_heads ? p.sk_grid / p.Hkv : p.sk_grid;
+        sk_g = G;
         if (tiles == 0 || T == 0) {
             n_valid = 0;
             g_first = 0;
         } else {
-            const int G = p.sk_grid;
             // the workgroup holding tile s is the largest g with g T / G <= s
             g_first = ((P + 1) * G - 1) / T;
             const int64_t g_last = ((P + tiles) * G - 1) / T;
             n_valid = (int)(g_last - g_first + 1);
         }
-        base = ((int64_t)bh + g_first) * p.rows + r;
+        const int64_t slot0 = p.sk_heads ? (int64_t)kvh * (p.B + G) + b + g_first
+                                         : (int64_t)bh + g_first;
+        base = slot0 * p.rows + r;
     } else {
         const int kv_len = seq_kv_len(sd, b);
         // the splits that hold keys of this request (the attention kernel
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     auto skip = [&](int s) -> bool {
         if (p.sk_grid == 0) return false;
         const int64_t g = g_first + s;
-        return g * T / p.sk_grid == (g + 1) * T / p.sk_grid;
+        return g * T / sk_g == (g + 1) * T / sk_g;
     };
 
     // the largest partial LSE; a NaN one (a NaN score in its share) wins, so

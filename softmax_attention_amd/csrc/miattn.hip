@@ -317,7 +317,12 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
         int per_cu = decode_per_cu(dev, p, D, bf16, paged, waves, cap);
         const int want = env_int("MIATTN_SK_PER_CU", 0);  // tuning override
         if (want > 0 && want < per_cu) per_cu = want;
-        const int G = compute_units(dev) * per_cu;
+        // by head -- the default for FP8 pools, whose 128-byte head rows gain
+        // from neighbouring workgroups reading the same cache rows
+        // (MIATTN_SK_HEADS=0/1 overrides) -- on a grid of whole groups of Hkv
+        const int sk_heads = env_int("MIATTN_SK_HEADS", p.k_scale != nullptr ? 1 : 0) ? 1 : 0;
+        int G = compute_units(dev) * per_cu;
+        if (sk_heads) G = std::max(1, G / p.Hkv) * p.Hkv;
         p.n_mblocks = 1;
         p.n_splits = 1;
         p.split_len = 0;
@@ -332,12 +337,14 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
         p.o_part = (float *)ws;
         p.lse_part = p.o_part + slots * p.rows * D;
         p.sk_grid = G;
+        p.sk_heads = sk_heads;
         e = timed_launch(0, stream, [&] {
             return miattn::launch_attn_fwd(p, D, bf16, paged, waves, cap, G, stream);
         });
         if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
         MergeParams m = merge_params(p, paged);
         m.sk_grid = G;
+        m.sk_heads = sk_heads;
         m.sk_bn = BN;
         m.sk_win_left = p.win_left;
         e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
