@@ -511,6 +511,11 @@ __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(const BwdParams 
     store_rows<D, BF16>(p.dk + koff, adk, p.scale, hl);
 }
 
+__global__ __launch_bounds__(256) void zero_fill_kernel(u32x4 *dst, size_t n16) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) dst[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 template <int D, bool BF16>
 hipError_t launch_d(const BwdParams &p, hipStream_t stream) {
     const int64_t nrows = (int64_t)p.B * p.Sq * p.Hq;
@@ -530,6 +535,14 @@ hipError_t launch_d(const BwdParams &p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream) {
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream,
+                       (u32x4 *)ptr, n16);
+    return hipGetLastError();
+}
 
 hipError_t launch_attn_bwd(const BwdParams &p, int D, bool bf16, hipStream_t stream) {
     if (D == 64) return bf16 ? launch_d<64, true>(p, stream) : launch_d<64, false>(p, stream);

@@ -153,6 +153,9 @@ struct BwdParams {
     float scale_log2;  // alpha log2(e)
 };
 hipError_t launch_attn_bwd(const BwdParams &p, int D, bool bf16, hipStream_t stream);
+// Zero `bytes` (a multiple of 16) at a 16-byte aligned device address with a
+// kernel (no memset node, so the call can sit inside a captured graph).
+hipError_t launch_zero_fill(void *ptr, size_t bytes, hipStream_t stream);
 
 // Paged KV-cache write (kv_write.hip): token n's K and V rows ([row_elems]
 // 16-bit values) go to pool row slot(n) -- slot_mapping[n], or in append mode

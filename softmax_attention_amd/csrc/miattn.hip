@@ -875,9 +875,9 @@ miattn_status attn_bwd(const void *q, const void *k, const void *v, const void *
     if (Sq == 0) {
         // no query: every key gradient is zero
         const size_t bytes = (size_t)B * Skv * Hkv * D * 2;
-        e = hipMemsetAsync(dk, 0, bytes, s);
-        if (e == hipSuccess) e = hipMemsetAsync(dv, 0, bytes, s);
-        return e == hipSuccess ? MIATTN_OK : hip_fail(e, "hipMemsetAsync");
+        e = miattn::launch_zero_fill(dk, bytes, s);
+        if (e == hipSuccess) e = miattn::launch_zero_fill(dv, bytes, s);
+        return e == hipSuccess ? MIATTN_OK : hip_fail(e, "zero fill kernel launch");
     }
     miattn::BwdParams p = {};
     p.q = (const uint16_t *)q;
@@ -909,8 +909,8 @@ miattn_status attn_bwd(const void *q, const void *k, const void *v, const void *
     p.lse2_rows = p.d_rows + nrows;
     if (Skv == 0) {
         // no key: every query gradient is zero
-        e = hipMemsetAsync(dq, 0, (size_t)B * Sq * Hq * D * 2, s);
-        return e == hipSuccess ? MIATTN_OK : hip_fail(e, "hipMemsetAsync");
+        e = miattn::launch_zero_fill(dq, (size_t)B * Sq * Hq * D * 2, s);
+        return e == hipSuccess ? MIATTN_OK : hip_fail(e, "zero fill kernel launch");
     }
     e = timed_launch(0, s, [&] { return miattn::launch_attn_bwd(p, D, dtype == MIATTN_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "backward kernel launch");

@@ -90,3 +90,20 @@ def test_is_deterministic():
 
 def test_larger_causal_gqa():
     bwd_case(1, 1024, 1024, 16, 4, 128, seed=408, what="s1024")
+
+
+@pytest.mark.parametrize("Sq,Skv", [(0, 40), (40, 0)])
+def test_empty_side_gives_zero_gradients(Sq, Skv):
+    # no query: dk = dv = 0; no key: dq = 0 (written by a fill kernel, over
+    # whatever the allocator handed out, several calls in a row)
+    say(f"bwd empty side Sq={Sq} Skv={Skv}")
+    q, k, v = workloads.dense_inputs(2, max(Sq, 1), max(Skv, 1), 4, 2, 64, seed=404)
+    q, k, v = q[:, :Sq].to(DEV), k[:, :Skv].to(DEV), v[:, :Skv].to(DEV)
+    o = torch.zeros_like(q)
+    lse = torch.full((2, 4, Sq), float("-inf"), device=DEV)
+    for _ in range(3):
+        torch.empty(1 << 24, dtype=torch.uint8, device=DEV).fill_(0xFF)  # recycle dirty memory
+        dq, dk, dv = mi.attn_bwd(q, k, v, o, q, lse)
+        torch.cuda.synchronize()
+        for g in (dq, dk, dv):
+            assert g.numel() == 0 or bool((g == 0).all())
