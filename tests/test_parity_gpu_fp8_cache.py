@@ -176,3 +176,35 @@ def test_full_size_decode_over_quantized_caches():
                                               w.block_table, w.page_size, cu, cache_fp8=True,
                                               k_scale=float(k_s), v_scale=float(v_s))
     compare(o, lse, o_ref, lse_ref, w.name + " fp8")
+
+
+@pytest.mark.parametrize("sq,D,page", [([1, 1, 1, 1], 128, 64), ([37, 5], 64, 16)])
+def test_fp8_pool_gives_the_bits_of_a_16bit_pool_of_its_values(monkeypatch, sq, D, page):
+    # with scales of 1 the FP8 path differs from the 16-bit one only in how a
+    # tile reaches LDS: under one schedule (three waves) and one split plan the
+    # outputs must be bitwise equal, whatever the magnitudes (codes up to 448)
+    say(f"fp8 vs 16-bit pool of the decoded values sq={sq} D={D} page={page}")
+    monkeypatch.setenv("MIATTN_WAVES", "3")
+    Hq, Hkv = 8, 2
+    lens = [900, 33, 2000, 64][:len(sq)]
+    lens = [max(L, s) for L, s in zip(lens, sq)]
+    B = len(lens)
+    max_pages = -(-max(lens) // page)
+    n_phys = B * max_pages + 1
+    g = torch.Generator().manual_seed(320)
+    bt = torch.randperm(n_phys, generator=g)[:B * max_pages].view(B, max_pages).to(torch.int32)
+    kc = fp8_codes((n_phys * page, Hkv, D), 321)
+    vc = fp8_codes((n_phys * page, Hkv, D), 322)
+    table = torch.tensor([oracle.e4m3_decode(c) for c in range(256)], dtype=torch.float64)
+    k16 = table[kc.view(torch.uint8).long()].to(torch.bfloat16)
+    v16 = table[vc.view(torch.uint8).long()].to(torch.bfloat16)
+    q = workloads.dense_inputs(1, sum(sq), 1, Hq, Hkv, D, seed=323)[0][0]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(sq)]), dtype=torch.int32, device=DEV)
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    args = (torch.tensor(lens, dtype=torch.int32, device=DEV), bt.to(DEV), cu, page)
+    mi.set_split_keys(256)
+    o8, l8 = mi.attn_fwd_paged_varlen(q.to(DEV), kc.to(DEV), vc.to(DEV), *args, k_scale=one,
+                                      v_scale=one)
+    o16, l16 = mi.attn_fwd_paged_varlen(q.to(DEV), k16.to(DEV), v16.to(DEV), *args)
+    torch.cuda.synchronize()
+    assert torch.equal(o8, o16) and torch.equal(l8, l16)
