@@ -179,6 +179,7 @@ struct SkBatch {
     SeqDesc sd;
     int bn;        // keys per tile
     int win_left;  // left window bound (-1: none)
+    int piece;     // plan weight of starting a piece, in tiles (see sk_weight)
 };
 
 // first key tile any query of request b (sq_b queries, len keys) can see:
@@ -198,6 +199,16 @@ __device__ __forceinline__ int sk_tiles(const SkBatch &s, int b) {
     return (len + s.bn - 1) / s.bn - sk_first_tile(s, len, sq_b);
 }
 
+// Plan weight of each (request, KV head) unit: its key tiles plus `piece`
+// for the cost of starting a piece of it (the page-table and first-tile
+// round trips before the unit's first tile lands, the partial store after its
+// last); none for a unit without tiles.  The unit's tiles sit at weight
+// offsets [piece, piece + tiles), so the workgroups' equal shares of the
+// weight give a workgroup that starts more pieces fewer tiles.
+__device__ __forceinline__ int sk_weight(const SkBatch &s, int tiles) {
+    return tiles > 0 ? tiles + s.piece : 0;
+}
+
 // inclusive prefix sum over the 64 lanes of a wave
 __device__ __forceinline__ int wave_incl_scan(int v) {
     const int lane = threadIdx.x & 63;
@@ -209,13 +220,13 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     return v;
 }
 
-// tiles of the whole batch (returned) and of the entries before `upto`
+// plan weight of the whole batch (returned) and of the entries before `upto`
 __device__ __forceinline__ int sk_sums(const SkBatch &s, int upto, int &before) {
     const int lane = threadIdx.x & 63;
     int total = 0, pre = 0;
     for (int c = 0; c < s.sd.B; c += 64) {
         const int b = c + lane;
-        const int t = b < s.sd.B ? sk_tiles(s, b) : 0;
+        const int t = b < s.sd.B ? sk_weight(s, sk_tiles(s, b)) : 0;
         const int incl = wave_incl_scan(t);
         const int incl_before = wave_incl_scan(b < upto ? t : 0);
         total += __shfl(incl, 63);
@@ -228,16 +239,16 @@ __device__ __forceinline__ int sk_sums(const SkBatch &s, int upto, int &before) 
     return __builtin_amdgcn_readfirstlane(total);
 }
 
-// the entry b whose tiles hold tile `at` of the sequence (hkv * pre_b <= at <
-// hkv * (pre_b + t_b)), with pre_b (tiles before it) and t_b; `at` must be
-// below the sequence's length
+// the entry b whose weight holds position `at` of the sequence (hkv * pre_b <=
+// at < hkv * (pre_b + t_b)), with pre_b (weight before it) and its weight t_b;
+// `at` must be below the sequence's length
 __device__ __forceinline__ void sk_find(const SkBatch &s, int hkv, int64_t at, int &b_out,
                                         int &pre_out, int &t_out) {
     const int lane = threadIdx.x & 63;
     int carry = 0;
     for (int c = 0; c < s.sd.B; c += 64) {
         const int b = c + lane;
-        const int t = b < s.sd.B ? sk_tiles(s, b) : 0;
+        const int t = b < s.sd.B ? sk_weight(s, sk_tiles(s, b)) : 0;
         const int incl = carry + wave_incl_scan(t);
         const int excl = incl - t;
         const bool hit = b < s.sd.B && (int64_t)hkv * excl <= at && at < (int64_t)hkv * incl;

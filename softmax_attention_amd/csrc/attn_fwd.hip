@@ -957,26 +957,29 @@ void attn_fwd_kernel(const FwdParams p) {
     const int units = p.B * p.Hkv * p.n_splits;
     if constexpr (SPLIT_ROLES) {
         if (p.sk_grid > 0) {
-            // Stream-K decode: the (batch, KV head) key sequences, heads
-            // fastest, form one sequence of T key tiles; workgroup g takes
-            // tiles [g T / G, (g+1) T / G) -- an equal share, whatever the
-            // lengths -- and writes one partial per unit it touches, to slot
-            // unit + g (the merge kernel finds the slots the same way).
+            // Stream-K decode: the (batch, KV head) units, heads fastest, form
+            // one sequence of plan weight T (each unit its key tiles plus the
+            // cost of starting a piece, sk_weight); workgroup g takes the
+            // weight [g T / G, (g+1) T / G) -- an equal share, whatever the
+            // lengths -- and writes one partial per unit whose tiles its share
+            // touches, to slot unit + g (the merge kernel finds the slots the
+            // same way).  A unit of w = piece + tiles holds its tiles at
+            // weight offsets [piece, w).
             const int g = blockIdx.x;
-            const SkBatch sb = {sd, BN, p.win_left};
+            const SkBatch sb = {sd, BN, p.win_left, p.sk_piece};
             int unused;
             if (p.sk_heads) {
-                // by head: share c = g / Hkv of head g % Hkv's T1 tiles (one
-                // head's tiles of every request, in request order); partial
+                // by head: share c = g / Hkv of head g % Hkv's weight T1 (one
+                // head's units of every request, in request order); partial
                 // slot kvh (B + G / Hkv) + b + c
                 const int kvh = g % p.Hkv, c = g / p.Hkv, shares = p.sk_grid / p.Hkv;
                 const int64_t T1 = sk_sums(sb, 0, unused);
                 const int64_t s0 = (int64_t)c * T1 / shares;
                 const int64_t s1 = (int64_t)(c + 1) * T1 / shares;
                 if (s0 >= s1) return;
-                int b, pre, tb;
-                sk_find(sb, 1, s0, b, pre, tb);
-                int off = (int)(s0 - pre);
+                int b, pre, wb;
+                sk_find(sb, 1, s0, b, pre, wb);
+                int off = (int)(s0 - pre);  // weight offset into request b
                 for (int64_t at = s0; at < s1; ++b, off = 0) {
                     const int len = seq_kv_len(sd, b);
                     int64_t unused_row0;
@@ -984,11 +987,15 @@ void attn_fwd_kernel(const FwdParams p) {
                     q_span(sd, b, unused_row0, sq_u);
                     const int t_first = sk_first_tile(sb, len, sq_u);
                     const int tiles = sk_tiles(sb, b);
-                    const int n = (int)min((int64_t)(tiles - off), s1 - at);
-                    if (n <= 0) continue;
-                    run(0, b, kvh, len, (t_first + off) * BN, min(len, (t_first + off + n) * BN),
+                    const int w = sk_weight(sb, tiles);
+                    // the share's part of the unit's tiles, as weight offsets
+                    const int lo = max(off, sb.piece);
+                    const int hi = (int)min((int64_t)w, off + (s1 - at));
+                    at += w - off;
+                    if (hi <= lo) continue;
+                    run(0, b, kvh, len, (t_first + lo - sb.piece) * BN,
+                        min(len, (t_first + hi - sb.piece) * BN),
                         (int64_t)kvh * (p.B + shares) + b + c, true);
-                    at += n;
                 }
                 return;
             }
@@ -996,11 +1003,11 @@ void attn_fwd_kernel(const FwdParams p) {
             const int64_t s0 = (int64_t)g * T / p.sk_grid;
             const int64_t s1 = (int64_t)(g + 1) * T / p.sk_grid;
             if (s0 >= s1) return;
-            int b0, pre0, t0;
-            sk_find(sb, p.Hkv, s0, b0, pre0, t0);
+            int b0, pre0, w0;
+            sk_find(sb, p.Hkv, s0, b0, pre0, w0);
             const int64_t rem = s0 - (int64_t)p.Hkv * pre0;
-            int u = b0 * p.Hkv + (int)(rem / t0);
-            int off = (int)(rem % t0);
+            int u = b0 * p.Hkv + (int)(rem / w0);
+            int off = (int)(rem % w0);  // weight offset into unit u
             for (int64_t at = s0; at < s1; ++u, off = 0) {
                 const int b = u / p.Hkv;
                 const int kvh = u - b * p.Hkv;
@@ -1011,11 +1018,13 @@ void attn_fwd_kernel(const FwdParams p) {
                 q_span(sd, b, unused_row0, sq_u);
                 const int t_first = sk_first_tile(sb, len, sq_u);
                 const int tiles = sk_tiles(sb, b);
-                const int n = (int)min((int64_t)(tiles - off), s1 - at);
-                if (n <= 0) continue;
-                run(0, b, kvh, len, (t_first + off) * BN, min(len, (t_first + off + n) * BN),
-                    (int64_t)u + g, true);
-                at += n;
+                const int w = sk_weight(sb, tiles);
+                const int lo = max(off, sb.piece);
+                const int hi = (int)min((int64_t)w, off + (s1 - at));
+                at += w - off;
+                if (hi <= lo) continue;
+                run(0, b, kvh, len, (t_first + lo - sb.piece) * BN,
+                    min(len, (t_first + hi - sb.piece) * BN), (int64_t)u + g, true);
             }
             return;
         }

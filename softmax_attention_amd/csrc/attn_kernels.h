@@ -96,6 +96,8 @@ struct FwdParams {
     // workgroups of one head split that head's key tiles, so the Hkv
     // workgroups g, g + 1, ... read the same cache rows together
     int sk_heads;
+    // stream-K: plan weight, in key tiles, of starting a piece of a unit
+    int sk_piece;
 };
 
 struct MergeParams {
@@ -112,8 +114,9 @@ struct MergeParams {
     int B, Sq, Hq, Hkv, G, rows, n_splits, split_len;
     // stream-K decode: grid size (0 otherwise), keys per tile and the length
     // clamp the attention kernel applies (max_pages * page_size, 0 for an
-    // empty cache), and the left window bound (-1: none)
-    int sk_grid, sk_bn, sk_cap, sk_win_left, sk_heads;
+    // empty cache), the left window bound (-1: none), the by-head plan and
+    // the plan weight of a piece -- all as the attention kernel had them
+    int sk_grid, sk_bn, sk_cap, sk_win_left, sk_heads, sk_piece;
 };
 
 // Launchers: return the hipGetLastError() status of the launch.  The

@@ -60,26 +60,29 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     int64_t T = 0;
     int64_t sk_g = 0;  // stream-K: workgroups sharing the sequence of T tiles
     if (p.sk_grid > 0) {
-        // Stream-K: the workgroups that touched this unit's tiles, [P, P +
-        // tiles) of the T-tile sequence; workgroup g held [g T / G, (g+1) T / G).
-        // (by head: the shares of head kvh over its own T tiles, slots
+        // Stream-K: the workgroups whose shares hold this unit's tiles, at
+        // [P + piece, P + piece + tiles) of the sequence of plan weight T
+        // (the unit starts at P); workgroup g held [g T / G, (g+1) T / G).
+        // (by head: the shares of head kvh over its own weight, slots
         // kvh (B + G / Hkv) + b + share)
-        const SkBatch sb = {sd, p.sk_bn, p.sk_win_left};
+        const SkBatch sb = {sd, p.sk_bn, p.sk_win_left, p.sk_piece};
         int before;
         const int64_t T1 = sk_sums(sb, b, before);
         T = p.sk_heads ? T1 : (int64_t)p.Hkv * T1;
         const int tiles = sk_tiles(sb, b);
         const int64_t P = p.sk_heads ? (int64_t)before
-                                     : (int64_t)p.Hkv * before + (int64_t)kvh * tiles;
+                                     : (int64_t)p.Hkv * before +
+                                           (int64_t)kvh * sk_weight(sb, tiles);
         const int G = p.sk_heads ? p.sk_grid / p.Hkv : p.sk_grid;
         sk_g = G;
         if (tiles == 0 || T == 0) {
             n_valid = 0;
             g_first = 0;
         } else {
-            // the workgroup holding tile s is the largest g with g T / G <= s
-            g_first = ((P + 1) * G - 1) / T;
-            const int64_t g_last = ((P + tiles) * G - 1) / T;
+            // the workgroup holding position s is the largest g with g T / G <= s
+            const int64_t first = P + p.sk_piece, last = P + p.sk_piece + tiles - 1;
+            g_first = ((first + 1) * G - 1) / T;
+            const int64_t g_last = ((last + 1) * G - 1) / T;
             n_valid = (int)(g_last - g_first + 1);
         }
         const int64_t slot0 = p.sk_heads ? (int64_t)kvh * (p.B + G) + b + g_first

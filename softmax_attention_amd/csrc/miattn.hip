@@ -81,6 +81,7 @@ struct DeviceState {
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
 int g_split_keys = 0;  // 0 = automatic
+constexpr int kSkPieceMax = 64;  // largest stream-K piece weight, in key tiles
 
 int compute_units(int dev) {
     std::lock_guard<std::mutex> lock(g_mu);
@@ -308,12 +309,13 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     p.sk_grid = 0;
 
     // Decode-shaped calls run stream-K: a grid of what the GPU holds at once,
-    // each workgroup an equal share of all (batch, KV head) key tiles, so no
-    // workgroup waits on a long request or for a dispatch slot.  A forced
-    // split length selects the split plan below instead.
-    // (the plan's tile sums are 32-bit: Hkv * B * tiles of the capacity)
+    // each workgroup an equal share of the plan weight of all (batch, KV head)
+    // units (their key tiles plus a cost per piece), so no workgroup waits on a
+    // long request or for a dispatch slot.  A forced split length selects the
+    // split plan below instead.  (The plan's sums are 32-bit: Hkv * B * the
+    // weight of a unit at the capacity.)
     if ((waves == 2 || waves == 3) && p.rows <= miattn::kRowsPerWave && split_keys <= 0 &&
-        bhs * cap_tiles < INT_MAX && env_int("MIATTN_STREAMK", 1)) {
+        bhs * (cap_tiles + kSkPieceMax) < INT_MAX && env_int("MIATTN_STREAMK", 1)) {
         int per_cu = decode_per_cu(dev, p, D, bf16, paged, waves, cap);
         const int want = env_int("MIATTN_SK_PER_CU", 0);  // tuning override
         if (want > 0 && want < per_cu) per_cu = want;
@@ -338,6 +340,12 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
         p.lse_part = p.o_part + slots * p.rows * D;
         p.sk_grid = G;
         p.sk_heads = sk_heads;
+        // A piece that starts mid-kernel waits ~10 us for its page-table entry
+        // and first tile (measured with in-kernel timestamps), about six
+        // tiles' worth of streaming: the plan weighs each piece that much, so
+        // a workgroup that starts more pieces gets fewer tiles.
+        // (MIATTN_SK_PIECE overrides, 0 .. kSkPieceMax.)
+        p.sk_piece = std::min(std::max(env_int("MIATTN_SK_PIECE", 6), 0), kSkPieceMax);
         e = timed_launch(0, stream, [&] {
             return miattn::launch_attn_fwd(p, D, bf16, paged, waves, cap, G, stream);
         });
@@ -347,6 +355,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
         m.sk_heads = sk_heads;
         m.sk_bn = BN;
         m.sk_win_left = p.win_left;
+        m.sk_piece = p.sk_piece;
         e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
         return MIATTN_OK;

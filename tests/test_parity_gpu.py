@@ -211,6 +211,21 @@ def test_streamk_decode_fewer_tiles_than_workgroups(page_size):
     paged_case(3, 1, 4, 2, 128, [5, 0, 40], page_size, seed=31, what="sk_tiny")
 
 
+@pytest.mark.parametrize("piece", [0, 1, 64])
+def test_streamk_plan_piece_weights(monkeypatch, piece):
+    # the plan weighs each piece of a unit `piece` tiles on top of its tiles;
+    # any weight must still cover every tile once and let the merge find
+    # every partial: long and short requests, one without keys, and a tiny
+    # batch with more workgroups than weight
+    monkeypatch.setenv("MIATTN_SK_PIECE", str(piece))
+    paged_case(8, 1, 32, 8, 128, [1, 0, 64, 65, 1000, 513, 2047, 300], 64, seed=23,
+               what=f"piece {piece}")
+    paged_case(3, 1, 4, 2, 128, [5, 0, 40], 16, seed=24, what=f"piece {piece} tiny")
+    monkeypatch.setenv("MIATTN_SK_HEADS", "1")
+    paged_case(6, 1, 16, 4, 64, [3, 700, 1, 0, 1500, 64], 32, dtype=torch.float16,
+               window=(200, -1), seed=25, what=f"piece {piece} by head")
+
+
 def test_streamk_decode_many_requests():
     # more batch entries than the plan kernel's 1024 threads (chunked prefix),
     # lengths 0..120 including zeros
