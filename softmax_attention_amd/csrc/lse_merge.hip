@@ -107,27 +107,50 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     auto max_nan = [](float a, float b) -> float {
         return a != a ? a : (b != b ? b : fmaxf(a, b));
     };
-    float M = -INFINITY;
-    for (int s = lane; s < n_valid; s += 64)
-        if (!skip(s)) M = max_nan(M, p.lse_part[base + (int64_t)s * stride]);
+    // lane s % 64 reads the LSE of split s (-inf for a skipped one); the
+    // first 64 stay in their lanes for the weights below
+    auto split_lse = [&](int s) -> float {
+        return s < n_valid && !skip(s) ? p.lse_part[base + (int64_t)s * stride] : -INFINITY;
+    };
+    const float ls0 = split_lse(lane);
+    float M = ls0;
+    for (int s = lane + 64; s < n_valid; s += 64) M = max_nan(M, split_lse(s));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = max_nan(M, __shfl_xor(M, off));
 
+    // o = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M), splits in
+    // ascending order; each split's LSE comes from its lane, and the partial
+    // rows are read four splits at a time (the loads first), so a row costs
+    // about one round trip per four splits rather than one per split
     float accv[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) accv[e] = 0.f;
     float den = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < n_valid; ++s) {
-            if (skip(s)) continue;
-            const int64_t idx = base + (int64_t)s * stride;
-            const float ls = p.lse_part[idx];
-            if (ls == -INFINITY) continue;
-            const float w = __expf(ls - M);
-            den += w;
-            const float *src = p.o_part + idx * D + lane * PER;
+        for (int c = 0; c < n_valid; c += 64) {
+            const float ls = c == 0 ? ls0 : split_lse(c + lane);
+            const int cnt = min(64, n_valid - c);
+            for (int q0 = 0; q0 < cnt; q0 += 4) {
+                float lq[4];
+                float ov[4][PER];
 #pragma unroll
-            for (int e = 0; e < PER; ++e) accv[e] += w * src[e];
+                for (int k = 0; k < 4; ++k) {
+                    // lanes past the last split hold -inf
+                    lq[k] = __shfl(ls, q0 + k);
+                    const float *src =
+                        p.o_part + (base + (int64_t)(c + q0 + k) * stride) * D + lane * PER;
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) ov[k][e] = lq[k] != -INFINITY ? src[e] : 0.f;
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if (lq[k] == -INFINITY) continue;
+                    const float w = __expf(lq[k] - M);
+                    den += w;
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) accv[e] += w * ov[k][e];
+                }
+            }
         }
     }
     const int h = kvh * p.G + gh;
