@@ -55,11 +55,13 @@ using namespace dev;
 
 
 // Waves per SIMD the register budget is sized for: the 8-wave schedule needs
-// its two waves per SIMD, and so do three two-wave decode workgroups (48 KB
-// of LDS each) on one CU; the 4-wave D = 256 schedule runs one workgroup per
-// CU.
-template <int D, int WAVES>
-constexpr int waves_per_eu() { return (WAVES == 8 || WAVES == 2 || WAVES == 3) ? 2 : 1; }
+// its two waves per SIMD, and so do two three-wave decode workgroups over FP8
+// pools on one CU; a 16-bit decode workgroup (96 KB of LDS at D = 128) and
+// the 4-wave D = 256 schedule run one workgroup per CU.
+template <int D, int WAVES, bool FP8>
+constexpr int waves_per_eu() {
+    return (WAVES == 8 || ((WAVES == 2 || WAVES == 3) && (FP8 || D < 128))) ? 2 : 1;
+}
 
 #ifndef MIATTN_READ_AHEAD
 #define MIATTN_READ_AHEAD 6
@@ -92,7 +94,8 @@ enum KvMode { kDense = 0, kPagedTile = 1, kPagedPiece = 2, kPagedTile8 = 3, kPag
 // GQADenseFwdOp stage 6); otherwise the logit is the scaled score itself.
 template <int D, bool BF16, int KV, int WAVES, bool CAP>
 __global__ __launch_bounds__(64 * WAVES)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu<D, WAVES>(), waves_per_eu<D, WAVES>())))
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<D, WAVES, (KV == kPagedTile8 || KV == kPagedPiece8)>(),
+                                   waves_per_eu<D, WAVES, (KV == kPagedTile8 || KV == kPagedPiece8)>())))
 void attn_fwd_kernel(const FwdParams p) {
     constexpr bool PAGED = KV != kDense;
     // FP8 pools: K and V hold E4M3FN codes (paging mode KV - 2), dequantized
@@ -103,7 +106,7 @@ void attn_fwd_kernel(const FwdParams p) {
     using H = Half<BF16>;
     using vec8 = typename H::vec8;
     constexpr int BM = rows_per_workgroup(WAVES);  // packed rows per workgroup
-    constexpr int BN = keys_per_tile(D, WAVES);    // keys per tile
+    constexpr int BN = keys_per_tile(D, WAVES, FP8);  // keys per tile
     constexpr int TILE_BYTES = BN * D * 2;         // one K (or V) tile
     constexpr int PIECES = TILE_BYTES / 1024;      // 1 KB direct loads per tile
     // The decode schedule (2 or 3 waves) splits the roles: wave 0 computes,
@@ -691,8 +694,7 @@ void attn_fwd_kernel(const FwdParams p) {
         // the tile three steps ahead land in the stage the previous step
         // freed; the same counted wait as above (all but the two youngest
         // steps' loads) and one barrier per step order the ring.
-        // ring depth: three stages for the two-wave decode workgroup, four
-        // otherwise
+        // ring depth: three stages for the decode workgroups, four otherwise
         constexpr int kStages = SPLIT_ROLES ? 3 : 4;
         f32x16 sc[NT];
         vec8 pb[PSTEPS];
@@ -852,9 +854,9 @@ void attn_fwd_kernel(const FwdParams p) {
             wait_vmcnt<0>();
         }
 #undef MIATTN_ST_STEP
-        // three stages (decode: 48 KB of LDS, three workgroups per CU): step k
-        // computes t0 while t2 loads; at its end the loads of the previous
-        // step (tile t1) must have landed -- all but this step's.
+        // three stages (decode: 96 KB of LDS at D = 128, one workgroup per
+        // CU): step k computes t0 while t2 loads; at its end the loads of the
+        // previous step (tile t1) must have landed -- all but this step's.
 #define MIATTN_ST3_STEP(K_CUR, V_CUR, K_NEW, V_NEW)                                     \
         {                                                                               \
             t2 = t1 < wg_end ? find_tile(t1 + BN, lo2, hi2) : wg_end;                   \
@@ -1095,7 +1097,8 @@ int blocks_per_cu() {
 
 template <int D, int W, bool CAP>
 int decode_blocks(const FwdParams &p, bool bf16, bool paged) {
-    const bool tile = p.page_shift >= __builtin_ctz(keys_per_tile(D, W));
+    const bool tile =
+        p.page_shift >= __builtin_ctz(keys_per_tile(D, W, paged && p.k_scale != nullptr));
     if constexpr (W == 3) {
         if (paged && p.k_scale != nullptr) {
             if (tile)
@@ -1124,7 +1127,8 @@ hipError_t launch_kv(const FwdParams &p, bool bf16, int grid, hipStream_t stream
 
 template <int D, int WAVES, bool CAP>
 hipError_t launch_w(const FwdParams &p, bool bf16, bool paged, int grid, hipStream_t stream) {
-    const bool tile = p.page_shift >= __builtin_ctz(keys_per_tile(D, WAVES));
+    const bool tile =
+        p.page_shift >= __builtin_ctz(keys_per_tile(D, WAVES, paged && p.k_scale != nullptr));
     if constexpr (WAVES == 3) {
         if (paged && p.k_scale != nullptr)
             return tile ? launch_kv<D, WAVES, kPagedTile8, CAP>(p, bf16, grid, stream)

@@ -29,11 +29,14 @@ constexpr int rows_per_workgroup(int waves) {
 }
 
 // Keys per KV tile.  8 waves: 64 keys (8 KB at D = 64, 16 KB at D = 128).
-// Streaming: 8 KB tiles (4096 / D keys), at least one 32-key score block (16
-// KB at D = 256); with four-stage rings a decode workgroup then takes 64 KB of
-// LDS and two fit on a CU.
-constexpr int keys_per_tile(int D, int waves) {
-    return waves == 8 ? 64 : (4096 / D > 32 ? 4096 / D : 32);
+// Decode-shaped (2 or 3 waves): 64 keys (16 KB at D = 128); the three-stage
+// K and V rings then take 96 KB and one workgroup runs per CU, which streamed
+// the paged decode 4-5 % faster than 32-key tiles with two workgroups per CU.
+// Over FP8 pools: tiles of 8 KB of 16-bit values (4096 / D keys, at least
+// one 32-key score block), so that the FP8 ring and the converted stages fit
+// two workgroups per CU.  D = 256 (4 waves): 32 keys (16 KB).
+constexpr int keys_per_tile(int D, int waves, bool fp8 = false) {
+    return waves == 8 ? 64 : waves == 4 ? 32 : fp8 ? (4096 / D > 32 ? 4096 / D : 32) : 64;
 }
 
 // Per-request extents of a call, as the attention kernel, its stream-K plan

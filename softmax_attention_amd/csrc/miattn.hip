@@ -300,7 +300,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     if (D <= 128 && (forced == 2 || forced == 3 || forced == 8)) waves = forced;
     if (waves == 2 && cap) waves = 3;  // the two-wave comparison schedule has no capped build
     if (p.k_scale != nullptr) waves = 3;  // FP8 pools: the three-wave schedule reads them
-    const int BN = miattn::keys_per_tile(D, waves);
+    const int BN = miattn::keys_per_tile(D, waves, p.k_scale != nullptr);
     const int BM = miattn::rows_per_workgroup(waves);
     p.n_mblocks = (p.rows + BM - 1) / BM;
     const int64_t bhs = (int64_t)p.B * p.Hkv;
