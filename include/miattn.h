@@ -63,10 +63,23 @@
  *     is set, which copies them to the host (synchronising the stream).
  *     Out-of-range entries are otherwise the caller's error, with undefined
  *     results.
- *   - The library keeps one split-KV workspace per device, grown with hipMalloc
- *     on first need; a call that needs no larger workspace allocates nothing.
- *     Calls that share a device and may run concurrently on different streams
- *     must not both use the workspace; calls on one stream are ordered.
+ *   - The library keeps one split-KV workspace per device (FP32 partial
+ *     results of split key ranges, and the backward's per-row statistics),
+ *     grown with hipMalloc on first need; a call that needs no larger
+ *     workspace allocates nothing.  A grown workspace replaces the old one
+ *     without freeing it (a HIP graph captured earlier may still use it):
+ *     retired buffers are freed only by miattn_release_workspace().
+ *   - Calls that use the workspace on different streams of one device are
+ *     ordered: a call on a stream other than the workspace's previous user's
+ *     first makes its stream wait for that use (an event).  Under stream
+ *     capture the library records no such dependency and cannot grow the
+ *     workspace (that call returns MIATTN_ERR_INVALID_ARG): run a call once
+ *     before capturing it, and do not replay a captured graph concurrently
+ *     with other calls of this library on the same device.
+ *   - The only environment variables read are MIATTN_VALIDATE (above) and
+ *     MIATTN_SPLIT_KEYS (keys per split-KV partition, as
+ *     miattn_set_split_keys; for debugging).  Every other choice of schedule
+ *     is fixed by the call's shapes.
  */
 #ifndef MIATTN_H
 #define MIATTN_H
@@ -94,7 +107,9 @@ typedef enum {
 } miattn_cache_dtype;
 
 /*
- * Dense attention forward.
+ * Dense attention forward (TileOPs "Attention Operators", GQADenseFwdOp
+ * stages 1, 4, 5 and 7; RL-Kernel "Standard Softmax Attention", Tensor
+ * Contract: scale, key_padding_mask and the causal rule).
  *
  *   q    device, [B, Sq, Hq, D]  dtype
  *   k    device, [B, Skv, Hkv, D] dtype   (may be NULL when Skv == 0)
@@ -105,19 +120,12 @@ typedef enum {
  *          0.0 included, is used verbatim; +-inf is refused
  *   causal 0 or 1: key j is visible to query i iff j <= p_i = i + Skv - Sq.
  *          Sq > Skv is accepted; its first Sq - Skv rows see no key
- *   window_left, window_right  sliding window: key j is visible to query i
- *          only if j >= p_i - window_left (when window_left != -1) and
- *          j <= p_i + window_right (when window_right != -1); -1 is
- *          unlimited, other negative values are refused (INVALID_ARG)
- *   softcap 0 for plain logits; c > 0 (finite) replaces each logit z by
- *          c * tanh(z / c); negative, infinite or NaN values are refused
  *   key_padding_mask  device, [B, Skv] bytes, nonzero = keep; NULL = no mask.
- *          Combined with the causal rule and the window by AND
+ *          Combined with the causal rule by AND
  *   o      device, [B, Sq, Hq, D] dtype, written in full
  *   lse    device, [B, Hq, Sq] float32, or NULL to skip it: the natural log of
- *          the softmax denominator, ln sum_j exp(logit_j) over the visible
- *          keys (with a softcap, of the capped logits).  A row that sees no
- *          key gets o = 0 and lse = -inf
+ *          the softmax denominator, ln sum_j exp(alpha q.k_j) over the visible
+ *          keys.  A row that sees no key gets o = 0 and lse = -inf
  *   dtype  MIATTN_BF16 or MIATTN_FP16, the type of q, k, v and o
  *   stream hipStream_t or NULL
  *
@@ -125,12 +133,32 @@ typedef enum {
  */
 miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B, int Hq,
                              int Hkv, int Sq, int Skv, int D, float scale, int causal,
-                             int window_left, int window_right, float softcap,
                              const uint8_t *key_padding_mask, void *o, float *lse,
                              miattn_dtype dtype, void *stream);
 
 /*
- * Paged attention forward (decode, Sq = 1, and chunked prefill, Sq > 1).
+ * attn_fwd_dense with a sliding window and a logit softcap (TileOPs
+ * "Attention Operators", GQADenseFwdOp stage 5: the window; stage 6: the
+ * capped logit).  All other arguments as for attn_fwd_dense.
+ *
+ *   window_left, window_right  key j is visible to query i only if
+ *          j >= p_i - window_left (when window_left != -1) and
+ *          j <= p_i + window_right (when window_right != -1); -1 is
+ *          unlimited, other negative values are refused (INVALID_ARG).
+ *          Combined with the causal rule and the padding mask by AND
+ *   softcap 0 for plain logits; c > 0 (finite) replaces each logit z by
+ *          c * tanh(z / c); negative, infinite or NaN values are refused.
+ *          lse is then the natural log of sum_j exp(capped logit_j)
+ */
+miattn_status attn_fwd_dense_ex(const void *q, const void *k, const void *v, int B, int Hq,
+                                int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                                const uint8_t *key_padding_mask, void *o, float *lse,
+                                int window_left, int window_right, float softcap,
+                                miattn_dtype dtype, void *stream);
+
+/*
+ * Paged attention forward (decode, Sq = 1, and chunked prefill, Sq > 1;
+ * TileOPs "Attention Operators", MHADecodePagedWithKVCacheFwdOp).
  *
  *   q        device, [B, Sq, Hq, D] dtype
  *   k_cache  device, [num_phys_pages * page_size, Hkv, D] dtype; the same bytes
@@ -145,8 +173,6 @@ miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B,
  *            at p >= ceil(len / page_size) are never read
  *   page_size a power of two >= 16 (others return MIATTN_ERR_UNSUPPORTED)
  *   causal   0 or 1: key j is visible to query i iff j <= p_i = i + len_b - Sq
- *   window_left, window_right, softcap  as for attn_fwd_dense, with p_i the
- *            position of query i in request b's own key range
  *   o, lse   as for attn_fwd_dense
  *   B, Sq, Hq, Hkv, D  as for attn_fwd_dense; max_pages > 0
  *   num_phys_pages  number of physical pages in each cache (only checked under
@@ -154,14 +180,28 @@ miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B,
  *   scale, dtype, stream  as for attn_fwd_dense
  *
  * Long key ranges are split across workgroups; the partial results (FP32
- * output rows and LSEs) are merged by a second kernel on the same stream.
+ * output rows and LSEs, in the library workspace) are merged by a second
+ * kernel on the same stream (MATE "QSA", Core Attention: the split-KV merge).
  */
 miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *real_seqlen_kv, const int32_t *block_table,
-                             int page_size, int causal, int window_left, int window_right,
-                             float softcap, void *o, float *lse, int B, int Sq,
+                             int page_size, int causal, void *o, float *lse, int B, int Sq,
                              int Hq, int Hkv, int D, int max_pages, int num_phys_pages,
                              float scale, miattn_dtype dtype, void *stream);
+
+/*
+ * attn_fwd_paged with a sliding window and a logit softcap (TileOPs
+ * "Attention Operators", GQAPagedFwdOp takes the window and softcap of
+ * GQADenseFwdOp stages 5 and 6).  window_left, window_right and softcap as
+ * for attn_fwd_dense_ex, with p_i the position of query i in request b's own
+ * key range; all other arguments as for attn_fwd_paged.
+ */
+miattn_status attn_fwd_paged_ex(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *real_seqlen_kv, const int32_t *block_table,
+                                int page_size, int causal, void *o, float *lse, int B, int Sq,
+                                int Hq, int Hkv, int D, int max_pages, int num_phys_pages,
+                                float scale, int window_left, int window_right, float softcap,
+                                miattn_dtype dtype, void *stream);
 
 /*
  * Packed (THD) attention forward: requests of different lengths in one call.
@@ -178,7 +218,7 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
  *        results but no access outside the tensors
  *   max_seqlen_q, max_seqlen_kv  the most queries / keys one request holds
  *        (they size the launch)
- *   causal, window_left, window_right, softcap, scale  as for attn_fwd_dense,
+ *   causal, window_left, window_right, softcap, scale  as for attn_fwd_dense_ex,
  *        with p_i = i + Skv_b - Sq_b inside request b
  *   sinks device, float32 [Hq] sink logits, or NULL: the head's sink enters
  *        the softmax denominator only, used as given; a +inf sink gives o = 0
@@ -323,7 +363,10 @@ miattn_status attn_bwd(const void *q, const void *k, const void *v, const void *
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *miattn_last_error(void);
 
-/* Frees the split-KV workspace of the current device (waits for the device). */
+/*
+ * Frees the workspace of the current device and every buffer it replaced
+ * (waits for the device).  No graph captured before may be replayed after it.
+ */
 miattn_status miattn_release_workspace(void);
 
 /*
@@ -332,6 +375,14 @@ miattn_status miattn_release_workspace(void);
  * that yields one split disables the merge.  Mainly for tests and tuning.
  */
 void miattn_set_split_keys(int keys_per_split);
+
+/*
+ * Stream-K decode plan control, for tests: the plan weight, in key tiles, of
+ * starting a piece of a (request, KV head) unit (0 .. 64; a negative value
+ * restores the default, 6).  Any weight covers every key tile exactly once;
+ * it only moves the boundaries between workgroups' shares.
+ */
+void miattn_set_streamk_piece(int tiles);
 
 /*
  * Kernel timing.  Between miattn_profile_start() and miattn_profile_stop(),

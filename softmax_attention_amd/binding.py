@@ -21,9 +21,10 @@ MIATTN_BF16, MIATTN_FP16 = 0, 1
 MIATTN_CACHE_BF16, MIATTN_CACHE_FP16, MIATTN_CACHE_FP8_E4M3 = 0, 1, 2
 
 # every symbol include/miattn.h declares
-EXPORTS = ("attn_fwd_dense", "attn_fwd_paged", "attn_fwd_varlen", "attn_fwd_paged_varlen",
-           "kv_cache_write", "attn_fwd_paged_append", "attn_bwd", "miattn_last_error", "miattn_release_workspace", "miattn_set_split_keys",
-           "miattn_profile_start", "miattn_profile_stop")
+EXPORTS = ("attn_fwd_dense", "attn_fwd_dense_ex", "attn_fwd_paged", "attn_fwd_paged_ex",
+           "attn_fwd_varlen", "attn_fwd_paged_varlen", "kv_cache_write", "attn_fwd_paged_append",
+           "attn_bwd", "miattn_last_error", "miattn_release_workspace", "miattn_set_split_keys",
+           "miattn_set_streamk_piece", "miattn_profile_start", "miattn_profile_stop")
 
 _lib = None
 
@@ -42,12 +43,18 @@ def lib() -> ctypes.CDLL:
                 "(or __graft_entry__.build()) first")
         L = ctypes.CDLL(LIB_PATH)
         P, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-        L.attn_fwd_dense.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f32, i32,
-                                     i32, i32, f32, P, P, P, i32, P]
+        L.attn_fwd_dense.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, P, P,
+                                     i32, P]
         L.attn_fwd_dense.restype = i32
-        L.attn_fwd_paged.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f32, P, P, i32, i32,
-                                     i32, i32, i32, i32, i32, f32, i32, P]
+        L.attn_fwd_dense_ex.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, P,
+                                        P, i32, i32, f32, i32, P]
+        L.attn_fwd_dense_ex.restype = i32
+        L.attn_fwd_paged.argtypes = [P, P, P, P, P, i32, i32, P, P, i32, i32, i32, i32, i32, i32,
+                                     i32, f32, i32, P]
         L.attn_fwd_paged.restype = i32
+        L.attn_fwd_paged_ex.argtypes = [P, P, P, P, P, i32, i32, P, P, i32, i32, i32, i32, i32,
+                                        i32, i32, f32, i32, i32, f32, i32, P]
+        L.attn_fwd_paged_ex.restype = i32
         L.attn_fwd_varlen.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                       i32, i32, i32, f32, P, P, P, i32, P]
         L.attn_fwd_varlen.restype = i32
@@ -71,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.miattn_release_workspace.restype = i32
         L.miattn_set_split_keys.argtypes = [i32]
         L.miattn_set_split_keys.restype = None
+        L.miattn_set_streamk_piece.argtypes = [i32]
+        L.miattn_set_streamk_piece.restype = None
         L.miattn_profile_start.argtypes = []
         L.miattn_profile_start.restype = None
         L.miattn_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double),
@@ -122,6 +131,34 @@ def _stream() -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _output(out: Optional[torch.Tensor], like: torch.Tensor) -> torch.Tensor:
+    """The caller's output tensor, checked against the shape, dtype and device
+    the kernels write (they write it in full, as dense row-major), or a new
+    one."""
+    if out is None:
+        return torch.empty_like(like)
+    if tuple(out.shape) != tuple(like.shape) or out.dtype != like.dtype:
+        raise ValueError(f"out must be {like.dtype} {tuple(like.shape)}, got {out.dtype} "
+                         f"{tuple(out.shape)}")
+    if out.device != like.device or not out.is_contiguous():
+        raise ValueError("out must be contiguous and on the queries' device")
+    return out
+
+
+def _lse_output(lse: Optional[torch.Tensor], shape, device, return_lse: bool):
+    """The caller's float32 LSE tensor of `shape` (checked), a new one, or None."""
+    if not return_lse:
+        return None
+    if lse is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape):
+        raise ValueError(f"lse must be float32 {tuple(shape)}, got {lse.dtype} "
+                         f"{tuple(lse.shape)}")
+    if lse.device != device or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous and on the queries' device")
+    return lse
+
+
 def attn_fwd_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale=None,
                    causal: bool = True, window=None, softcap=None,
                    key_padding_mask: Optional[torch.Tensor] = None,
@@ -152,15 +189,19 @@ def attn_fwd_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale=N
             raise ValueError(f"key_padding_mask must be [B, Skv] = [{B}, {Skv}]")
         mask = key_padding_mask.to(device=q.device, dtype=torch.bool).contiguous()
         mask = mask.view(torch.uint8)
-    o = out if out is not None else torch.empty_like(q)
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    st = lib().attn_fwd_dense(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Sq, Skv, D, _scale(scale),
-                              int(bool(causal)), *_window(window), _softcap(softcap),
-                              _ptr(mask), _ptr(o),
-                              _ptr(lse) if return_lse else None, code, _stream())
+    o = _output(out, q)
+    lse = _lse_output(lse, (B, Hq, Sq), q.device, return_lse)
+    if window is None and not softcap:
+        st = lib().attn_fwd_dense(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Sq, Skv, D,
+                                  _scale(scale), int(bool(causal)), _ptr(mask), _ptr(o),
+                                  _ptr(lse), code, _stream())
+    else:
+        st = lib().attn_fwd_dense_ex(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Sq, Skv, D,
+                                     _scale(scale), int(bool(causal)), _ptr(mask), _ptr(o),
+                                     _ptr(lse), *_window(window), _softcap(softcap), code,
+                                     _stream())
     _check(st)
-    return o, (lse if return_lse else None)
+    return o, lse
 
 
 def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -207,16 +248,17 @@ def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     q = q.contiguous()
     k_cache, v_cache = k_cache.contiguous(), v_cache.contiguous()
     real_seqlen_kv, block_table = real_seqlen_kv.contiguous(), block_table.contiguous()
-    o = out if out is not None else torch.empty_like(q)
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    st = lib().attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(real_seqlen_kv),
-                              _ptr(block_table), int(page_size), int(bool(causal)),
-                              *_window(window), _softcap(softcap), _ptr(o),
-                              _ptr(lse) if return_lse else None, B, Sq, Hq, Hkv, D,
-                              block_table.shape[1], n_pages, _scale(scale), code, _stream())
+    o = _output(out, q)
+    lse = _lse_output(lse, (B, Hq, Sq), q.device, return_lse)
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(real_seqlen_kv), _ptr(block_table),
+            int(page_size), int(bool(causal)), _ptr(o), _ptr(lse), B, Sq, Hq, Hkv, D,
+            block_table.shape[1], n_pages, _scale(scale))
+    if window is None and not softcap:
+        st = lib().attn_fwd_paged(*args, code, _stream())
+    else:
+        st = lib().attn_fwd_paged_ex(*args, *_window(window), _softcap(softcap), code, _stream())
     _check(st)
-    return o, (lse if return_lse else None)
+    return o, lse
 
 
 def _offsets(cu: torch.Tensor, device, name: str) -> torch.Tensor:
@@ -275,15 +317,14 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     mq = _max_len(cq) if max_seqlen_q is None else int(max_seqlen_q)
     mk = _max_len(ck) if max_seqlen_kv is None else int(max_seqlen_kv)
     sk = _sinks_arg(sinks, Hq, q.device)
-    o = out if out is not None else torch.empty_like(q)
-    if return_lse and lse is None:
-        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    o = _output(out, q)
+    lse = _lse_output(lse, (Hq, total_q), q.device, return_lse)
     st = lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cq), _ptr(ck), B, total_q,
                                total_kv, mq, mk, Hq, Hkv, D, _scale(scale), int(bool(causal)),
                                *_window(window), _softcap(softcap), _ptr(sk), _ptr(o),
-                               _ptr(lse) if return_lse else None, code, _stream())
+                               _ptr(lse), code, _stream())
     _check(st)
-    return o, (lse if return_lse else None)
+    return o, lse
 
 
 def _pool_kind(q, k_cache, v_cache, k_scale, v_scale):
@@ -352,18 +393,17 @@ def attn_fwd_paged_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     q = q.contiguous()
     k_cache, v_cache = k_cache.contiguous(), v_cache.contiguous()
     cache_seqlens, block_table = cache_seqlens.contiguous(), block_table.contiguous()
-    o = out if out is not None else torch.empty_like(q)
-    if return_lse and lse is None:
-        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    o = _output(out, q)
+    lse = _lse_output(lse, (Hq, total_q), q.device, return_lse)
     st = lib().attn_fwd_paged_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
                                      _ptr(block_table), _ptr(cq), int(page_size),
                                      int(bool(causal)), *_window(window), _softcap(softcap),
-                                     _ptr(sk), _ptr(o), _ptr(lse) if return_lse else None, B,
+                                     _ptr(sk), _ptr(o), _ptr(lse), B,
                                      total_q, mq, Hq, Hkv, D, block_table.shape[1], n_pages,
                                      _scale(scale), code, cache, _ptr(k_scale), _ptr(v_scale),
                                      _stream())
     _check(st)
-    return o, (lse if return_lse else None)
+    return o, lse
 
 
 def _pool_geometry(k_pages: torch.Tensor, Hkv: int, D: int) -> int:
@@ -455,18 +495,17 @@ def attn_fwd_paged_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Ten
     mq = _max_len(cq) if max_seqlen_q is None else int(max_seqlen_q)
     q, k_new, v_new = q.contiguous(), k_new.contiguous(), v_new.contiguous()
     cache_seqlens, block_table = cache_seqlens.contiguous(), block_table.contiguous()
-    o = out if out is not None else torch.empty_like(q)
-    if return_lse and lse is None:
-        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    o = _output(out, q)
+    lse = _lse_output(lse, (Hq, total_q), dev, return_lse)
     _check(lib().attn_fwd_paged_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                        _ptr(v_cache), _ptr(cache_seqlens), _ptr(block_table),
                                        _ptr(cq), int(page_size), int(bool(causal)),
                                        _softcap(softcap), _ptr(o),
-                                       _ptr(lse) if return_lse else None, B, total_q, mq, Hq,
+                                       _ptr(lse), B, total_q, mq, Hq,
                                        Hkv, D, block_table.shape[1], num_slots // page_size,
                                        _scale(scale), code, cache, _ptr(k_scale),
                                        _ptr(v_scale), _stream()))
-    return o, (lse if return_lse else None)
+    return o, lse
 
 
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
@@ -503,6 +542,12 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
 def set_split_keys(keys_per_split: int) -> None:
     """Keys per split-KV partition (0 = automatic)."""
     lib().miattn_set_split_keys(int(keys_per_split))
+
+
+def set_streamk_piece(tiles: int) -> None:
+    """Stream-K decode plan weight of starting a piece, in key tiles (tests;
+    a negative value restores the default)."""
+    lib().miattn_set_streamk_piece(int(tiles))
 
 
 def release_workspace() -> None:

@@ -22,7 +22,7 @@
 //     straight into LDS ring stages with buffer_load ... lds (no registers),
 //     ordered by counted vmcnt waits and an LDS-only barrier.  Schedules
 //     (WAVES): 8 waves in two groups alternating MFMA and softmax phases over
-//     64-key tiles (prefill, D <= 128); 2 or 3 waves where wave 0 computes
+//     64-key tiles (prefill, D <= 128); 3 waves where wave 0 computes
 //     and the others only load (decode, D <= 128), optionally as a persistent
 //     stream-K grid that gives every workgroup an equal share of all key
 //     tiles; 4 waves that all load and compute (D = 256).
@@ -60,7 +60,7 @@ using namespace dev;
 // the 4-wave D = 256 schedule run one workgroup per CU.
 template <int D, int WAVES, bool FP8>
 constexpr int waves_per_eu() {
-    return (WAVES == 8 || ((WAVES == 2 || WAVES == 3) && (FP8 || D < 128))) ? 2 : 1;
+    return (WAVES == 8 || (WAVES == 3 && (FP8 || D < 128))) ? 2 : 1;
 }
 
 #ifndef MIATTN_READ_AHEAD
@@ -109,11 +109,11 @@ void attn_fwd_kernel(const FwdParams p) {
     constexpr int BN = keys_per_tile(D, WAVES, FP8);  // keys per tile
     constexpr int TILE_BYTES = BN * D * 2;         // one K (or V) tile
     constexpr int PIECES = TILE_BYTES / 1024;      // 1 KB direct loads per tile
-    // The decode schedule (2 or 3 waves) splits the roles: wave 0 computes,
+    // The decode schedule (3 waves) splits the roles: wave 0 computes,
     // the other waves issue every load (one loading wave streams only about
     // half of what a CU's memory path takes).  Otherwise each wave issues an
     // equal share.
-    constexpr bool SPLIT_ROLES = WAVES == 2 || WAVES == 3;
+    constexpr bool SPLIT_ROLES = WAVES == 3;
     constexpr int LOADERS = SPLIT_ROLES ? WAVES - 1 : WAVES;
     constexpr int PPW = PIECES / LOADERS;          // 1 KB pieces per loading wave
     constexpr int NT = BN / 32;                    // 32-key score blocks per tile
@@ -959,74 +959,44 @@ void attn_fwd_kernel(const FwdParams p) {
     const int units = p.B * p.Hkv * p.n_splits;
     if constexpr (SPLIT_ROLES) {
         if (p.sk_grid > 0) {
-            // Stream-K decode: the (batch, KV head) units, heads fastest, form
-            // one sequence of plan weight T (each unit its key tiles plus the
-            // cost of starting a piece, sk_weight); workgroup g takes the
-            // weight [g T / G, (g+1) T / G) -- an equal share, whatever the
-            // lengths -- and writes one partial per unit whose tiles its share
-            // touches, to slot unit + g (the merge kernel finds the slots the
-            // same way).  A unit of w = piece + tiles holds its tiles at
-            // weight offsets [piece, w).
+            // Stream-K decode, by head: workgroup g serves KV head g % Hkv, and
+            // the G / Hkv workgroups of one head cut that head's sequence of
+            // (request) units -- plan weight T1, each unit its key tiles plus
+            // the cost of starting a piece of it (sk_weight) -- into equal
+            // shares: share c = g / Hkv takes the weight [c T1 / S, (c+1) T1 / S)
+            // whatever the lengths, and writes one partial per unit whose tiles
+            // it touches, to slot kvh (B + S) + b + c (the merge kernel finds the
+            // slots the same way).  The Hkv workgroups g, g + 1, ... run side by
+            // side and read the same cache rows.  A unit of weight w = piece +
+            // tiles holds its tiles at weight offsets [piece, w).
             const int g = blockIdx.x;
             const SkBatch sb = {sd, BN, p.win_left, p.sk_piece};
             int unused;
-            if (p.sk_heads) {
-                // by head: share c = g / Hkv of head g % Hkv's weight T1 (one
-                // head's units of every request, in request order); partial
-                // slot kvh (B + G / Hkv) + b + c
-                const int kvh = g % p.Hkv, c = g / p.Hkv, shares = p.sk_grid / p.Hkv;
-                const int64_t T1 = sk_sums(sb, 0, unused);
-                const int64_t s0 = (int64_t)c * T1 / shares;
-                const int64_t s1 = (int64_t)(c + 1) * T1 / shares;
-                if (s0 >= s1) return;
-                int b, pre, wb;
-                sk_find(sb, 1, s0, b, pre, wb);
-                int off = (int)(s0 - pre);  // weight offset into request b
-                for (int64_t at = s0; at < s1; ++b, off = 0) {
-                    const int len = seq_kv_len(sd, b);
-                    int64_t unused_row0;
-                    int sq_u;
-                    q_span(sd, b, unused_row0, sq_u);
-                    const int t_first = sk_first_tile(sb, len, sq_u);
-                    const int tiles = sk_tiles(sb, b);
-                    const int w = sk_weight(sb, tiles);
-                    // the share's part of the unit's tiles, as weight offsets
-                    const int lo = max(off, sb.piece);
-                    const int hi = (int)min((int64_t)w, off + (s1 - at));
-                    at += w - off;
-                    if (hi <= lo) continue;
-                    run(0, b, kvh, len, (t_first + lo - sb.piece) * BN,
-                        min(len, (t_first + hi - sb.piece) * BN),
-                        (int64_t)kvh * (p.B + shares) + b + c, true);
-                }
-                return;
-            }
-            const int64_t T = (int64_t)p.Hkv * sk_sums(sb, 0, unused);
-            const int64_t s0 = (int64_t)g * T / p.sk_grid;
-            const int64_t s1 = (int64_t)(g + 1) * T / p.sk_grid;
+            const int kvh = g % p.Hkv, c = g / p.Hkv, shares = p.sk_grid / p.Hkv;
+            const int64_t T1 = sk_sums(sb, 0, unused);
+            const int64_t s0 = (int64_t)c * T1 / shares;
+            const int64_t s1 = (int64_t)(c + 1) * T1 / shares;
             if (s0 >= s1) return;
-            int b0, pre0, w0;
-            sk_find(sb, p.Hkv, s0, b0, pre0, w0);
-            const int64_t rem = s0 - (int64_t)p.Hkv * pre0;
-            int u = b0 * p.Hkv + (int)(rem / w0);
-            int off = (int)(rem % w0);  // weight offset into unit u
-            for (int64_t at = s0; at < s1; ++u, off = 0) {
-                const int b = u / p.Hkv;
-                const int kvh = u - b * p.Hkv;
-                // (the unit's tiles start at the first one its window reaches)
+            int b, pre, wb;
+            sk_find(sb, 1, s0, b, pre, wb);
+            int off = (int)(s0 - pre);  // weight offset into request b
+            for (int64_t at = s0; at < s1; ++b, off = 0) {
                 const int len = seq_kv_len(sd, b);
                 int64_t unused_row0;
                 int sq_u;
                 q_span(sd, b, unused_row0, sq_u);
+                // (the unit's tiles start at the first one its window reaches)
                 const int t_first = sk_first_tile(sb, len, sq_u);
                 const int tiles = sk_tiles(sb, b);
                 const int w = sk_weight(sb, tiles);
+                // the share's part of the unit's tiles, as weight offsets
                 const int lo = max(off, sb.piece);
                 const int hi = (int)min((int64_t)w, off + (s1 - at));
                 at += w - off;
                 if (hi <= lo) continue;
                 run(0, b, kvh, len, (t_first + lo - sb.piece) * BN,
-                    min(len, (t_first + hi - sb.piece) * BN), (int64_t)u + g, true);
+                    min(len, (t_first + hi - sb.piece) * BN),
+                    (int64_t)kvh * (p.B + shares) + b + c, true);
             }
             return;
         }
@@ -1035,13 +1005,7 @@ void attn_fwd_kernel(const FwdParams p) {
     // count allows, consecutive workgroups of one XCD share a (batch, KV head)
     // so its K/V stays in that XCD's L2.  Causal row blocks run heaviest first.
     int rank, unit;
-    if (p.xcd_units > 0 && p.xcd_unit_major) {
-        // each XCD finishes the row blocks of one unit before the next, so its
-        // L2 holds one (batch, KV head)'s K/V at a time
-        const int s = blockIdx.x >> 3;
-        unit = (blockIdx.x & 7) * p.xcd_units + s / p.n_mblocks;
-        rank = s % p.n_mblocks;
-    } else if (p.xcd_units > 0) {
+    if (p.xcd_units > 0) {
         const int s = blockIdx.x >> 3;
         unit = (blockIdx.x & 7) * p.xcd_units + s % p.xcd_units;
         rank = s / p.xcd_units;
@@ -1144,8 +1108,7 @@ hipError_t launch_w(const FwdParams &p, bool bf16, bool paged, int grid, hipStre
 }  // namespace
 
 // Schedules per head dimension: D <= 128 has the 8-wave prefill schedule and
-// the 3-wave decode schedule (plus the 2-wave one, plain logits only, kept
-// for comparison); D = 256 the 4-wave streaming schedule.
+// the 3-wave decode schedule; D = 256 the 4-wave streaming schedule.
 template <int D, bool CAP>
 hipError_t launch_attn_fwd_dc(const FwdParams &p, bool bf16, bool paged, int waves, int grid,
                               hipStream_t stream) {
@@ -1154,8 +1117,6 @@ hipError_t launch_attn_fwd_dc(const FwdParams &p, bool bf16, bool paged, int wav
     } else {
         if (waves == 8) return launch_w<D, 8, CAP>(p, bf16, paged, grid, stream);
         if (waves == 3) return launch_w<D, 3, CAP>(p, bf16, paged, grid, stream);
-        if constexpr (!CAP)
-            if (waves == 2) return launch_w<D, 2, CAP>(p, bf16, paged, grid, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -1164,8 +1125,6 @@ template <int D, bool CAP>
 int decode_blocks_per_cu_dc(const FwdParams &p, bool bf16, bool paged, int waves) {
     if constexpr (D <= 128) {
         if (waves == 3) return decode_blocks<D, 3, CAP>(p, bf16, paged);
-        if constexpr (!CAP)
-            if (waves == 2) return decode_blocks<D, 2, CAP>(p, bf16, paged);
     }
     return 0;
 }

@@ -25,11 +25,11 @@ constexpr int kRowsPerWave = 32;  // one 32x32 MFMA column block
 //     computes, waves 1 and 2 issue all loads -- and 4 waves for D = 256):
 //     each step computes one tile while later tiles load.
 constexpr int rows_per_workgroup(int waves) {
-    return (waves == 2 || waves == 3) ? kRowsPerWave : kRowsPerWave * waves;
+    return waves == 3 ? kRowsPerWave : kRowsPerWave * waves;
 }
 
 // Keys per KV tile.  8 waves: 64 keys (8 KB at D = 64, 16 KB at D = 128).
-// Decode-shaped (2 or 3 waves): 64 keys (16 KB at D = 128); the three-stage
+// Decode-shaped (3 waves): 64 keys (16 KB at D = 128); the three-stage
 // K and V rings then take 96 KB and one workgroup runs per CU, which streamed
 // the paged decode 4-5 % faster than 32-key tiles with two workgroups per CU.
 // Over FP8 pools: tiles of 8 KB of 16-bit values (4096 / D keys, at least
@@ -92,13 +92,12 @@ struct FwdParams {
     float cap_x, cap_k2;
     int q_mode;        // 0: q as given; 1: q negated (alpha < 0); 2: q zeroed (alpha == 0)
     int xcd_units;     // (batch*KV head, split) units per XCD, or 0 for linear order
-    int xcd_unit_major;  // with xcd_units: an XCD runs all row blocks of a unit, then the next
-    int heads_inner;     // units ordered (batch, split, KV head) instead of (batch, KV head, split)
-    int sk_grid;  // stream-K decode (split-role schedule): grid size G, or 0
-    // stream-K by head: workgroup g serves KV head g % Hkv, and the G / Hkv
-    // workgroups of one head split that head's key tiles, so the Hkv
-    // workgroups g, g + 1, ... read the same cache rows together
-    int sk_heads;
+    int heads_inner;   // units ordered (batch, split, KV head) instead of (batch, KV head, split)
+    // stream-K decode (split-role schedule): grid size G (a multiple of Hkv),
+    // or 0.  Workgroup g serves KV head g % Hkv, and the G / Hkv workgroups of
+    // one head split that head's key tiles, so the Hkv workgroups g, g + 1,
+    // ... read the same cache rows together
+    int sk_grid;
     // stream-K: plan weight, in key tiles, of starting a piece of a unit
     int sk_piece;
 };
@@ -117,9 +116,9 @@ struct MergeParams {
     int B, Sq, Hq, Hkv, G, rows, n_splits, split_len;
     // stream-K decode: grid size (0 otherwise), keys per tile and the length
     // clamp the attention kernel applies (max_pages * page_size, 0 for an
-    // empty cache), the left window bound (-1: none), the by-head plan and
-    // the plan weight of a piece -- all as the attention kernel had them
-    int sk_grid, sk_bn, sk_cap, sk_win_left, sk_heads, sk_piece;
+    // empty cache), the left window bound (-1: none) and the plan weight of a
+    // piece -- all as the attention kernel had them
+    int sk_grid, sk_bn, sk_cap, sk_win_left, sk_piece;
 };
 
 // Launchers: return the hipGetLastError() status of the launch.  The
@@ -129,7 +128,7 @@ struct MergeParams {
 template <int D, bool CAP>
 hipError_t launch_attn_fwd_dc(const FwdParams &p, bool bf16, bool paged, int waves, int grid,
                               hipStream_t stream);
-// Workgroups of the decode-shaped (2 or 3 wave) attention kernel one CU runs
+// Workgroups of the decode-shaped (3-wave) attention kernel one CU runs
 // at once (0 if unknown).
 template <int D, bool CAP>
 int decode_blocks_per_cu_dc(const FwdParams &p, bool bf16, bool paged, int waves);

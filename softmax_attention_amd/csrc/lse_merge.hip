@@ -56,37 +56,32 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
     // rows apart, from row `base` on.
     int n_valid;
     int64_t base, stride = p.rows;
-    int64_t g_first = 0;  // stream-K: the first workgroup (slot = unit + workgroup)
-    int64_t T = 0;
-    int64_t sk_g = 0;  // stream-K: workgroups sharing the sequence of T tiles
+    int64_t g_first = 0;  // stream-K: the first share holding this unit's tiles
+    int64_t T = 0;        // stream-K: plan weight of this head's sequence
+    int64_t sk_g = 0;     // stream-K: shares that cut it
     if (p.sk_grid > 0) {
-        // Stream-K: the workgroups whose shares hold this unit's tiles, at
-        // [P + piece, P + piece + tiles) of the sequence of plan weight T
-        // (the unit starts at P); workgroup g held [g T / G, (g+1) T / G).
-        // (by head: the shares of head kvh over its own weight, slots
-        // kvh (B + G / Hkv) + b + share)
+        // Stream-K (by head): the shares of KV head kvh's plan weight T held
+        // this unit's tiles, at [P + piece, P + piece + tiles) of that
+        // sequence (the unit starts at P); share c held [c T / S, (c+1) T / S)
+        // and wrote slot kvh (B + S) + b + c.
         const SkBatch sb = {sd, p.sk_bn, p.sk_win_left, p.sk_piece};
         int before;
-        const int64_t T1 = sk_sums(sb, b, before);
-        T = p.sk_heads ? T1 : (int64_t)p.Hkv * T1;
+        T = sk_sums(sb, b, before);
         const int tiles = sk_tiles(sb, b);
-        const int64_t P = p.sk_heads ? (int64_t)before
-                                     : (int64_t)p.Hkv * before +
-                                           (int64_t)kvh * sk_weight(sb, tiles);
-        const int G = p.sk_heads ? p.sk_grid / p.Hkv : p.sk_grid;
+        const int64_t P = before;
+        const int G = p.sk_grid / p.Hkv;
         sk_g = G;
         if (tiles == 0 || T == 0) {
             n_valid = 0;
             g_first = 0;
         } else {
-            // the workgroup holding position s is the largest g with g T / G <= s
+            // the share holding position s is the largest c with c T / S <= s
             const int64_t first = P + p.sk_piece, last = P + p.sk_piece + tiles - 1;
             g_first = ((first + 1) * G - 1) / T;
             const int64_t g_last = ((last + 1) * G - 1) / T;
             n_valid = (int)(g_last - g_first + 1);
         }
-        const int64_t slot0 = p.sk_heads ? (int64_t)kvh * (p.B + G) + b + g_first
-                                         : (int64_t)bh + g_first;
+        const int64_t slot0 = (int64_t)kvh * (p.B + G) + b + g_first;
         base = slot0 * p.rows + r;
     } else {
         const int kv_len = seq_kv_len(sd, b);
@@ -95,7 +90,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
         n_valid = min(p.n_splits, (kv_len + p.split_len - 1) / p.split_len);
         base = (int64_t)bh * p.n_splits * p.rows + r;
     }
-    // stream-K: a workgroup whose share is empty (T < G) wrote nothing
+    // stream-K: a share that is empty (T < shares) wrote nothing
     auto skip = [&](int s) -> bool {
         if (p.sk_grid == 0) return false;
         const int64_t g = g_first + s;

@@ -70,18 +70,35 @@ bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 constexpr int kMaxDevices = 64;
 
+// The split-KV workspace of one device.  It grows by allocating a larger
+// buffer; the old one is retired, not freed, because a HIP graph captured
+// earlier may still name it in its kernel nodes.  Retired buffers are freed
+// only by miattn_release_workspace().  Calls on different streams are
+// ordered on the device: a call on another stream than the workspace's last
+// user first waits for an event recorded behind that use (not under stream
+// capture, where the caller orders graph replays).
 struct DeviceState {
     void *ws = nullptr;  // split-KV partials
     size_t ws_bytes = 0;
+    std::vector<void *> retired;
+    hipStream_t last_stream = nullptr;  // last (non-capturing) stream that used ws
+    hipEvent_t last_use = nullptr;      // recorded on last_stream after that use
+    bool used = false;
     int cus = 0;
-    // decode kernel occupancy: [3 waves][D 128][bf16][paged][capped logits][FP8 pools]
-    int decode_per_cu[2][2][2][2][2][2] = {};
+    // decode kernel occupancy: [D 128][bf16][paged][capped logits][FP8 pools]
+    int decode_per_cu[2][2][2][2][2] = {};
 };
 
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
 int g_split_keys = 0;  // 0 = automatic
 constexpr int kSkPieceMax = 64;  // largest stream-K piece weight, in key tiles
+// A piece of a stream-K unit that starts mid-kernel waits ~10 us for its
+// page-table entry and first tile (measured with in-kernel timestamps), about
+// six tiles' worth of streaming: the plan weighs each piece that much, so a
+// workgroup that starts more pieces gets fewer tiles.
+constexpr int kSkPieceDefault = 6;
+int g_sk_piece = kSkPieceDefault;
 
 int compute_units(int dev) {
     std::lock_guard<std::mutex> lock(g_mu);
@@ -96,38 +113,61 @@ int compute_units(int dev) {
 }
 
 // Decode workgroups one CU runs at once (occupancy API, cached).
-int decode_per_cu(int dev, const miattn::FwdParams &p, int D, bool bf16, bool paged, int waves,
-                  bool cap) {
+int decode_per_cu(int dev, const miattn::FwdParams &p, int D, bool bf16, bool paged, bool cap) {
     std::lock_guard<std::mutex> lock(g_mu);
-    int &slot =
-        g_dev[dev].decode_per_cu[waves == 3][D == 128][bf16][paged][cap][p.k_scale != nullptr];
+    int &slot = g_dev[dev].decode_per_cu[D == 128][bf16][paged][cap][p.k_scale != nullptr];
     if (slot == 0) {
-        const int n = miattn::attn_fwd_decode_blocks_per_cu(p, D, bf16, paged, waves, cap);
+        const int n = miattn::attn_fwd_decode_blocks_per_cu(p, D, bf16, paged, 3, cap);
         slot = n > 0 ? n : -1;
     }
     return slot > 0 ? slot : 1;
 }
 
-miattn_status workspace(int dev, size_t bytes, void **out) {
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
+// The workspace for a call on `stream`, at least `bytes` large; the call's
+// kernels must then be followed by workspace_done(dev, stream).
+miattn_status workspace(int dev, hipStream_t stream, size_t bytes, void **out) {
     std::lock_guard<std::mutex> lock(g_mu);
     DeviceState &d = g_dev[dev];
+    const bool cap = capturing(stream);
     if (d.ws_bytes < bytes) {
-        if (d.ws) {
-            hipError_t e = hipFree(d.ws);  // waits for work that may still use it
-            d.ws = nullptr;
-            d.ws_bytes = 0;
-            if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
-        }
+        if (cap)
+            return fail(MIATTN_ERR_INVALID_ARG,
+                        "the split-KV workspace must grow to %zu bytes, which cannot happen "
+                        "under stream capture: run the call once before capturing it",
+                        bytes);
         // grow with headroom so that a slightly larger call does not reallocate
         const size_t want = bytes + bytes / 4;
-        hipError_t e = hipMalloc(&d.ws, want);
-        if (e != hipSuccess) {
-            d.ws = nullptr;
-            return hip_fail(e, "hipMalloc(split-KV workspace)");
-        }
+        void *fresh = nullptr;
+        hipError_t e = hipMalloc(&fresh, want);
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc(split-KV workspace)");
+        if (d.ws) d.retired.push_back(d.ws);
+        d.ws = fresh;
         d.ws_bytes = want;
     }
+    if (!cap && d.used && d.last_stream != stream) {
+        // the previous user ran on another stream: order this call after it
+        hipError_t e = hipStreamWaitEvent(stream, d.last_use, 0);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(workspace)");
+    }
     *out = d.ws;
+    return MIATTN_OK;
+}
+
+miattn_status workspace_done(int dev, hipStream_t stream) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState &d = g_dev[dev];
+    if (capturing(stream)) return MIATTN_OK;
+    hipError_t e = hipSuccess;
+    if (!d.last_use) e = hipEventCreateWithFlags(&d.last_use, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(d.last_use, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(workspace)");
+    d.last_stream = stream;
+    d.used = true;
     return MIATTN_OK;
 }
 
@@ -293,73 +333,56 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     p.rows = p.Sq * p.G;
     // D <= 128: the 8-wave ping-pong schedule for prefill, a three-wave
     // streaming workgroup (one computing, two loading) for decode-shaped calls
-    // (all packed rows in one MFMA column block); D = 256: the 4-wave
-    // streaming schedule.
+    // (all packed rows in one MFMA column block) and for FP8 pools; D = 256:
+    // the 4-wave streaming schedule.
     int waves = D == 256 ? 4 : (p.rows > miattn::kRowsPerWave ? 8 : 3);
-    const int forced = env_int("MIATTN_WAVES", 0);
-    if (D <= 128 && (forced == 2 || forced == 3 || forced == 8)) waves = forced;
-    if (waves == 2 && cap) waves = 3;  // the two-wave comparison schedule has no capped build
     if (p.k_scale != nullptr) waves = 3;  // FP8 pools: the three-wave schedule reads them
     const int BN = miattn::keys_per_tile(D, waves, p.k_scale != nullptr);
     const int BM = miattn::rows_per_workgroup(waves);
     p.n_mblocks = (p.rows + BM - 1) / BM;
     const int64_t bhs = (int64_t)p.B * p.Hkv;
     const int64_t cap_tiles = capacity > 0 ? (capacity + BN - 1) / BN : 1;
-    int split_keys = g_split_keys > 0 ? g_split_keys : env_int("MIATTN_SPLIT_KEYS", 0);
+    const int split_keys = g_split_keys > 0 ? g_split_keys : env_int("MIATTN_SPLIT_KEYS", 0);
     p.sk_grid = 0;
 
     // Decode-shaped calls run stream-K: a grid of what the GPU holds at once,
-    // each workgroup an equal share of the plan weight of all (batch, KV head)
-    // units (their key tiles plus a cost per piece), so no workgroup waits on a
-    // long request or for a dispatch slot.  A forced split length selects the
-    // split plan below instead.  (The plan's sums are 32-bit: Hkv * B * the
-    // weight of a unit at the capacity.)
-    if ((waves == 2 || waves == 3) && p.rows <= miattn::kRowsPerWave && split_keys <= 0 &&
-        bhs * (cap_tiles + kSkPieceMax) < INT_MAX && env_int("MIATTN_STREAMK", 1)) {
-        int per_cu = decode_per_cu(dev, p, D, bf16, paged, waves, cap);
-        const int want = env_int("MIATTN_SK_PER_CU", 0);  // tuning override
-        if (want > 0 && want < per_cu) per_cu = want;
-        // by head (neighbouring workgroups read the same cache rows; measured
-        // faster for FP8 pools and, with 64-key tiles, for 16-bit ones; the
-        // interleaved plan stays selectable with MIATTN_SK_HEADS=0) -- on a
-        // grid of whole groups of Hkv
-        const int sk_heads = env_int("MIATTN_SK_HEADS", 1) ? 1 : 0;
-        int G = compute_units(dev) * per_cu;
-        if (sk_heads) G = std::max(1, G / p.Hkv) * p.Hkv;
+    // each workgroup an equal share of the plan weight of one KV head's
+    // (request) units -- their key tiles plus a cost per piece -- so no
+    // workgroup waits on a long request or for a dispatch slot.  A forced
+    // split length selects the split plan below instead.  (The plan's sums
+    // are 32-bit: B * the weight of a unit at the capacity.)
+    if (waves == 3 && p.rows <= miattn::kRowsPerWave && split_keys <= 0 &&
+        (int64_t)p.B * (cap_tiles + kSkPieceMax) < INT_MAX) {
+        const int per_cu = decode_per_cu(dev, p, D, bf16, paged, cap);
+        // whole groups of Hkv workgroups: workgroup g serves KV head g % Hkv
+        const int G = std::max(1, compute_units(dev) * per_cu / p.Hkv) * p.Hkv;
         p.n_mblocks = 1;
         p.n_splits = 1;
         p.split_len = 0;
         p.xcd_units = 0;
-        p.xcd_unit_major = 0;
         p.heads_inner = 0;
-        const int64_t slots = bhs + G;  // partial slot of (unit u, workgroup g): u + g
+        // partial slot of (KV head h, request b, share c): h (B + G / Hkv) + b + c
+        const int64_t slots = bhs + G;
         void *ws = nullptr;
         miattn_status st =
-            workspace(dev, (size_t)slots * p.rows * (D + 1) * sizeof(float), &ws);
+            workspace(dev, stream, (size_t)slots * p.rows * (D + 1) * sizeof(float), &ws);
         if (st != MIATTN_OK) return st;
         p.o_part = (float *)ws;
         p.lse_part = p.o_part + slots * p.rows * D;
         p.sk_grid = G;
-        p.sk_heads = sk_heads;
-        // A piece that starts mid-kernel waits ~10 us for its page-table entry
-        // and first tile (measured with in-kernel timestamps), about six
-        // tiles' worth of streaming: the plan weighs each piece that much, so
-        // a workgroup that starts more pieces gets fewer tiles.
-        // (MIATTN_SK_PIECE overrides, 0 .. kSkPieceMax.)
-        p.sk_piece = std::min(std::max(env_int("MIATTN_SK_PIECE", 6), 0), kSkPieceMax);
+        p.sk_piece = g_sk_piece;
         e = timed_launch(0, stream, [&] {
             return miattn::launch_attn_fwd(p, D, bf16, paged, waves, cap, G, stream);
         });
         if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
         MergeParams m = merge_params(p, paged);
         m.sk_grid = G;
-        m.sk_heads = sk_heads;
         m.sk_bn = BN;
         m.sk_win_left = p.win_left;
         m.sk_piece = p.sk_piece;
         e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
-        return MIATTN_OK;
+        return workspace_done(dev, stream);
     }
 
     // Split the key axis when the (row block, batch, KV head) units alone
@@ -401,14 +424,13 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
                     (long long)grid, INT_MAX);
     const int64_t units = bhs * n_splits;
     p.xcd_units = (units % 8 == 0) ? (int)(units / 8) : 0;
-    p.xcd_unit_major = env_int("MIATTN_XCD_ORDER", 0);
     // split decode: the KV heads of one key range run side by side
-    p.heads_inner = env_int("MIATTN_HEADS_INNER", (n_splits > 1 && p.n_mblocks == 1) ? 1 : 0);
+    p.heads_inner = (n_splits > 1 && p.n_mblocks == 1) ? 1 : 0;
 
     if (n_splits > 1) {
         const int64_t nrow = n_splits * bhs * p.rows;
         void *ws = nullptr;
-        miattn_status st = workspace(dev, (size_t)nrow * (D + 1) * sizeof(float), &ws);
+        miattn_status st = workspace(dev, stream, (size_t)nrow * (D + 1) * sizeof(float), &ws);
         if (st != MIATTN_OK) return st;
         p.o_part = (float *)ws;
         p.lse_part = p.o_part + nrow * D;
@@ -423,6 +445,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
         MergeParams m = merge_params(p, paged);
         e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+        return workspace_done(dev, stream);
     }
     return MIATTN_OK;
 }
@@ -691,9 +714,18 @@ extern "C" {
 
 miattn_status attn_fwd_dense(const void *q, const void *k, const void *v, int B, int Hq,
                              int Hkv, int Sq, int Skv, int D, float scale, int causal,
-                             int window_left, int window_right, float softcap,
                              const uint8_t *key_padding_mask, void *o, float *lse,
                              miattn_dtype dtype, void *stream) {
+    return dense_call(q, k, v, B, Hq, Hkv, Sq, Skv, D, scale, causal, -1, -1, 0.f,
+                      key_padding_mask, false, nullptr, nullptr, 0, 0, nullptr, o, lse, dtype,
+                      stream);
+}
+
+miattn_status attn_fwd_dense_ex(const void *q, const void *k, const void *v, int B, int Hq,
+                                int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                                const uint8_t *key_padding_mask, void *o, float *lse,
+                                int window_left, int window_right, float softcap,
+                                miattn_dtype dtype, void *stream) {
     return dense_call(q, k, v, B, Hq, Hkv, Sq, Skv, D, scale, causal, window_left,
                       window_right, softcap, key_padding_mask, false, nullptr, nullptr, 0, 0,
                       nullptr, o, lse, dtype, stream);
@@ -712,10 +744,20 @@ miattn_status attn_fwd_varlen(const void *q, const void *k, const void *v,
 
 miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_cache,
                              const int32_t *real_seqlen_kv, const int32_t *block_table,
-                             int page_size, int causal, int window_left, int window_right,
-                             float softcap, void *o, float *lse, int B, int Sq,
+                             int page_size, int causal, void *o, float *lse, int B, int Sq,
                              int Hq, int Hkv, int D, int max_pages, int num_phys_pages,
                              float scale, miattn_dtype dtype, void *stream) {
+    return paged_call(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, causal, -1,
+                      -1, 0.f, false, nullptr, 0, nullptr, o, lse, B, Sq, Hq, Hkv, D, max_pages,
+                      num_phys_pages, scale, dtype, stream);
+}
+
+miattn_status attn_fwd_paged_ex(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *real_seqlen_kv, const int32_t *block_table,
+                                int page_size, int causal, void *o, float *lse, int B, int Sq,
+                                int Hq, int Hkv, int D, int max_pages, int num_phys_pages,
+                                float scale, int window_left, int window_right, float softcap,
+                                miattn_dtype dtype, void *stream) {
     return paged_call(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, causal,
                       window_left, window_right, softcap, false, nullptr, 0, nullptr, o, lse, B,
                       Sq, Hq, Hkv, D, max_pages, num_phys_pages, scale, dtype, stream);
@@ -913,37 +955,49 @@ miattn_status attn_bwd(const void *q, const void *k, const void *v, const void *
     p.scale_log2 = alpha * 1.4426950408889634f;
     const size_t nrows = (size_t)B * Hq * Sq;
     void *ws = nullptr;
-    st = workspace(dev, nrows * 2 * sizeof(float), &ws);
-    if (st != MIATTN_OK) return st;
-    p.d_rows = (float *)ws;
-    p.lse2_rows = p.d_rows + nrows;
     if (Skv == 0) {
         // no key: every query gradient is zero
         e = miattn::launch_zero_fill(dq, (size_t)B * Sq * Hq * D * 2, s);
         return e == hipSuccess ? MIATTN_OK : hip_fail(e, "zero fill kernel launch");
     }
+    st = workspace(dev, s, nrows * 2 * sizeof(float), &ws);
+    if (st != MIATTN_OK) return st;
+    p.d_rows = (float *)ws;
+    p.lse2_rows = p.d_rows + nrows;
     e = timed_launch(0, s, [&] { return miattn::launch_attn_bwd(p, D, dtype == MIATTN_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
-    return MIATTN_OK;
+    return workspace_done(dev, s);
 }
 
 miattn_status miattn_release_workspace(void) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MIATTN_ERR_UNSUPPORTED, "device %d", dev);
     std::lock_guard<std::mutex> lock(g_mu);
     DeviceState &d = g_dev[dev];
-    if (d.ws) {
-        e = hipFree(d.ws);
-        d.ws = nullptr;
-        d.ws_bytes = 0;
-        if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+    if (d.ws) d.retired.push_back(d.ws);
+    d.ws = nullptr;
+    d.ws_bytes = 0;
+    miattn_status st = MIATTN_OK;
+    for (void *ptr : d.retired) {
+        e = hipFree(ptr);  // waits for work that may still use it
+        if (e != hipSuccess && st == MIATTN_OK) st = hip_fail(e, "hipFree(workspace)");
     }
-    return MIATTN_OK;
+    d.retired.clear();
+    if (d.last_use) (void)hipEventDestroy(d.last_use);
+    d.last_use = nullptr;
+    d.used = false;
+    d.last_stream = nullptr;
+    return st;
 }
 
 void miattn_set_split_keys(int keys_per_split) {
     g_split_keys = keys_per_split > 0 ? keys_per_split : 0;
+}
+
+void miattn_set_streamk_piece(int tiles) {
+    g_sk_piece = tiles < 0 ? kSkPieceDefault : std::min(tiles, kSkPieceMax);
 }
 
 void miattn_profile_start(void) {

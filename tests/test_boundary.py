@@ -34,14 +34,90 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+# ctypes kind of each C parameter type the header uses
+_KINDS = {"int": "i32", "float": "f32", "int64_t": "i64", "miattn_dtype": "i32",
+          "miattn_cache_dtype": "i32"}
+
+
+def declared_prototypes():
+    """{name: [parameter kind, ...]} for every function include/miattn.h declares;
+    a kind is 'ptr' for any pointer, else the ctypes width of the scalar."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    protos = {}
+    for m in re.finditer(r"\b(?:miattn_status|void|const char\s*\*)\s*(\w+)\s*\(([^)]*)\)\s*;",
+                         text):
+        params = [p.strip() for p in m.group(2).split(",")]
+        kinds = []
+        for prm in params:
+            if prm in ("void", ""):
+                continue
+            if "*" in prm:
+                kinds.append("ptr")
+                continue
+            typ = " ".join(prm.replace("const ", "").split()[:-1])
+            kinds.append(_KINDS[typ])
+        protos[m.group(1)] = kinds
+    return protos
+
+
+def _kind(ct):
+    if ct in (ctypes.c_int, ctypes.c_int32):
+        return "i32"
+    if ct is ctypes.c_float:
+        return "f32"
+    if ct in (ctypes.c_int64, ctypes.c_longlong):
+        return "i64"
+    if ct is ctypes.c_void_p or ct is ctypes.c_char_p or issubclass(ct, ctypes._Pointer):
+        return "ptr"
+    raise AssertionError(f"unexpected ctypes type {ct}")
+
+
+def test_binding_argtypes_match_the_header_prototypes():
+    # the binding passes exactly the arguments the header declares, in order:
+    # a caller built against the header and the binding agree on every slot
+    protos = declared_prototypes()
+    L = mi.lib()
+    for name, kinds in protos.items():
+        got = [_kind(t) for t in getattr(L, name).argtypes]
+        assert got == kinds, (name, got, kinds)
+
+
+def test_headline_entry_points_have_the_contract_signatures():
+    # attn_fwd_dense(q, k, v, B, Hq, Hkv, Sq, Skv, D, scale, causal,
+    #                key_padding_mask, o, lse, dtype, stream) and
+    # attn_fwd_paged(q, k_cache, v_cache, real_seqlen_kv, block_table,
+    #                page_size, causal, o, lse, B, Sq, Hq, Hkv, D, max_pages,
+    #                num_phys_pages, scale, dtype, stream)
+    protos = declared_prototypes()
+    assert protos["attn_fwd_dense"] == ["ptr"] * 3 + ["i32"] * 6 + ["f32", "i32"] + \
+        ["ptr"] * 3 + ["i32", "ptr"]
+    assert protos["attn_fwd_paged"] == ["ptr"] * 5 + ["i32"] * 2 + ["ptr"] * 2 + \
+        ["i32"] * 7 + ["f32", "i32", "ptr"]
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    dense_sig = re.search(r"attn_fwd_dense\(([^)]*)\)", text).group(1)
+    names = [p.split()[-1].lstrip("*") for p in dense_sig.split(",")]
+    assert names == ["q", "k", "v", "B", "Hq", "Hkv", "Sq", "Skv", "D", "scale", "causal",
+                     "key_padding_mask", "o", "lse", "dtype", "stream"], names
+    paged_sig = re.search(r"attn_fwd_paged\(([^)]*)\)", text).group(1)
+    names = [p.split()[-1].lstrip("*") for p in paged_sig.split(",")]
+    assert names == ["q", "k_cache", "v_cache", "real_seqlen_kv", "block_table", "page_size",
+                     "causal", "o", "lse", "B", "Sq", "Hq", "Hkv", "D", "max_pages",
+                     "num_phys_pages", "scale", "dtype", "stream"], names
+
+
 def dense(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, Hq=8, Hkv=2, Sq=4, Skv=4, D=128, scale=NAN, causal=1,
              wl=-1, wr=-1, softcap=0.0, mask=None, o=FAKE, lse=None, dtype=0, stream=None)
+    ex = any(x in kw for x in ("wl", "wr", "softcap"))
     a.update(kw)
     L = mi.lib()
-    st = L.attn_fwd_dense(a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Skv"],
-                          a["D"], a["scale"], a["causal"], a["wl"], a["wr"], a["softcap"],
-                          a["mask"], a["o"], a["lse"], a["dtype"], a["stream"])
+    head = (a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Skv"], a["D"],
+            a["scale"], a["causal"], a["mask"], a["o"], a["lse"])
+    if ex:
+        st = L.attn_fwd_dense_ex(*head, a["wl"], a["wr"], a["softcap"], a["dtype"], a["stream"])
+    else:
+        st = L.attn_fwd_dense(*head, a["dtype"], a["stream"])
     return st, L.miattn_last_error().decode()
 
 
@@ -49,13 +125,16 @@ def paged(**kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, bt=FAKE, page_size=64, causal=1, wl=-1,
              wr=-1, softcap=0.0, o=FAKE, lse=None, B=2, Sq=1, Hq=8, Hkv=2, D=128, max_pages=4,
              n_phys=8, scale=NAN, dtype=0, stream=None)
+    ex = any(x in kw for x in ("wl", "wr", "softcap"))
     a.update(kw)
     L = mi.lib()
-    st = L.attn_fwd_paged(a["q"], a["kc"], a["vc"], a["lens"], a["bt"], a["page_size"],
-                          a["causal"], a["wl"], a["wr"], a["softcap"], a["o"], a["lse"], a["B"],
-                          a["Sq"], a["Hq"], a["Hkv"],
-                          a["D"], a["max_pages"], a["n_phys"], a["scale"], a["dtype"],
-                          a["stream"])
+    head = (a["q"], a["kc"], a["vc"], a["lens"], a["bt"], a["page_size"], a["causal"], a["o"],
+            a["lse"], a["B"], a["Sq"], a["Hq"], a["Hkv"], a["D"], a["max_pages"], a["n_phys"],
+            a["scale"])
+    if ex:
+        st = L.attn_fwd_paged_ex(*head, a["wl"], a["wr"], a["softcap"], a["dtype"], a["stream"])
+    else:
+        st = L.attn_fwd_paged(*head, a["dtype"], a["stream"])
     return st, L.miattn_last_error().decode()
 
 
@@ -63,8 +142,8 @@ def paged(**kw):
     (dict(Hq=30, Hkv=8), 1, "Hq (30) not divisible by Hkv (8)"),
     (dict(D=96), 2, "D=96 unsupported"),
     (dict(D=0), 1, "D=0"),
-    (dict(B=-1), 1, "negative dimension"),
-    (dict(Sq=-3), 1, "negative dimension"),
+    (dict(B=-1), 1, "B=-1"),
+    (dict(Sq=-3), 1, "Sq=-3"),
     (dict(Skv=-2), 1, "Skv=-2"),
     (dict(Hkv=0), 1, "head counts"),
     (dict(dtype=7), 2, "dtype 7"),
@@ -108,7 +187,17 @@ def test_dense_empty_calls_are_ok_without_touching_the_device():
     (dict(D=512), 2, "D=512 unsupported"),
     (dict(max_pages=1 << 30, page_size=64), 2, "exceeds"),
     (dict(wl=-3), 1, "window_left=-3"),
+    (dict(wr=-4), 1, "window_right=-4"),
     (dict(softcap=-0.5), 1, "softcap"),
+    (dict(B=-2), 1, "B=-2"),
+    (dict(Sq=-1), 1, "Sq=-1"),
+    (dict(Hkv=-1), 1, "head counts"),
+    (dict(o=FAKE + 4), 1, "o not 16-byte aligned"),
+    (dict(lse=FAKE + 1), 1, "lse not 4-byte aligned"),
+    (dict(vc=FAKE + 8), 1, "v_cache not 16-byte aligned"),
+    (dict(causal=3), 1, "causal=3"),
+    (dict(dtype=5), 2, "dtype 5"),
+    (dict(scale=-math.inf), 1, "scale must be finite"),
 ])
 def test_paged_refusals(kw, status, needle):
     st, msg = paged(**kw)
@@ -271,3 +360,29 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         binding.lib()
+
+
+def test_binding_checks_caller_outputs():
+    # a caller-supplied out / lse must match what the kernels write in full
+    import torch
+    like = torch.zeros(2, 3, 4, 64, dtype=torch.bfloat16)
+    assert binding._output(None, like).shape == like.shape
+    ok = torch.empty_like(like)
+    assert binding._output(ok, like) is ok
+    for bad, needle in ((torch.empty(2, 3, 4, 32, dtype=torch.bfloat16), "out must be"),
+                        (torch.empty(2, 3, 4, 64, dtype=torch.float32), "out must be"),
+                        (torch.empty(2, 3, 64, 4, dtype=torch.bfloat16).transpose(2, 3),
+                         "contiguous"),
+                        (torch.empty(2, 3, 4, 64, dtype=torch.bfloat16, device="meta"),
+                         "device")):
+        with pytest.raises(ValueError, match=needle):
+            binding._output(bad, like)
+    dev = like.device
+    assert binding._lse_output(None, (2, 4, 3), dev, False) is None
+    assert binding._lse_output(None, (2, 4, 3), dev, True).dtype == torch.float32
+    for bad, needle in ((torch.empty(2, 4, 2), "lse must be"),
+                        (torch.empty(2, 4, 3, dtype=torch.float64), "lse must be"),
+                        (torch.empty(2, 3, 4).transpose(1, 2), "contiguous"),
+                        (torch.empty(2, 4, 3, device="meta"), "device")):
+        with pytest.raises(ValueError, match=needle):
+            binding._lse_output(bad, (2, 4, 3), dev, True)

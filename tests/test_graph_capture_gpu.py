@@ -84,3 +84,69 @@ def test_graph_prefill_and_backward():
 
     fresh = lambda i: [torch.randn_like(q.float()).to(q.dtype), torch.randn_like(do.float()).to(do.dtype)]
     check_replays(run, [q, do], fresh)
+
+
+def big_decode(seed):
+    # more requests and a longer cache than small_decode: needs a larger
+    # split-KV workspace than anything before it
+    g = torch.Generator().manual_seed(seed)
+    B, Hq, Hkv, D, ps, n_phys = 64, 32, 8, 128, 64, 1200
+    lens = torch.randint(500, 1200, (B,), generator=g).to(torch.int32)
+    bt = torch.randint(0, n_phys, (B, 19), generator=g).to(torch.int32)
+    q = torch.randn(B, 1, Hq, D, generator=g).to(torch.bfloat16)
+    kc = torch.randn(n_phys * ps, Hkv, D, generator=g).to(torch.bfloat16)
+    vc = torch.randn(n_phys * ps, Hkv, D, generator=g).to(torch.bfloat16)
+    return [t.to(DEV) for t in (q, kc, vc, lens, bt)] + [ps]
+
+
+def test_graph_replays_after_the_workspace_grew():
+    # a graph captured while the workspace was small keeps its address; an
+    # eager call that grows the workspace must not free it under the graph
+    say("graph: replay after the workspace grew")
+    mi.release_workspace()
+    q, kc, vc, lens, bt, ps = small_decode(504)
+    run = lambda: mi.attn_fwd_paged(q, kc, vc, lens, bt, ps)
+    want = [t.clone() for t in run()]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            outs = run()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    bq, bkc, bvc, blens, bbt, bps = big_decode(505)
+    for i in range(3):
+        big = mi.attn_fwd_paged(bq, bkc, bvc, blens, bbt, bps)  # grows the workspace (once)
+        torch.cuda.synchronize()
+        torch.empty(1 << 24, dtype=torch.uint8, device=DEV).fill_(0xFF)  # reuse freed memory
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, want):
+            assert torch.equal(a, b), f"replay {i} after growth differs from the eager call"
+        assert not torch.isnan(big[0]).any()
+
+
+def test_calls_on_two_streams_share_the_workspace_safely():
+    # two decode calls in flight on two streams at once: the second waits for
+    # the first's use of the workspace, so each equals its single-stream result
+    say("workspace shared by two streams")
+    a = small_decode(506)
+    b = big_decode(507)
+    ref_a = [t.clone() for t in mi.attn_fwd_paged(*a)]
+    ref_b = [t.clone() for t in mi.attn_fwd_paged(*b)]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for i in range(4):
+        with torch.cuda.stream(s1):
+            out_b = mi.attn_fwd_paged(*b)
+        with torch.cuda.stream(s2):
+            out_a = mi.attn_fwd_paged(*a)
+        torch.cuda.synchronize()
+        for x, y in zip(out_a, ref_a):
+            assert torch.equal(x, y), f"round {i}: stream 2's call differs"
+        for x, y in zip(out_b, ref_b):
+            assert torch.equal(x, y), f"round {i}: stream 1's call differs"

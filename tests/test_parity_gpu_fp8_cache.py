@@ -178,16 +178,17 @@ def test_full_size_decode_over_quantized_caches():
     compare(o, lse, o_ref, lse_ref, w.name + " fp8")
 
 
-@pytest.mark.parametrize("sq,D,page", [([1, 1, 1, 1], 64, 64), ([37, 5], 64, 16)])
-def test_fp8_pool_gives_the_bits_of_a_16bit_pool_of_its_values(monkeypatch, sq, D, page):
+@pytest.mark.parametrize("sq,D,page", [([1, 1, 1, 1], 64, 64), ([1, 1], 64, 16)])
+def test_fp8_pool_gives_the_bits_of_a_16bit_pool_of_its_values(sq, D, page):
     # with scales of 1 the FP8 path differs from the 16-bit one only in how a
-    # tile reaches LDS: under one schedule (three waves), one key tile (64 keys
-    # at D = 64 for both; at D = 128 the 16-bit decode takes 64-key tiles and
-    # the FP8 one 32-key tiles, which changes the rounding order) and one split
-    # plan the outputs must be bitwise equal, whatever the magnitudes (codes up
-    # to 448)
+    # tile reaches LDS: decode-shaped calls at D = 64 run one schedule (three
+    # waves) with one key tile (64 keys) for both pool types, so under one
+    # split plan the outputs must be bitwise equal, whatever the magnitudes
+    # (codes up to 448).  (At D = 128 the 16-bit decode takes 64-key tiles and
+    # the FP8 one 32-key tiles, which changes the rounding order; prefill-shaped
+    # 16-bit calls run the 8-wave schedule.  Those FP8 paths are compared with
+    # the oracle above.)
     say(f"fp8 vs 16-bit pool of the decoded values sq={sq} D={D} page={page}")
-    monkeypatch.setenv("MIATTN_WAVES", "3")
     Hq, Hkv = 8, 2
     lens = [900, 33, 2000, 64][:len(sq)]
     lens = [max(L, s) for L, s in zip(lens, sq)]

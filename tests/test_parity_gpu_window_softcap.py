@@ -12,8 +12,8 @@ import torch
 import oracle
 import softmax_attention_amd as mi
 from softmax_attention_amd import workloads
-from tests.parity import check_full, check_sampled
-from tests.test_parity_gpu import (DEV, _reset_split, _sample_rows, dense_case, padding_mask,
+from tests.parity import check_full
+from tests.test_parity_gpu import (DEV, _reset_split, dense_case, padding_mask,
                                    paged_case, run_dense, say)
 
 pytestmark = pytest.mark.gpu
@@ -123,12 +123,10 @@ def test_full_size_causal_gqa_prefill_window_softcap():
     say(f"{w.name} window=(1023, -1) softcap=50")
     o, lse = run_dense(w.q, w.k, w.v, scale=w.scale, causal=True, window=(1023, -1),
                        softcap=50.0)
-    rows = _sample_rows(w.B, w.Sq, w.Hq, 256, seed=12, extra=[(0, 1023, 3), (1, 1024, 5),
-                                                             (0, 4095, 31)])
-    o_ref, lse_ref = oracle.attn_dense_rows(w.q, w.k, w.v, rows, scale=w.scale, causal=True,
-                                            window=(1023, -1), softcap=50.0)
-    check_sampled(o, lse, rows, o_ref, lse_ref, w.name)
-    assert not torch.isnan(o).any() and torch.isfinite(lse).all()
+    # every output row (the window leaves ~44 % of the pairs: ~10 s of oracle)
+    o_ref, lse_ref = oracle.attn_dense(w.q, w.k, w.v, scale=w.scale, causal=True,
+                                       window=(1023, -1), softcap=50.0)
+    check_full(o, lse, o_ref, lse_ref, w.name)
 
 
 def test_full_size_paged_decode_window():
