@@ -8,7 +8,7 @@ with inputs resident in HBM.  The same line carries:
                 MFMA peak (its average duration from HIP events recorded by
                 the library around each launch, on the launch stream);
   device        compute units and the GPU clock sampled (amdsmi) while the
-                prefill ran;
+                prefill's warm-up and timed calls ran;
   paged_decode  KV bytes/s of the paged decode workload (B=64, Sq=1, Hq=32,
                 Hkv=8, D=128, page 64, lengths U[512, 8192]) against HBM peak,
                 over whole calls (attention kernel + LSE merge) issued back to
@@ -232,9 +232,9 @@ def time_prefill(mi, w, steps, warmup, clock):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     call = lambda i: mi.attn_fwd_dense(q, k, v, scale=w.scale, causal=True, out=o, lse=lse)
-    n_warm = warm(call, warmup)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with clock:
+    with clock:  # sampled over the warm-up (>= 0.5 s of calls) and the timed calls
+        n_warm = warm(call, warmup)
         mi.profile_start()
         start.record()
         for i in range(steps):

@@ -13,15 +13,20 @@ MFMA operands, accumulates the products dv = P^T dO, dk = alpha dS^T q and
 dq = alpha dS k in FP32, and rounds each gradient to the dtype.  Each summed
 term thus carries a relative error of at most u from the operand rounding,
 FP32 work adds errors far below 2^-14 of the magnitudes entering it, and the
-final rounding adds u |g|.  So, per element,
+final rounding adds u |g|.  Below the dtype's smallest normal value (2^-14
+for fp16) a rounding error is bounded in absolute terms instead, by eta = half
+the subnormal spacing (2^-25 for fp16, 2^-134 for bf16), once per rounded
+operand and once for the output.  So, per element,
 
-    |g - g_ref| <= u A_round + 2^-14 A_fp32 + u |g_ref|,
+    |g - g_ref| <= u A_round + 2^-14 A_fp32 + eta (A_count + 1) + u |g_ref|,
 
 with A_round the sum of the absolute values of the element's terms (e.g.
-sum_i P_ij |dO_id| for dv) and A_fp32 the same with |dS| replaced by
+sum_i P_ij |dO_id| for dv), A_fp32 the same with |dS| replaced by
 P (|dO|.|v| + |D|), which bounds the FP32 error of dS even where dP - D
-cancels.  These magnitudes are computed here in fp64 from the same inputs
-(they set the bound only; the expected values are the oracle's)."""
+cancels, and A_count the same with each rounded operand (P or dS) replaced
+by 1 on the visible pairs.  These magnitudes are computed here in fp64 from
+the same inputs (they set the bound only; the expected values are the
+oracle's)."""
 import numpy as np
 import pytest
 import torch
@@ -40,9 +45,13 @@ def unit_roundoff(dtype):
     return 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -11
 
 
+def subnormal_half_step(dtype):
+    return 2.0 ** -134 if dtype == torch.bfloat16 else 2.0 ** -25
+
+
 def term_magnitudes(q, k, v, o, do, lse, scale, causal):
-    """(dq, dk, dv) term magnitudes: A_round and A_fp32 of each gradient
-    element, fp64, in the BSHD layouts of the gradients."""
+    """(dq, dk, dv) term magnitudes: A_round, A_fp32 and A_count of each
+    gradient element, fp64, in the BSHD layouts of the gradients."""
     B, Sq, Hq, D = q.shape
     Skv, Hkv = k.shape[1], k.shape[2]
     G = Hq // Hkv
@@ -57,7 +66,9 @@ def term_magnitudes(q, k, v, o, do, lse, scale, causal):
     j = torch.arange(Skv)[None, :]
     vis = (j <= i + Skv - Sq) if causal else torch.ones(Sq, Skv, dtype=torch.bool)
     arg = s - lsef[..., None]
-    P = torch.where(vis & torch.isfinite(lsef)[..., None], torch.exp(arg), torch.zeros_like(s))
+    live = vis & torch.isfinite(lsef)[..., None]
+    P = torch.where(live, torch.exp(arg), torch.zeros_like(s))
+    ones = live.to(torch.float64)
     dP = torch.matmul(dof, vf.transpose(-1, -2).contiguous())
     Drow = (dof * of).sum(-1)
     dS = P * (dP - Drow[..., None])
@@ -73,17 +84,21 @@ def term_magnitudes(q, k, v, o, do, lse, scale, causal):
     dk_r = per_kv(a * torch.matmul(dS.abs().transpose(-1, -2).contiguous(), qf.abs()))
     dk_f = per_kv(a * torch.matmul(dS_f32.transpose(-1, -2).contiguous(), qf.abs()))
     dv_r = per_kv(torch.matmul(P.transpose(-1, -2).contiguous(), dof.abs()))
+    dq_c = a * torch.matmul(ones, kf.abs())
+    dk_c = per_kv(a * torch.matmul(ones.transpose(-1, -2).contiguous(), qf.abs()))
+    dv_c = per_kv(torch.matmul(ones.transpose(-1, -2).contiguous(), dof.abs()))
     bshd = lambda x: x.permute(0, 2, 1, 3).contiguous().numpy()
-    return ((bshd(dq_r), bshd(dq_f)), (dk_r.numpy(), dk_f.numpy()), (dv_r.numpy(), dv_r.numpy()))
+    return ((bshd(dq_r), bshd(dq_f), bshd(dq_c)), (dk_r.numpy(), dk_f.numpy(), dk_c.numpy()),
+            (dv_r.numpy(), dv_r.numpy(), dv_c.numpy()))
 
 
-def check_grad(g, ref, mags, u, what):
+def check_grad(g, ref, mags, u, eta, what):
     g = g.detach().cpu().to(torch.float64).numpy()
     assert g.shape == ref.shape, (what, g.shape, ref.shape)
     assert not np.isnan(g).any(), f"{what}: NaN"
-    a_round, a_f32 = mags
+    a_round, a_f32, a_count = mags
     err = np.abs(g - ref)
-    bound = u * a_round + FP32_SLACK * a_f32 + u * np.abs(ref)
+    bound = u * a_round + FP32_SLACK * a_f32 + eta * (a_count + 1.0) + u * np.abs(ref)
     bad = err > bound
     if bad.any():
         idx = np.argwhere(bad)[:5].tolist()
@@ -108,9 +123,10 @@ def bwd_case(B, Sq, Skv, Hq, Hkv, D, *, dtype=torch.bfloat16, causal=True, scale
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attn_bwd(q, k, v, o, do, lse, scale=scale, causal=causal)
     mq, mk, mv = term_magnitudes(q, k, v, o, do, lse, scale, causal)
-    u = unit_roundoff(dtype)
-    used = [check_grad(dq, rq, mq, u, what + " dq"), check_grad(dk, rk, mk, u, what + " dk"),
-            check_grad(dv, rv, mv, u, what + " dv")]
+    u, eta = unit_roundoff(dtype), subnormal_half_step(dtype)
+    used = [check_grad(dq, rq, mq, u, eta, what + " dq"),
+            check_grad(dk, rk, mk, u, eta, what + " dk"),
+            check_grad(dv, rv, mv, u, eta, what + " dv")]
     say(f"bwd {what}: worst element used {max(used):.2f} of its bound")
     return used
 
