@@ -190,6 +190,32 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
                              float scale, miattn_dtype dtype, void *stream);
 
 /*
+ * attn_fwd_paged for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results as attn_fwd_paged, but the
+ * split-KV partials go to a fixed scratch array of 32 MiB that the library
+ * holds on every GPU it runs on until the process ends (its address is looked
+ * up once per device); the call allocates nothing, never uses the library
+ * workspace, and ignores MIATTN_VALIDATE.
+ *
+ *   - A call whose partials would exceed 32 MiB returns
+ *     MIATTN_ERR_UNSUPPORTED and enqueues nothing.  (Decode with Sq = 1 and
+ *     Hq / Hkv = 4 at D = 128 needs about 8.3 KB per (request, KV head) plus
+ *     about 2 MB; calls whose key ranges are not split need none.)
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents; no part of it needs to start at zero (each call writes
+ *     every partial it merges).  Calls that overlap in time on one GPU --
+ *     issued on different streams without ordering, or graph replays beside
+ *     eager calls -- race on it and give undefined results.
+ */
+miattn_status attn_fwd_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                     const int32_t *real_seqlen_kv, const int32_t *block_table,
+                                     int page_size, int causal, void *o, float *lse, int B,
+                                     int Sq, int Hq, int Hkv, int D, int max_pages,
+                                     int num_phys_pages, float scale, miattn_dtype dtype,
+                                     void *stream);
+
+/*
  * attn_fwd_paged with a sliding window and a logit softcap (TileOPs
  * "Attention Operators", GQAPagedFwdOp takes the window and softcap of
  * GQADenseFwdOp stages 5 and 6).  window_left, window_right and softcap as

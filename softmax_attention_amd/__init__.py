@@ -7,8 +7,9 @@ seeded synthetic workload generators.
 from .binding import (MiattnError, attn_bwd, attn_fwd_dense, attn_fwd_paged, attn_fwd_paged_append,
                       attn_fwd_paged_varlen, attn_fwd_varlen, kv_cache_write, lib,
                       profile_start, profile_stop, release_workspace, set_split_keys,
-                      set_streamk_piece)
+                      set_streamk_piece, attn_fwd_paged_noalloc)
 
 __all__ = ["MiattnError", "attn_bwd", "attn_fwd_dense", "attn_fwd_paged", "attn_fwd_paged_append",
            "attn_fwd_paged_varlen", "attn_fwd_varlen", "kv_cache_write", "lib", "profile_start",
-           "profile_stop", "release_workspace", "set_split_keys", "set_streamk_piece"]
+           "profile_stop", "release_workspace", "set_split_keys", "set_streamk_piece",
+           "attn_fwd_paged_noalloc"]

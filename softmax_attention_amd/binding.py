@@ -22,6 +22,7 @@ MIATTN_CACHE_BF16, MIATTN_CACHE_FP16, MIATTN_CACHE_FP8_E4M3 = 0, 1, 2
 
 # every symbol include/miattn.h declares
 EXPORTS = ("attn_fwd_dense", "attn_fwd_dense_ex", "attn_fwd_paged", "attn_fwd_paged_ex",
+           "attn_fwd_paged_noalloc",
            "attn_fwd_varlen", "attn_fwd_paged_varlen", "kv_cache_write", "attn_fwd_paged_append",
            "attn_bwd", "miattn_last_error", "miattn_release_workspace", "miattn_set_split_keys",
            "miattn_set_streamk_piece", "miattn_profile_start", "miattn_profile_stop")
@@ -55,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_paged_ex.argtypes = [P, P, P, P, P, i32, i32, P, P, i32, i32, i32, i32, i32,
                                         i32, i32, f32, i32, i32, f32, i32, P]
         L.attn_fwd_paged_ex.restype = i32
+        L.attn_fwd_paged_noalloc.argtypes = L.attn_fwd_paged.argtypes
+        L.attn_fwd_paged_noalloc.restype = i32
         L.attn_fwd_varlen.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                       i32, i32, i32, f32, P, P, P, i32, P]
         L.attn_fwd_varlen.restype = i32
@@ -204,19 +207,8 @@ def attn_fwd_dense(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale=N
     return o, lse
 
 
-def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                   real_seqlen_kv: torch.Tensor, block_table: torch.Tensor, page_size: int, *,
-                   causal: bool = True, scale=None, window=None, softcap=None,
-                   out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None, return_lse: bool = True
-                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Paged attention forward on the current stream.
-
-    q [B,Sq,Hq,D]; k_cache/v_cache [pages*page_size, Hkv, D] or
-    [pages, page_size, Hkv, D]; real_seqlen_kv int32 [B] (cache length, the Sq
-    query tokens included); block_table int32 [B, max_pages]; window and
-    softcap as for attn_fwd_dense, the window placed at each request's own
-    query positions."""
+def _paged_geometry(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size):
+    """Checks of a uniform paged call; returns (n_pages, Hkv, D, B, Sq, Hq)."""
     if q.dim() != 4:
         raise ValueError("q must be rank 4 (BSHD)")
     if k_cache.shape != v_cache.shape:
@@ -235,7 +227,7 @@ def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         raise ValueError("q and the caches must share one dtype")
     if real_seqlen_kv.dtype != torch.int32 or block_table.dtype != torch.int32:
         raise ValueError("real_seqlen_kv and block_table must be int32")
-    code = _dtype_code(q)
+    _dtype_code(q)
     if not all(t.is_cuda and t.device == q.device
                for t in (q, k_cache, v_cache, real_seqlen_kv, block_table)):
         raise ValueError("q, the caches, real_seqlen_kv and block_table must be on one GPU device")
@@ -245,6 +237,25 @@ def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         raise ValueError("head dim of the caches differs from q")
     if block_table.dim() != 2 or block_table.shape[0] != B or real_seqlen_kv.shape != (B,):
         raise ValueError("block_table must be [B, max_pages] and real_seqlen_kv [B]")
+    return n_pages, Hkv, D, B, Sq, Hq
+
+
+def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   real_seqlen_kv: torch.Tensor, block_table: torch.Tensor, page_size: int, *,
+                   causal: bool = True, scale=None, window=None, softcap=None,
+                   out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, return_lse: bool = True
+                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Paged attention forward on the current stream.
+
+    q [B,Sq,Hq,D]; k_cache/v_cache [pages*page_size, Hkv, D] or
+    [pages, page_size, Hkv, D]; real_seqlen_kv int32 [B] (cache length, the Sq
+    query tokens included); block_table int32 [B, max_pages]; window and
+    softcap as for attn_fwd_dense, the window placed at each request's own
+    query positions."""
+    n_pages, Hkv, D, B, Sq, Hq = _paged_geometry(q, k_cache, v_cache, real_seqlen_kv,
+                                                 block_table, page_size)
+    code = _dtype_code(q)
     q = q.contiguous()
     k_cache, v_cache = k_cache.contiguous(), v_cache.contiguous()
     real_seqlen_kv, block_table = real_seqlen_kv.contiguous(), block_table.contiguous()
@@ -259,6 +270,32 @@ def attn_fwd_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         st = lib().attn_fwd_paged_ex(*args, *_window(window), _softcap(softcap), code, _stream())
     _check(st)
     return o, lse
+
+
+def attn_fwd_paged_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           real_seqlen_kv: torch.Tensor, block_table: torch.Tensor,
+                           page_size: int, *, out: torch.Tensor, lse: Optional[torch.Tensor],
+                           causal: bool = True, scale=None) -> None:
+    """attn_fwd_paged through the library's allocation-free entry point: the
+    caller passes out (and lse, or None) already allocated; the split-KV
+    partials go to the library's fixed per-GPU scratch (calls that overlap on
+    one GPU race on it)."""
+    if out is None:
+        raise ValueError("out must be given: this entry point allocates nothing")
+    n_pages, Hkv, D, B, Sq, Hq = _paged_geometry(q, k_cache, v_cache, real_seqlen_kv,
+                                                 block_table, page_size)
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("real_seqlen_kv", real_seqlen_kv), ("block_table", block_table)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous: this entry point allocates nothing")
+    o = _output(out, q)
+    if lse is not None:
+        lse = _lse_output(lse, (B, Hq, Sq), q.device, True)
+    _check(lib().attn_fwd_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(real_seqlen_kv), _ptr(block_table), int(page_size),
+                                        int(bool(causal)), _ptr(o), _ptr(lse), B, Sq, Hq, Hkv, D,
+                                        block_table.shape[1], n_pages, _scale(scale),
+                                        _dtype_code(q), _stream()))
 
 
 def _offsets(cu: torch.Tensor, device, name: str) -> torch.Tensor:

@@ -171,6 +171,55 @@ miattn_status workspace_done(int dev, hipStream_t stream) {
     return MIATTN_OK;
 }
 
+// ---------------------------------------------------------------- fixed scratch
+
+// Scratch of the allocation-free entry point (attn_fwd_paged_noalloc): the
+// split-KV partials live in this file-scope device array instead of the
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in): the device address of each GPU's copy comes
+// from hipGetSymbolAddress, looked up once per device with that device
+// current, and only that address reaches the kernels.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void *g_scratch_addr[kMaxDevices] = {};
+
+miattn_status scratch_address(int dev, void **out) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (!g_scratch_addr[dev]) {
+        void *ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(MIATTN_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_addr[dev] = ptr;
+    }
+    *out = g_scratch_addr[dev];
+    return MIATTN_OK;
+}
+
+// Where a call's split-KV partials go: the library workspace (grown on
+// demand), or the fixed scratch of this device (no allocation; a call that
+// would need more is refused).
+struct PartialsSource {
+    bool fixed = false;
+};
+
+miattn_status partials(const PartialsSource &src, int dev, hipStream_t stream, size_t bytes,
+                       void **out) {
+    if (!src.fixed) return workspace(dev, stream, bytes, out);
+    if (bytes > kScratchBytes)
+        return fail(MIATTN_ERR_UNSUPPORTED,
+                    "the call needs %zu bytes of split-KV scratch; the allocation-free entry "
+                    "point holds at most %zu",
+                    bytes, kScratchBytes);
+    return scratch_address(dev, out);
+}
+
+miattn_status partials_done(const PartialsSource &src, int dev, hipStream_t stream) {
+    return src.fixed ? MIATTN_OK : workspace_done(dev, stream);
+}
+
 // ---------------------------------------------------------------- timing
 
 struct Timing {
@@ -323,7 +372,7 @@ MergeParams merge_params(const FwdParams &p, bool paged) {
 }
 
 miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, bool cap,
-                  hipStream_t stream) {
+                  hipStream_t stream, const PartialsSource &src = PartialsSource()) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -365,7 +414,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
         const int64_t slots = bhs + G;
         void *ws = nullptr;
         miattn_status st =
-            workspace(dev, stream, (size_t)slots * p.rows * (D + 1) * sizeof(float), &ws);
+            partials(src, dev, stream, (size_t)slots * p.rows * (D + 1) * sizeof(float), &ws);
         if (st != MIATTN_OK) return st;
         p.o_part = (float *)ws;
         p.lse_part = p.o_part + slots * p.rows * D;
@@ -382,7 +431,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
         m.sk_piece = p.sk_piece;
         e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
-        return workspace_done(dev, stream);
+        return partials_done(src, dev, stream);
     }
 
     // Split the key axis when the (row block, batch, KV head) units alone
@@ -430,7 +479,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     if (n_splits > 1) {
         const int64_t nrow = n_splits * bhs * p.rows;
         void *ws = nullptr;
-        miattn_status st = workspace(dev, stream, (size_t)nrow * (D + 1) * sizeof(float), &ws);
+        miattn_status st = partials(src, dev, stream, (size_t)nrow * (D + 1) * sizeof(float), &ws);
         if (st != MIATTN_OK) return st;
         p.o_part = (float *)ws;
         p.lse_part = p.o_part + nrow * D;
@@ -445,7 +494,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
         MergeParams m = merge_params(p, paged);
         e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
-        return workspace_done(dev, stream);
+        return partials_done(src, dev, stream);
     }
     return MIATTN_OK;
 }
@@ -563,7 +612,8 @@ miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache
                          miattn_dtype dtype, void *stream,
                          const miattn::KvWriteParams *append = nullptr,
                          int cache_dtype = -1,  // -1: 16-bit pools of the inputs' dtype
-                         const float *k_scale = nullptr, const float *v_scale = nullptr) {
+                         const float *k_scale = nullptr, const float *v_scale = nullptr,
+                         const PartialsSource &src = PartialsSource()) {
     g_err[0] = '\0';
     // (a packed call without query rows has nothing to check q and o against)
     miattn_status st = check_common(q, o, lse, B, (packed && total_q == 0) ? 0 : Sq, Hq, Hkv,
@@ -616,7 +666,9 @@ miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache
     int page_shift = 0;
     while ((1 << page_shift) < page_size) ++page_shift;
 
-    if (env_int("MIATTN_VALIDATE", 0) == 1) {
+    // (the allocation-free entry point skips it: the check copies to host
+    // vectors and synchronises the stream)
+    if (!src.fixed && env_int("MIATTN_VALIDATE", 0) == 1) {
         // opt-in check of the device metadata (synchronises the stream)
         std::vector<int32_t> lens(B), bt((size_t)B * max_pages);
         hipStream_t s = (hipStream_t)stream;
@@ -705,7 +757,8 @@ miattn_status paged_call(const void *q, const void *k_cache, const void *v_cache
         if (e != hipSuccess) return hip_fail(e, "KV write kernel launch");
         p.kv_append = 1;
     }
-    return run(p, D, dtype == MIATTN_BF16, true, capacity, softcap > 0.f, (hipStream_t)stream);
+    return run(p, D, dtype == MIATTN_BF16, true, capacity, softcap > 0.f, (hipStream_t)stream,
+               src);
 }
 
 }  // namespace
@@ -750,6 +803,19 @@ miattn_status attn_fwd_paged(const void *q, const void *k_cache, const void *v_c
     return paged_call(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, causal, -1,
                       -1, 0.f, false, nullptr, 0, nullptr, o, lse, B, Sq, Hq, Hkv, D, max_pages,
                       num_phys_pages, scale, dtype, stream);
+}
+
+miattn_status attn_fwd_paged_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                     const int32_t *real_seqlen_kv, const int32_t *block_table,
+                                     int page_size, int causal, void *o, float *lse, int B,
+                                     int Sq, int Hq, int Hkv, int D, int max_pages,
+                                     int num_phys_pages, float scale, miattn_dtype dtype,
+                                     void *stream) {
+    PartialsSource fixed;
+    fixed.fixed = true;
+    return paged_call(q, k_cache, v_cache, real_seqlen_kv, block_table, page_size, causal, -1,
+                      -1, 0.f, false, nullptr, 0, nullptr, o, lse, B, Sq, Hq, Hkv, D, max_pages,
+                      num_phys_pages, scale, dtype, stream, nullptr, -1, nullptr, nullptr, fixed);
 }
 
 miattn_status attn_fwd_paged_ex(const void *q, const void *k_cache, const void *v_cache,
