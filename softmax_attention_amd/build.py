@@ -31,6 +31,9 @@ FLAGS = [
     "-fPIC",
     "-Wall",
     "-Wno-unused-function",
+    # a variable read before it is written is a bug here (work mappings, plans)
+    "-Werror=uninitialized",
+    "-Werror=sometimes-uninitialized",
     # keep the compiler from forming packed-FP32 instructions (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",

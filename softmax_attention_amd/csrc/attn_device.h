@@ -83,10 +83,17 @@ __device__ __forceinline__ u32x2 fp8x4_to_half4(uint32_t w) {
 // read gathers differ in the mask's upper bits, so the two chunk pairs that
 // neighbouring 16-lane groups fetch never share a bank.  Measured on gfx950:
 // ~190 B/clk/CU for the K reads and ~124 B/clk/CU for the transposing reads.
+// For D = 64 a row is half the banks (row parity picks the half) and has 8
+// chunk positions: bits 1, 2, 3 of the row go to bits 2, 1, 0 of the mask, so
+// the 8 rows of one parity among 16 consecutive rows take 8 distinct
+// positions (K reads), and rows 4m and 4m + 2 -- which a transposing read
+// gathers together with their 4 chunks -- take disjoint halves of the
+// positions (SQ_LDS_BANK_CONFLICT 0; the earlier mapping had every
+// transposing read conflict two ways).
 template <int D>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (D == 64)
-        return ((row >> 1) & 3) * 2 + ((row >> 3) & 1);
+        return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
     else
         return ((row & 3) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
 }

@@ -248,9 +248,76 @@ void attn_fwd_kernel(const FwdParams p) {
             hi = __ballot(keep1);
         }
     };
-    // first tile start >= j that holds a kept key (or wg_end)
+    // Tile summary of the mask, taken once: bit n of mask_any (mask_all) is set
+    // when tile tile_begin + n BN holds a kept key (only kept keys), for the
+    // first 64 tiles of this workgroup's range -- lane n reads tile n's bytes.
+    // Inside that window the steps then need no mask load for tiles that are
+    // fully kept or fully masked; past it (or for a partly kept tile) they
+    // read the tile's bytes.
+    uint64_t mask_any = 0, mask_all = 0;
+    if (has_mask) {
+        // one pass covers 1 KB of keys (16 per lane) = 1024 / BN tiles of
+        // BN / 16 lanes each; bytes past the keys or past wg_end count as
+        // masked.  Rows that are not 16-byte aligned are read bytewise.
+        constexpr int TPP = 1024 / BN;
+        constexpr int LPT = BN / 16;
+        constexpr uint64_t kLaneGroup = LPT >= 64 ? ~0ull : ((1ull << LPT) - 1);
+        const bool vec = (((uintptr_t)mrow) & 15) == 0;
+        const int lim = min(kv_len, wg_end);
+#pragma unroll 1
+        for (int pass = 0; pass < 64 / TPP; ++pass) {
+            const int j = tile_begin + pass * 1024 + 16 * lane;
+            bool any = false, all = false;
+            if (j < lim) {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+                if (vec && j + 16 <= lim) {
+                    const u32x4 x = *(const u32x4 *)(mrow + j);
+                    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+                } else {
+                    for (int i = 0; i < 16; ++i)
+                        if (j + i < lim && mrow[j + i] != 0) w[i >> 2] |= 0xffu << (8 * (i & 3));
+                }
+                // a byte is kept when nonzero: fold each byte to its top bit
+                uint32_t nz_any = 0u, nz_all = 0x80808080u;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t t = ((w[q] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[q];
+                    nz_any |= t & 0x80808080u;
+                    nz_all &= t;
+                }
+                any = nz_any != 0u;
+                all = (nz_all & 0x80808080u) == 0x80808080u && j + 16 <= lim;
+            }
+            const uint64_t ba = __ballot(any), bb = __ballot(all);
+#pragma unroll
+            for (int t = 0; t < TPP; ++t) {
+                const uint64_t ga = (ba >> (t * LPT)) & kLaneGroup;
+                const uint64_t gb = (bb >> (t * LPT)) & kLaneGroup;
+                mask_any |= (uint64_t)(ga != 0) << (pass * TPP + t);
+                mask_all |= (uint64_t)(gb == kLaneGroup) << (pass * TPP + t);
+            }
+        }
+    }
+    const int mask_window_end = tile_begin + 64 * BN;  // first tile the summary does not cover
+    // first tile start >= j that holds a kept key (or wg_end), with its mask bits
     auto find_tile = [&](int j, uint64_t &lo, uint64_t &hi) __attribute__((always_inline)) -> int {
         if (!has_mask) return j;
+        if (j < mask_window_end) {
+            const uint64_t rest = mask_any >> ((j - tile_begin) / BN);
+            if (rest == 0) {
+                j = mask_window_end;
+            } else {
+                j += __builtin_ctzll(rest) * BN;
+                if (j >= wg_end) return wg_end;
+                if ((mask_all >> ((j - tile_begin) / BN)) & 1) {
+                    lo = kLoMask;
+                    hi = ~0ull;
+                } else {
+                    tile_bits(j, lo, hi);
+                }
+                return j;
+            }
+        }
         for (; j < wg_end; j += BN) {
             tile_bits(j, lo, hi);
             if (lo | hi) return j;
@@ -1005,7 +1072,15 @@ void attn_fwd_kernel(const FwdParams p) {
     // count allows, consecutive workgroups of one XCD share a (batch, KV head)
     // so its K/V stays in that XCD's L2.  Causal row blocks run heaviest first.
     int rank, unit;
-    if (p.xcd_units > 0) {
+    if (p.xcd_units > 0 && !p.causal) {
+        // every row block weighs the same: each XCD runs its units one after
+        // another (units u = xcd, xcd + 8, ... interleaved over the XCDs, so
+        // that units of different lengths spread over all of them)
+        const int s = blockIdx.x >> 3;
+        unit = (blockIdx.x & 7) + 8 * (s / p.n_mblocks);
+        rank = s % p.n_mblocks;
+    } else if (p.xcd_units > 0) {
+        // causal: heaviest row blocks first, the units of each XCD interleaved
         const int s = blockIdx.x >> 3;
         unit = (blockIdx.x & 7) * p.xcd_units + s % p.xcd_units;
         rank = s / p.xcd_units;
