@@ -846,7 +846,12 @@ void attn_fwd_kernel(const FwdParams p) {
         };
         // FP8 stage -> 16-bit stage: lane l's 16 bytes of piece e are chunks
         // 2 l_col8 and 2 l_col8 + 1 (d 0..7 and 8..15 of the piece) of key row
-        // e RPP8 + l_row8
+        // e RPP8 + l_row8.  The two rows that share a bank half within one
+        // 16-lane write pass (rows 2k, 2k + 1 at D = 128; rows 4k + i, 4k + i
+        // + 2 at D = 64) write their halves in opposite order, so a pass
+        // stores 16 distinct chunk positions (otherwise every pass conflicts
+        // two ways: SQ_LDS_BANK_CONFLICT was 36 % of the LDS-active cycles).
+        const int half_flip = (l_row8 >> (D == 64 ? 1 : 0)) & 1;
         auto convert8 = [&](int stage, uint8_t *dk, uint8_t *dv) __attribute__((always_inline)) {
             if (!conv) return;
             const uint8_t *fk = fK[stage], *fv = fV[stage];
@@ -855,11 +860,12 @@ void attn_fwd_kernel(const FwdParams p) {
                 const u32x4 kw = *(const u32x4 *)(fk + e * 1024 + 16 * lane);
                 const u32x4 vw = *(const u32x4 *)(fv + e * 1024 + 16 * lane);
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const u32x2 k01 = fp8x4_to_half4<BF16>(kw[2 * h]);
-                    const u32x2 k23 = fp8x4_to_half4<BF16>(kw[2 * h + 1]);
-                    const u32x2 v01 = fp8x4_to_half4<BF16>(vw[2 * h]);
-                    const u32x2 v23 = fp8x4_to_half4<BF16>(vw[2 * h + 1]);
+                for (int h0 = 0; h0 < 2; ++h0) {
+                    const int h = h0 ^ half_flip;
+                    const u32x2 k01 = fp8x4_to_half4<BF16>(h ? kw[2] : kw[0]);
+                    const u32x2 k23 = fp8x4_to_half4<BF16>(h ? kw[3] : kw[1]);
+                    const u32x2 v01 = fp8x4_to_half4<BF16>(h ? vw[2] : vw[0]);
+                    const u32x2 v23 = fp8x4_to_half4<BF16>(h ? vw[3] : vw[1]);
                     const int at = tile_off<D>(e * RPP8 + l_row8, 2 * l_col8 + h);
                     *(u32x4 *)(dk + at) = u32x4{k01[0], k01[1], k23[0], k23[1]};
                     *(u32x4 *)(dv + at) = u32x4{v01[0], v01[1], v23[0], v23[1]};

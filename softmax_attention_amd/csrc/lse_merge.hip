@@ -12,7 +12,7 @@
 // A head's sink logit, when given, joins the merged denominator once
 // (GQAVarlenFwdOp / GQAPagedFwdOp: denominator only, used as given).
 //
-// One wave per packed row; lane l owns D/64 consecutive output elements.
+// One wave per packed row, reading partial rows with 16-byte loads.
 #include "attn_kernels.h"
 
 #include "attn_device.h"
@@ -32,7 +32,6 @@ __device__ __forceinline__ uint16_t to_half_bits(float x) {
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
-    constexpr int PER = D / 64;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t gr = (int64_t)blockIdx.x * 4 + wave;
@@ -113,40 +112,52 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = max_nan(M, __shfl_xor(M, off));
 
-    // o = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M), splits in
-    // ascending order; each split's LSE comes from its lane, and the partial
-    // rows are read four splits at a time (the loads first), so a row costs
-    // about one round trip per four splits rather than one per split
-    float accv[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) accv[e] = 0.f;
+    // o = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M), in FP32.  A partial
+    // row is D floats: D / 4 lanes hold it with 16-byte loads, so the wave
+    // reads SPI = 256 / D splits per load instruction -- lane group g = lane /
+    // (D / 4) takes splits g, g + SPI, ... in ascending order -- and up to
+    // four such loads per lane are issued before any is used.  The groups'
+    // sums are added at the end (a fixed order: the result does not depend
+    // on timing).
+    constexpr int LPR = D / 4;       // lanes per partial row
+    constexpr int SPI = 64 / LPR;    // splits per load instruction
+    const int grp = lane / LPR, pos = lane % LPR;
+    f32x4 accv = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
     if (M != -INFINITY) {
         for (int c = 0; c < n_valid; c += 64) {
             const float ls = c == 0 ? ls0 : split_lse(c + lane);
             const int cnt = min(64, n_valid - c);
-            for (int q0 = 0; q0 < cnt; q0 += 4) {
+            for (int q0 = 0; q0 < cnt; q0 += 4 * SPI) {
                 float lq[4];
-                float ov[4][PER];
+                f32x4 ov[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
+                    const int s = q0 + k * SPI + grp;  // this group's split (within chunk c)
                     // lanes past the last split hold -inf
-                    lq[k] = __shfl(ls, q0 + k);
-                    const float *src =
-                        p.o_part + (base + (int64_t)(c + q0 + k) * stride) * D + lane * PER;
-#pragma unroll
-                    for (int e = 0; e < PER; ++e) ov[k][e] = lq[k] != -INFINITY ? src[e] : 0.f;
+                    lq[k] = __shfl(ls, min(s, 63));
+                    ov[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (s < cnt && lq[k] != -INFINITY)
+                        ov[k] = *(const f32x4 *)(p.o_part +
+                                                 (base + (int64_t)(c + s) * stride) * D + 4 * pos);
                 }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    if (lq[k] == -INFINITY) continue;
+                    const int s = q0 + k * SPI + grp;
+                    if (s >= cnt || lq[k] == -INFINITY) continue;
                     const float w = __expf(lq[k] - M);
                     den += w;
-#pragma unroll
-                    for (int e = 0; e < PER; ++e) accv[e] += w * ov[k][e];
+                    accv += w * ov[k];
                 }
             }
         }
+    }
+    // add the lane groups' partial sums (groups differ in lane bits >= log2 LPR)
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+        den += __shfl_xor(den, off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accv[e] += __shfl_xor(accv[e], off);
     }
     const int h = kvh * p.G + gh;
     float inv = den != 0.f ? 1.f / den : 0.f;
@@ -164,9 +175,14 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
             lse_out = mx + __logf(den2);
         }
     }
-    uint16_t *dst = p.o + ((q_row0 + i) * p.Hq + h) * D + lane * PER;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) dst[e] = to_half_bits<BF16>(accv[e] * inv);
+    if (grp == 0) {
+        uint16_t *dst = p.o + ((q_row0 + i) * p.Hq + h) * D + 4 * pos;
+        const u32x2 packed = {(uint32_t)to_half_bits<BF16>(accv[0] * inv) |
+                                  ((uint32_t)to_half_bits<BF16>(accv[1] * inv) << 16),
+                              (uint32_t)to_half_bits<BF16>(accv[2] * inv) |
+                                  ((uint32_t)to_half_bits<BF16>(accv[3] * inv) << 16)};
+        *(u32x2 *)dst = packed;
+    }
     if (p.lse != nullptr && lane == 0) {
         if (p.cu_q)  // packed: [Hq, total_q]
             p.lse[(int64_t)h * p.total_q + q_row0 + i] = lse_out;
