@@ -846,12 +846,15 @@ void attn_fwd_kernel(const FwdParams p) {
         };
         // FP8 stage -> 16-bit stage: lane l's 16 bytes of piece e are chunks
         // 2 l_col8 and 2 l_col8 + 1 (d 0..7 and 8..15 of the piece) of key row
-        // e RPP8 + l_row8.  The two rows that share a bank half within one
-        // 16-lane write pass (rows 2k, 2k + 1 at D = 128; rows 4k + i, 4k + i
-        // + 2 at D = 64) write their halves in opposite order, so a pass
-        // stores 16 distinct chunk positions (otherwise every pass conflicts
-        // two ways: SQ_LDS_BANK_CONFLICT was 36 % of the LDS-active cycles).
-        const int half_flip = (l_row8 >> (D == 64 ? 1 : 0)) & 1;
+        // e RPP8 + l_row8.  A 16-byte LDS write is served in groups of lanes
+        // 8k..8k+7 with 8k+32..8k+39 (the grouping under which the counters
+        // read zero conflicts for the row-per-16-lanes stores of the backward
+        // and nonzero here).  At D >= 128 the two lane halves write rows whose
+        // swizzles differ in a bit above bit 0, so their chunks would take the
+        // same 8 positions: the upper lanes write their halves in the opposite
+        // order.  At D = 64 the swizzle already gives rows 8 apart opposite
+        // chunk parity.
+        const int half_flip = D == 64 ? 0 : (lane >> 5) & 1;
         auto convert8 = [&](int stage, uint8_t *dk, uint8_t *dv) __attribute__((always_inline)) {
             if (!conv) return;
             const uint8_t *fk = fK[stage], *fv = fV[stage];

@@ -159,6 +159,7 @@ struct BwdParams {
     int causal;
     float scale;       // alpha
     float scale_log2;  // alpha log2(e)
+    int down_wgs;      // bwd_dkdv workgroups 0 .. down_wgs - 1 walk their row tiles downwards
 };
 hipError_t launch_attn_bwd(const BwdParams &p, int D, bool bf16, hipStream_t stream);
 // Zero `bytes` (a multiple of 16) at a 16-byte aligned device address with a

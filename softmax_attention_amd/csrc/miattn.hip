@@ -1019,6 +1019,8 @@ miattn_status attn_bwd(const void *q, const void *k, const void *v, const void *
     const float alpha = resolve_scale(scale, D);
     p.scale = alpha;
     p.scale_log2 = alpha * 1.4426950408889634f;
+    // bwd_dkdv runs one workgroup per CU: the first wave is one per CU
+    p.down_wgs = compute_units(dev);
     const size_t nrows = (size_t)B * Hq * Sq;
     void *ws = nullptr;
     if (Skv == 0) {

@@ -171,6 +171,14 @@ def test_is_deterministic():
     assert all(torch.equal(x, y) for x, y in zip(a, b))
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_more_key_blocks_than_cus(causal):
+    # 64 KV heads x 5 key blocks = 320 dk/dv workgroups: the first wave (one
+    # per CU) walks its row tiles down, the rest walk up; G = 3 makes a tile
+    # step cross head boundaries in both directions
+    bwd_case(1, 40, 600, 192, 64, 64, causal=causal, seed=409, what=f"waves causal={causal}")
+
+
 def test_larger_causal_gqa():
     bwd_case(1, 1024, 1024, 16, 4, 128, seed=408, what="s1024")
 
