@@ -147,21 +147,29 @@ __device__ __forceinline__ float sum_halves(float x) {
 // Request extents, clamped so that malformed offsets or lengths cannot
 // address rows outside the tensors: packed offsets into [0, total], lengths
 // into [0, the per-request maximum], paged lengths into [0, cap].
+//
+// The tables are read as constant memory (the kernels never write them): with
+// a wave-uniform index the read goes through the scalar cache and never
+// waits on the vector memory counter, which the K/V rings count on.
+__device__ __forceinline__ int32_t table_at(const int32_t *t, int i) {
+    return ((__attribute__((address_space(4))) const int32_t *)t)[i];
+}
+
 __device__ __forceinline__ void q_span(const SeqDesc &s, int b, int64_t &row0, int &len) {
     if (!s.cu_q) {
         row0 = (int64_t)b * s.sq;
         len = s.sq;
         return;
     }
-    const int a = min(max(s.cu_q[b], 0), s.total_q);
-    const int e = min(max(s.cu_q[b + 1], a), s.total_q);
+    const int a = min(max(table_at(s.cu_q, b), 0), s.total_q);
+    const int e = min(max(table_at(s.cu_q, b + 1), a), s.total_q);
     row0 = a;
     len = min(e - a, s.sq);
 }
 
 __device__ __forceinline__ int seq_kv_len(const SeqDesc &s, int b) {
     if (s.seqlen) {
-        int64_t len = s.seqlen[b];
+        int64_t len = table_at(s.seqlen, b);
         if (s.append) {  // the chunk's own keys follow the cached ones
             int64_t row0;
             int sq_b;
@@ -171,14 +179,14 @@ __device__ __forceinline__ int seq_kv_len(const SeqDesc &s, int b) {
         return (int)min(max(len, (int64_t)0), (int64_t)s.cap);
     }
     if (!s.cu_kv) return s.skv;
-    const int a = min(max(s.cu_kv[b], 0), s.total_kv);
-    const int e = min(max(s.cu_kv[b + 1], a), s.total_kv);
+    const int a = min(max(table_at(s.cu_kv, b), 0), s.total_kv);
+    const int e = min(max(table_at(s.cu_kv, b + 1), a), s.total_kv);
     return min(e - a, s.skv);
 }
 
 // first key row of request b in a dense (possibly packed) K/V tensor
 __device__ __forceinline__ int64_t seq_kv_row0(const SeqDesc &s, int b) {
-    return s.cu_kv ? (int64_t)min(max(s.cu_kv[b], 0), s.total_kv) : (int64_t)b * s.skv;
+    return s.cu_kv ? (int64_t)min(max(table_at(s.cu_kv, b), 0), s.total_kv) : (int64_t)b * s.skv;
 }
 
 // Stream-K plan over the key tiles of all requests.

@@ -148,283 +148,34 @@ void attn_fwd_kernel(const FwdParams p) {
                         (PAGED && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0,
                         PAGED ? p.kv_append : 0};
 
-    // ---- one unit of work: the key range [kbeg, kend) of row block `mblock`
-    // of (batch b, KV head kvh), whose length is kv_len; a split result goes
-    // to partial slot `slot`, a whole result straight to o and lse.
-    auto run = [&](const int mblock, const int b, const int kvh, const int kv_len,
-                   const int kbeg, const int kend, const int64_t slot,
-                   const bool partial) __attribute__((always_inline)) {
-    // this request's queries: packed rows q_row0 .. q_row0 + sq_b - 1
-    int64_t q_row0;
-    int sq_b;
-    q_span(sd, b, q_row0, sq_b);
-    const int rows_b = sq_b * p.G;  // its packed rows
-    if (mblock * BM >= rows_b) return;  // a shorter request: no rows in this block
-    const int delta = kv_len - sq_b;  // query i sits at key position p_i = i + delta
-
-    // Keys query i may see before the padding mask (TileOPs "Attention
-    // Operators", GQADenseFwdOp stage 5): [key_lo(i), key_hi(i)], both
-    // nondecreasing in i.  (The host keeps i + delta + win_right in range.)
-    auto key_hi = [&](int i) __attribute__((always_inline)) -> int {
-        int h = kv_len - 1;
-        if (p.causal) h = min(h, i + delta);
-        if (p.win_right >= 0) h = min(h, i + delta + p.win_right);
-        return h;
-    };
-    auto key_lo = [&](int i) __attribute__((always_inline)) -> int {
-        return p.win_left >= 0 ? max(0, i + delta - p.win_left) : 0;
-    };
-
-    const int row0 = mblock * BM;
-    const int row_last = min(rows_b, row0 + BM) - 1;
-    const int wg_end = min(kend, key_hi(row_last / p.G) + 1);
-    // the first tile (on the kbeg + n BN grid) that holds a key this
-    // workgroup's rows may see
-    const int wg_begin = max(kbeg, key_lo(row0 / p.G));
-    const int tile_begin = wg_begin >= wg_end ? wg_end : kbeg + (wg_begin - kbeg) / BN * BN;
-
-    const int wrow0 = row0 + (SPLIT_ROLES ? 0 : wave * kRowsPerWave);
-    const bool wave_active = (!SPLIT_ROLES || wave == 0) && wrow0 < rows_b;
-    const int wrow_last = min(rows_b, wrow0 + kRowsPerWave) - 1;
-    // keys in [wave_full_begin, wave_full_end) are visible to every row of
-    // this wave (mask aside); keys outside [wave_begin, wave_end) to none
-    const int wave_end = !wave_active ? kbeg : min(kend, key_hi(wrow_last / p.G) + 1);
-    const int wave_full_end = !wave_active ? kbeg : min(kend, key_hi(wrow0 / p.G) + 1);
-    const int wave_begin = key_lo(wrow0 / p.G);
-    const int wave_full_begin = key_lo(wrow_last / p.G);
-    // does this wave compute on the tile starting at key t?
-    auto sees = [&](int t) __attribute__((always_inline)) -> bool {
-        return wave_active && t < wave_end && t + BN > wave_begin;
-    };
-    auto full_tile = [&](int t) __attribute__((always_inline)) -> bool {
-        return t + BN <= wave_full_end && t >= wave_full_begin;
-    };
-
-    // ---- this lane's query row (the column it holds in every MFMA tile)
-    const int my_row = wrow0 + l32;
-    const bool row_ok = my_row < rows_b;
-    const int my_i = my_row / p.G;
-    const int my_gh = my_row - my_i * p.G;
-    const int my_last = !row_ok ? -1 : key_hi(my_i);
-    const int my_first = key_lo(my_i);
-
-    // ---- Q for the whole kernel: B operand, lane = row, 8 d-values per k-step.
-    // The host folds the sign of the scale into Q (an exact sign flip) and
-    // turns a zero scale into a zero Q, so the kernel always scales by c > 0
-    // and the row max stays a max.
+    // ---- the computing wave's state for its current unit: the key limits of
+    // its row, Q, the output accumulator, the running max and denominator
+    const bool has_mask = !PAGED && p.mask != nullptr;
+    int my_last = -1, my_first = 0;
     vec8 qf[KSTEPS];
-    {
+    f32x16 acc[DT];
+    float m_run = -INFINITY;  // running (possibly stale) max, scaled log2 units
+    float l_run = 0.f;        // this lane's part of the running denominator
+
+    // Q of this lane's row (at qrow) as the B operand -- 8 d-values per
+    // k-step -- and a fresh accumulator.  The host folds the sign of the
+    // scale into Q (an exact sign flip) and turns a zero scale into a zero Q,
+    // so the kernel always scales by c > 0 and the row max stays a max.
+    auto begin_rows = [&](const uint16_t *qrow, const bool row_ok) __attribute__((always_inline)) {
         const uint32_t flip = p.q_mode == 1 ? 0x80008000u : 0u;
         const bool load_q = row_ok && p.q_mode != 2;
-        const uint16_t *qrow =
-            p.q + ((q_row0 + my_i) * p.Hq + (int64_t)kvh * p.G + my_gh) * D;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4 raw = {0u, 0u, 0u, 0u};
             if (load_q) raw = *(const u32x4 *)(qrow + 16 * ks + 8 * hl) ^ flip;
             qf[ks] = __builtin_bit_cast(vec8, raw);
         }
-    }
-
-    f32x16 acc[DT];
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+        for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-    float m_run = -INFINITY;  // running (possibly stale) max, scaled log2 units
-    float l_run = 0.f;        // this lane's part of the running denominator
-
-    // ---- key padding mask: one bit per key of a tile, wave-uniform
-    const bool has_mask = !PAGED && p.mask != nullptr;
-    const uint8_t *mrow = has_mask ? p.mask + (int64_t)b * p.Skv : nullptr;
-    constexpr uint64_t kLoMask = BN >= 64 ? ~0ull : ((1ull << (BN & 63)) - 1);
-    auto tile_bits = [&](int j0, uint64_t &lo, uint64_t &hi) __attribute__((always_inline)) {
-        const int j = j0 + lane;
-        const bool keep0 = (lane < BN) && j < kv_len && mrow[j] != 0;
-        lo = __ballot(keep0) & kLoMask;
-        hi = 0;
-        if (BN > 64) {
-            const bool keep1 = j + 64 < kv_len && mrow[j + 64] != 0;
-            hi = __ballot(keep1);
-        }
-    };
-    // Tile summary of the mask, taken once: bit n of mask_any (mask_all) is set
-    // when tile tile_begin + n BN holds a kept key (only kept keys), for the
-    // first 64 tiles of this workgroup's range -- lane n reads tile n's bytes.
-    // Inside that window the steps then need no mask load for tiles that are
-    // fully kept or fully masked; past it (or for a partly kept tile) they
-    // read the tile's bytes.
-    uint64_t mask_any = 0, mask_all = 0;
-    if (has_mask) {
-        // one pass covers 1 KB of keys (16 per lane) = 1024 / BN tiles of
-        // BN / 16 lanes each; bytes past the keys or past wg_end count as
-        // masked.  Rows that are not 16-byte aligned are read bytewise.
-        constexpr int TPP = 1024 / BN;
-        constexpr int LPT = BN / 16;
-        constexpr uint64_t kLaneGroup = LPT >= 64 ? ~0ull : ((1ull << LPT) - 1);
-        const bool vec = (((uintptr_t)mrow) & 15) == 0;
-        const int lim = min(kv_len, wg_end);
-#pragma unroll 1
-        for (int pass = 0; pass < 64 / TPP; ++pass) {
-            const int j = tile_begin + pass * 1024 + 16 * lane;
-            bool any = false, all = false;
-            if (j < lim) {
-                uint32_t w[4] = {0u, 0u, 0u, 0u};
-                if (vec && j + 16 <= lim) {
-                    const u32x4 x = *(const u32x4 *)(mrow + j);
-                    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
-                } else {
-                    for (int i = 0; i < 16; ++i)
-                        if (j + i < lim && mrow[j + i] != 0) w[i >> 2] |= 0xffu << (8 * (i & 3));
-                }
-                // a byte is kept when nonzero: fold each byte to its top bit
-                uint32_t nz_any = 0u, nz_all = 0x80808080u;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t t = ((w[q] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[q];
-                    nz_any |= t & 0x80808080u;
-                    nz_all &= t;
-                }
-                any = nz_any != 0u;
-                all = (nz_all & 0x80808080u) == 0x80808080u && j + 16 <= lim;
-            }
-            const uint64_t ba = __ballot(any), bb = __ballot(all);
-#pragma unroll
-            for (int t = 0; t < TPP; ++t) {
-                const uint64_t ga = (ba >> (t * LPT)) & kLaneGroup;
-                const uint64_t gb = (bb >> (t * LPT)) & kLaneGroup;
-                mask_any |= (uint64_t)(ga != 0) << (pass * TPP + t);
-                mask_all |= (uint64_t)(gb == kLaneGroup) << (pass * TPP + t);
-            }
-        }
-    }
-    const int mask_window_end = tile_begin + 64 * BN;  // first tile the summary does not cover
-    // first tile start >= j that holds a kept key (or wg_end), with its mask bits
-    auto find_tile = [&](int j, uint64_t &lo, uint64_t &hi) __attribute__((always_inline)) -> int {
-        if (!has_mask) return j;
-        if (j < mask_window_end) {
-            const uint64_t rest = mask_any >> ((j - tile_begin) / BN);
-            if (rest == 0) {
-                j = mask_window_end;
-            } else {
-                j += __builtin_ctzll(rest) * BN;
-                if (j >= wg_end) return wg_end;
-                if ((mask_all >> ((j - tile_begin) / BN)) & 1) {
-                    lo = kLoMask;
-                    hi = ~0ull;
-                } else {
-                    tile_bits(j, lo, hi);
-                }
-                return j;
-            }
-        }
-        for (; j < wg_end; j += BN) {
-            tile_bits(j, lo, hi);
-            if (lo | hi) return j;
-        }
-        return wg_end;
-    };
-
-    // ---- HBM -> LDS, no registers: each 1 KB piece of a tile is one
-    // buffer_load_dwordx4 ... lds (lane l fills bytes [16l, 16l+16) of the
-    // piece); piece e*WAVES + wave is this wave's e-th and covers RPP
-    // consecutive keys.  The load's base address is scalar (block-table
-    // entries are read through the scalar cache) and each lane adds a small
-    // offset: its key, and the chunk that the swizzle puts at its position.
-    // Keys past the end load the last key (finite data, masked later).
-    //
-    // The buffer form, unlike global_load_lds, is not a FLAT instruction: the
-    // compiler then counts the LDS reads that follow (lgkmcnt(n)) instead of
-    // waiting for all of them whenever a direct load is in flight.
-    constexpr int RPP = 512 / D;                                // keys per piece
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);    // wave-uniform
-    const int loader = SPLIT_ROLES ? wave_u - 1 : wave_u;  // this wave's index among the loaders
-    const bool loads = !SPLIT_ROLES || wave_u >= 1;
-    const int l_dr = lane / (D / 8);   // this lane's key within a piece
-    const int l_pos = lane % (D / 8);  // this lane's 16-byte position in the row
-    const int64_t hstride = (int64_t)p.Hkv * D;  // elements between consecutive keys
-    const int row_bytes = p.Hkv * D * 2;
-    int l_chunk[PPW];  // byte offset, within its key row, of the chunk this lane fetches
-#pragma unroll
-    for (int e = 0; e < PPW; ++e)
-        l_chunk[e] = 16 * (l_pos ^ swz<D>((e * LOADERS + loader) * RPP + l_dr));
-    const int64_t head_off = (int64_t)kvh * D + (PAGED ? 0 : seq_kv_row0(sd, b) * hstride);
-    typedef __attribute__((address_space(4))) const int32_t const_i32;
-    const_i32 *bt_row =
-        PAGED ? (const_i32 *)(p.block_table + (int64_t)b * p.max_pages) : nullptr;
-    // Where a tile lies in one page (always, for dense K/V) a single buffer
-    // descriptor based at the tile's first key serves all pieces and each
-    // lane clamps its own key; with smaller pages each piece gets its own
-    // base.  (The scalar unit is shared by the CU's waves, so the per-step
-    // scalar address arithmetic is kept small.)
-    constexpr bool tile_in_page = KVP != kPagedPiece;
-    int l_key[PPW];  // this lane's key row within the tile, per piece
-#pragma unroll
-    for (int e = 0; e < PPW; ++e) l_key[e] = (e * LOADERS + loader) * RPP + l_dr;
-    auto cache_row = [&](int32_t phys, int j) __attribute__((always_inline)) -> int64_t {
-        // (page ids clamped into the cache, so that a malformed table cannot
-        // address memory outside it)
-        return ((int64_t)min(max(phys, 0), p.num_pages - 1) << p.page_shift) +
-               (j & ((1 << p.page_shift) - 1));
-    };
-    // first tile holding a visible key (wg_end if none), with its mask bits
-    uint64_t first_lo = ~0ull, first_hi = ~0ull;
-    const int first_tile = find_tile(tile_begin, first_lo, first_hi);
-    // Block-table entry of the page holding tile j (of the first tile for a
-    // tile past the range).  With whole-tile pages the schedules read it a
-    // step before the tile's loads are issued, so that the scalar load's
-    // latency stays off the issue path.
-    auto tile_page = [&](int j) __attribute__((always_inline)) -> int32_t {
-        if constexpr (KVP == kPagedTile)
-            return bt_row[(j < wg_end ? j : first_tile) >> p.page_shift];
-        else
-            return 0;
-    };
-    // Loads of tile j0 into stage dst; `phys` is tile_page(j0).
-    auto issue = [&](int j0, int32_t phys, const uint16_t *src, uint8_t *dst) __attribute__((always_inline)) {
-        // A tile past the range keeps the ring's load count but fetches almost
-        // nothing: every lane reads the same 16 bytes of the first tile.
-        const bool pad = j0 >= wg_end;
-        const int keep = pad ? 0 : -1;  // lane offsets are and-ed with this (no branch)
-        if (pad) j0 = first_tile;
-        if constexpr (tile_in_page) {
-            int64_t row = j0;
-            if constexpr (PAGED) row = cache_row(phys, j0);
-            const uint16_t *base = src + head_off + row * hstride;
-            const int last = kv_len - 1 - j0;  // last valid key row of the tile
-#pragma unroll
-            for (int e = 0; e < PPW; ++e)
-                buffer_load_lds16(base, BN * row_bytes,
-                                  (lds_void *)(dst + (e * LOADERS + loader) * 1024),
-                                  (min(l_key[e], last) * row_bytes + l_chunk[e]) & keep);
-        } else {
-            // pages smaller than a tile: each of the tile's pages (at most
-            // BN / 16) is looked up once -- all reads issued before any is
-            // waited for -- and each piece picks its own
-            constexpr int kTilePages = BN / 16;
-            const int pg0 = j0 >> p.page_shift;
-            const int pg_last = (kv_len - 1) >> p.page_shift;
-            int32_t phys[kTilePages];
-#pragma unroll
-            for (int q = 0; q < kTilePages; ++q) phys[q] = bt_row[min(pg0 + q, pg_last)];
-#pragma unroll
-            for (int e = 0; e < PPW; ++e) {
-                const int jr = min(j0 + (e * LOADERS + loader) * RPP, kv_len - 1);
-                const int qi = (jr >> p.page_shift) - pg0;
-                int32_t pe = phys[0];
-#pragma unroll
-                for (int q = 1; q < kTilePages; ++q) pe = qi == q ? phys[q] : pe;
-                buffer_load_lds16(src + head_off + cache_row(pe, jr) * hstride, RPP * row_bytes,
-                                  (lds_void *)(dst + (e * LOADERS + loader) * 1024),
-                                  (min(l_dr, kv_len - 1 - jr) * row_bytes + l_chunk[e]) & keep);
-            }
-        }
-    };
-    // K of tile kt and V of tile vt (page entries pk and pv_)
-    auto issue_kv = [&](int kt, int32_t pk, uint8_t *dk, int vt, int32_t pv_, uint8_t *dv) __attribute__((always_inline)) {
-        if (!loads) return;
-        issue(kt, pk, p.k, dk);
-        issue(vt, pv_, p.v, dv);
+            for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+        m_run = -INFINITY;
+        l_run = 0.f;
     };
 
     // (an FP8 pool's key scale multiplies every raw score, so it joins the
@@ -622,6 +373,283 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int kk = 0; kk < PSTEPS; ++kk) acc[t0 + t] = H::mfma(a[t][kk], pb[kk], acc[t0 + t]);
         }
+    };
+
+
+    // ---- HBM -> LDS, no registers: each 1 KB piece of a tile is one
+    // buffer_load_dwordx4 ... lds (lane l fills bytes [16l, 16l+16) of the
+    // piece); piece e*WAVES + wave is this wave's e-th and covers RPP
+    // consecutive keys.  The load's base address is scalar (block-table
+    // entries are read through the scalar cache) and each lane adds a small
+    // offset: its key, and the chunk that the swizzle puts at its position.
+    // Keys past the end load the last key (finite data, masked later).
+    //
+    // The buffer form, unlike global_load_lds, is not a FLAT instruction: the
+    // compiler then counts the LDS reads that follow (lgkmcnt(n)) instead of
+    // waiting for all of them whenever a direct load is in flight.
+    constexpr int RPP = 512 / D;                                // keys per piece
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);    // wave-uniform
+    const int loader = SPLIT_ROLES ? wave_u - 1 : wave_u;  // this wave's index among the loaders
+    const bool loads = !SPLIT_ROLES || wave_u >= 1;
+    const int l_dr = lane / (D / 8);   // this lane's key within a piece
+    const int l_pos = lane % (D / 8);  // this lane's 16-byte position in the row
+    const int64_t hstride = (int64_t)p.Hkv * D;  // elements between consecutive keys
+    const int row_bytes = p.Hkv * D * 2;
+    int l_chunk[PPW];  // byte offset, within its key row, of the chunk this lane fetches
+#pragma unroll
+    for (int e = 0; e < PPW; ++e)
+        l_chunk[e] = 16 * (l_pos ^ swz<D>((e * LOADERS + loader) * RPP + l_dr));
+    // Where a tile lies in one page (always, for dense K/V) a single buffer
+    // descriptor based at the tile's first key serves all pieces and each
+    // lane clamps its own key; with smaller pages each piece gets its own
+    // base.  (The scalar unit is shared by the CU's waves, so the per-step
+    // scalar address arithmetic is kept small.)
+    constexpr bool tile_in_page = KVP != kPagedPiece;
+    typedef __attribute__((address_space(4))) const int32_t const_i32;
+    int l_key[PPW];  // this lane's key row within the tile, per piece
+#pragma unroll
+    for (int e = 0; e < PPW; ++e) l_key[e] = (e * LOADERS + loader) * RPP + l_dr;
+    auto cache_row = [&](int32_t phys, int j) __attribute__((always_inline)) -> int64_t {
+        // (page ids clamped into the cache, so that a malformed table cannot
+        // address memory outside it)
+        return ((int64_t)min(max(phys, 0), p.num_pages - 1) << p.page_shift) +
+               (j & ((1 << p.page_shift) - 1));
+    };
+
+    // a split result: the normalised FP32 output row and its natural-log LSE
+    // at partial row `part`
+    auto store_partial = [&](const int64_t part, const float inv, const float lse_v) __attribute__((always_inline)) {
+        float *op = p.o_part + part * D;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int d0 = 32 * t + 8 * w + 4 * hl;
+                const f32x4 v4 = {acc[t][4 * w] * inv, acc[t][4 * w + 1] * inv,
+                                  acc[t][4 * w + 2] * inv, acc[t][4 * w + 3] * inv};
+                *(f32x4 *)(op + d0) = v4;
+            }
+        if (hl == 0) p.lse_part[part] = lse_v;
+    };
+
+    // Keys query i of a request with kv_len keys may see before the padding
+    // mask (TileOPs "Attention Operators", GQADenseFwdOp stage 5): [key_lo,
+    // key_hi], both nondecreasing in i; the query sits at key position i +
+    // delta.  (The host keeps i + delta + win_right in range.)
+    auto key_hi_of = [&](int i, int kv_len, int delta) __attribute__((always_inline)) -> int {
+        int h = kv_len - 1;
+        if (p.causal) h = min(h, i + delta);
+        if (p.win_right >= 0) h = min(h, i + delta + p.win_right);
+        return h;
+    };
+    auto key_lo_of = [&](int i, int delta) __attribute__((always_inline)) -> int {
+        return p.win_left >= 0 ? max(0, i + delta - p.win_left) : 0;
+    };
+
+    // ---- one unit of work: the key range [kbeg, kend) of row block `mblock`
+    // of (batch b, KV head kvh), whose length is kv_len; a split result goes
+    // to partial slot `slot`, a whole result straight to o and lse.
+    auto run = [&](const int mblock, const int b, const int kvh, const int kv_len,
+                   const int kbeg, const int kend, const int64_t slot,
+                   const bool partial) __attribute__((always_inline)) {
+    // this request's queries: packed rows q_row0 .. q_row0 + sq_b - 1
+    int64_t q_row0;
+    int sq_b;
+    q_span(sd, b, q_row0, sq_b);
+    const int rows_b = sq_b * p.G;  // its packed rows
+    if (mblock * BM >= rows_b) return;  // a shorter request: no rows in this block
+    const int delta = kv_len - sq_b;  // query i sits at key position p_i = i + delta
+
+    auto key_hi = [&](int i) __attribute__((always_inline)) -> int {
+        return key_hi_of(i, kv_len, delta);
+    };
+    auto key_lo = [&](int i) __attribute__((always_inline)) -> int { return key_lo_of(i, delta); };
+
+    const int row0 = mblock * BM;
+    const int row_last = min(rows_b, row0 + BM) - 1;
+    const int wg_end = min(kend, key_hi(row_last / p.G) + 1);
+    // the first tile (on the kbeg + n BN grid) that holds a key this
+    // workgroup's rows may see
+    const int wg_begin = max(kbeg, key_lo(row0 / p.G));
+    const int tile_begin = wg_begin >= wg_end ? wg_end : kbeg + (wg_begin - kbeg) / BN * BN;
+
+    const int wrow0 = row0 + (SPLIT_ROLES ? 0 : wave * kRowsPerWave);
+    const bool wave_active = (!SPLIT_ROLES || wave == 0) && wrow0 < rows_b;
+    const int wrow_last = min(rows_b, wrow0 + kRowsPerWave) - 1;
+    // keys in [wave_full_begin, wave_full_end) are visible to every row of
+    // this wave (mask aside); keys outside [wave_begin, wave_end) to none
+    const int wave_end = !wave_active ? kbeg : min(kend, key_hi(wrow_last / p.G) + 1);
+    const int wave_full_end = !wave_active ? kbeg : min(kend, key_hi(wrow0 / p.G) + 1);
+    const int wave_begin = key_lo(wrow0 / p.G);
+    const int wave_full_begin = key_lo(wrow_last / p.G);
+    // does this wave compute on the tile starting at key t?
+    auto sees = [&](int t) __attribute__((always_inline)) -> bool {
+        return wave_active && t < wave_end && t + BN > wave_begin;
+    };
+    auto full_tile = [&](int t) __attribute__((always_inline)) -> bool {
+        return t + BN <= wave_full_end && t >= wave_full_begin;
+    };
+
+    // ---- this lane's query row (the column it holds in every MFMA tile)
+    const int my_row = wrow0 + l32;
+    const bool row_ok = my_row < rows_b;
+    const int my_i = my_row / p.G;
+    const int my_gh = my_row - my_i * p.G;
+    my_last = !row_ok ? -1 : key_hi(my_i);
+    my_first = key_lo(my_i);
+    begin_rows(p.q + ((q_row0 + my_i) * p.Hq + (int64_t)kvh * p.G + my_gh) * D, row_ok);
+
+    // ---- key padding mask: one bit per key of a tile, wave-uniform
+    const uint8_t *mrow = has_mask ? p.mask + (int64_t)b * p.Skv : nullptr;
+    constexpr uint64_t kLoMask = BN >= 64 ? ~0ull : ((1ull << (BN & 63)) - 1);
+    auto tile_bits = [&](int j0, uint64_t &lo, uint64_t &hi) __attribute__((always_inline)) {
+        const int j = j0 + lane;
+        const bool keep0 = (lane < BN) && j < kv_len && mrow[j] != 0;
+        lo = __ballot(keep0) & kLoMask;
+        hi = 0;
+        if (BN > 64) {
+            const bool keep1 = j + 64 < kv_len && mrow[j + 64] != 0;
+            hi = __ballot(keep1);
+        }
+    };
+    // Tile summary of the mask, taken once: bit n of mask_any (mask_all) is set
+    // when tile tile_begin + n BN holds a kept key (only kept keys), for the
+    // first 64 tiles of this workgroup's range -- lane n reads tile n's bytes.
+    // Inside that window the steps then need no mask load for tiles that are
+    // fully kept or fully masked; past it (or for a partly kept tile) they
+    // read the tile's bytes.
+    uint64_t mask_any = 0, mask_all = 0;
+    if (has_mask) {
+        // one pass covers 1 KB of keys (16 per lane) = 1024 / BN tiles of
+        // BN / 16 lanes each; bytes past the keys or past wg_end count as
+        // masked.  Rows that are not 16-byte aligned are read bytewise.
+        constexpr int TPP = 1024 / BN;
+        constexpr int LPT = BN / 16;
+        constexpr uint64_t kLaneGroup = LPT >= 64 ? ~0ull : ((1ull << LPT) - 1);
+        const bool vec = (((uintptr_t)mrow) & 15) == 0;
+        const int lim = min(kv_len, wg_end);
+#pragma unroll 1
+        for (int pass = 0; pass < 64 / TPP; ++pass) {
+            const int j = tile_begin + pass * 1024 + 16 * lane;
+            bool any = false, all = false;
+            if (j < lim) {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+                if (vec && j + 16 <= lim) {
+                    const u32x4 x = *(const u32x4 *)(mrow + j);
+                    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+                } else {
+                    for (int i = 0; i < 16; ++i)
+                        if (j + i < lim && mrow[j + i] != 0) w[i >> 2] |= 0xffu << (8 * (i & 3));
+                }
+                // a byte is kept when nonzero: fold each byte to its top bit
+                uint32_t nz_any = 0u, nz_all = 0x80808080u;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t t = ((w[q] & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w[q];
+                    nz_any |= t & 0x80808080u;
+                    nz_all &= t;
+                }
+                any = nz_any != 0u;
+                all = (nz_all & 0x80808080u) == 0x80808080u && j + 16 <= lim;
+            }
+            const uint64_t ba = __ballot(any), bb = __ballot(all);
+#pragma unroll
+            for (int t = 0; t < TPP; ++t) {
+                const uint64_t ga = (ba >> (t * LPT)) & kLaneGroup;
+                const uint64_t gb = (bb >> (t * LPT)) & kLaneGroup;
+                mask_any |= (uint64_t)(ga != 0) << (pass * TPP + t);
+                mask_all |= (uint64_t)(gb == kLaneGroup) << (pass * TPP + t);
+            }
+        }
+    }
+    const int mask_window_end = tile_begin + 64 * BN;  // first tile the summary does not cover
+    // first tile start >= j that holds a kept key (or wg_end), with its mask bits
+    auto find_tile = [&](int j, uint64_t &lo, uint64_t &hi) __attribute__((always_inline)) -> int {
+        if (!has_mask) return j;
+        if (j < mask_window_end) {
+            const uint64_t rest = mask_any >> ((j - tile_begin) / BN);
+            if (rest == 0) {
+                j = mask_window_end;
+            } else {
+                j += __builtin_ctzll(rest) * BN;
+                if (j >= wg_end) return wg_end;
+                if ((mask_all >> ((j - tile_begin) / BN)) & 1) {
+                    lo = kLoMask;
+                    hi = ~0ull;
+                } else {
+                    tile_bits(j, lo, hi);
+                }
+                return j;
+            }
+        }
+        for (; j < wg_end; j += BN) {
+            tile_bits(j, lo, hi);
+            if (lo | hi) return j;
+        }
+        return wg_end;
+    };
+
+    const int64_t head_off = (int64_t)kvh * D + (PAGED ? 0 : seq_kv_row0(sd, b) * hstride);
+    const_i32 *bt_row =
+        PAGED ? (const_i32 *)(p.block_table + (int64_t)b * p.max_pages) : nullptr;
+    // first tile holding a visible key (wg_end if none), with its mask bits
+    uint64_t first_lo = ~0ull, first_hi = ~0ull;
+    const int first_tile = find_tile(tile_begin, first_lo, first_hi);
+    // Block-table entry of the page holding tile j (of the first tile for a
+    // tile past the range).  With whole-tile pages the schedules read it a
+    // step before the tile's loads are issued, so that the scalar load's
+    // latency stays off the issue path.
+    auto tile_page = [&](int j) __attribute__((always_inline)) -> int32_t {
+        if constexpr (KVP == kPagedTile)
+            return bt_row[(j < wg_end ? j : first_tile) >> p.page_shift];
+        else
+            return 0;
+    };
+    // Loads of tile j0 into stage dst; `phys` is tile_page(j0).
+    auto issue = [&](int j0, int32_t phys, const uint16_t *src, uint8_t *dst) __attribute__((always_inline)) {
+        // A tile past the range keeps the ring's load count but fetches almost
+        // nothing: every lane reads the same 16 bytes of the first tile.
+        const bool pad = j0 >= wg_end;
+        const int keep = pad ? 0 : -1;  // lane offsets are and-ed with this (no branch)
+        if (pad) j0 = first_tile;
+        if constexpr (tile_in_page) {
+            int64_t row = j0;
+            if constexpr (PAGED) row = cache_row(phys, j0);
+            const uint16_t *base = src + head_off + row * hstride;
+            const int last = kv_len - 1 - j0;  // last valid key row of the tile
+#pragma unroll
+            for (int e = 0; e < PPW; ++e)
+                buffer_load_lds16(base, BN * row_bytes,
+                                  (lds_void *)(dst + (e * LOADERS + loader) * 1024),
+                                  (min(l_key[e], last) * row_bytes + l_chunk[e]) & keep);
+        } else {
+            // pages smaller than a tile: each of the tile's pages (at most
+            // BN / 16) is looked up once -- all reads issued before any is
+            // waited for -- and each piece picks its own
+            constexpr int kTilePages = BN / 16;
+            const int pg0 = j0 >> p.page_shift;
+            const int pg_last = (kv_len - 1) >> p.page_shift;
+            int32_t phys[kTilePages];
+#pragma unroll
+            for (int q = 0; q < kTilePages; ++q) phys[q] = bt_row[min(pg0 + q, pg_last)];
+#pragma unroll
+            for (int e = 0; e < PPW; ++e) {
+                const int jr = min(j0 + (e * LOADERS + loader) * RPP, kv_len - 1);
+                const int qi = (jr >> p.page_shift) - pg0;
+                int32_t pe = phys[0];
+#pragma unroll
+                for (int q = 1; q < kTilePages; ++q) pe = qi == q ? phys[q] : pe;
+                buffer_load_lds16(src + head_off + cache_row(pe, jr) * hstride, RPP * row_bytes,
+                                  (lds_void *)(dst + (e * LOADERS + loader) * 1024),
+                                  (min(l_dr, kv_len - 1 - jr) * row_bytes + l_chunk[e]) & keep);
+            }
+        }
+    };
+    // K of tile kt and V of tile vt (page entries pk and pv_)
+    auto issue_kv = [&](int kt, int32_t pk, uint8_t *dk, int vt, int32_t pv_, uint8_t *dv) __attribute__((always_inline)) {
+        if (!loads) return;
+        issue(kt, pk, p.k, dk);
+        issue(vt, pv_, p.v, dv);
     };
 
     if constexpr (WAVES == 8) {
@@ -846,15 +874,7 @@ void attn_fwd_kernel(const FwdParams p) {
         };
         // FP8 stage -> 16-bit stage: lane l's 16 bytes of piece e are chunks
         // 2 l_col8 and 2 l_col8 + 1 (d 0..7 and 8..15 of the piece) of key row
-        // e RPP8 + l_row8.  A 16-byte LDS write is served in groups of lanes
-        // 8k..8k+7 with 8k+32..8k+39 (the grouping under which the counters
-        // read zero conflicts for the row-per-16-lanes stores of the backward
-        // and nonzero here).  At D >= 128 the two lane halves write rows whose
-        // swizzles differ in a bit above bit 0, so their chunks would take the
-        // same 8 positions: the upper lanes write their halves in the opposite
-        // order.  At D = 64 the swizzle already gives rows 8 apart opposite
-        // chunk parity.
-        const int half_flip = D == 64 ? 0 : (lane >> 5) & 1;
+        // e RPP8 + l_row8, written to their swizzled positions.
         auto convert8 = [&](int stage, uint8_t *dk, uint8_t *dv) __attribute__((always_inline)) {
             if (!conv) return;
             const uint8_t *fk = fK[stage], *fv = fV[stage];
@@ -863,8 +883,7 @@ void attn_fwd_kernel(const FwdParams p) {
                 const u32x4 kw = *(const u32x4 *)(fk + e * 1024 + 16 * lane);
                 const u32x4 vw = *(const u32x4 *)(fv + e * 1024 + 16 * lane);
 #pragma unroll
-                for (int h0 = 0; h0 < 2; ++h0) {
-                    const int h = h0 ^ half_flip;
+                for (int h = 0; h < 2; ++h) {
                     const u32x2 k01 = fp8x4_to_half4<BF16>(h ? kw[2] : kw[0]);
                     const u32x2 k23 = fp8x4_to_half4<BF16>(h ? kw[3] : kw[1]);
                     const u32x2 v01 = fp8x4_to_half4<BF16>(h ? vw[2] : vw[0]);
@@ -1015,18 +1034,7 @@ void attn_fwd_kernel(const FwdParams p) {
                 p.lse[((int64_t)b * p.Hq + my_h) * p.Sq + my_i] = lse_v;
         }
     } else {
-        const int64_t part = slot * p.rows + my_row;
-        float *op = p.o_part + part * D;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const int d0 = 32 * t + 8 * w + 4 * hl;
-                const f32x4 v4 = {acc[t][4 * w] * inv, acc[t][4 * w + 1] * inv,
-                                  acc[t][4 * w + 2] * inv, acc[t][4 * w + 3] * inv};
-                *(f32x4 *)(op + d0) = v4;
-            }
-        if (hl == 0) p.lse_part[part] = lse_v;
+        store_partial(slot * p.rows + my_row, inv, lse_v);
     }
 
     };
