@@ -826,20 +826,36 @@ void attn_fwd_kernel(const FwdParams p) {
         // arrays.  Step n: wave 0 computes tile n from 16-bit stage n & 1;
         // wave 2 converts tile n + 1 (landed during step n - 1); wave 1 issues
         // tile n + S8 into the FP8 stage tile n left, then waits for tile
-        // n + 2 -- S8 - 2 tiles stay in flight.  A piece (1 KB) holds RPP8
-        // whole key rows, lane l its 16 bytes (16 d-values) at offset 16 l.
-        // (Tiles of a paged call follow one another: there is no padding mask.)
+        // n + 2 -- S8 - 2 tiles stay in flight.  (Tiles of a paged call
+        // follow one another: there is no padding mask.)
+        //
+        // A piece (1 KB) holds, at lane l's 16 bytes, the 16-byte chunk f_chunk
+        // (16 d-values) of key row piece_row(e) + f_row -- an order chosen for
+        // the conversion's 16-bit writes: a 16-byte LDS write is served eight
+        // lanes at a time, and those eight must fall in one 128-byte half of
+        // the 256-byte bank line, on distinct banks, or the write takes twice
+        // as long (measured: every lane order that spreads eight lanes over
+        // both halves doubles the write's LDS cycles, as SQ_LDS_BANK_CONFLICT
+        // cycles).  Lanes 8k..8k+7 therefore hold rows r and r + 8 -- whose
+        // swizzles put their chunks in the same half and apart in bank -- and
+        // four chunks of each.  A piece's rows lie in one aligned 16-row block.
         constexpr int S8 = 4;                // FP8 ring stages
-        constexpr int U16 = D / 16;          // 16-byte pieces per key row
-        constexpr int RPP8 = 1024 / D;       // key rows per 1 KB piece
+        constexpr int U16 = D / 16;          // 16-byte chunks per FP8 key row
+        constexpr int CG = U16 / 4;          // groups of four chunks per row
         constexpr int STAGE8 = BN * D;       // bytes of one FP8 K (or V) tile
         constexpr int PC8 = STAGE8 / 1024;   // pieces per tensor and tile
+        static_assert(CG == 1 || CG == 2, "FP8 pools: D = 64 or 128");
         static_assert((S8 - 2) * 2 * PC8 <= 63, "the counted wait fits vmcnt");
         __shared__ __attribute__((aligned(1024))) uint8_t fK[S8][STAGE8];
         __shared__ __attribute__((aligned(1024))) uint8_t fV[S8][STAGE8];
         const uint8_t *k8 = (const uint8_t *)p.k, *v8 = (const uint8_t *)p.v;
         const int row8 = p.Hkv * D;  // bytes between consecutive keys
-        const int l_row8 = lane / U16, l_col8 = lane % U16;
+        const int f_g = lane >> 3, f_i = lane & 7;
+        const int f_row = f_g / CG + 8 * (f_i >> 2);     // row within the piece's rows
+        const int f_chunk = 4 * (f_g % CG) + (f_i & 3);  // 16-byte chunk within the row
+        // first row of piece e's rows (within the tile), and of its 16-row block
+        auto piece_row = [](int e) { return 16 * (e / CG) + (8 / CG) * (e % CG); };
+        auto piece_block = [](int e) { return 16 * (e / CG); };
         const bool dma = wave_u == 1, conv = wave_u == 2;
         auto issue8 = [&](int j0, int stage) __attribute__((always_inline)) {
             if (!dma) return;
@@ -855,26 +871,28 @@ void attn_fwd_kernel(const FwdParams p) {
                     cache_row(bt_row[j0 >> p.page_shift], j0) * row8 + (int64_t)kvh * D;
 #pragma unroll
                 for (int e = 0; e < PC8; ++e) {
-                    const int vo = (min(e * RPP8 + l_row8, last) * row8 + 16 * l_col8) & keep;
+                    const int vo = (min(piece_row(e) + f_row, last) * row8 + 16 * f_chunk) & keep;
                     buffer_load_lds16(k8 + off, BN * row8, (lds_void *)(dk + e * 1024), vo);
                     buffer_load_lds16(v8 + off, BN * row8, (lds_void *)(dv + e * 1024), vo);
                 }
             } else {
-                // pages smaller than a tile: a piece's rows lie in one page
+                // pages smaller than a tile (16 keys or more): a piece's 16-row
+                // block lies in one page
 #pragma unroll
                 for (int e = 0; e < PC8; ++e) {
-                    const int jr = min(j0 + e * RPP8, kv_len - 1);
+                    const int jr = min(j0 + piece_block(e), kv_len - 1);
                     const int64_t off =
                         cache_row(bt_row[jr >> p.page_shift], jr) * row8 + (int64_t)kvh * D;
-                    const int vo = (min(l_row8, kv_len - 1 - jr) * row8 + 16 * l_col8) & keep;
-                    buffer_load_lds16(k8 + off, RPP8 * row8, (lds_void *)(dk + e * 1024), vo);
-                    buffer_load_lds16(v8 + off, RPP8 * row8, (lds_void *)(dv + e * 1024), vo);
+                    const int in_block = piece_row(e) - piece_block(e) + f_row;
+                    const int vo = (min(in_block, kv_len - 1 - jr) * row8 + 16 * f_chunk) & keep;
+                    buffer_load_lds16(k8 + off, 16 * row8, (lds_void *)(dk + e * 1024), vo);
+                    buffer_load_lds16(v8 + off, 16 * row8, (lds_void *)(dv + e * 1024), vo);
                 }
             }
         };
-        // FP8 stage -> 16-bit stage: lane l's 16 bytes of piece e are chunks
-        // 2 l_col8 and 2 l_col8 + 1 (d 0..7 and 8..15 of the piece) of key row
-        // e RPP8 + l_row8, written to their swizzled positions.
+        // FP8 stage -> 16-bit stage: lane l's 16 bytes of piece e become the
+        // 16-bit chunks 2 f_chunk and 2 f_chunk + 1 of key row piece_row(e) +
+        // f_row, written to their swizzled positions.
         auto convert8 = [&](int stage, uint8_t *dk, uint8_t *dv) __attribute__((always_inline)) {
             if (!conv) return;
             const uint8_t *fk = fK[stage], *fv = fV[stage];
@@ -888,7 +906,7 @@ void attn_fwd_kernel(const FwdParams p) {
                     const u32x2 k23 = fp8x4_to_half4<BF16>(h ? kw[3] : kw[1]);
                     const u32x2 v01 = fp8x4_to_half4<BF16>(h ? vw[2] : vw[0]);
                     const u32x2 v23 = fp8x4_to_half4<BF16>(h ? vw[3] : vw[1]);
-                    const int at = tile_off<D>(e * RPP8 + l_row8, 2 * l_col8 + h);
+                    const int at = tile_off<D>(piece_row(e) + f_row, 2 * f_chunk + h);
                     *(u32x4 *)(dk + at) = u32x4{k01[0], k01[1], k23[0], k23[1]};
                     *(u32x4 *)(dv + at) = u32x4{v01[0], v01[1], v23[0], v23[1]};
                 }
