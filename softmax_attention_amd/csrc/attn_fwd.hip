@@ -23,9 +23,10 @@
 //     ordered by counted vmcnt waits and an LDS-only barrier.  Schedules
 //     (WAVES): 8 waves in two groups alternating MFMA and softmax phases over
 //     64-key tiles (prefill, D <= 128); 3 waves where wave 0 computes
-//     and the others only load (decode, D <= 128), optionally as a persistent
-//     stream-K grid that gives every workgroup an equal share of all key
-//     tiles; 4 waves that all load and compute (D = 256).
+//     and the others only load (decode, D <= 128; over FP8 pools one wave
+//     loads and two convert), optionally as a persistent stream-K grid that
+//     gives every workgroup an equal share of all key tiles; 4 waves that all
+//     load and compute (D = 256).
 //   * scores: S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}: K (from LDS) is
 //     the A operand, Q (held in registers for the whole kernel) the B operand.
 //     Each lane then holds 16 scores per 32-key block for ONE query row (its
@@ -55,9 +56,9 @@ using namespace dev;
 
 
 // Waves per SIMD the register budget is sized for: the 8-wave schedule needs
-// its two waves per SIMD, and so do two three-wave decode workgroups over FP8
-// pools on one CU; a 16-bit decode workgroup (96 KB of LDS at D = 128) and
-// the 4-wave D = 256 schedule run one workgroup per CU.
+// its two waves per SIMD, and so do two decode workgroups over FP8 pools (four
+// waves each) on one CU; a 16-bit decode workgroup (96 KB of LDS at D = 128)
+// and the 4-wave D = 256 schedule run one workgroup per CU.
 template <int D, int WAVES, bool FP8>
 constexpr int waves_per_eu() {
     return (WAVES == 8 || (WAVES == 3 && (FP8 || D < 128))) ? 2 : 1;
@@ -90,10 +91,15 @@ __device__ __forceinline__ void sched_read_ahead() {
 // looks up its own page); the last two again over FP8 E4M3FN pools.
 enum KvMode { kDense = 0, kPagedTile = 1, kPagedPiece = 2, kPagedTile8 = 3, kPagedPiece8 = 4 };
 
+// Waves of a workgroup: the schedule's WAVES, and over FP8 pools a second
+// converting wave beside them
+template <int WAVES, int KV>
+constexpr int group_waves() { return (KV == kPagedTile8 || KV == kPagedPiece8) ? WAVES + 1 : WAVES; }
+
 // CAP: logits are capped (c tanh(z / c), TileOPs "Attention Operators",
 // GQADenseFwdOp stage 6); otherwise the logit is the scaled score itself.
 template <int D, bool BF16, int KV, int WAVES, bool CAP>
-__global__ __launch_bounds__(64 * WAVES)
+__global__ __launch_bounds__((64 * group_waves<WAVES, KV>()))
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, WAVES, (KV == kPagedTile8 || KV == kPagedPiece8)>(),
                                    waves_per_eu<D, WAVES, (KV == kPagedTile8 || KV == kPagedPiece8)>())))
 void attn_fwd_kernel(const FwdParams p) {
@@ -817,14 +823,16 @@ void attn_fwd_kernel(const FwdParams p) {
         };
         if constexpr (FP8) {
         // ---- FP8 pools.  Wave 1 moves E4M3FN key and value tiles HBM -> LDS
-        // with direct loads into an S8-stage FP8 ring; wave 2 converts each
-        // landed tile into the 16-bit MFMA type, written to one of two 16-bit
-        // stages in the swizzled layout of the 16-bit tiles, so wave 0 runs
-        // the 16-bit path unchanged.  The roles stay apart: no wave reads LDS
+        // with direct loads into an S8-stage FP8 ring; waves 2 and 3 convert
+        // each landed tile, half of its pieces each, into the 16-bit MFMA type,
+        // written to one of two 16-bit stages in the swizzled layout of the
+        // 16-bit tiles, so wave 0 runs the 16-bit path unchanged.  (With one
+        // converting wave the conversion set the pace: 130 us per decode
+        // launch against 114 with two, the same bits.)  The roles stay apart: no wave reads LDS
         // while direct loads of its own are in flight (the compiler would
         // make it wait for all of them), so the stages need not be separate
         // arrays.  Step n: wave 0 computes tile n from 16-bit stage n & 1;
-        // wave 2 converts tile n + 1 (landed during step n - 1); wave 1 issues
+        // waves 2, 3 convert tile n + 1 (landed during step n - 1); wave 1 issues
         // tile n + S8 into the FP8 stage tile n left, then waits for tile
         // n + 2 -- S8 - 2 tiles stay in flight.  (Tiles of a paged call
         // follow one another: there is no padding mask.)
@@ -856,7 +864,7 @@ void attn_fwd_kernel(const FwdParams p) {
         // first row of piece e's rows (within the tile), and of its 16-row block
         auto piece_row = [](int e) { return 16 * (e / CG) + (8 / CG) * (e % CG); };
         auto piece_block = [](int e) { return 16 * (e / CG); };
-        const bool dma = wave_u == 1, conv = wave_u == 2;
+        const bool dma = wave_u == 1, conv = wave_u >= 2;
         auto issue8 = [&](int j0, int stage) __attribute__((always_inline)) {
             if (!dma) return;
             uint8_t *dk = fK[stage], *dv = fV[stage];
@@ -896,8 +904,10 @@ void attn_fwd_kernel(const FwdParams p) {
         auto convert8 = [&](int stage, uint8_t *dk, uint8_t *dv) __attribute__((always_inline)) {
             if (!conv) return;
             const uint8_t *fk = fK[stage], *fv = fV[stage];
+            const int half = wave_u - 2;  // this converting wave's half of the pieces
 #pragma unroll
-            for (int e = 0; e < PC8; ++e) {
+            for (int e2 = 0; e2 < PC8 / 2; ++e2) {
+                const int e = half * (PC8 / 2) + e2;
                 const u32x4 kw = *(const u32x4 *)(fk + e * 1024 + 16 * lane);
                 const u32x4 vw = *(const u32x4 *)(fv + e * 1024 + 16 * lane);
 #pragma unroll
@@ -1155,7 +1165,7 @@ void attn_fwd_kernel(const FwdParams p) {
 
 template <int D, bool BF16, int KV, int WAVES, bool CAP>
 hipError_t launch_one(const FwdParams &p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, KV, WAVES, CAP>), dim3(grid), dim3(64 * WAVES),
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, KV, WAVES, CAP>), dim3(grid), dim3(64 * group_waves<WAVES, KV>()),
                        0, stream, p);
     return hipGetLastError();
 }
@@ -1164,7 +1174,7 @@ template <int D, bool BF16, int KV, int WAVES, bool CAP>
 int blocks_per_cu() {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, attn_fwd_kernel<D, BF16, KV, WAVES, CAP>, 64 * WAVES, 0) != hipSuccess)
+            &n, attn_fwd_kernel<D, BF16, KV, WAVES, CAP>, 64 * group_waves<WAVES, KV>(), 0) != hipSuccess)
         return 0;
     return n;
 }
