@@ -13,10 +13,15 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmiattn.so")
-# (source, extra defines): attn_fwd.hip is compiled once per (head dim,
-# logit kind) pair, each unit holding that pair's kernels, so the units build
-# in parallel
-UNITS = [("attn_fwd.hip", [f"-DMIATTN_KD={d}", f"-DMIATTN_KCAP={c}"])
+# (source, extra flags): attn_fwd.hip is compiled once per (head dim, logit
+# kind) pair, each unit holding that pair's kernels, so the units build in
+# parallel.  The D = 256 kernels keep their MFMA results in vector registers:
+# with the compiler's default (accumulation registers) their 128 accumulators
+# were copied between register files around every tile (~1800 copies per
+# kernel; kernel 574 -> 470 us on the wide-group chunked prefill), while the
+# same choice made the D <= 128 decode and the backward slower.
+_VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+UNITS = [("attn_fwd.hip", [f"-DMIATTN_KD={d}", f"-DMIATTN_KCAP={c}"] + (_VGPR_MFMA if d == 256 else []))
          for d in (64, 128, 256) for c in (0, 1)] + [("lse_merge.hip", []), ("kv_write.hip", []),
                                                   ("attn_bwd.hip", []), ("miattn.hip", [])]
 SOURCES = sorted({u[0] for u in UNITS})
