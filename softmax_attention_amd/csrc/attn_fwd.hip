@@ -1192,7 +1192,7 @@ int decode_blocks(const FwdParams &p, bool bf16, bool paged) {
                         : blocks_per_cu<D, false, kPagedPiece8, W, CAP>();
         }
     }
-    if (p.k_scale != nullptr) return 0;  // FP8 pools: the three-wave schedule only
+    if (p.k_scale != nullptr) return 0;  // FP8 pools: the decode (WAVES = 3) schedule only
     if (!paged)
         return bf16 ? blocks_per_cu<D, true, kDense, W, CAP>()
                     : blocks_per_cu<D, false, kDense, W, CAP>();
@@ -1218,7 +1218,7 @@ hipError_t launch_w(const FwdParams &p, bool bf16, bool paged, int grid, hipStre
             return tile ? launch_kv<D, WAVES, kPagedTile8, CAP>(p, bf16, grid, stream)
                         : launch_kv<D, WAVES, kPagedPiece8, CAP>(p, bf16, grid, stream);
     }
-    if (p.k_scale != nullptr) return hipErrorInvalidValue;  // FP8 pools: three waves only
+    if (p.k_scale != nullptr) return hipErrorInvalidValue;  // FP8 pools: the WAVES = 3 schedule only
     if (!paged) return launch_kv<D, WAVES, kDense, CAP>(p, bf16, grid, stream);
     if (tile)
         return launch_kv<D, WAVES, kPagedTile, CAP>(p, bf16, grid, stream);

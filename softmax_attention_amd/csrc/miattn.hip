@@ -382,10 +382,10 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     p.rows = p.Sq * p.G;
     // D <= 128: the 8-wave ping-pong schedule for prefill, a three-wave
     // streaming workgroup (one computing, two loading) for decode-shaped calls
-    // (all packed rows in one MFMA column block) and for FP8 pools; D = 256:
-    // the 4-wave streaming schedule.
+    // (all packed rows in one MFMA column block) and for FP8 pools (there one
+    // loading and two converting waves); D = 256: the 4-wave streaming schedule.
     int waves = D == 256 ? 4 : (p.rows > miattn::kRowsPerWave ? 8 : 3);
-    if (p.k_scale != nullptr) waves = 3;  // FP8 pools: the three-wave schedule reads them
+    if (p.k_scale != nullptr) waves = 3;
     const int BN = miattn::keys_per_tile(D, waves, p.k_scale != nullptr);
     const int BM = miattn::rows_per_workgroup(waves);
     p.n_mblocks = (p.rows + BM - 1) / BM;

@@ -75,6 +75,14 @@ def test_fp8_decode_streamk():
     fp8_case([1] * len(lens), lens, 32, 8, 128, 64, seed=300, what="decode")
 
 
+@pytest.mark.parametrize("D,page", [(128, 16), (64, 64), (64, 16)])
+def test_fp8_decode_streamk_head_dims_and_pages(D, page):
+    # each 1 KB piece of an FP8 tile holds rows r and r + 8 of one aligned
+    # 16-row block: with 16-key pages a piece still lies in one page
+    lens = [1, 17, 0, 64, 65, 1000, 513, 2047, 300, 31]
+    fp8_case([1] * len(lens), lens, 16, 4, D, page, seed=304 + D + page, what=f"decode D{D} p{page}")
+
+
 def test_fp8_decode_split_plan_d64_fp16_small_pages():
     lens = [1, 0, 64, 65, 1000, 513, 2047, 300]
     fp8_case([1] * len(lens), lens, 8, 2, 64, 16, dtype=torch.float16, split_keys=128,
