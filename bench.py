@@ -546,7 +546,12 @@ def main():
         f"{achieved:.1f} TFLOP/s, clock {clk}")
 
     dev_facts = device_facts()
-    dev_facts["clock_during_prefill"] = clk
+    # amdsmi's current graphics clock, sampled every 2 ms while the prefill
+    # ran; its readings (a mean near 1 GHz with dips to a few hundred MHz on
+    # this part) do not match the busy clock the counters give over the
+    # kernels (GRBM_GUI_ACTIVE per XCD / kernel time: 2.1-2.5 GHz in the
+    # rocprofv3 counter passes), which is the figure to use
+    dev_facts["amdsmi_gfx_clock_during_prefill"] = clk
     line = {
         "metric": METRIC,
         "value": value,
