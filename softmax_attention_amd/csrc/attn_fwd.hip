@@ -22,11 +22,12 @@
 //     straight into LDS ring stages with buffer_load ... lds (no registers),
 //     ordered by counted vmcnt waits and an LDS-only barrier.  Schedules
 //     (WAVES): 8 waves in two groups alternating MFMA and softmax phases over
-//     64-key tiles (prefill, D <= 128); 3 waves where wave 0 computes
+//     16 KB tiles (prefill, D <= 128); 3 waves where wave 0 computes
 //     and the others only load (decode, D <= 128; over FP8 pools one wave
 //     loads and two convert), optionally as a persistent stream-K grid that
 //     gives every workgroup an equal share of all key tiles; 4 waves that all
-//     load and compute (D = 256).
+//     load and compute over 32-key tiles (D = 256, and dense prefill at
+//     D = 64, several workgroups per CU).
 //   * scores: S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16}: K (from LDS) is
 //     the A operand, Q (held in registers for the whole kernel) the B operand.
 //     Each lane then holds 16 scores per 32-key block for ONE query row (its
@@ -58,10 +59,15 @@ using namespace dev;
 // Waves per SIMD the register budget is sized for: the 8-wave schedule needs
 // its two waves per SIMD, and so do two decode workgroups over FP8 pools (four
 // waves each) on one CU; a 16-bit decode workgroup (96 KB of LDS at D = 128)
-// and the 4-wave D = 256 schedule run one workgroup per CU.
+// and the 4-wave D = 256 schedule run one workgroup per CU.  The 4-wave
+// schedule at D = 64 (32 KB of LDS) is held to three waves' registers per
+// SIMD, so that several workgroups share a CU and the hardware interleaves
+// their softmax and MFMA work: on the key-padding MHA (D = 64, fp16) this ran
+// 85 -> 80 us against the 8-wave ping-pong, whose softmax phase there is about
+// 2.7 times its MFMA phase.
 template <int D, int WAVES, bool FP8>
 constexpr int waves_per_eu() {
-    return (WAVES == 8 || (WAVES == 3 && (FP8 || D < 128))) ? 2 : 1;
+    return (WAVES == 4 && D == 64) ? 3 : (WAVES == 8 || (WAVES == 3 && (FP8 || D < 128))) ? 2 : 1;
 }
 
 #ifndef MIATTN_READ_AHEAD
@@ -305,10 +311,22 @@ void attn_fwd_kernel(const FwdParams p) {
                 const float e0 = fast_exp2(arg(sc[t][8 * u + 2 * e]));
                 const float e1 = fast_exp2(arg(sc[t][8 * u + 2 * e + 1]));
                 packed[e] = pack_half2<BF16>(e0, e1);
-                if (e & 1)
-                    rs1 = add_pair<BF16>(packed[e], rs1);
-                else
-                    rs0 = add_pair<BF16>(packed[e], rs0);
+                // For bf16 the denominator sums P in FP32 before rounding: in
+                // a row dominated by one key, that key's P (up to 2^kLazy)
+                // rounded to bf16 (8 significant bits) would carry up to 2^-8
+                // of relative error into l and the lse.  fp16 (11 bits, error
+                // <= 2^-11) sums the rounded pair with one dot product.
+                if constexpr (BF16) {
+                    if (e & 1)
+                        rs1 += e0 + e1;
+                    else
+                        rs0 += e0 + e1;
+                } else {
+                    if (e & 1)
+                        rs1 = add_pair<BF16>(packed[e], rs1);
+                    else
+                        rs0 = add_pair<BF16>(packed[e], rs0);
+                }
             }
             pb[kk] = __builtin_bit_cast(vec8, packed);
         }
@@ -682,7 +700,12 @@ void attn_fwd_kernel(const FwdParams p) {
         f32x16 sc[NT];
         vec8 pb[PSTEPS];
         float corr_pending = 1.f;
+        // The wave in its MFMA phase issues at raised priority, so that the
+        // matrix core is fed first and the other wave's softmax fills the
+        // remaining issue cycles (measured 293 -> 289 us on the causal GQA
+        // prefill).
         auto mma_phase = [&](int cur, int prev, const uint8_t *sk, const uint8_t *sv) __attribute__((always_inline)) {
+            __builtin_amdgcn_s_setprio(1);
             const bool do_qk = sees(cur);
             const bool do_pv = prev >= 0 && sees(prev);
             if (do_pv && corr_pending != 1.f) {
@@ -702,6 +725,7 @@ void attn_fwd_kernel(const FwdParams p) {
                 pv(sv, pb);
                 sched_read_ahead<2 * DT * PSTEPS, DT * PSTEPS>();
             }
+            __builtin_amdgcn_s_setprio(0);
         };
         auto softmax_phase = [&](int tile, uint64_t lo, uint64_t hi) __attribute__((always_inline)) {
             if (!(tile >= 0 && sees(tile))) return;
@@ -1228,13 +1252,16 @@ hipError_t launch_w(const FwdParams &p, bool bf16, bool paged, int grid, hipStre
 }  // namespace
 
 // Schedules per head dimension: D <= 128 has the 8-wave prefill schedule and
-// the 3-wave decode schedule; D = 256 the 4-wave streaming schedule.
+// the 3-wave decode schedule, D = 64 also the 4-wave streaming schedule for
+// dense prefill; D = 256 the 4-wave streaming schedule.
 template <int D, bool CAP>
 hipError_t launch_attn_fwd_dc(const FwdParams &p, bool bf16, bool paged, int waves, int grid,
                               hipStream_t stream) {
     if constexpr (D == 256) {
         if (waves == 4) return launch_w<256, 4, CAP>(p, bf16, paged, grid, stream);
     } else {
+        if constexpr (D == 64)
+            if (waves == 4 && !paged) return launch_kv<D, 4, kDense, CAP>(p, bf16, grid, stream);
         if (waves == 8) return launch_w<D, 8, CAP>(p, bf16, paged, grid, stream);
         if (waves == 3) return launch_w<D, 3, CAP>(p, bf16, paged, grid, stream);
     }

@@ -20,10 +20,11 @@ constexpr int kRowsPerWave = 32;  // one 32x32 MFMA column block
 //     alternate, phase by phase, between an MFMA phase (QK^T of one tile and
 //     P.V of the previous one) and a softmax phase, so each SIMD always has
 //     one wave feeding the matrix core while the other runs VALU work
-//     ("ping-pong"); used for D <= 128 prefill.
+//     ("ping-pong"); used for D <= 128 prefill (paged only at D = 64).
 //   streaming (3 waves for decode-shaped calls with D <= 128 -- wave 0
-//     computes, waves 1 and 2 issue all loads -- and 4 waves for D = 256):
-//     each step computes one tile while later tiles load.
+//     computes, waves 1 and 2 issue all loads -- and 4 waves for D = 256 and
+//     for dense prefill at D = 64): each step computes one tile while later
+//     tiles load.
 constexpr int rows_per_workgroup(int waves) {
     return waves == 3 ? kRowsPerWave : kRowsPerWave * waves;
 }

@@ -98,6 +98,8 @@ constexpr int kSkPieceMax = 64;  // largest stream-K piece weight, in key tiles
 // six tiles' worth of streaming: the plan weighs each piece that much, so a
 // workgroup that starts more pieces gets fewer tiles.
 constexpr int kSkPieceDefault = 6;
+// Fewest key tiles a planned (not forced) split of a prefill-shaped call holds.
+constexpr int64_t kMinSplitTiles = 8;
 int g_sk_piece = kSkPieceDefault;
 
 int compute_units(int dev) {
@@ -380,11 +382,12 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
 
     p.G = p.Hq / p.Hkv;
     p.rows = p.Sq * p.G;
-    // D <= 128: the 8-wave ping-pong schedule for prefill, a three-wave
-    // streaming workgroup (one computing, two loading) for decode-shaped calls
-    // (all packed rows in one MFMA column block) and for FP8 pools (there one
+    // D <= 128: the 8-wave ping-pong schedule for prefill (at D = 64 over dense
+    // K/V the 4-wave streaming schedule instead), a three-wave streaming
+    // workgroup (one computing, two loading) for decode-shaped calls (all
+    // packed rows in one MFMA column block) and for FP8 pools (there one
     // loading and two converting waves); D = 256: the 4-wave streaming schedule.
-    int waves = D == 256 ? 4 : (p.rows > miattn::kRowsPerWave ? 8 : 3);
+    int waves = D == 256 ? 4 : (p.rows > miattn::kRowsPerWave ? ((D == 64 && !paged) ? 4 : 8) : 3);
     if (p.k_scale != nullptr) waves = 3;
     const int BN = miattn::keys_per_tile(D, waves, p.k_scale != nullptr);
     const int BM = miattn::rows_per_workgroup(waves);
@@ -460,6 +463,9 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
             tiles_per = (span_tiles + want - 1) / want;
         }
     }
+    // (a planned split holds at least kMinSplitTiles key tiles: shorter ones
+    // cost more in partial stores and the merge launch than they balance)
+    if (split_keys <= 0 && tiles_per < kMinSplitTiles) tiles_per = kMinSplitTiles;
     if (tiles_per < 1) tiles_per = 1;
     if (tiles_per > cap_tiles) tiles_per = cap_tiles;
     const int64_t n_splits = (cap_tiles + tiles_per - 1) / tiles_per;

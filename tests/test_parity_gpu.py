@@ -70,6 +70,30 @@ def test_tiny_workload_full():
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
+def test_lse_of_a_row_dominated_by_one_key(D):
+    # Every row sees one key at score 0 in the first key tile, one key at
+    # score 3.46875 (2^(3.46875 log2 e) = 32.097 relative to the first tile's
+    # max, below the lazy-max threshold, so that P is not 1) in the second,
+    # and keys at -30 elsewhere.  Rounded to bf16, P = 32.097 becomes 32: a
+    # denominator of rounded P would be 33 instead of 33.097 and the lse off
+    # by 2.9e-3, beyond the 2e-3 bound.
+    Skv, Sq = 260, 70
+    q = torch.zeros(1, Sq, 2, D)
+    q[..., 0] = 1.0
+    b = torch.full((Skv,), -30.0)
+    b[0] = 0.0
+    b[130] = 3.46875
+    k = torch.zeros(1, Skv, 1, D)
+    k[0, :, 0, 0] = b
+    v = workloads.dense_inputs(1, 1, Skv, 1, 1, D, seed=41)[2]
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    say(f"row dominated by one key D={D}")
+    o, lse = run_dense(q, k, v, scale=1.0, causal=False)
+    o_ref, lse_ref = oracle.attn_dense(q, k, v, scale=1.0, causal=False)
+    check_full(o, lse, o_ref, lse_ref, f"dominant key D={D}")
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 def test_dense_causal_gqa_ragged(D, dtype):
     # 300 rows x 4 heads = 1200 packed rows -> 10 row blocks, a ragged last one;

@@ -144,9 +144,14 @@ def test_fp8_append_writes_quantized_and_reads_back(causal, cap):
     vp = fp8_codes((n_phys, page_size, Hkv, D), 309)
     tq = sum(sq)
     q, kn, vn = workloads.dense_inputs(1, tq, tq, Hq, Hkv, D, seed=310)
-    q, kn, vn = q[0], kn[0] * 3, vn[0] * 3
+    # Values stay within |V| <= 448 vs = 2.24: with P rounded to bf16 (unit
+    # roundoff u = 2^-8) the output can be off by about u max|V|, which the
+    # bound's absolute term (1e-2) covers only up to |V| = 2.56.  (The new
+    # values, 0.75 N(0, 1) at scale 0.005, use the same code range as
+    # 3 N(0, 1) at scale 0.02.)
+    q, kn, vn = q[0], kn[0] * 3, vn[0] * 0.75
     cu = torch.tensor(np.concatenate([[0], np.cumsum(sq)]), dtype=torch.int32)
-    ks, vs = 0.05, 0.02
+    ks, vs = 0.05, 0.005
     k_s, v_s = scales(ks, vs)
     kd, vd = kp.to(DEV), vp.to(DEV)
     o, lse = mi.attn_fwd_paged_append(q.to(DEV), kn.to(DEV), vn.to(DEV), kd, vd,
