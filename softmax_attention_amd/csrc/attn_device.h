@@ -300,6 +300,13 @@ __device__ __forceinline__ float add_pair(uint32_t pk, float acc) {
 // arithmetic and saves rescaling O for almost every tile.
 constexpr float kLazy = 8.0f;
 
+// Unmasked tiles take their exponentials against the running max without
+// forming their own max first; the max is formed (and the running max
+// raised) only for a tile in which some lane's sum of exponentials exceeds
+// this (so that every P <= 2^24, which keeps l and the FP32 output sums far
+// from overflow for any |V| up to 2^70).
+constexpr float kFastSum = 16777216.0f;  // 2^24
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // in bits 6:4, lgkmcnt in bits 11:8; a field at its maximum does not wait).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }

@@ -236,8 +236,9 @@ void attn_fwd_kernel(const FwdParams p) {
     };
 
     // ---- online softmax of one tile's scores: masks (MASKED tiles only), the
-    // lazy max update, P rounded to 16 bits as the B operand of P.V, and the
-    // running denominator.  Branch-free, so that the scheduler can interleave
+    // lazy max update (unmasked tiles: only when their exponentials against
+    // the running max would leave the range kFastSum allows), P rounded to 16
+    // bits as the B operand of P.V, and the running denominator.  Branch-free, so that the scheduler can interleave
     // it with the next tile's QK^T MFMAs.  Returns the factor the output
     // accumulator must be multiplied by (1 when the max did not move).
     auto softmax = [&](auto masked_tag, int j0, uint64_t mlo, uint64_t mhi, f32x16 (&sc)[NT],
@@ -265,6 +266,73 @@ void attn_fwd_kernel(const FwdParams p) {
                 }
             }
         }
+        // The tile's exponentials against offset m_off (the running max, or
+        // 0 while it is -inf), rounded to 16 bits into pb; returns this
+        // lane's part of their sum.
+        auto exps = [&](const float m_off) __attribute__((always_inline)) -> float {
+            // exp2 argument of raw score s: the logit minus the running max
+            const float cap_off = cap_k2 - m_off;
+            auto arg = [&](float s) __attribute__((always_inline)) -> float {
+                if constexpr (CAP) {
+                    // capped logit in log2 units: cap_k2 tanh(x) with
+                    // tanh(x) = 1 - 2 / (e^{2x} + 1), which needs no sign
+                    // split (e^{2x} -> 0 gives -1, -> inf gives 1)
+                    const float r = __builtin_amdgcn_rcpf(fast_exp2(s * cap_x) + 1.f);
+                    const float a = __builtin_fmaf(r, -2.f * cap_k2, cap_off);
+                    // a hidden key (s = -inf) would get r = 1, a finite logit
+                    return (MASKED && s == -INFINITY) ? -INFINITY : a;
+                } else {
+                    return __builtin_fmaf(s, c, -m_off);
+                }
+            };
+            float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < PSTEPS; ++kk) {
+                const int t = kk >> 1, u = kk & 1;
+                u32x4 packed;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float e0 = fast_exp2(arg(sc[t][8 * u + 2 * e]));
+                    const float e1 = fast_exp2(arg(sc[t][8 * u + 2 * e + 1]));
+                    packed[e] = pack_half2<BF16>(e0, e1);
+                    // For bf16 the denominator sums P in FP32 before rounding:
+                    // in a row dominated by one key, that key's P rounded to
+                    // bf16 (8 significant bits) would carry up to 2^-8 of
+                    // relative error into l and the lse.  fp16 (11 bits,
+                    // error <= 2^-11) sums the rounded pair with one dot product.
+                    if constexpr (BF16) {
+                        if (e & 1)
+                            rs1 += e0 + e1;
+                        else
+                            rs0 += e0 + e1;
+                    } else {
+                        if (e & 1)
+                            rs1 = add_pair<BF16>(packed[e], rs1);
+                        else
+                            rs0 = add_pair<BF16>(packed[e], rs0);
+                    }
+                }
+                pb[kk] = __builtin_bit_cast(vec8, packed);
+            }
+            return rs0 + rs1;
+        };
+
+        if constexpr (!MASKED) {
+            // An unmasked tile first takes its exponentials against the
+            // running max as it stands, without forming the tile's max: the
+            // max only guards the exponentials' range, so as long as every
+            // lane's sum stays at most kFastSum (each P at most 2^24) the
+            // result is the same in exact arithmetic and O needs no
+            // rescaling.  A row that has not seen a key (running max -inf)
+            // gets infinite exponentials, which send the tile through the
+            // max below like a sum over the limit.  (A NaN score gives a NaN
+            // sum, which passes the test and goes on into l, as below.)
+            const float rs = exps(m_run);
+            if (!__any(rs > kFastSum)) {
+                l_run += rs;
+                return 1.f;
+            }
+        }
         // row max of the raw scores (the logit is increasing in the raw
         // score, capped or not, so the max logit is the logit of the max)
         float mx = -INFINITY;
@@ -273,8 +341,6 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
         mx = max_halves(mx);
-        // capped logit in log2 units: cap_k2 tanh(x) with tanh(x) = 1 - 2 / (e^{2x} + 1),
-        // which needs no sign split (e^{2x} -> 0 gives -1, -> inf gives 1)
         float tile_max;
         if constexpr (CAP)
             tile_max = (mx == -INFINITY)
@@ -287,50 +353,8 @@ void attn_fwd_kernel(const FwdParams p) {
         const float m_new = raise ? fmaxf(m_run, tile_max) : m_run;
         const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
         m_run = m_new;
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        // exp2 argument of raw score s: the logit minus the running max
-        const float cap_off = cap_k2 - m_use;
-        auto arg = [&](float s) __attribute__((always_inline)) -> float {
-            if constexpr (CAP) {
-                const float r = __builtin_amdgcn_rcpf(fast_exp2(s * cap_x) + 1.f);
-                const float a = __builtin_fmaf(r, -2.f * cap_k2, cap_off);
-                // a hidden key (s = -inf) would get r = 1, a finite logit
-                return (MASKED && s == -INFINITY) ? -INFINITY : a;
-            } else {
-                return __builtin_fmaf(s, c, -m_use);
-            }
-        };
-
-        float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < PSTEPS; ++kk) {
-            const int t = kk >> 1, u = kk & 1;
-            u32x4 packed;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float e0 = fast_exp2(arg(sc[t][8 * u + 2 * e]));
-                const float e1 = fast_exp2(arg(sc[t][8 * u + 2 * e + 1]));
-                packed[e] = pack_half2<BF16>(e0, e1);
-                // For bf16 the denominator sums P in FP32 before rounding: in
-                // a row dominated by one key, that key's P (up to 2^kLazy)
-                // rounded to bf16 (8 significant bits) would carry up to 2^-8
-                // of relative error into l and the lse.  fp16 (11 bits, error
-                // <= 2^-11) sums the rounded pair with one dot product.
-                if constexpr (BF16) {
-                    if (e & 1)
-                        rs1 += e0 + e1;
-                    else
-                        rs0 += e0 + e1;
-                } else {
-                    if (e & 1)
-                        rs1 = add_pair<BF16>(packed[e], rs1);
-                    else
-                        rs0 = add_pair<BF16>(packed[e], rs0);
-                }
-            }
-            pb[kk] = __builtin_bit_cast(vec8, packed);
-        }
-        l_run = __builtin_fmaf(l_run, corr, rs0 + rs1);
+        const float rs = exps((m_new == -INFINITY) ? 0.f : m_new);
+        l_run = __builtin_fmaf(l_run, corr, rs);
         return corr;
     };
 
