@@ -7,8 +7,10 @@ with inputs resident in HBM.  The same line carries:
   roofline      the attention kernel's achieved rate against the dense bf16
                 MFMA peak (its average duration from HIP events recorded by
                 the library around each launch, on the launch stream);
-  device        compute units and the GPU clock sampled (amdsmi) while the
-                prefill's warm-up and timed calls ran;
+  device        compute units, the published peaks, and the busy clock the
+                rocprofv3 counters give over the prefill kernel (GRBM_GUI_ACTIVE
+                per XCD / kernel time, from the committed counter record,
+                while the kernel sources match it);
   paged_decode  KV bytes/s of the paged decode workload (B=64, Sq=1, Hq=32,
                 Hkv=8, D=128, page 64, lengths U[512, 8192]) against HBM peak,
                 over whole calls (attention kernel + LSE merge) issued back to
@@ -38,7 +40,6 @@ import argparse
 import json
 import os
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -108,70 +109,16 @@ def kv_bytes(kv_lens, Hkv, D, elem_bytes=2):
 # ---------------------------------------------------------------- device facts
 
 
-class ClockSampler:
-    """Samples the GPU's current graphics clock (amdsmi) every few ms while
-    active; best effort: reports the reason when the clock cannot be read."""
-
-    def __init__(self):
-        self.samples = []
-        self.error = None
-        self._h = None
-        self._stop = threading.Event()
-        self._thread = None
-        try:
-            import amdsmi
-            import torch
-            pr = torch.cuda.get_device_properties(0)
-            bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
-            amdsmi.amdsmi_init()
-            self._amdsmi = amdsmi
-            self._h = amdsmi.amdsmi_get_processor_handle_from_bdf(bdf)
-            self._read()
-        except Exception as e:  # noqa: BLE001 -- the figure is optional
-            self.error = f"{type(e).__name__}: {e}"[:160]
-            self._h = None
-
-    def _read(self):
-        info = self._amdsmi.amdsmi_get_clock_info(self._h, self._amdsmi.AmdSmiClkType.GFX)
-        return float(info["clk"])
-
-    def _loop(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self._read())
-            except Exception as e:  # noqa: BLE001
-                self.error = f"{type(e).__name__}: {e}"[:160]
-                return
-            time.sleep(0.002)
-
-    def __enter__(self):
-        self.samples = []
-        if self._h is not None:
-            self._stop.clear()
-            self._thread = threading.Thread(target=self._loop, daemon=True)
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
-            self._thread = None
-
-    def summary(self):
-        if not self.samples:
-            return {"mean_mhz": None, "samples": 0, "error": self.error}
-        s = sorted(self.samples)
-        return {"mean_mhz": sum(s) / len(s), "min_mhz": s[0], "max_mhz": s[-1],
-                "samples": len(s)}
-
-
 def device_facts():
     import torch
     pr = torch.cuda.get_device_properties(0)
     return {"name": pr.name, "arch": pr.gcnArchName, "compute_units": pr.multi_processor_count,
             "peak_bf16_tflops": PEAK_BF16_TFLOPS, "peak_hbm_gbs": PEAK_HBM_GBS,
-            "peak_basis": "AMD's published MI355X figures (256 CU, 2.4 GHz; HBM3E 8 TB/s)"}
+            "peak_basis": "AMD's published MI355X figures (256 CU, 2.4 GHz; HBM3E 8 TB/s)",
+            "busy_clock_ghz": measured_traffic("prefill", "busy_clock_ghz"),
+            "busy_clock_basis": "GRBM_GUI_ACTIVE per XCD / the prefill kernel's average "
+                                "duration, rocprofv3 counter pass of this bench "
+                                "(profiles/traffic.json; null once the kernel changed)"}
 
 
 # ---------------------------------------------------------------- timing helpers
@@ -225,7 +172,7 @@ def med(xs):
 # ---------------------------------------------------------------- legs
 
 
-def time_prefill(mi, w, steps, warmup, clock):
+def time_prefill(mi, w, steps, warmup):
     import torch
     dev = "cuda:0"
     q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
@@ -233,15 +180,14 @@ def time_prefill(mi, w, steps, warmup, clock):
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     call = lambda i: mi.attn_fwd_dense(q, k, v, scale=w.scale, causal=True, out=o, lse=lse)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with clock:  # sampled over the warm-up (>= 0.5 s of calls) and the timed calls
-        n_warm = warm(call, warmup)
-        mi.profile_start()
-        start.record()
-        for i in range(steps):
-            call(i)
-        end.record()
-        torch.cuda.synchronize()
-        prof = mi.profile_stop()
+    n_warm = warm(call, warmup)
+    mi.profile_start()
+    start.record()
+    for i in range(steps):
+        call(i)
+    end.record()
+    torch.cuda.synchronize()
+    prof = mi.profile_stop()
     total_ms = start.elapsed_time(end)
     return total_ms / steps, prof["attn_ms"] / max(prof["attn_launches"], 1), n_warm
 
@@ -534,24 +480,16 @@ def main():
         print(json.dumps(time_other_configs(mi, max(args.steps, 50))), flush=True)
         return
 
-    clock = ClockSampler()
     w = workloads.make(2)
     flops = 4.0 * w.D * visible_pairs(w.B, w.Hq, w.Sq, [w.Skv] * w.B, True)
     log(f"prefill {w.name}: {flops / 1e9:.1f} GFLOP per call")
-    ms_step, ms_kernel, n_warm = time_prefill(mi, w, args.steps, args.warmup, clock)
+    ms_step, ms_kernel, n_warm = time_prefill(mi, w, args.steps, args.warmup)
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (ms_kernel * 1e-3) / 1e12
-    clk = clock.summary()
     log(f"prefill {ms_step * 1e3:.1f} us/step, kernel {ms_kernel * 1e3:.1f} us, "
-        f"{achieved:.1f} TFLOP/s, clock {clk}")
+        f"{achieved:.1f} TFLOP/s")
 
     dev_facts = device_facts()
-    # amdsmi's current graphics clock, sampled every 2 ms while the prefill
-    # ran; its readings (a mean near 1 GHz with dips to a few hundred MHz on
-    # this part) do not match the busy clock the counters give over the
-    # kernels (GRBM_GUI_ACTIVE per XCD / kernel time: 2.1-2.5 GHz in the
-    # rocprofv3 counter passes), which is the figure to use
-    dev_facts["amdsmi_gfx_clock_during_prefill"] = clk
     line = {
         "metric": METRIC,
         "value": value,
