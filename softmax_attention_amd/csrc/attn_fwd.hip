@@ -67,7 +67,9 @@ using namespace dev;
 // 2.7 times its MFMA phase.
 template <int D, int WAVES, bool FP8>
 constexpr int waves_per_eu() {
-    return (WAVES == 4 && D == 64) ? 3 : (WAVES == 8 || (WAVES == 3 && (FP8 || D < 128))) ? 2 : 1;
+    return WAVES == kPairWaves ? 1
+           : (WAVES == 4 && D == 64) ? 3
+           : (WAVES == 8 || (WAVES == 3 && (FP8 || D < 128))) ? 2 : 1;
 }
 
 #ifndef MIATTN_READ_AHEAD
@@ -100,7 +102,9 @@ enum KvMode { kDense = 0, kPagedTile = 1, kPagedPiece = 2, kPagedTile8 = 3, kPag
 // Waves of a workgroup: the schedule's WAVES, and over FP8 pools a second
 // converting wave beside them
 template <int WAVES, int KV>
-constexpr int group_waves() { return (KV == kPagedTile8 || KV == kPagedPiece8) ? WAVES + 1 : WAVES; }
+constexpr int group_waves() {
+    return WAVES == kPairWaves ? 4 : (KV == kPagedTile8 || KV == kPagedPiece8) ? WAVES + 1 : WAVES;
+}
 
 // CAP: logits are capped (c tanh(z / c), TileOPs "Attention Operators",
 // GQADenseFwdOp stage 6); otherwise the logit is the scaled score itself.
@@ -117,23 +121,29 @@ void attn_fwd_kernel(const FwdParams p) {
     constexpr int KVP = FP8 ? KV - 2 : KV;
     using H = Half<BF16>;
     using vec8 = typename H::vec8;
+    // Paired decode: two adjacent KV heads, waves 0 and 1 computing one each;
+    // an LDS row (and the segment loaded per key) holds both heads' DL = 2 D
+    // values.
+    constexpr bool PAIR = WAVES == kPairWaves;
+    constexpr int DL = PAIR ? 2 * D : D;           // values per LDS key row
     constexpr int BM = rows_per_workgroup(WAVES);  // packed rows per workgroup
     constexpr int BN = keys_per_tile(D, WAVES, FP8);  // keys per tile
-    constexpr int TILE_BYTES = BN * D * 2;         // one K (or V) tile
+    constexpr int TILE_BYTES = BN * DL * 2;        // one K (or V) tile
     constexpr int PIECES = TILE_BYTES / 1024;      // 1 KB direct loads per tile
     // The decode schedule (3 waves) splits the roles: wave 0 computes,
     // the other waves issue every load (one loading wave streams only about
     // half of what a CU's memory path takes).  Otherwise each wave issues an
     // equal share.
-    constexpr bool SPLIT_ROLES = WAVES == 3;
-    constexpr int LOADERS = SPLIT_ROLES ? WAVES - 1 : WAVES;
+    constexpr bool SPLIT_ROLES = WAVES == 3 || PAIR;
+    constexpr int NCOMP = PAIR ? 2 : 1;            // computing waves of the split roles
+    constexpr int LOADERS = PAIR ? 2 : SPLIT_ROLES ? WAVES - 1 : WAVES;
     constexpr int PPW = PIECES / LOADERS;          // 1 KB pieces per loading wave
     constexpr int NT = BN / 32;                    // 32-key score blocks per tile
     constexpr int KSTEPS = D / 16;                 // MFMA k-steps over D
     constexpr int DT = D / 32;                     // 32-wide d blocks of O^T
     constexpr int PSTEPS = BN / 16;                // MFMA k-steps over the tile's keys
     static_assert(PIECES % LOADERS == 0, "whole 1 KB pieces per loading wave");
-    static_assert(!FP8 || SPLIT_ROLES, "FP8 pools are read by the split-role schedule");
+    static_assert(!FP8 || (SPLIT_ROLES && !PAIR), "FP8 pools are read by the split-role schedule");
 
     // K and V rings of four stages each (128 KB of LDS with 16 KB tiles, one
     // workgroup per CU); separate arrays so that the compiler can tell a load
@@ -164,6 +174,7 @@ void attn_fwd_kernel(const FwdParams p) {
     // its row, Q, the output accumulator, the running max and denominator
     const bool has_mask = !PAGED && p.mask != nullptr;
     int my_last = -1, my_first = 0;
+    int64_t slot_head_stride = 0;  // paired stream-K: partial slots between the two heads
     vec8 qf[KSTEPS];
     f32x16 acc[DT];
     float m_run = -INFINITY;  // running (possibly stale) max, scaled log2 units
@@ -205,9 +216,13 @@ void attn_fwd_kernel(const FwdParams p) {
     //   V (transposing read): in each 16-lane group g, lane 4r+q reads row
     //   4*(g/2) + r (+8 for k-slots 4..7) of the 16-key step, d-columns
     //   32t + 16*(g%2) + 4q .. +3.
+    // (paired: computing wave w reads the half of each row that holds head
+    // kvh + w, chunks [w D / 8, (w + 1) D / 8); the swizzle only permutes a
+    // row's chunks within aligned groups of 16, so each head keeps its half)
+    const int hc = PAIR ? (wave & 1) * (D / 8) : 0;
     int k_addr[KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) k_addr[ks] = tile_off<D>(l32, 2 * ks + hl);
+    for (int ks = 0; ks < KSTEPS; ++ks) k_addr[ks] = tile_off<DL>(l32, hc + 2 * ks + hl);
     const int tr_g = lane >> 4;
     const int tr_row = 4 * (tr_g >> 1) + ((lane & 15) >> 2);
     const int tr_col = 16 * (tr_g & 1) + 4 * (lane & 3);
@@ -216,8 +231,8 @@ void attn_fwd_kernel(const FwdParams p) {
     for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int col = 32 * t + tr_col;
-            v_addr[t][h] = tile_off<D>(tr_row + 8 * h, col >> 3) + (col & 7) * 2;
+            const int col = 8 * hc + 32 * t + tr_col;
+            v_addr[t][h] = tile_off<DL>(tr_row + 8 * h, col >> 3) + (col & 7) * 2;
         }
 
     // ---- S^T = K Q^T for one tile (K from an LDS stage)
@@ -229,7 +244,7 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
                 const vec8 a = __builtin_bit_cast(
-                    vec8, *(const u32x4 *)(sk + k_addr[ks] + 32 * t * (2 * D)));
+                    vec8, *(const u32x4 *)(sk + k_addr[ks] + 32 * t * (2 * DL)));
                 sc[t] = H::mfma(a, qf[ks], sc[t]);
             }
         }
@@ -365,7 +380,7 @@ void attn_fwd_kernel(const FwdParams p) {
         for (int t = 0; t < DT; ++t)
 #pragma unroll
             for (int kk = 0; kk < PSTEPS; ++kk) {
-                const int step = 16 * kk * (2 * D);
+                const int step = 16 * kk * (2 * DL);
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_s16x4 *)(sv + v_addr[t][0] + step));
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -391,7 +406,7 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int c = 0; c < CH; ++c)
                     a[c] = __builtin_bit_cast(
-                        vec8, *(const u32x4 *)(sk + k_addr[k0 + c] + 32 * t * (2 * D)));
+                        vec8, *(const u32x4 *)(sk + k_addr[k0 + c] + 32 * t * (2 * DL)));
                 __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
 #pragma unroll
                 for (int c = 0; c < CH; ++c) sc[t] = H::mfma(a[c], qf[k0 + c], sc[t]);
@@ -407,7 +422,7 @@ void attn_fwd_kernel(const FwdParams p) {
             for (int t = 0; t < TB; ++t)
 #pragma unroll
                 for (int kk = 0; kk < PSTEPS; ++kk) {
-                    const int step = 16 * kk * (2 * D);
+                    const int step = 16 * kk * (2 * DL);
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (lds_s16x4 *)(sv + v_addr[t0 + t][0] + step));
                     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -435,18 +450,18 @@ void attn_fwd_kernel(const FwdParams p) {
     // The buffer form, unlike global_load_lds, is not a FLAT instruction: the
     // compiler then counts the LDS reads that follow (lgkmcnt(n)) instead of
     // waiting for all of them whenever a direct load is in flight.
-    constexpr int RPP = 512 / D;                                // keys per piece
+    constexpr int RPP = 512 / DL;                               // keys per piece
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);    // wave-uniform
-    const int loader = SPLIT_ROLES ? wave_u - 1 : wave_u;  // this wave's index among the loaders
-    const bool loads = !SPLIT_ROLES || wave_u >= 1;
-    const int l_dr = lane / (D / 8);   // this lane's key within a piece
-    const int l_pos = lane % (D / 8);  // this lane's 16-byte position in the row
+    const int loader = SPLIT_ROLES ? wave_u - NCOMP : wave_u;  // this wave's index among the loaders
+    const bool loads = !SPLIT_ROLES || wave_u >= NCOMP;
+    const int l_dr = lane / (DL / 8);   // this lane's key within a piece
+    const int l_pos = lane % (DL / 8);  // this lane's 16-byte position in the row
     const int64_t hstride = (int64_t)p.Hkv * D;  // elements between consecutive keys
     const int row_bytes = p.Hkv * D * 2;
     int l_chunk[PPW];  // byte offset, within its key row, of the chunk this lane fetches
 #pragma unroll
     for (int e = 0; e < PPW; ++e)
-        l_chunk[e] = 16 * (l_pos ^ swz<D>((e * LOADERS + loader) * RPP + l_dr));
+        l_chunk[e] = 16 * (l_pos ^ swz<DL>((e * LOADERS + loader) * RPP + l_dr));
     // Where a tile lies in one page (always, for dense K/V) a single buffer
     // descriptor based at the tile's first key serves all pieces and each
     // lane clamps its own key; with smaller pages each piece gets its own
@@ -522,7 +537,10 @@ void attn_fwd_kernel(const FwdParams p) {
     const int tile_begin = wg_begin >= wg_end ? wg_end : kbeg + (wg_begin - kbeg) / BN * BN;
 
     const int wrow0 = row0 + (SPLIT_ROLES ? 0 : wave * kRowsPerWave);
-    const bool wave_active = (!SPLIT_ROLES || wave == 0) && wrow0 < rows_b;
+    const bool wave_active = (!SPLIT_ROLES || wave < NCOMP) && wrow0 < rows_b;
+    // the KV head this wave's rows read (paired: kvh + the computing wave's
+    // index; loading waves keep kvh, whose Q they load but never use)
+    const int hw = kvh + ((PAIR && wave_u < NCOMP) ? wave_u : 0);
     const int wrow_last = min(rows_b, wrow0 + kRowsPerWave) - 1;
     // keys in [wave_full_begin, wave_full_end) are visible to every row of
     // this wave (mask aside); keys outside [wave_begin, wave_end) to none
@@ -545,7 +563,7 @@ void attn_fwd_kernel(const FwdParams p) {
     const int my_gh = my_row - my_i * p.G;
     my_last = !row_ok ? -1 : key_hi(my_i);
     my_first = key_lo(my_i);
-    begin_rows(p.q + ((q_row0 + my_i) * p.Hq + (int64_t)kvh * p.G + my_gh) * D, row_ok);
+    begin_rows(p.q + ((q_row0 + my_i) * p.Hq + (int64_t)hw * p.G + my_gh) * D, row_ok);
 
     // ---- key padding mask: one bit per key of a tile, wave-uniform
     const uint8_t *mrow = has_mask ? p.mask + (int64_t)b * p.Skv : nullptr;
@@ -1067,7 +1085,7 @@ void attn_fwd_kernel(const FwdParams p) {
     // or k -- makes l NaN, and the NaN goes on into o and lse)
     float inv = l_tot != 0.f ? 1.f / l_tot : 0.f;
     float lse_v = l_tot != 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-    const int my_h = kvh * p.G + my_gh;
+    const int my_h = hw * p.G + my_gh;
     if (!partial && p.sinks != nullptr) {
         // The head's sink logit joins the denominator only, used as given
         // (TileOPs "Attention Operators", GQAVarlenFwdOp / GQAPagedFwdOp): a
@@ -1110,7 +1128,8 @@ void attn_fwd_kernel(const FwdParams p) {
                 p.lse[((int64_t)b * p.Hq + my_h) * p.Sq + my_i] = lse_v;
         }
     } else {
-        store_partial(slot * p.rows + my_row, inv, lse_v);
+        // (paired: head kvh + 1's slots follow head kvh's at a fixed stride)
+        store_partial((slot + (hw - kvh) * slot_head_stride) * p.rows + my_row, inv, lse_v);
     }
 
     };
@@ -1119,20 +1138,25 @@ void attn_fwd_kernel(const FwdParams p) {
     const int units = p.B * p.Hkv * p.n_splits;
     if constexpr (SPLIT_ROLES) {
         if (p.sk_grid > 0) {
-            // Stream-K decode, by head: workgroup g serves KV head g % Hkv, and
-            // the G / Hkv workgroups of one head cut that head's sequence of
+            // Stream-K decode, by head: workgroup g serves head unit g % U (KV
+            // head g % Hkv, or the pair 2 (g % U), 2 (g % U) + 1 when paired),
+            // and the S = G / U workgroups of one unit cut its sequence of
             // (request) units -- plan weight T1, each unit its key tiles plus
             // the cost of starting a piece of it (sk_weight) -- into equal
-            // shares: share c = g / Hkv takes the weight [c T1 / S, (c+1) T1 / S)
-            // whatever the lengths, and writes one partial per unit whose tiles
-            // it touches, to slot kvh (B + S) + b + c (the merge kernel finds the
-            // slots the same way).  The Hkv workgroups g, g + 1, ... run side by
-            // side and read the same cache rows.  A unit of weight w = piece +
-            // tiles holds its tiles at weight offsets [piece, w).
+            // shares: share c = g / U takes the weight [c T1 / S, (c+1) T1 / S)
+            // whatever the lengths, and writes one partial per unit (and head)
+            // whose tiles it touches, to slot h (B + S) + b + c for head h
+            // (the merge kernel finds the slots the same way).  The U
+            // workgroups g, g + 1, ... run side by side and read the same cache
+            // rows.  A unit of weight w = piece + tiles holds its tiles at
+            // weight offsets [piece, w).
             const int g = blockIdx.x;
             const SkBatch sb = {sd, BN, p.win_left, p.sk_piece};
             int unused;
-            const int kvh = g % p.Hkv, c = g / p.Hkv, shares = p.sk_grid / p.Hkv;
+            // head units: one KV head, or a pair of adjacent heads
+            const int U = PAIR ? p.Hkv / 2 : p.Hkv;
+            const int kvh = (g % U) * (PAIR ? 2 : 1), c = g / U, shares = p.sk_grid / U;
+            slot_head_stride = p.B + shares;
             const int64_t T1 = sk_sums(sb, 0, unused);
             const int64_t s0 = (int64_t)c * T1 / shares;
             const int64_t s1 = (int64_t)(c + 1) * T1 / shares;
@@ -1161,6 +1185,8 @@ void attn_fwd_kernel(const FwdParams p) {
             return;
         }
     }
+    // (paired kernels are launched for stream-K plans only)
+    if constexpr (PAIR) return;
     // Workgroups are dispatched round-robin over the 8 XCDs; when the unit
     // count allows, consecutive workgroups of one XCD share a (batch, KV head)
     // so its K/V stays in that XCD's L2.  Causal row blocks run heaviest first.
@@ -1275,9 +1301,10 @@ hipError_t launch_w(const FwdParams &p, bool bf16, bool paged, int grid, hipStre
 
 }  // namespace
 
-// Schedules per head dimension: D <= 128 has the 8-wave prefill schedule and
-// the 3-wave decode schedule, D = 64 also the 4-wave streaming schedule for
-// dense prefill; D = 256 the 4-wave streaming schedule.
+// Schedules per head dimension: D <= 128 has the 8-wave prefill schedule, the
+// 3-wave decode schedule and the paired decode schedule, D = 64 also the
+// 4-wave streaming schedule for dense prefill; D = 256 the 4-wave streaming
+// schedule.
 template <int D, bool CAP>
 hipError_t launch_attn_fwd_dc(const FwdParams &p, bool bf16, bool paged, int waves, int grid,
                               hipStream_t stream) {
@@ -1288,6 +1315,7 @@ hipError_t launch_attn_fwd_dc(const FwdParams &p, bool bf16, bool paged, int wav
             if (waves == 4 && !paged) return launch_kv<D, 4, kDense, CAP>(p, bf16, grid, stream);
         if (waves == 8) return launch_w<D, 8, CAP>(p, bf16, paged, grid, stream);
         if (waves == 3) return launch_w<D, 3, CAP>(p, bf16, paged, grid, stream);
+        if (waves == kPairWaves) return launch_w<D, kPairWaves, CAP>(p, bf16, paged, grid, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -1296,6 +1324,7 @@ template <int D, bool CAP>
 int decode_blocks_per_cu_dc(const FwdParams &p, bool bf16, bool paged, int waves) {
     if constexpr (D <= 128) {
         if (waves == 3) return decode_blocks<D, 3, CAP>(p, bf16, paged);
+        if (waves == kPairWaves) return decode_blocks<D, kPairWaves, CAP>(p, bf16, paged);
     }
     return 0;
 }

@@ -25,8 +25,13 @@ constexpr int kRowsPerWave = 32;  // one 32x32 MFMA column block
 //     computes, waves 1 and 2 issue all loads -- and 4 waves for D = 256 and
 //     for dense prefill at D = 64): each step computes one tile while later
 //     tiles load.
+//   paired decode (WAVES = 5 in the kernel template; four waves run): the
+//     decode schedule for two adjacent KV heads at once -- waves 0 and 1
+//     compute one head each, waves 2 and 3 load both heads' rows of every key
+//     (one contiguous 4 D-byte segment instead of two 2 D-byte ones).
+constexpr int kPairWaves = 5;
 constexpr int rows_per_workgroup(int waves) {
-    return waves == 3 ? kRowsPerWave : kRowsPerWave * waves;
+    return (waves == 3 || waves == kPairWaves) ? kRowsPerWave : kRowsPerWave * waves;
 }
 
 // Keys per KV tile.  8 waves: 8192 / D keys, 16 KB per K or V tile (128 keys
@@ -38,9 +43,13 @@ constexpr int rows_per_workgroup(int waves) {
 // the paged decode 4-5 % faster than 32-key tiles with two workgroups per CU.
 // Over FP8 pools: tiles of 8 KB of 16-bit values (4096 / D keys, at least
 // one 32-key score block), so that the FP8 ring and the converted stages fit
-// two workgroups per CU.  D = 256 (4 waves): 32 keys (16 KB).
+// two workgroups per CU.  D = 256 (4 waves): 32 keys (16 KB).  Paired decode:
+// 4096 / D keys (16 KB holding both heads' rows).
 constexpr int keys_per_tile(int D, int waves, bool fp8 = false) {
-    return waves == 8 ? 8192 / D : waves == 4 ? 32 : fp8 ? (4096 / D > 32 ? 4096 / D : 32) : 64;
+    return waves == 8 ? 8192 / D
+           : waves == 4 ? 32
+           : waves == kPairWaves ? 4096 / D
+           : fp8 ? (4096 / D > 32 ? 4096 / D : 32) : 64;
 }
 
 // Per-request extents of a call, as the attention kernel, its stream-K plan
@@ -97,10 +106,11 @@ struct FwdParams {
     int q_mode;        // 0: q as given; 1: q negated (alpha < 0); 2: q zeroed (alpha == 0)
     int xcd_units;     // (batch*KV head, split) units per XCD, or 0 for linear order
     int heads_inner;   // units ordered (batch, split, KV head) instead of (batch, KV head, split)
-    // stream-K decode (split-role schedule): grid size G (a multiple of Hkv),
-    // or 0.  Workgroup g serves KV head g % Hkv, and the G / Hkv workgroups of
-    // one head split that head's key tiles, so the Hkv workgroups g, g + 1,
-    // ... read the same cache rows together
+    // stream-K decode (split-role schedules): grid size G (a multiple of U =
+    // Hkv / KV heads per workgroup), or 0.  Workgroup g serves the head unit
+    // g % U (KV head g % U, or heads 2 (g % U) and 2 (g % U) + 1 when
+    // paired), and the G / U workgroups of one unit split its key tiles, so
+    // the U workgroups g, g + 1, ... read the same cache rows together
     int sk_grid;
     // stream-K: plan weight, in key tiles, of starting a piece of a unit
     int sk_piece;
@@ -120,9 +130,10 @@ struct MergeParams {
     int B, Sq, Hq, Hkv, G, rows, n_splits, split_len;
     // stream-K decode: grid size (0 otherwise), keys per tile and the length
     // clamp the attention kernel applies (max_pages * page_size, 0 for an
-    // empty cache), the left window bound (-1: none) and the plan weight of a
-    // piece -- all as the attention kernel had them
-    int sk_grid, sk_bn, sk_cap, sk_win_left, sk_piece;
+    // empty cache), the left window bound (-1: none), the plan weight of a
+    // piece and the KV heads one workgroup served (1, or 2 when paired) --
+    // all as the attention kernel had them
+    int sk_grid, sk_bn, sk_cap, sk_win_left, sk_piece, sk_hpw;
 };
 
 // Launchers: return the hipGetLastError() status of the launch.  The

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams p) {
         T = sk_sums(sb, b, before);
         const int tiles = sk_tiles(sb, b);
         const int64_t P = before;
-        const int G = p.sk_grid / p.Hkv;
+        const int G = p.sk_grid * p.sk_hpw / p.Hkv;  // shares per KV head
         sk_g = G;
         if (tiles == 0 || T == 0) {
             n_valid = 0;

@@ -85,8 +85,8 @@ struct DeviceState {
     hipEvent_t last_use = nullptr;      // recorded on last_stream after that use
     bool used = false;
     int cus = 0;
-    // decode kernel occupancy: [D 128][bf16][paged][capped logits][FP8 pools]
-    int decode_per_cu[2][2][2][2][2] = {};
+    // decode kernel occupancy: [D 128][bf16][paged][capped logits][16-bit, FP8 pools, paired]
+    int decode_per_cu[2][2][2][2][3] = {};
 };
 
 std::mutex g_mu;
@@ -115,11 +115,13 @@ int compute_units(int dev) {
 }
 
 // Decode workgroups one CU runs at once (occupancy API, cached).
-int decode_per_cu(int dev, const miattn::FwdParams &p, int D, bool bf16, bool paged, bool cap) {
+int decode_per_cu(int dev, const miattn::FwdParams &p, int D, bool bf16, bool paged, bool cap,
+                  int waves) {
     std::lock_guard<std::mutex> lock(g_mu);
-    int &slot = g_dev[dev].decode_per_cu[D == 128][bf16][paged][cap][p.k_scale != nullptr];
+    const int variant = waves == miattn::kPairWaves ? 2 : p.k_scale != nullptr ? 1 : 0;
+    int &slot = g_dev[dev].decode_per_cu[D == 128][bf16][paged][cap][variant];
     if (slot == 0) {
-        const int n = miattn::attn_fwd_decode_blocks_per_cu(p, D, bf16, paged, 3, cap);
+        const int n = miattn::attn_fwd_decode_blocks_per_cu(p, D, bf16, paged, waves, cap);
         slot = n > 0 ? n : -1;
     }
     return slot > 0 ? slot : 1;
@@ -370,6 +372,7 @@ MergeParams merge_params(const FwdParams &p, bool paged) {
     m.split_len = p.split_len;
     m.sk_cap = (paged && p.num_pages > 0) ? (p.max_pages << p.page_shift) : 0;
     m.sk_win_left = -1;
+    m.sk_hpw = 1;
     return m;
 }
 
@@ -389,12 +392,24 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     // loading and two converting waves); D = 256: the 4-wave streaming schedule.
     int waves = D == 256 ? 4 : (p.rows > miattn::kRowsPerWave ? ((D == 64 && !paged) ? 4 : 8) : 3);
     if (p.k_scale != nullptr) waves = 3;
+    const int split_keys = g_split_keys > 0 ? g_split_keys : env_int("MIATTN_SPLIT_KEYS", 0);
+    // Decode-shaped calls over 16-bit K/V with an even number of KV heads run
+    // the paired schedule (stream-K only): one workgroup reads both heads'
+    // rows of each key as one contiguous segment (512 bytes at D = 128),
+    // which streams faster than two 256-byte segments read by two workgroups.
+    auto streamk_fits = [&](int w) {
+        const int64_t bn = miattn::keys_per_tile(D, w, p.k_scale != nullptr);
+        const int64_t ct = capacity > 0 ? (capacity + bn - 1) / bn : 1;
+        return (int64_t)p.B * (ct + kSkPieceMax) < INT_MAX;
+    };
+    if (waves == 3 && p.k_scale == nullptr && p.Hkv % 2 == 0 && D <= 128 &&
+        p.rows <= miattn::kRowsPerWave && split_keys <= 0 && streamk_fits(miattn::kPairWaves))
+        waves = miattn::kPairWaves;
     const int BN = miattn::keys_per_tile(D, waves, p.k_scale != nullptr);
     const int BM = miattn::rows_per_workgroup(waves);
     p.n_mblocks = (p.rows + BM - 1) / BM;
     const int64_t bhs = (int64_t)p.B * p.Hkv;
     const int64_t cap_tiles = capacity > 0 ? (capacity + BN - 1) / BN : 1;
-    const int split_keys = g_split_keys > 0 ? g_split_keys : env_int("MIATTN_SPLIT_KEYS", 0);
     p.sk_grid = 0;
 
     // Decode-shaped calls run stream-K: a grid of what the GPU holds at once,
@@ -403,18 +418,22 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     // workgroup waits on a long request or for a dispatch slot.  A forced
     // split length selects the split plan below instead.  (The plan's sums
     // are 32-bit: B * the weight of a unit at the capacity.)
-    if (waves == 3 && p.rows <= miattn::kRowsPerWave && split_keys <= 0 &&
-        (int64_t)p.B * (cap_tiles + kSkPieceMax) < INT_MAX) {
-        const int per_cu = decode_per_cu(dev, p, D, bf16, paged, cap);
-        // whole groups of Hkv workgroups: workgroup g serves KV head g % Hkv
-        const int G = std::max(1, compute_units(dev) * per_cu / p.Hkv) * p.Hkv;
+    if (waves == miattn::kPairWaves ||
+        (waves == 3 && p.rows <= miattn::kRowsPerWave && split_keys <= 0 &&
+         (int64_t)p.B * (cap_tiles + kSkPieceMax) < INT_MAX)) {
+        const int per_cu = decode_per_cu(dev, p, D, bf16, paged, cap, waves);
+        // whole groups of U workgroups: workgroup g serves head unit g % U (a
+        // KV head, or a pair of them)
+        const int hpw = waves == miattn::kPairWaves ? 2 : 1;
+        const int U = p.Hkv / hpw;
+        const int G = std::max(1, compute_units(dev) * per_cu / U) * U;
         p.n_mblocks = 1;
         p.n_splits = 1;
         p.split_len = 0;
         p.xcd_units = 0;
         p.heads_inner = 0;
-        // partial slot of (KV head h, request b, share c): h (B + G / Hkv) + b + c
-        const int64_t slots = bhs + G;
+        // partial slot of (KV head h, request b, share c): h (B + G / U) + b + c
+        const int64_t slots = bhs + (int64_t)G * hpw;
         void *ws = nullptr;
         miattn_status st =
             partials(src, dev, stream, (size_t)slots * p.rows * (D + 1) * sizeof(float), &ws);
@@ -432,6 +451,7 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
         m.sk_bn = BN;
         m.sk_win_left = p.win_left;
         m.sk_piece = p.sk_piece;
+        m.sk_hpw = hpw;
         e = timed_launch(1, stream, [&] { return miattn::launch_lse_merge(m, D, bf16, stream); });
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
         return partials_done(src, dev, stream);
