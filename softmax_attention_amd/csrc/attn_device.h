@@ -224,14 +224,18 @@ __device__ __forceinline__ int sk_weight(const SkBatch &s, int tiles) {
     return tiles > 0 ? tiles + s.piece : 0;
 }
 
-// inclusive prefix sum over the 64 lanes of a wave
+// inclusive prefix sum over the 64 lanes of a wave, with DPP moves (no LDS
+// round trips): shifts by 1, 2, 4 and 8 lanes within each row of 16 (a lane
+// whose source lies outside its row adds 0), then row 0's total into row 1
+// and row 2's into row 3 (row_bcast:15), then the total of rows 0-1 into
+// rows 2 and 3 (row_bcast:31)
 __device__ __forceinline__ int wave_incl_scan(int v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(v, off);
-        if (lane >= off) v += t;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return v;
 }
 
