@@ -60,15 +60,15 @@ using namespace dev;
 // its two waves per SIMD, and so do two decode workgroups over FP8 pools (four
 // waves each) on one CU; a 16-bit decode workgroup (96 KB of LDS at D = 128)
 // and the 4-wave D = 256 schedule run one workgroup per CU.  The 4-wave
-// schedule at D = 64 (32 KB of LDS) is held to three waves' registers per
-// SIMD, so that several workgroups share a CU and the hardware interleaves
-// their softmax and MFMA work: on the key-padding MHA (D = 64, fp16) this ran
+// schedule at D = 64 (24 KB of LDS) is held to four waves' registers per SIMD
+// (128), so that four workgroups share a CU and the hardware interleaves their
+// softmax and MFMA work: on the key-padding MHA (D = 64, fp16) this ran
 // 85 -> 80 us against the 8-wave ping-pong, whose softmax phase there is about
 // 2.7 times its MFMA phase.
 template <int D, int WAVES, bool FP8>
 constexpr int waves_per_eu() {
     return WAVES == kPairWaves ? 1
-           : (WAVES == 4 && D == 64) ? 3
+           : (WAVES == 4 && D == 64) ? 4
            : (WAVES == 8 || (WAVES == 3 && (FP8 || D < 128))) ? 2 : 1;
 }
 
@@ -861,8 +861,10 @@ void attn_fwd_kernel(const FwdParams p) {
         // the tile three steps ahead land in the stage the previous step
         // freed; the same counted wait as above (all but the two youngest
         // steps' loads) and one barrier per step order the ring.
-        // ring depth: three stages for the decode workgroups, four otherwise
-        constexpr int kStages = SPLIT_ROLES ? 3 : 4;
+        // ring depth: three stages for the decode workgroups and the D = 64
+        // prefill (24 KB of LDS: 77 -> 70 us on the key-padding MHA against
+        // four stages), four otherwise
+        constexpr int kStages = (SPLIT_ROLES || (WAVES == 4 && D == 64)) ? 3 : 4;
         f32x16 sc[NT];
         vec8 pb[PSTEPS];
         uint64_t lo0 = first_lo, hi0 = first_hi, lo1 = ~0ull, hi1 = ~0ull, lo2 = ~0ull,
