@@ -272,6 +272,47 @@ def test_streamk_dense_decode():
     check_full(o, lse, o_ref, lse_ref, "sk_dense")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hkv", [1, 2, 3, 6])
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_paired_and_single_head_decode(D, Hkv, page_size):
+    # an even KV head count runs the paired decode (one workgroup reads two
+    # adjacent heads' rows), an odd one the one-head decode; both against the
+    # oracle, over lengths with empty, one-key and ragged requests
+    lens = [0, 1, 33, 511, 1200, 64, 2500]
+    paged_case(len(lens), 1, 4 * Hkv, Hkv, D, lens, page_size, seed=60 + Hkv + D,
+               what=f"decode Hkv={Hkv} D={D}")
+
+
+def rising_scores_case(Sq, Skv, Hq, Hkv, D, step, what):
+    # q = e_0, k_j = b_j e_0 with b_j = step * (j // 64) + N(0, 0.25): every
+    # 64 keys the scores jump by `step`, so unmasked tiles whose exponentials
+    # against a running max set on earlier keys would exceed the 2^24 range
+    # take the tile max (and raise the running max), and the others do not
+    g = torch.Generator().manual_seed(70 + D)
+    q = torch.zeros(1, Sq, Hq, D)
+    q[..., 0] = 1.0
+    b = step * (torch.arange(Skv) // 64).float() + 0.5 * torch.randn(Skv, generator=g)
+    k = torch.zeros(1, Skv, Hkv, D)
+    k[0, :, :, 0] = b[:, None]
+    k[0, :, :, 1:] = 0.1 * torch.randn(Skv, Hkv, D - 1, generator=g)
+    v = torch.randn(1, Skv, Hkv, D, generator=g)
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    say(f"rising scores {what} Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv} D={D} step={step}")
+    o, lse = run_dense(q, k, v, scale=1.0, causal=False)
+    o_ref, lse_ref = oracle.attn_dense(q, k, v, scale=1.0, causal=False)
+    check_full(o, lse, o_ref, lse_ref, f"rising {what}")
+
+
+@pytest.mark.parametrize("step", [3.0, 9.0, 40.0])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rising_scores_across_tiles(D, step):
+    # prefill-shaped (the 8-wave schedule at D = 128, the streaming ones at
+    # D = 64 and 256) and decode-shaped (stream-K) calls
+    rising_scores_case(70, 700, 2, 1, D, step, "prefill")
+    rising_scores_case(1, 1500, 8, 2, D, step, "decode")
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_paged_decode_head_dims(D):
     paged_case(4, 1, 16, 4, D, [700, 33, 1, 1500], 32, seed=22, what=f"decode_d{D}")
