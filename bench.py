@@ -535,7 +535,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": call_gbs, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": call_gbs / PEAK_HBM_GBS,
                          "traffic": measured_traffic("decode"),
-                         "kernel": "attn_fwd_kernel<128, true, 1, 3, false> (D, bf16, paged K/V, 3 waves, plain logits, stream-K) + lse_merge_kernel<128, true>",
+                         "kernel": "attn_fwd_kernel<128, true, 1, 5, false> (D, bf16, paged K/V, paired decode: two KV heads per workgroup, plain logits, stream-K) + lse_merge_kernel<128, true>",
                          "attn_kernel_avg_us": d["attn_kernel_ms"] * 1e3,
                          "attn_kernel_gbs": kern_gbs,
                          "attn_kernel_frac": kern_gbs / PEAK_HBM_GBS,

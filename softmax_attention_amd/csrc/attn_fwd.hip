@@ -145,9 +145,9 @@ void attn_fwd_kernel(const FwdParams p) {
     static_assert(PIECES % LOADERS == 0, "whole 1 KB pieces per loading wave");
     static_assert(!FP8 || (SPLIT_ROLES && !PAIR), "FP8 pools are read by the split-role schedule");
 
-    // K and V rings of four stages each (128 KB of LDS with 16 KB tiles, one
-    // workgroup per CU); separate arrays so that the compiler can tell a load
-    // into one stage from reads of another
+    // K and V rings of up to four stages each (the schedules use three or
+    // four); separate arrays so that the compiler can tell a load into one
+    // stage from reads of another
     __shared__ __attribute__((aligned(1024))) uint8_t sK0[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sV0[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sK1[TILE_BYTES];
@@ -729,13 +729,13 @@ void attn_fwd_kernel(const FwdParams p) {
         // A wave's scores go from its MFMA phase to its next softmax phase,
         // its probabilities from there to its next MFMA phase.
         //
-        // K and V have rings of four stages (128 KB of LDS at D = 128, one
+        // K and V have rings of three stages (96 KB of LDS at D = 128, one
         // workgroup per CU).  Step k reads K(k) and V(k-1) and issues the
-        // loads of K(k+3) and V(k+2) into the stages step k-1 freed, so a load
-        // has three steps to land: the L2/MALL round trip stays hidden.  Every
-        // step issues the same number of loads (pad loads for tiles past the
-        // range), so one counted wait -- all but the two youngest steps'
-        // loads -- orders the ring.
+        // loads of K(k+2) and V(k+1) into the stages step k-1 freed, so a load
+        // has two steps to land.  (Four stages, loads three steps ahead,
+        // measured 3.5 % slower, the same bits.)  Every step issues the same
+        // number of loads (pad loads for tiles past the range), so one counted
+        // wait -- all but the youngest step's loads -- orders the ring.
         static_assert(PPW == 1 || PPW == 2, "counted waits below assume 1 or 2 loads per tile");
 
         const int group = wave >> 2;
@@ -779,29 +779,28 @@ void attn_fwd_kernel(const FwdParams p) {
                 corr_pending = softmax(std::true_type{}, tile, lo, hi, sc, pb);
         };
 
-        // upcoming tiles t0 (current), t1, t2, t3 with their mask bits;
-        // tiles past the workgroup's range read as wg_end
+        // upcoming tiles t0 (current), t1, t2 with their mask bits; tiles
+        // past the workgroup's range read as wg_end
         uint64_t lo0 = ~0ull, hi0 = ~0ull, lo1 = ~0ull, hi1 = ~0ull, lo2 = ~0ull, hi2 = ~0ull,
-                 lo3 = ~0ull, hi3 = ~0ull, plo = ~0ull, phi = ~0ull;
+                 plo = ~0ull, phi = ~0ull;
         int t0 = first_tile;
         lo0 = first_lo;
         hi0 = first_hi;
         int t1 = t0 < wg_end ? find_tile(t0 + BN, lo1, hi1) : wg_end;
-        int t2 = t1 < wg_end ? find_tile(t1 + BN, lo2, hi2) : wg_end;
-        int t3 = wg_end;
+        int t2 = wg_end;
         int prev = -1;
         const bool any_tile = t0 < wg_end;
-        int32_t pg_next = 0, pg_t2 = 0;  // page entries of the next K tile and of t2
-        // one step: K(t0) in K_CUR, V(prev) in V_PREV; K(t3) -> K_NEW, V(t2) -> V_NEW.
+        int32_t pg_next = 0, pg_t1 = 0;  // page entries of the next K tile and of t1
+        // one step: K(t0) in K_CUR, V(prev) in V_PREV; K(t2) -> K_NEW, V(t1) -> V_NEW.
         // The step with t0 == wg_end only finishes P.V of the last tile; steps
-        // after it find no blockIdx.x and issue pad loads.  (A macro, expanded
+        // after it find no visible tile and issue pad loads.  (A macro, expanded
         // in the loop below: the step holds the workgroup barriers, which the
         // compiler mishandled inside a lambda -- it deleted the computation.)
 #define MIATTN_PP_STEP(K_CUR, V_PREV, K_NEW, V_NEW)                                     \
         {                                                                               \
-            t3 = t2 < wg_end ? find_tile(t2 + BN, lo3, hi3) : wg_end;                   \
-            issue_kv(t3, pg_next, K_NEW, t2, pg_t2, V_NEW);                             \
-            pg_t2 = pg_next;                                                            \
+            t2 = t1 < wg_end ? find_tile(t1 + BN, lo2, hi2) : wg_end;                   \
+            issue_kv(t2, pg_next, K_NEW, t1, pg_t1, V_NEW);                             \
+            pg_t1 = pg_next;                                                            \
             if (group == 0) /* phase A */                                               \
                 mma_phase(t0, prev, K_CUR, V_PREV);                                     \
             else                                                                        \
@@ -813,14 +812,13 @@ void attn_fwd_kernel(const FwdParams p) {
                 mma_phase(t0, prev, K_CUR, V_PREV);                                     \
             /* (the next page entry is read here: a scalar load in flight during */    \
             /* the phases would force every LDS wait there to lgkmcnt(0)) */            \
-            pg_next = tile_page(t3 + BN);                                               \
-            /* the loads issued two steps ago hold K(t1) and V(t0) */                   \
-            wait_vmcnt<4 * PPW>();                                                      \
+            pg_next = tile_page(t2 + BN);                                               \
+            /* the loads issued a step ago hold K(t1) and V(t0) */                      \
+            wait_vmcnt<2 * PPW>();                                                      \
             ring_barrier();                                                             \
             prev = t0; plo = lo0; phi = hi0;                                            \
             t0 = t1; lo0 = lo1; hi0 = hi1;                                              \
             t1 = t2; lo1 = lo2; hi1 = hi2;                                              \
-            t2 = t3; lo2 = lo3; hi2 = hi3;                                              \
         }
 
         // A workgroup without a visible tile skips the ring altogether.  Inside
@@ -828,28 +826,26 @@ void attn_fwd_kernel(const FwdParams p) {
         // which LDS array each direct load writes, and a load that might not
         // have been issued would make it wait for all of them before each read.
         if (any_tile) {
-            // prologue: steps -3, -2, -1 of loads (K(t0) with a pad V; K(t1),
-            // V(t0); K(t2), V(t1)), then wait for the first
+            // prologue: steps -2, -1 of loads (K(t0) with a pad V; K(t1),
+            // V(t0)), then wait for the first
             {
-                const int32_t g0 = tile_page(t0), g1 = tile_page(t1), g2 = tile_page(t2);
-                issue_kv(t0, g0, sK0, wg_end, g0, sV3);
+                const int32_t g0 = tile_page(t0), g1 = tile_page(t1);
+                issue_kv(t0, g0, sK0, wg_end, g0, sV2);
                 issue_kv(t1, g1, sK1, t0, g0, sV0);
-                issue_kv(t2, g2, sK2, t1, g1, sV1);
-                pg_t2 = g2;
-                pg_next = tile_page(t2 + BN);
+                pg_t1 = g1;
+                pg_next = tile_page(t1 + BN);
             }
-            wait_vmcnt<4 * PPW>();
+            wait_vmcnt<2 * PPW>();
             ring_barrier();
             // The shared arrays are named only here, in the kernel body, and
             // handed to the helpers as pointers.  The loop leaves only after a
-            // whole round of four steps: an exit between steps makes the
-            // compiler merge the ring states of all four into the loop header
+            // whole round of three steps: an exit between steps makes the
+            // compiler merge the ring states of all three into the loop header
             // and wait for every load there.
             do {
-                MIATTN_PP_STEP(sK0, sV3, sK3, sV2)  // k % 4 == 0
-                MIATTN_PP_STEP(sK1, sV0, sK0, sV3)  // k % 4 == 1
-                MIATTN_PP_STEP(sK2, sV1, sK1, sV0)  // k % 4 == 2
-                MIATTN_PP_STEP(sK3, sV2, sK2, sV1)  // k % 4 == 3
+                MIATTN_PP_STEP(sK0, sV2, sK2, sV1)  // k % 3 == 0
+                MIATTN_PP_STEP(sK1, sV0, sK0, sV2)  // k % 3 == 1
+                MIATTN_PP_STEP(sK2, sV1, sK1, sV0)  // k % 3 == 2
             } while (prev < wg_end);
             // no load may still be writing this workgroup's LDS when it exits
             wait_vmcnt<0>();
