@@ -1108,16 +1108,28 @@ void attn_fwd_kernel(const FwdParams p) {
 
     if (!partial) {
         uint16_t *orow = p.o + ((q_row0 + my_i) * p.Hq + my_h) * D;
+        // Registers 4w..4w+3 of block t hold d = 32t + 8w + 4 hl + 0..3.  The
+        // two lanes of a row (hl = 0, 1) trade halves with v_permlane32_swap
+        // so that each holds 8 consecutive values: lane hl stores d = 32t +
+        // 8(w + hl) + 0..7 for w = 0, 2, a row's two lanes 32 contiguous
+        // bytes -- half the store instructions, each writing 16 bytes per lane
+        // (causal GQA prefill 274 -> 268 us; both lanes of a row are active or
+        // neither).
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // registers 4w..4w+3 hold d = 32t + 8w + 4*hl + 0..3
-                const int d0 = 32 * t + 8 * w + 4 * hl;
-                const u32x2 packed = {pack_half2<BF16>(acc[t][4 * w] * inv, acc[t][4 * w + 1] * inv),
-                                      pack_half2<BF16>(acc[t][4 * w + 2] * inv,
-                                                       acc[t][4 * w + 3] * inv)};
-                *(u32x2 *)(orow + d0) = packed;
+            for (int w = 0; w < 4; w += 2) {
+                auto pk = [&](int r) __attribute__((always_inline)) {
+                    return pack_half2<BF16>(acc[t][r] * inv, acc[t][r + 1] * inv);
+                };
+                // (the swap trades lanes 32..63 of its first operand with lanes
+                // 0..31 of its second)
+                const auto lo = __builtin_amdgcn_permlane32_swap(pk(4 * w), pk(4 * w + 4), false, false);
+                const auto hi =
+                    __builtin_amdgcn_permlane32_swap(pk(4 * w + 2), pk(4 * w + 6), false, false);
+                const u32x4 packed = {(uint32_t)lo[0], (uint32_t)hi[0], (uint32_t)lo[1],
+                                      (uint32_t)hi[1]};
+                *(u32x4 *)(orow + 32 * t + 8 * (w + hl)) = packed;
             }
         if (p.lse != nullptr && hl == 0) {
             if (p.cu_q)  // packed: [Hq, total_q]
