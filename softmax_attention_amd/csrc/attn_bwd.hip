@@ -145,18 +145,25 @@ __device__ __forceinline__ void pack_scores(const f32x16 &x,
 }
 
 // store 32 rows x D of a 32x32-block accumulator set (lane = row, registers
-// 4w..4w+3 of block t = d 32t + 8w + 4hl + 0..3), scaled
+// 4w..4w+3 of block t = d 32t + 8w + 4hl + 0..3), scaled.  The two lanes of
+// a row (hl = 0, 1; both active or neither) trade halves with
+// v_permlane32_swap, which swaps lanes 32..63 of its first operand with lanes
+// 0..31 of its second, so that lane hl stores d = 32t + 8(w + hl) + 0..7 as
+// one 16-byte store for w = 0, 2.
 template <int D, bool BF16>
 __device__ __forceinline__ void store_rows(uint16_t *row_ptr, const f32x16 (&acc)[D / 32],
                                            float s, int hl) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int d0 = 32 * t + 8 * w + 4 * hl;
-            const u32x2 packed = {pack_half2<BF16>(acc[t][4 * w] * s, acc[t][4 * w + 1] * s),
-                                  pack_half2<BF16>(acc[t][4 * w + 2] * s, acc[t][4 * w + 3] * s)};
-            *(u32x2 *)(row_ptr + d0) = packed;
+        for (int w = 0; w < 4; w += 2) {
+            auto pk = [&](int r) __attribute__((always_inline)) {
+                return pack_half2<BF16>(acc[t][r] * s, acc[t][r + 1] * s);
+            };
+            const auto lo = __builtin_amdgcn_permlane32_swap(pk(4 * w), pk(4 * w + 4), false, false);
+            const auto hi = __builtin_amdgcn_permlane32_swap(pk(4 * w + 2), pk(4 * w + 6), false, false);
+            const u32x4 packed = {(uint32_t)lo[0], (uint32_t)hi[0], (uint32_t)lo[1], (uint32_t)hi[1]};
+            *(u32x4 *)(row_ptr + 32 * t + 8 * (w + hl)) = packed;
         }
 }
 
