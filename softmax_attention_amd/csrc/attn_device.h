@@ -111,17 +111,23 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Cache-policy operand of a buffer load: the non-temporal (streaming) hint,
+// for data that no other workgroup reads again.
+constexpr int kLoadNonTemporal = 2;
+
 // One buffer_load_dwordx4 ... lds: lane l copies the 16 bytes at
 // base + voffset(l) to dst + 16 l, bypassing registers; offsets at or past
-// num_bytes read as zero.  (The body exists in the device pass only: the host
+// num_bytes read as zero.  POLICY is the load's cache-policy operand (0 or
+// kLoadNonTemporal).  (The body exists in the device pass only: the host
 // pass has no buffer-resource type and would otherwise drop the kernels'
 // launch stubs.)
+template <int POLICY = 0>
 __device__ __forceinline__ void buffer_load_lds16(const void *base, int num_bytes, lds_void *dst,
                                                   int voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, num_bytes, kBufferFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voffset, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voffset, 0, 0, POLICY);
 #endif
 }
 

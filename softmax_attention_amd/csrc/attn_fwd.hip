@@ -143,6 +143,12 @@ void attn_fwd_kernel(const FwdParams p) {
     constexpr int DT = D / 32;                     // 32-wide d blocks of O^T
     constexpr int PSTEPS = BN / 16;                // MFMA k-steps over the tile's keys
     static_assert(PIECES % LOADERS == 0, "whole 1 KB pieces per loading wave");
+    // The decode schedules stream K/V that no other workgroup reads again:
+    // their loads carry the non-temporal hint (paged decode: kernel 184 ->
+    // 163 us, call 195 -> 173 us; FP8 pools 107 -> 104 us).  The prefill
+    // schedules share each tile between workgroups through L2 and keep the
+    // default policy (the hint there: causal GQA prefill 276-282 -> 291-293 us).
+    constexpr int LOAD_POLICY = SPLIT_ROLES ? kLoadNonTemporal : 0;
     static_assert(!FP8 || (SPLIT_ROLES && !PAIR), "FP8 pools are read by the split-role schedule");
 
     // K and V rings of up to four stages each (the schedules use three or
@@ -685,9 +691,9 @@ void attn_fwd_kernel(const FwdParams p) {
             const int last = kv_len - 1 - j0;  // last valid key row of the tile
 #pragma unroll
             for (int e = 0; e < PPW; ++e)
-                buffer_load_lds16(base, BN * row_bytes,
-                                  (lds_void *)(dst + (e * LOADERS + loader) * 1024),
-                                  (min(l_key[e], last) * row_bytes + l_chunk[e]) & keep);
+                buffer_load_lds16<LOAD_POLICY>(base, BN * row_bytes,
+                                               (lds_void *)(dst + (e * LOADERS + loader) * 1024),
+                                               (min(l_key[e], last) * row_bytes + l_chunk[e]) & keep);
         } else {
             // pages smaller than a tile: each of the tile's pages (at most
             // BN / 16) is looked up once -- all reads issued before any is
@@ -705,9 +711,10 @@ void attn_fwd_kernel(const FwdParams p) {
                 int32_t pe = phys[0];
 #pragma unroll
                 for (int q = 1; q < kTilePages; ++q) pe = qi == q ? phys[q] : pe;
-                buffer_load_lds16(src + head_off + cache_row(pe, jr) * hstride, RPP * row_bytes,
-                                  (lds_void *)(dst + (e * LOADERS + loader) * 1024),
-                                  (min(l_dr, kv_len - 1 - jr) * row_bytes + l_chunk[e]) & keep);
+                buffer_load_lds16<LOAD_POLICY>(
+                    src + head_off + cache_row(pe, jr) * hstride, RPP * row_bytes,
+                    (lds_void *)(dst + (e * LOADERS + loader) * 1024),
+                    (min(l_dr, kv_len - 1 - jr) * row_bytes + l_chunk[e]) & keep);
             }
         }
     };
@@ -944,8 +951,8 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int e = 0; e < PC8; ++e) {
                     const int vo = (min(piece_row(e) + f_row, last) * row8 + 16 * f_chunk) & keep;
-                    buffer_load_lds16(k8 + off, BN * row8, (lds_void *)(dk + e * 1024), vo);
-                    buffer_load_lds16(v8 + off, BN * row8, (lds_void *)(dv + e * 1024), vo);
+                    buffer_load_lds16<LOAD_POLICY>(k8 + off, BN * row8, (lds_void *)(dk + e * 1024), vo);
+                    buffer_load_lds16<LOAD_POLICY>(v8 + off, BN * row8, (lds_void *)(dv + e * 1024), vo);
                 }
             } else {
                 // pages smaller than a tile (16 keys or more): a piece's 16-row
@@ -957,8 +964,8 @@ void attn_fwd_kernel(const FwdParams p) {
                         cache_row(bt_row[jr >> p.page_shift], jr) * row8 + (int64_t)kvh * D;
                     const int in_block = piece_row(e) - piece_block(e) + f_row;
                     const int vo = (min(in_block, kv_len - 1 - jr) * row8 + 16 * f_chunk) & keep;
-                    buffer_load_lds16(k8 + off, 16 * row8, (lds_void *)(dk + e * 1024), vo);
-                    buffer_load_lds16(v8 + off, 16 * row8, (lds_void *)(dv + e * 1024), vo);
+                    buffer_load_lds16<LOAD_POLICY>(k8 + off, 16 * row8, (lds_void *)(dk + e * 1024), vo);
+                    buffer_load_lds16<LOAD_POLICY>(v8 + off, 16 * row8, (lds_void *)(dv + e * 1024), vo);
                 }
             }
         };
@@ -1129,7 +1136,14 @@ void attn_fwd_kernel(const FwdParams p) {
                     __builtin_amdgcn_permlane32_swap(pk(4 * w + 2), pk(4 * w + 6), false, false);
                 const u32x4 packed = {(uint32_t)lo[0], (uint32_t)hi[0], (uint32_t)lo[1],
                                       (uint32_t)hi[1]};
-                *(u32x4 *)(orow + 32 * t + 8 * (w + hl)) = packed;
+                // (streaming stores in the D = 64 four-wave schedule, four
+                // workgroups per CU: key-padding MHA 70.5 -> 68.5 us; the
+                // prefill schedules measured no change)
+                u32x4 *const dst = (u32x4 *)(orow + 32 * t + 8 * (w + hl));
+                if constexpr (WAVES == 4 && D == 64)
+                    __builtin_nontemporal_store(packed, dst);
+                else
+                    *dst = packed;
             }
         if (p.lse != nullptr && hl == 0) {
             if (p.cu_q)  // packed: [Hq, total_q]
