@@ -99,11 +99,14 @@ __device__ __forceinline__ void sched_read_ahead() {
 // looks up its own page); the last two again over FP8 E4M3FN pools.
 enum KvMode { kDense = 0, kPagedTile = 1, kPagedPiece = 2, kPagedTile8 = 3, kPagedPiece8 = 4 };
 
-// Waves of a workgroup: the schedule's WAVES, and over FP8 pools a second
-// converting wave beside them
+// Waves of a workgroup: the schedule's WAVES (the paired decode: two
+// computing and two loading waves); over FP8 pools one computing, one
+// loading and two converting waves, or paired two computing, one loading and
+// four converting waves
 template <int WAVES, int KV>
 constexpr int group_waves() {
-    return WAVES == kPairWaves ? 4 : (KV == kPagedTile8 || KV == kPagedPiece8) ? WAVES + 1 : WAVES;
+    return (KV == kPagedTile8 || KV == kPagedPiece8) ? (WAVES == kPairWaves ? 7 : WAVES + 1)
+                                                     : (WAVES == kPairWaves ? 4 : WAVES);
 }
 
 // CAP: logits are capped (c tanh(z / c), TileOPs "Attention Operators",
@@ -149,7 +152,7 @@ void attn_fwd_kernel(const FwdParams p) {
     // schedules share each tile between workgroups through L2 and keep the
     // default policy (the hint there: causal GQA prefill 276-282 -> 291-293 us).
     constexpr int LOAD_POLICY = SPLIT_ROLES ? kLoadNonTemporal : 0;
-    static_assert(!FP8 || (SPLIT_ROLES && !PAIR), "FP8 pools are read by the split-role schedule");
+    static_assert(!FP8 || SPLIT_ROLES, "FP8 pools are read by the split-role schedules");
 
     // K and V rings of up to four stages each (the schedules use three or
     // four); separate arrays so that the compiler can tell a load into one
@@ -909,7 +912,10 @@ void attn_fwd_kernel(const FwdParams p) {
         // waves 2, 3 convert tile n + 1 (landed during step n - 1); wave 1 issues
         // tile n + S8 into the FP8 stage tile n left, then waits for tile
         // n + 2 -- S8 - 2 tiles stay in flight.  (Tiles of a paged call
-        // follow one another: there is no padding mask.)
+        // follow one another: there is no padding mask.)  Paired (two
+        // adjacent KV heads, 2 D-byte FP8 segments per key): waves 0 and 1
+        // compute, wave 2 loads and waves 3-6 convert, a quarter each (FP8
+        // decode kernel 104.5 -> 102 us; with two converting waves 117 us).
         //
         // A piece (1 KB) holds, at lane l's 16 bytes, the 16-byte chunk f_chunk
         // (16 d-values) of key row piece_row(e) + f_row -- an order chosen for
@@ -922,11 +928,13 @@ void attn_fwd_kernel(const FwdParams p) {
         // swizzles put their chunks in the same half and apart in bank -- and
         // four chunks of each.  A piece's rows lie in one aligned 16-row block.
         constexpr int S8 = 4;                // FP8 ring stages
-        constexpr int U16 = D / 16;          // 16-byte chunks per FP8 key row
+        constexpr int U16 = DL / 16;         // 16-byte chunks per FP8 key row
         constexpr int CG = U16 / 4;          // groups of four chunks per row
-        constexpr int STAGE8 = BN * D;       // bytes of one FP8 K (or V) tile
+        constexpr int STAGE8 = BN * DL;      // bytes of one FP8 K (or V) tile
         constexpr int PC8 = STAGE8 / 1024;   // pieces per tensor and tile
-        static_assert(CG == 1 || CG == 2, "FP8 pools: D = 64 or 128");
+        constexpr int NCONV = PAIR ? 4 : 2;  // converting waves
+        static_assert(PC8 % NCONV == 0, "whole pieces per converting wave");
+        static_assert(CG == 1 || CG == 2 || CG == 4, "FP8 pools: 64, 128 or 256 values per key row");
         static_assert((S8 - 2) * 2 * PC8 <= 63, "the counted wait fits vmcnt");
         __shared__ __attribute__((aligned(1024))) uint8_t fK[S8][STAGE8];
         __shared__ __attribute__((aligned(1024))) uint8_t fV[S8][STAGE8];
@@ -938,7 +946,9 @@ void attn_fwd_kernel(const FwdParams p) {
         // first row of piece e's rows (within the tile), and of its 16-row block
         auto piece_row = [](int e) { return 16 * (e / CG) + (8 / CG) * (e % CG); };
         auto piece_block = [](int e) { return 16 * (e / CG); };
-        const bool dma = wave_u == 1, conv = wave_u >= 2;
+        // (roles: the NCOMP computing waves, then the loading wave, then
+        // the two converting waves)
+        const bool dma = wave_u == NCOMP, conv = wave_u > NCOMP;
         auto issue8 = [&](int j0, int stage) __attribute__((always_inline)) {
             if (!dma) return;
             uint8_t *dk = fK[stage], *dv = fV[stage];
@@ -978,10 +988,10 @@ void attn_fwd_kernel(const FwdParams p) {
         auto convert8 = [&](int stage, uint8_t *dk, uint8_t *dv) __attribute__((always_inline)) {
             if (!conv) return;
             const uint8_t *fk = fK[stage], *fv = fV[stage];
-            const int half = wave_u - 2;  // this converting wave's half of the pieces
+            const int cw = wave_u - NCOMP - 1;  // this converting wave's share of the pieces
 #pragma unroll
-            for (int e2 = 0; e2 < PC8 / 2; ++e2) {
-                const int e = half * (PC8 / 2) + e2;
+            for (int e2 = 0; e2 < PC8 / NCONV; ++e2) {
+                const int e = cw * (PC8 / NCONV) + e2;
                 const u32x4 kw = *(const u32x4 *)(fk + e * 1024 + 16 * lane);
                 const u32x4 vw = *(const u32x4 *)(fv + e * 1024 + 16 * lane);
 #pragma unroll
@@ -990,7 +1000,7 @@ void attn_fwd_kernel(const FwdParams p) {
                     const u32x2 k23 = fp8x4_to_half4<BF16>(h ? kw[3] : kw[1]);
                     const u32x2 v01 = fp8x4_to_half4<BF16>(h ? vw[2] : vw[0]);
                     const u32x2 v23 = fp8x4_to_half4<BF16>(h ? vw[3] : vw[1]);
-                    const int at = tile_off<D>(piece_row(e) + f_row, 2 * f_chunk + h);
+                    const int at = tile_off<DL>(piece_row(e) + f_row, 2 * f_chunk + h);
                     *(u32x4 *)(dk + at) = u32x4{k01[0], k01[1], k23[0], k23[1]};
                     *(u32x4 *)(dv + at) = u32x4{v01[0], v01[1], v23[0], v23[1]};
                 }
@@ -1284,7 +1294,7 @@ template <int D, int W, bool CAP>
 int decode_blocks(const FwdParams &p, bool bf16, bool paged) {
     const bool tile =
         p.page_shift >= __builtin_ctz(keys_per_tile(D, W, paged && p.k_scale != nullptr));
-    if constexpr (W == 3) {
+    if constexpr (W == 3 || W == kPairWaves) {
         if (paged && p.k_scale != nullptr) {
             if (tile)
                 return bf16 ? blocks_per_cu<D, true, kPagedTile8, W, CAP>()
@@ -1293,7 +1303,7 @@ int decode_blocks(const FwdParams &p, bool bf16, bool paged) {
                         : blocks_per_cu<D, false, kPagedPiece8, W, CAP>();
         }
     }
-    if (p.k_scale != nullptr) return 0;  // FP8 pools: the decode (WAVES = 3) schedule only
+    if (p.k_scale != nullptr) return 0;  // FP8 pools: the decode schedules only
     if (!paged)
         return bf16 ? blocks_per_cu<D, true, kDense, W, CAP>()
                     : blocks_per_cu<D, false, kDense, W, CAP>();
@@ -1314,12 +1324,12 @@ template <int D, int WAVES, bool CAP>
 hipError_t launch_w(const FwdParams &p, bool bf16, bool paged, int grid, hipStream_t stream) {
     const bool tile =
         p.page_shift >= __builtin_ctz(keys_per_tile(D, WAVES, paged && p.k_scale != nullptr));
-    if constexpr (WAVES == 3) {
+    if constexpr (WAVES == 3 || WAVES == kPairWaves) {
         if (paged && p.k_scale != nullptr)
             return tile ? launch_kv<D, WAVES, kPagedTile8, CAP>(p, bf16, grid, stream)
                         : launch_kv<D, WAVES, kPagedPiece8, CAP>(p, bf16, grid, stream);
     }
-    if (p.k_scale != nullptr) return hipErrorInvalidValue;  // FP8 pools: the WAVES = 3 schedule only
+    if (p.k_scale != nullptr) return hipErrorInvalidValue;  // FP8 pools: the decode schedules only
     if (!paged) return launch_kv<D, WAVES, kDense, CAP>(p, bf16, grid, stream);
     if (tile)
         return launch_kv<D, WAVES, kPagedTile, CAP>(p, bf16, grid, stream);

@@ -85,8 +85,9 @@ struct DeviceState {
     hipEvent_t last_use = nullptr;      // recorded on last_stream after that use
     bool used = false;
     int cus = 0;
-    // decode kernel occupancy: [D 128][bf16][paged][capped logits][16-bit, FP8 pools, paired]
-    int decode_per_cu[2][2][2][2][3] = {};
+    // decode kernel occupancy: [D 128][bf16][paged][capped logits][16-bit, FP8 pools, paired,
+    // paired over FP8 pools]
+    int decode_per_cu[2][2][2][2][4] = {};
 };
 
 std::mutex g_mu;
@@ -118,7 +119,8 @@ int compute_units(int dev) {
 int decode_per_cu(int dev, const miattn::FwdParams &p, int D, bool bf16, bool paged, bool cap,
                   int waves) {
     std::lock_guard<std::mutex> lock(g_mu);
-    const int variant = waves == miattn::kPairWaves ? 2 : p.k_scale != nullptr ? 1 : 0;
+    const int variant =
+        (waves == miattn::kPairWaves ? 2 : 0) + (p.k_scale != nullptr ? 1 : 0);
     int &slot = g_dev[dev].decode_per_cu[D == 128][bf16][paged][cap][variant];
     if (slot == 0) {
         const int n = miattn::attn_fwd_decode_blocks_per_cu(p, D, bf16, paged, waves, cap);
@@ -393,16 +395,16 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     int waves = D == 256 ? 4 : (p.rows > miattn::kRowsPerWave ? ((D == 64 && !paged) ? 4 : 8) : 3);
     if (p.k_scale != nullptr) waves = 3;
     const int split_keys = g_split_keys > 0 ? g_split_keys : env_int("MIATTN_SPLIT_KEYS", 0);
-    // Decode-shaped calls over 16-bit K/V with an even number of KV heads run
-    // the paired schedule (stream-K only): one workgroup reads both heads'
-    // rows of each key as one contiguous segment (512 bytes at D = 128),
-    // which streams faster than two 256-byte segments read by two workgroups.
+    // Decode-shaped calls with an even number of KV heads run the paired
+    // schedule (stream-K only): one workgroup reads both heads' rows of each
+    // key as one contiguous segment (512 bytes at D = 128, 256 over FP8
+    // pools), which streams faster than two segments read by two workgroups.
     auto streamk_fits = [&](int w) {
         const int64_t bn = miattn::keys_per_tile(D, w, p.k_scale != nullptr);
         const int64_t ct = capacity > 0 ? (capacity + bn - 1) / bn : 1;
         return (int64_t)p.B * (ct + kSkPieceMax) < INT_MAX;
     };
-    if (waves == 3 && p.k_scale == nullptr && p.Hkv % 2 == 0 && D <= 128 &&
+    if (waves == 3 && p.Hkv % 2 == 0 && D <= 128 &&
         p.rows <= miattn::kRowsPerWave && split_keys <= 0 && streamk_fits(miattn::kPairWaves))
         waves = miattn::kPairWaves;
     const int BN = miattn::keys_per_tile(D, waves, p.k_scale != nullptr);
