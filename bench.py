@@ -555,7 +555,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": call8, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": call8 / PEAK_HBM_GBS,
                          "traffic": measured_traffic("decode_fp8"),
-                         "kernel": "attn_fwd_kernel<128, true, 3, 3, false> (D, bf16, FP8 pages, 3 waves, plain logits, stream-K) + lse_merge_kernel<128, true>",
+                         "kernel": "attn_fwd_kernel<128, true, 3, 5, false> (D, bf16, FP8 pages, paired decode: two KV heads per workgroup, plain logits, stream-K) + lse_merge_kernel<128, true>",
                          "attn_kernel_avg_us": d8["attn_kernel_ms"] * 1e3,
                          "attn_kernel_gbs": kern8, "attn_kernel_frac": kern8 / PEAK_HBM_GBS,
                          "merge_kernel_avg_us": d8["merge_kernel_ms"] * 1e3}}
