@@ -83,6 +83,22 @@ def test_fp8_decode_streamk_head_dims_and_pages(D, page):
     fp8_case([1] * len(lens), lens, 16, 4, D, page, seed=304 + D + page, what=f"decode D{D} p{page}")
 
 
+@pytest.mark.parametrize("Hkv,D,page", [(3, 128, 64), (3, 64, 16), (6, 128, 16), (6, 64, 64)])
+def test_fp8_decode_paired_and_single_head(Hkv, D, page):
+    # an even number of KV heads runs the paired schedule (both heads' FP8
+    # rows of a key in one segment, four converting waves), an odd one the
+    # one-head schedule
+    lens = [1, 17, 0, 64, 65, 1000, 513, 300, 31]
+    fp8_case([1] * len(lens), lens, 4 * Hkv, Hkv, D, page, seed=330 + Hkv + D + page,
+             what=f"decode Hkv{Hkv} D{D} p{page}")
+
+
+def test_fp8_paired_decode_window_softcap_sinks():
+    lens = [900, 40, 20, 2000, 1, 0]
+    fp8_case([1] * len(lens), lens, 16, 4, 128, 64, window=(300, -1), softcap=25.0,
+             sinks=make_sinks(16, 331), seed=331, what="paired decode window softcap sinks")
+
+
 def test_fp8_decode_split_plan_d64_fp16_small_pages():
     lens = [1, 0, 64, 65, 1000, 513, 2047, 300]
     fp8_case([1] * len(lens), lens, 8, 2, 64, 16, dtype=torch.float16, split_keys=128,
