@@ -207,13 +207,17 @@ def test_full_size_decode_over_quantized_caches():
     compare(o, lse, o_ref, lse_ref, w.name + " fp8")
 
 
-@pytest.mark.parametrize("sq,D,page", [([1, 1, 1, 1], 64, 64), ([1, 1], 64, 16)])
-def test_fp8_pool_gives_the_bits_of_a_16bit_pool_of_its_values(sq, D, page):
+@pytest.mark.parametrize("sq,D,page,split", [([1, 1, 1, 1], 64, 64, 256), ([1, 1], 64, 16, 256),
+                                              ([1, 1, 1, 1], 128, 64, 0), ([1, 1, 1], 128, 16, 0)])
+def test_fp8_pool_gives_the_bits_of_a_16bit_pool_of_its_values(sq, D, page, split):
     # with scales of 1 the FP8 path differs from the 16-bit one only in how a
-    # tile reaches LDS: decode-shaped calls at D = 64 run one schedule (three
-    # waves) with one key tile (64 keys) for both pool types, so under one
-    # split plan the outputs must be bitwise equal, whatever the magnitudes
-    # (codes up to 448).  (At D = 128 the 16-bit decode takes 64-key tiles and
+    # tile reaches LDS: under a split plan, decode-shaped calls at D = 64 run
+    # one schedule (three waves) with one key tile (64 keys) for both pool
+    # types; under the stream-K plan (no forced split), decode-shaped calls
+    # with an even KV head count run the paired schedule with 32-key tiles at
+    # D = 128 for both -- the production FP8 decode shape.  Either way the
+    # outputs must be bitwise equal, whatever the magnitudes (codes up to 448).
+    # (Under a split plan at D = 128 the 16-bit decode takes 64-key tiles and
     # the FP8 one 32-key tiles, which changes the rounding order; prefill-shaped
     # 16-bit calls run the 8-wave schedule.  Those FP8 paths are compared with
     # the oracle above.)
@@ -235,9 +239,10 @@ def test_fp8_pool_gives_the_bits_of_a_16bit_pool_of_its_values(sq, D, page):
     cu = torch.tensor(np.concatenate([[0], np.cumsum(sq)]), dtype=torch.int32, device=DEV)
     one = torch.ones(1, dtype=torch.float32, device=DEV)
     args = (torch.tensor(lens, dtype=torch.int32, device=DEV), bt.to(DEV), cu, page)
-    mi.set_split_keys(256)
+    mi.set_split_keys(split)
     o8, l8 = mi.attn_fwd_paged_varlen(q.to(DEV), kc.to(DEV), vc.to(DEV), *args, k_scale=one,
                                       v_scale=one)
     o16, l16 = mi.attn_fwd_paged_varlen(q.to(DEV), k16.to(DEV), v16.to(DEV), *args)
     torch.cuda.synchronize()
+    mi.set_split_keys(0)
     assert torch.equal(o8, o16) and torch.equal(l8, l16)
