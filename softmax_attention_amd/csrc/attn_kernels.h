@@ -25,10 +25,12 @@ constexpr int kRowsPerWave = 32;  // one 32x32 MFMA column block
 //     computes, waves 1 and 2 issue all loads -- and 4 waves for D = 256 and
 //     for dense prefill at D = 64): each step computes one tile while later
 //     tiles load.
-//   paired decode (WAVES = 5 in the kernel template; four waves run): the
-//     decode schedule for two adjacent KV heads at once -- waves 0 and 1
-//     compute one head each, waves 2 and 3 load both heads' rows of every key
-//     (one contiguous 4 D-byte segment instead of two 2 D-byte ones).
+//   paired decode (WAVES = 5 in the kernel template; four waves run, seven
+//     over FP8 pools): the decode schedule for two adjacent KV heads at once
+//     -- waves 0 and 1 compute one head each, waves 2 and 3 load both heads'
+//     rows of every key (one contiguous 4 D-byte segment instead of two
+//     2 D-byte ones); over FP8 pools wave 2 loads the 2 D-byte FP8 segments
+//     and waves 3-6 convert them.
 constexpr int kPairWaves = 5;
 constexpr int rows_per_workgroup(int waves) {
     return (waves == 3 || waves == kPairWaves) ? kRowsPerWave : kRowsPerWave * waves;
@@ -44,7 +46,7 @@ constexpr int rows_per_workgroup(int waves) {
 // Over FP8 pools: tiles of 8 KB of 16-bit values (4096 / D keys, at least
 // one 32-key score block), so that the FP8 ring and the converted stages fit
 // two workgroups per CU.  D = 256 (4 waves): 32 keys (16 KB).  Paired decode:
-// 4096 / D keys (16 KB holding both heads' rows).
+// 4096 / D keys (16 KB holding both heads' rows), over FP8 pools too.
 constexpr int keys_per_tile(int D, int waves, bool fp8 = false) {
     return waves == 8 ? 8192 / D
            : waves == 4 ? 32

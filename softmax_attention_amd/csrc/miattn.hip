@@ -391,7 +391,8 @@ miattn_status run(FwdParams p, int D, bool bf16, bool paged, int64_t capacity, b
     // K/V the 4-wave streaming schedule instead), a three-wave streaming
     // workgroup (one computing, two loading) for decode-shaped calls (all
     // packed rows in one MFMA column block) and for FP8 pools (there one
-    // loading and two converting waves); D = 256: the 4-wave streaming schedule.
+    // loading and two converting waves; decode-shaped calls may pair heads,
+    // below); D = 256: the 4-wave streaming schedule.
     int waves = D == 256 ? 4 : (p.rows > miattn::kRowsPerWave ? ((D == 64 && !paged) ? 4 : 8) : 3);
     if (p.k_scale != nullptr) waves = 3;
     const int split_keys = g_split_keys > 0 ? g_split_keys : env_int("MIATTN_SPLIT_KEYS", 0);
